@@ -1,0 +1,119 @@
+"""CPU float64 oracle for batched weighted isotonic regression (ctypes binding).
+
+TEST INFRASTRUCTURE ONLY: the checker, not the product.  Only the test suite,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may import
+this module.  It shares no code with the GPU library and never imports it.
+
+The arithmetic lives in ``iso_oracle.c`` (pool adjacent violators in float64,
+page "Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Sec. 1
+and Sec. 2.1 Eq. (1); semantics from the "torchisotonic" PyPI page, section
+"Semantics").  This module only marshals numpy arrays.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "iso_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+OK = 0
+EINVAL = -1
+EWEIGHT = -3
+
+
+def build() -> str:
+    """Compile liboracle.so with gcc (plain C, no fast-math, no FMA contraction)."""
+    cmd = [
+        "gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-std=c11", "-fPIC", "-shared",
+        "-pthread", "-o", _LIB + ".tmp", _SRC, "-lm",
+    ]
+    subprocess.run(cmd, check=True)
+    os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        bp = ctypes.POINTER(ctypes.c_uint8)
+        lib.iso_oracle_fit.restype = ctypes.c_int
+        lib.iso_oracle_fit.argtypes = [
+            dp, dp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, ctypes.c_double, ctypes.c_double,
+            dp, bp, bp, bp, ctypes.c_int,
+        ]
+        lib.iso_oracle_vjp.restype = ctypes.c_int
+        lib.iso_oracle_vjp.argtypes = [dp, bp, bp, bp, dp, ctypes.c_int64, ctypes.c_int64, dp]
+        _lib = lib
+    return _lib
+
+
+def _dptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _bptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.POINTER(ctypes.c_uint8))
+
+
+def _as2d(a):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+    if a.ndim == 1:
+        a = a[None, :]
+    return a
+
+
+def fit(y, w=None, increasing=True, y_min=None, y_max=None, threads=1):
+    """Fit every row of y.  Returns (z, block_start, clipped, row_nan, status).
+
+    y, w: array-like [rows, n] or [n] (cast to float64 exactly for float32 data).
+    z has the shape of the 2-D view; block_start / clipped are uint8 [rows, n];
+    row_nan is uint8 [rows]; status is OK or EWEIGHT (rows with a finite weight
+    <= 0 are NaN).
+    """
+    lib = _load()
+    y2 = _as2d(y)
+    rows, n = y2.shape
+    w2 = None
+    if w is not None:
+        w2 = _as2d(w)
+        if w2.shape != y2.shape:
+            raise ValueError("w must have the shape of y")
+    lo = -np.inf if y_min is None else float(y_min)
+    hi = np.inf if y_max is None else float(y_max)
+    z = np.empty((rows, n), dtype=np.float64)
+    bs = np.empty((rows, n), dtype=np.uint8)
+    cl = np.empty((rows, n), dtype=np.uint8)
+    rn = np.zeros(rows, dtype=np.uint8)
+    st = lib.iso_oracle_fit(_dptr(y2), _dptr(w2), rows, n, 1 if increasing else 0, lo, hi,
+                            _dptr(z), _bptr(bs), _bptr(cl), _bptr(rn), int(threads))
+    if st == EINVAL:
+        raise ValueError("invalid arguments")
+    return z, bs, cl, rn, st
+
+
+def vjp(g, block_start, clipped=None, row_nan=None, w=None):
+    """grad_y = w_j * sum_{i in B(j)} g_i [not clipped_i] / W_B over the given partition."""
+    lib = _load()
+    g2 = _as2d(g)
+    rows, n = g2.shape
+    bs = np.ascontiguousarray(np.asarray(block_start, dtype=np.uint8).reshape(rows, n))
+    cl = None if clipped is None else np.ascontiguousarray(np.asarray(clipped, dtype=np.uint8).reshape(rows, n))
+    rn = None if row_nan is None else np.ascontiguousarray(np.asarray(row_nan, dtype=np.uint8).reshape(rows))
+    w2 = None if w is None else _as2d(w)
+    out = np.empty((rows, n), dtype=np.float64)
+    st = lib.iso_oracle_vjp(_dptr(g2), _bptr(bs), _bptr(cl), _bptr(rn), _dptr(w2), rows, n, _dptr(out))
+    if st != OK:
+        raise ValueError("invalid arguments")
+    return out
