@@ -1,0 +1,147 @@
+/*
+ * iso.h - C ABI of the batched weighted isotonic-regression library (libiso.so)
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  For every row r of a rows x n matrix y with positive
+ * weights w, the fit z_r is the non-decreasing (or non-increasing) sequence
+ * closest to y_r in weighted least squares, Eq. (1) of "Merge Hulls Without
+ * Copying Vertices: GPU Isotonic Regression", Sec. 2.1.  It is computed as the
+ * slope sequence of the lower convex hull of the cumulative sum diagram
+ * P_k = (W_k, S_k), W_k = sum_{i<=k} w_i, S_k = sum_{i<=k} w_i y_i (same page,
+ * Sec. 2.1 Eq. (2), Sec. 3 and 4): element i takes the slope of the hull edge
+ * over [W_{i-1}, W_i].  The semantics are those of the "torchisotonic" PyPI
+ * page, section "Semantics": strictly positive weights, optional clipping of
+ * the result to [y_min, y_max] after the fit, and a row holding a NaN comes
+ * back as NaN.
+ *
+ * Memory and streams.  Every pointer argument named *_dev is device memory
+ * owned by the caller.  The library allocates nothing and never synchronises
+ * inside iso_fit / iso_vjp: their kernels are queued on `stream` (a
+ * hipStream_t passed as void*; NULL = the legacy default stream) and read the
+ * inputs / write the outputs in stream order.  Matrices are row-major and
+ * contiguous: element (r, i) is at index r * n + i.  Supported element types
+ * are float32 and float64; all accumulation is in float64.
+ *
+ * Errors.  Functions return ISO_OK (0) or a negative code.  Argument errors
+ * (ISO_EINVAL) are detected on the host before anything is queued.  Data
+ * errors are found on the device: a finite weight <= 0 makes the row come back
+ * NaN and records ISO_EWEIGHT, which iso_status reports after the call has
+ * completed.  A NaN or infinity in y or w is not an error: the row comes back
+ * all NaN (an infinity is outside the contract and is treated like a NaN).
+ */
+#ifndef ISO_H
+#define ISO_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* element types */
+#define ISO_F32 0
+#define ISO_F64 1
+
+/* return codes */
+#define ISO_OK 0
+#define ISO_EINVAL (-1)  /* bad argument, detected on the host; nothing queued   */
+#define ISO_EHIP (-2)    /* a HIP launch or runtime call failed                   */
+#define ISO_EWEIGHT (-3) /* a finite weight <= 0 in some row (that row is NaN)    */
+
+/*
+ * Partition handle for the backward pass: which elements start a pooled block
+ * of the fit, which elements were clipped, and which rows came back NaN.  The
+ * struct lives in host memory and only holds pointers into caller-owned
+ * device memory (`blocks_mem` of iso_fit) plus sizes; iso_fit fills it in
+ * without synchronising.  `w_dev` is borrowed from the iso_fit call and must
+ * stay valid until the last iso_vjp that uses the handle.
+ *
+ *   start_bits_dev[r * words + q] bit b = 1 iff element 64q + b of row r starts
+ *       a block (its left point P_{i} is a vertex of the row's hull; element 0
+ *       always starts one);
+ *   clip_bits_dev[r * words + q] bit b = 1 iff the unclipped fit of that
+ *       element lies strictly outside [y_min, y_max];
+ *   row_nan_dev[r] = 1 iff row r came back NaN;
+ *   words = ceil(n / 64).
+ */
+typedef struct iso_blocks {
+    uint64_t* start_bits_dev;
+    uint64_t* clip_bits_dev;
+    uint32_t* row_nan_dev;
+    const void* w_dev;
+    int64_t rows;
+    int64_t n;
+    int64_t words;
+    int dtype;
+    int valid;
+} iso_blocks;
+
+/*
+ * Bytes of device workspace iso_fit needs for a rows x n problem of the given
+ * dtype (at least 256; 256-byte alignment is required).  The workspace holds
+ * the status word read by iso_status and, for rows longer than one chunk, the
+ * chunk hulls, segment descriptors and per-chunk records of the merge tree
+ * (first page, Sec. 3.3-3.4).  Returns 0 for invalid sizes.
+ */
+size_t iso_workspace_bytes(int64_t rows, int64_t n, int dtype);
+
+/* Bytes of device memory backing an iso_blocks handle for rows x n. */
+size_t iso_blocks_bytes(int64_t rows, int64_t n);
+
+/*
+ * Fit every row (first page, Sec. 2-4; PyPI page, "Semantics").
+ *
+ *   y_dev        [rows, n] of dtype, read only.
+ *   w_dev        [rows, n] of dtype, read only, or NULL for unit weights.
+ *                Weights must be strictly positive.
+ *   increasing   1 for a non-decreasing fit, 0 for non-increasing.
+ *   y_min, y_max clip bounds applied after the fit; -INFINITY / +INFINITY (or
+ *                NaN) mean "no bound".  y_min > y_max is ISO_EINVAL.
+ *   dtype        ISO_F32 or ISO_F64, the type of y, w and fit.
+ *   fit_dev      [rows, n] of dtype, written.  May not alias y or w.
+ *   blocks_out   host struct filled with the partition handle, or NULL.
+ *   blocks_mem_dev  iso_blocks_bytes(rows, n) bytes of device memory backing
+ *                the handle, or NULL (then blocks_out must be NULL too, and no
+ *                block bits are written).
+ *   workspace_dev   iso_workspace_bytes(rows, n, dtype) bytes, 256-aligned.
+ *                One workspace may serve only one call in flight at a time.
+ *   stream       hipStream_t as void*.
+ *
+ * rows == 0 or n == 0 queues nothing and returns ISO_OK.
+ */
+int iso_fit(const void* y_dev, const void* w_dev, int64_t rows, int64_t n, int increasing,
+            double y_min, double y_max, int dtype, void* fit_dev, iso_blocks* blocks_out,
+            void* blocks_mem_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * Vector-Jacobian product of the fit with respect to y (first page,
+ * Appendix C: the product averages over the solver's blocks; weighted form
+ * derived from Eq. (1)): for j in block B,
+ *     grad_y[j] = w_j * sum_{i in B, clip inactive at i} grad[i] / sum_{i in B} w_i,
+ * which is the block mean of the unclipped gradient when w = 1.  Rows that
+ * came back NaN give NaN.
+ *
+ *   grad_dev      [rows, n] of blocks->dtype, read only.
+ *   blocks        handle filled by iso_fit (host struct).
+ *   grad_y_dev    [rows, n] of blocks->dtype, written.
+ *   workspace_dev iso_workspace_bytes(rows, n, dtype) bytes (may be the fit's).
+ */
+int iso_vjp(const void* grad_dev, const iso_blocks* blocks, void* grad_y_dev, void* workspace_dev,
+            size_t workspace_bytes, void* stream);
+
+/*
+ * Synchronises `stream` and returns the data error of the most recent iso_fit
+ * that used this workspace: ISO_OK or ISO_EWEIGHT (ISO_EHIP if the read fails,
+ * ISO_EINVAL for a NULL workspace).
+ */
+int iso_status(const void* workspace_dev, void* stream);
+
+/* Static, human-readable text for a return code. */
+const char* iso_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ISO_H */

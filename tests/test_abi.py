@@ -1,0 +1,135 @@
+"""The C ABI library builds, loads, exports every declared symbol, and rejects
+bad arguments on the host before anything is queued (no GPU needed).
+
+Arguments are those of include/iso.h; every call below fails validation, so
+no HIP call is made and no device memory is touched (the pointers are never
+dereferenced on this path).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "iso.h")
+LIB = os.path.join(ROOT, "weighted_isotonic_regression_row_amd", "libiso.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(iso_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libiso.so not built (run __graft_entry__.build())")
+    import weighted_isotonic_regression_row_amd as iso
+    return iso.load_library()
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    assert fns == sorted(["iso_blocks_bytes", "iso_fit", "iso_status", "iso_strerror", "iso_vjp",
+                          "iso_workspace_bytes"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (iso_\w+)$", out, flags=re.M))
+    for fn in declared_functions():
+        assert fn in exported, fn
+        assert hasattr(lib, fn)
+
+
+def test_binding_lists_the_same_symbols():
+    import weighted_isotonic_regression_row_amd as iso
+    assert sorted(iso.SYMBOLS) == declared_functions()
+
+
+def test_sizes(lib):
+    assert lib.iso_workspace_bytes(-1, 5, 0) == 0
+    assert lib.iso_workspace_bytes(5, 5, 7) == 0
+    assert lib.iso_workspace_bytes(1000, 5000, 0) >= 256
+    small = lib.iso_workspace_bytes(1000, 5000, 0)
+    big = lib.iso_workspace_bytes(32, 1 << 22, 1)
+    assert big > 32 * (1 << 22) * 16  # chunk hulls of long rows live in the workspace
+    assert small < 4096
+    assert lib.iso_blocks_bytes(4, 130) >= 2 * 4 * 3 * 8 + 4 * 4
+    assert lib.iso_blocks_bytes(-1, 3) == 0
+
+
+def test_strerror(lib):
+    assert lib.iso_strerror(0) == b"success"
+    assert b"positive" in lib.iso_strerror(-3)
+    assert lib.iso_strerror(-99) == b"unknown error"
+
+
+def _fit(lib, y=256, w=None, rows=2, n=3, inc=1, lo=-math.inf, hi=math.inf, dt=0, fit=512, bo=None, bm=None,
+         ws=4096, wsb=1 << 20, stream=None):
+    import weighted_isotonic_regression_row_amd as iso
+    return lib.iso_fit(y, w, rows, n, inc, lo, hi, dt, fit, bo, bm, ws, wsb, stream)
+
+
+def test_fit_rejects_bad_arguments_on_host(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    E = iso.ISO_EINVAL
+    assert _fit(lib, rows=-1) == E
+    assert _fit(lib, n=-1) == E
+    assert _fit(lib, dt=2) == E
+    assert _fit(lib, inc=2) == E
+    assert _fit(lib, lo=1.0, hi=0.0) == E
+    assert _fit(lib, y=None) == E
+    assert _fit(lib, fit=None) == E
+    assert _fit(lib, ws=None) == E
+    assert _fit(lib, ws=4096 + 8) == E           # misaligned workspace
+    assert _fit(lib, wsb=8) == E                 # workspace too small
+    big = lib.iso_workspace_bytes(2, 20000, 0)
+    assert _fit(lib, n=20000, wsb=big - 1) == E
+    assert _fit(lib, fit=256) == E               # output aliases y
+    bc = iso.IsoBlocksC()
+    assert _fit(lib, bo=ctypes.byref(bc)) == E   # handle without memory
+    assert _fit(lib, bm=8192) == E               # memory without handle
+
+
+def test_fit_empty_is_a_noop(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    bc = iso.IsoBlocksC()
+    assert _fit(lib, rows=0, y=None, fit=None, ws=None, bo=ctypes.byref(bc), bm=8192) == iso.ISO_OK
+    assert bc.valid == 1 and bc.rows == 0
+    assert _fit(lib, n=0, y=None, fit=None, ws=None) == iso.ISO_OK
+    # NaN bounds mean "no bound"
+    assert _fit(lib, rows=0, lo=math.nan, hi=math.nan) == iso.ISO_OK
+
+
+def test_vjp_rejects_bad_arguments_on_host(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    bc = iso.IsoBlocksC()
+    assert lib.iso_vjp(256, ctypes.byref(bc), 512, 4096, 1 << 20, None) == iso.ISO_EINVAL  # invalid handle
+    assert lib.iso_vjp(256, None, 512, 4096, 1 << 20, None) == iso.ISO_EINVAL
+    bc.valid = 1
+    bc.rows, bc.n, bc.words, bc.dtype = 2, 3, 1, 0
+    bc.start_bits_dev, bc.clip_bits_dev, bc.row_nan_dev = 8192, 8192 + 256, 8192 + 512
+    assert lib.iso_vjp(None, ctypes.byref(bc), 512, 4096, 1 << 20, None) == iso.ISO_EINVAL
+    assert lib.iso_vjp(256, ctypes.byref(bc), 512, 4096, 1, None) == iso.ISO_EINVAL
+    bc.dtype = 5
+    assert lib.iso_vjp(256, ctypes.byref(bc), 512, 4096, 1 << 20, None) == iso.ISO_EINVAL
+
+
+def test_status_without_calls(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    assert lib.iso_status(None, None) == iso.ISO_EINVAL
+    assert lib.iso_status(123456, None) == iso.ISO_OK  # no fit used this workspace
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    import weighted_isotonic_regression_row_amd as iso
+    with pytest.raises(ValueError):
+        iso.iso_fit(torch.zeros(3, 4))

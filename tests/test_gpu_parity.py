@@ -1,0 +1,205 @@
+"""GPU parity: the HIP path against the CPU float64 oracle on the same seeded
+inputs, element by element, at the tolerances of tests/gpu_helpers.py.
+
+Covers the five workloads at full size (the 32 x 2^22 one compared on sampled
+rows, all rows checked for their invariants), ragged sizes around the wave,
+group, chunk and single-workgroup limits, the data families, block partitions,
+the backward pass, NaN rows and weight errors, and run-to-run determinism.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_helpers import (check_fit, gpu_blocks, gpu_fit, oracle_fit, scale_of, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _print(*a):
+    print(*a, flush=True)
+
+
+@pytest.mark.parametrize("k", [1, 2, 3])
+def test_config_full_size(k):
+    wl = workloads.CONFIGS[k]()
+    _print(f"config {k}: {wl.name} {wl.y.shape}")
+    fit, b, *_ = gpu_fit(wl)
+    z, bs, cl, rn, st = oracle_fit(wl)
+    check_fit(fit.cpu().numpy(), z, wl.y, wl.y.dtype, wl.increasing, wl.name)
+
+
+def test_config4_calibration_full():
+    wl = workloads.cfg4_calibration()
+    _print(f"config 4: {wl.name} {wl.y.shape}")
+    fit, b, *_ = gpu_fit(wl)
+    z, bs, cl, rn, st = oracle_fit(wl)
+    check_fit(fit.cpu().numpy(), z, wl.y, wl.y.dtype, wl.increasing, wl.name)
+    gs, gc, grn = gpu_blocks(b)
+    assert grn[0] == 0
+    np.testing.assert_array_equal(gc, cl)  # clip flags follow the (equal) fit
+
+
+def test_config5_dense_full_sampled_rows():
+    wl = workloads.cfg5_dense()
+    _print(f"config 5: {wl.name} {wl.y.shape}")
+    fit, b, *_ = gpu_fit(wl)
+    f = fit.cpu().numpy()
+    rows = [0, 13, 31]
+    z, *_ = oracle_fit(wl, rows=rows)
+    check_fit(f[rows], z, wl.y[rows], wl.y.dtype, True, wl.name)
+    # every row: monotone up to rounding and the weighted sum preserved
+    s = scale_of(wl.y)
+    assert np.all(np.diff(f, axis=1) >= -1e-12 * s)
+    lhs = np.einsum("ij,ij->i", wl.w, f)
+    rhs = np.einsum("ij,ij->i", wl.w, wl.y)
+    assert np.all(np.abs(lhs - rhs) <= 1e-9 * np.abs(wl.w * wl.y).sum(axis=1))
+
+
+SIZES = [1, 2, 3, 63, 64, 65, 127, 129, 1000, 4095, 4096, 4097, 8191, 8192, 8193, 12289, 20001, 65537]
+
+
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_ragged_sizes(n, dtype):
+    for kind, weights, inc, clip in [("noise", "uniform", True, None), ("trend_noise", "unit", False, (-0.2, 0.9))]:
+        wl = workloads.family(kind, 3, n, seed=n % 97, dtype=dtype, weights=weights, increasing=inc)
+        if clip:
+            wl.y_min, wl.y_max = clip
+        fit, *_ = gpu_fit(wl)
+        z, *_ = oracle_fit(wl)
+        check_fit(fit.cpu().numpy(), z, wl.y, dtype, inc, f"{wl.name} n={n}")
+
+
+@pytest.mark.parametrize("kind", workloads.FAMILIES)
+@pytest.mark.parametrize("n", [5000, 50000])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_families(kind, n, dtype):
+    if kind == "consecutive" and n > 5000:
+        n = 20000
+    for weights in ("unit", "uniform", "extreme"):
+        wl = workloads.family(kind, 2, n, seed=3, dtype=dtype, weights=weights)
+        fit, *_ = gpu_fit(wl)
+        z, *_ = oracle_fit(wl)
+        check_fit(fit.cpu().numpy(), z, wl.y, dtype, True, f"{wl.name}")
+
+
+@pytest.mark.parametrize("n", [700, 5000, 30000])
+def test_block_starts_match_oracle_on_tie_free_data(n):
+    wl = workloads.family("trend_noise", 4, n, seed=11, dtype=np.float64, weights="uniform")
+    fit, b, *_ = gpu_fit(wl)
+    gs, gc, grn = gpu_blocks(b)
+    z, bs, cl, rn, _ = oracle_fit(wl)
+    for r in range(wl.rows):
+        starts = np.nonzero(bs[r])[0]
+        means = z[r][starts]
+        gaps = np.diff(means)
+        if gaps.size and gaps.min() < 1e-9 * scale_of(wl.y):
+            continue  # near-tie: the partition is not unique to this precision
+        np.testing.assert_array_equal(gs[r], bs[r])
+    assert not grn.any()
+
+
+def test_partition_is_valid_on_tie_data():
+    # integer data with many exact ties: the GPU's own blocks must be blocks of
+    # its fit (constant inside, the block's weighted mean)
+    wl = workloads.family("ties", 3, 9000, seed=5, dtype=np.float64, weights="unit")
+    fit, b, *_ = gpu_fit(wl)
+    f = fit.cpu().numpy()
+    gs, gc, grn = gpu_blocks(b)
+    for r in range(wl.rows):
+        st = np.nonzero(gs[r])[0].tolist() + [wl.n]
+        assert st[0] == 0
+        for a, e in zip(st[:-1], st[1:]):
+            m = wl.y[r, a:e].mean()
+            assert np.all(np.abs(f[r, a:e] - m) <= 1e-12 * max(1.0, abs(m)))
+
+
+@pytest.mark.parametrize("n", [512, 5000, 20000, 70001])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_vjp_matches_oracle(n, dtype):
+    import weighted_isotonic_regression_row_amd as iso
+    wl = workloads.family("trend_noise", 3, n, seed=n % 89, dtype=dtype, weights="uniform", increasing=(n % 2 == 0))
+    wl.y_min, wl.y_max = 0.1, 0.8
+    r = workloads.rng(123)
+    g = r.standard_normal(wl.y.shape).astype(dtype)
+    fit, b, y, w = gpu_fit(wl)
+    gy = iso.iso_vjp(to_dev(g), b).cpu().numpy().astype(np.float64)
+    gs, gc, grn = gpu_blocks(b)
+    # the oracle's VJP on the GPU's own partition (the first page's rule for
+    # ties; on this data the partitions also agree, checked above)
+    ref = oracle.vjp(g.astype(np.float64), gs, gc, grn, None if wl.w is None else wl.w.astype(np.float64))
+    tol = (1e-12 if dtype == np.float64 else 2e-6) * max(1.0, np.abs(ref).max())
+    assert np.max(np.abs(gy - ref)) <= tol
+
+
+def test_config3_soft_rank_forward_backward():
+    import weighted_isotonic_regression_row_amd as iso
+    wl = workloads.cfg3_soft_rank()
+    fit, b, y, w = gpu_fit(wl)
+    z, bs, cl, rn, _ = oracle_fit(wl)
+    check_fit(fit.cpu().numpy(), z, wl.y, wl.y.dtype, True, wl.name)
+    gy = iso.iso_vjp(to_dev(wl.g), b).cpu().numpy().astype(np.float64)
+    ref = oracle.vjp(wl.g.astype(np.float64), bs, cl, rn)
+    # every row is one block: the VJP is the row mean of g
+    assert bs[:, 1:].sum() == 0
+    np.testing.assert_allclose(gy, ref, rtol=0, atol=2e-6)
+    gs, *_ = gpu_blocks(b)
+    np.testing.assert_array_equal(gs, bs)
+
+
+@pytest.mark.parametrize("n", [300, 20000])
+def test_nan_rows_and_weight_errors(n):
+    import weighted_isotonic_regression_row_amd as iso
+    r = workloads.rng(7)
+    y = r.standard_normal((5, n))
+    w = r.random((5, n)) + 0.1
+    y[1, n // 3] = np.nan
+    w[2, n // 2] = np.nan
+    y[3, -1] = np.inf
+    w[4, 0] = -1.0
+    wl = workloads.Workload("nan_rows", y, w, True)
+    fit, b, yd, wd = gpu_fit(wl, check=False)
+    f = fit.cpu().numpy()
+    z, *_ = oracle_fit(wl)
+    check_fit(f, z, y, np.float64, True, "nan rows")
+    assert np.isnan(f[1:]).all() and not np.isnan(f[0]).any()
+    gs, gc, grn = gpu_blocks(b)
+    assert list(grn) == [0, 1, 1, 1, 1]
+    with pytest.raises(ValueError):
+        iso.iso_fit(yd, wd, True)
+    # weight error only: still reported when no row has a NaN
+    wl2 = workloads.Workload("w0", y[[0, 4]].copy(), w[[0, 4]].copy(), True)
+    with pytest.raises(ValueError):
+        iso.iso_fit(to_dev(wl2.y), to_dev(wl2.w))
+    # NaN rows alone are not an error
+    iso.iso_fit(to_dev(y[[0, 1]]), to_dev(w[[0, 1]]), check=True)
+    g = np.ones_like(y)
+    gy = iso.iso_vjp(to_dev(g), b).cpu().numpy()
+    assert np.isnan(gy[1:]).all() and np.isfinite(gy[0]).all()
+
+
+@pytest.mark.parametrize("shape", [(200, 5000), (2, 300000)])
+def test_deterministic(shape):
+    import torch
+    import weighted_isotonic_regression_row_amd as iso
+    wl = workloads.family("trend_noise", shape[0], shape[1], seed=2, dtype=np.float32, weights="uniform")
+    y, w = to_dev(wl.y), to_dev(wl.w)
+    f0, _ = iso.iso_fit(y, w, blocks=False, check=False)
+    f0 = f0.clone()
+    for _ in range(5):
+        f1, _ = iso.iso_fit(y, w, blocks=False, check=False)
+        assert torch.equal(f0, f1)
+
+
+def test_empty_inputs():
+    import torch
+    import weighted_isotonic_regression_row_amd as iso
+    for shape in [(0, 10), (4, 0)]:
+        y = torch.empty(shape, dtype=torch.float64, device="cuda:0")
+        f, b = iso.iso_fit(y)
+        assert f.shape == shape
+        g = iso.iso_vjp(torch.empty(shape, dtype=torch.float64, device="cuda:0"), b)
+        assert g.shape == shape

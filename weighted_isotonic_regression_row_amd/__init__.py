@@ -1,0 +1,226 @@
+"""Batched weighted isotonic regression on AMD Instinct MI355X (gfx950).
+
+Thin ctypes binding over libiso.so, whose C ABI is declared in include/iso.h.
+The binding only marshals arguments: torch supplies device memory and the
+current HIP stream; every step of the fit and of its backward pass runs in
+the library's HIP kernels.  There is no CPU fallback: without the built
+library (or without a GPU) the calls raise.
+
+    fit, blocks = iso_fit(y, w, increasing=True, y_min=None, y_max=None)
+    grad_y = iso_vjp(grad, blocks)
+
+The fit of each row is the weighted least-squares monotone sequence (page
+"Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Eq. (1)),
+with the semantics of the "torchisotonic" PyPI page ("Semantics").
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch  # loaded first: libiso.so then binds to torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libiso.so")
+
+ISO_F32 = 0
+ISO_F64 = 1
+ISO_OK = 0
+ISO_EINVAL = -1
+ISO_EHIP = -2
+ISO_EWEIGHT = -3
+
+SYMBOLS = ("iso_workspace_bytes", "iso_blocks_bytes", "iso_fit", "iso_vjp", "iso_status", "iso_strerror")
+
+
+class IsoBlocksC(ctypes.Structure):
+    """Mirror of struct iso_blocks (include/iso.h)."""
+
+    _fields_ = [
+        ("start_bits_dev", ctypes.c_void_p),
+        ("clip_bits_dev", ctypes.c_void_p),
+        ("row_nan_dev", ctypes.c_void_p),
+        ("w_dev", ctypes.c_void_p),
+        ("rows", ctypes.c_int64),
+        ("n", ctypes.c_int64),
+        ("words", ctypes.c_int64),
+        ("dtype", ctypes.c_int),
+        ("valid", ctypes.c_int),
+    ]
+
+
+class IsoError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str | None = None):
+    """Load libiso.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise ImportError(f"{p} is missing: build it with weighted_isotonic_regression_row_amd.build.build()")
+    lib = ctypes.CDLL(p)
+    vp, i64, c_int, c_size, c_double = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+    lib.iso_workspace_bytes.restype = c_size
+    lib.iso_workspace_bytes.argtypes = [i64, i64, c_int]
+    lib.iso_blocks_bytes.restype = c_size
+    lib.iso_blocks_bytes.argtypes = [i64, i64]
+    lib.iso_fit.restype = c_int
+    lib.iso_fit.argtypes = [vp, vp, i64, i64, c_int, c_double, c_double, c_int, vp,
+                            ctypes.POINTER(IsoBlocksC), vp, vp, c_size, vp]
+    lib.iso_vjp.restype = c_int
+    lib.iso_vjp.argtypes = [vp, ctypes.POINTER(IsoBlocksC), vp, vp, c_size, vp]
+    lib.iso_status.restype = c_int
+    lib.iso_status.argtypes = [vp, vp]
+    lib.iso_strerror.restype = ctypes.c_char_p
+    lib.iso_strerror.argtypes = [c_int]
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def strerror(code: int) -> str:
+    try:
+        return load_library().iso_strerror(int(code)).decode()
+    except ImportError:
+        return f"error {code}"
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return ISO_F32
+    if t.dtype == torch.float64:
+        return ISO_F64
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or float64)")
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def iso_workspace_bytes(rows: int, n: int, dtype: torch.dtype) -> int:
+    code = ISO_F32 if dtype == torch.float32 else ISO_F64
+    return int(load_library().iso_workspace_bytes(rows, n, code))
+
+
+def iso_blocks_bytes(rows: int, n: int) -> int:
+    return int(load_library().iso_blocks_bytes(rows, n))
+
+
+def workspace(rows: int, n: int, dtype: torch.dtype, device) -> torch.Tensor:
+    """Allocate a workspace tensor (uint8, 256-byte aligned by torch's allocator)."""
+    return torch.empty(max(iso_workspace_bytes(rows, n, dtype), 256), dtype=torch.uint8, device=device)
+
+
+class Blocks:
+    """Partition handle of a fit (struct iso_blocks plus the memory behind it)."""
+
+    def __init__(self, c: IsoBlocksC, mem: torch.Tensor, w: torch.Tensor | None, shape):
+        self.c = c
+        self.mem = mem
+        self.w = w  # keeps the borrowed weights alive
+        self.shape = shape
+
+    def bits(self):
+        """(start_bits, clip_bits, row_nan) as device tensors (views of the memory)."""
+        rows, words = self.c.rows, self.c.words
+        m = self.mem
+        nb = rows * words * 8
+        stride = (nb + 255) // 256 * 256
+        sb = m[:nb].view(torch.int64).view(rows, words)
+        cb = m[stride:stride + nb].view(torch.int64).view(rows, words)
+        rn = m[2 * stride:2 * stride + 4 * rows].view(torch.int32)
+        return sb, cb, rn
+
+
+def _as_rows(t: torch.Tensor) -> torch.Tensor:
+    if t.dim() == 1:
+        return t.unsqueeze(0)
+    if t.dim() != 2:
+        raise ValueError("expected a [rows, n] or [n] tensor")
+    return t
+
+
+def iso_fit(y: torch.Tensor, w: torch.Tensor | None = None, increasing: bool = True,
+            y_min: float | None = None, y_max: float | None = None, *, out: torch.Tensor | None = None,
+            blocks: bool = True, ws: torch.Tensor | None = None, check: bool = True):
+    """Fit every row of y on the GPU.  Returns (fit, blocks or None).
+
+    y, w: [rows, n] (or [n]) contiguous float32/float64 device tensors of one
+    dtype; w None means unit weights.  check=True synchronises once to raise
+    ValueError if a weight was not strictly positive (those rows are NaN).
+    """
+    if not y.is_cuda:
+        raise ValueError("iso_fit runs on the GPU: y must be a device tensor")
+    lib = load_library()
+    shape = y.shape
+    y2 = _as_rows(y)
+    if not y2.is_contiguous():
+        raise ValueError("y must be contiguous")
+    rows, n = y2.shape
+    dt = _dtype_code(y2)
+    w2 = None
+    if w is not None:
+        w2 = _as_rows(w)
+        if w2.shape != y2.shape or w2.dtype != y2.dtype or w2.device != y2.device or not w2.is_contiguous():
+            raise ValueError("w must be a contiguous tensor of y's shape, dtype and device")
+    if out is None:
+        out = torch.empty_like(y2)
+    if ws is None:
+        ws = workspace(rows, n, y2.dtype, y2.device)
+    bc = IsoBlocksC()
+    mem = None
+    if blocks:
+        mem = torch.empty(max(iso_blocks_bytes(rows, n), 256), dtype=torch.uint8, device=y2.device)
+    lo = -math.inf if y_min is None else float(y_min)
+    hi = math.inf if y_max is None else float(y_max)
+    code = lib.iso_fit(y2.data_ptr(), None if w2 is None else w2.data_ptr(), rows, n, 1 if increasing else 0,
+                       lo, hi, dt, out.data_ptr(), ctypes.byref(bc) if blocks else None,
+                       None if mem is None else mem.data_ptr(), ws.data_ptr(), ws.numel(),
+                       _stream_ptr(y2.device))
+    if code != ISO_OK:
+        raise IsoError(code, "iso_fit")
+    if check:
+        st = lib.iso_status(ws.data_ptr(), _stream_ptr(y2.device))
+        if st == ISO_EWEIGHT:
+            raise ValueError("weights must be strictly positive")
+        if st != ISO_OK:
+            raise IsoError(st, "iso_status")
+    return out.view(shape), (Blocks(bc, mem, w2, shape) if blocks else None)
+
+
+def iso_vjp(grad: torch.Tensor, blocks: Blocks, *, out: torch.Tensor | None = None,
+            ws: torch.Tensor | None = None) -> torch.Tensor:
+    """grad_y = w_j * sum_{i in B(j), clip inactive} grad_i / sum_{i in B(j)} w_i."""
+    lib = load_library()
+    g2 = _as_rows(grad)
+    rows, n = blocks.c.rows, blocks.c.n
+    if tuple(g2.shape) != (rows, n) or not g2.is_contiguous():
+        raise ValueError("grad must be a contiguous tensor of the fit's shape")
+    if _dtype_code(g2) != blocks.c.dtype:
+        raise ValueError("grad must have the fit's dtype")
+    if out is None:
+        out = torch.empty_like(g2)
+    if ws is None:
+        ws = workspace(rows, n, g2.dtype, g2.device)
+    code = lib.iso_vjp(g2.data_ptr(), ctypes.byref(blocks.c), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                       _stream_ptr(g2.device))
+    if code != ISO_OK:
+        raise IsoError(code, "iso_vjp")
+    return out.view(blocks.shape)
+
+
+def iso_status(ws: torch.Tensor) -> int:
+    return int(load_library().iso_status(ws.data_ptr(), _stream_ptr(ws.device)))
+
+
+__all__ = ["iso_fit", "iso_vjp", "iso_status", "iso_workspace_bytes", "iso_blocks_bytes", "workspace",
+           "Blocks", "IsoError", "load_library", "SYMBOLS"]

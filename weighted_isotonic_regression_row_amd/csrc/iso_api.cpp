@@ -1,0 +1,174 @@
+// C ABI of libiso.so: argument checks, workspace layout, launches, status.
+// The operations are specified in include/iso.h.
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <atomic>
+#include <mutex>
+#include <unordered_map>
+
+#include "../../include/iso.h"
+#include "iso_internal.hpp"
+
+namespace {
+
+// Every iso_fit call gets a fresh epoch; a data error is recorded on the
+// device as max(status, epoch << 8 | code), so the status word never needs
+// clearing and iso_status only reports errors of the latest call that used
+// the workspace.
+std::atomic<unsigned long long> g_epoch{0};
+std::mutex g_mu;
+std::unordered_map<const void*, unsigned long long> g_last_epoch;
+
+bool valid_dtype(int d) { return d == ISO_F32 || d == ISO_F64; }
+
+}  // namespace
+
+extern "C" {
+
+size_t iso_workspace_bytes(int64_t rows, int64_t n, int dtype) {
+    if (rows < 0 || n < 0 || !valid_dtype(dtype)) return 0;
+    return iso::make_layout(rows, n).total;
+}
+
+size_t iso_blocks_bytes(int64_t rows, int64_t n) {
+    if (rows < 0 || n < 0) return 0;
+    const size_t words = (size_t)((n + 63) / 64);
+    const size_t bits = iso::align256(8 * words * (size_t)rows);
+    return 2 * bits + iso::align256(4 * (size_t)rows) + 256;
+}
+
+int iso_fit(const void* y, const void* w, int64_t rows, int64_t n, int increasing, double y_min, double y_max,
+            int dtype, void* fit, iso_blocks* blocks_out, void* blocks_mem, void* workspace,
+            size_t workspace_bytes, void* stream) {
+    if (rows < 0 || n < 0 || !valid_dtype(dtype)) return ISO_EINVAL;
+    if (increasing != 0 && increasing != 1) return ISO_EINVAL;
+    if ((blocks_out == nullptr) != (blocks_mem == nullptr)) return ISO_EINVAL;
+    if (isnan(y_min)) y_min = -INFINITY;
+    if (isnan(y_max)) y_max = INFINITY;
+    if (y_min > y_max) return ISO_EINVAL;
+    if (n > (int64_t)INT32_MAX) return ISO_EINVAL;
+    const int64_t words = (n + 63) / 64;
+    if (blocks_out) {
+        memset(blocks_out, 0, sizeof(*blocks_out));
+        char* bm = (char*)blocks_mem;
+        const size_t bits = iso::align256(8 * (size_t)words * (size_t)rows);
+        blocks_out->start_bits_dev = (uint64_t*)bm;
+        blocks_out->clip_bits_dev = (uint64_t*)(bm + bits);
+        blocks_out->row_nan_dev = (uint32_t*)(bm + 2 * bits);
+        blocks_out->w_dev = w;
+        blocks_out->rows = rows;
+        blocks_out->n = n;
+        blocks_out->words = words;
+        blocks_out->dtype = dtype;
+        blocks_out->valid = 0;
+    }
+    if (rows == 0 || n == 0) {
+        if (blocks_out) blocks_out->valid = 1;
+        return ISO_OK;
+    }
+    if (!y || !fit || !workspace) return ISO_EINVAL;
+    if (((uintptr_t)workspace & 255u) != 0) return ISO_EINVAL;
+    if (blocks_mem && ((uintptr_t)blocks_mem & 255u) != 0) return ISO_EINVAL;
+    const iso::Layout L = iso::make_layout(rows, n);
+    if (workspace_bytes < L.total) return ISO_EINVAL;
+    if (L.m > 0 && rows * L.m > (int64_t)UINT32_MAX) return ISO_EINVAL;
+    if (L.m == 0 && rows > (int64_t)UINT32_MAX) return ISO_EINVAL;
+    const size_t esz = dtype == ISO_F32 ? 4 : 8;
+    const size_t bytes = (size_t)rows * (size_t)n * esz;
+    const char* fb = (const char*)fit;
+    auto overlaps = [&](const void* p) {
+        const char* b = (const char*)p;
+        return p && b < fb + bytes && fb < b + bytes;
+    };
+    if (overlaps(y) || overlaps(w)) return ISO_EINVAL;
+
+    const unsigned long long epoch = ++g_epoch;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        g_last_epoch[workspace] = epoch;
+    }
+    iso::FitLaunch a{};
+    a.y = y;
+    a.w = w;
+    a.fit = fit;
+    a.rows = rows;
+    a.n = n;
+    a.increasing = increasing;
+    a.dtype = dtype;
+    a.lo = y_min;
+    a.hi = y_max;
+    a.start_bits = blocks_out ? blocks_out->start_bits_dev : nullptr;
+    a.clip_bits = blocks_out ? blocks_out->clip_bits_dev : nullptr;
+    a.row_nan = blocks_out ? blocks_out->row_nan_dev : nullptr;
+    a.words = words;
+    a.ws = (char*)workspace;
+    a.L = L;
+    a.epoch = epoch;
+    a.stream = (hipStream_t)stream;
+    if (iso::launch_fit(a) != hipSuccess) return ISO_EHIP;
+    if (blocks_out) blocks_out->valid = 1;
+    return ISO_OK;
+}
+
+int iso_vjp(const void* grad, const iso_blocks* blocks, void* grad_y, void* workspace, size_t workspace_bytes,
+            void* stream) {
+    if (!blocks || !blocks->valid) return ISO_EINVAL;
+    if (blocks->rows < 0 || blocks->n < 0 || !valid_dtype(blocks->dtype)) return ISO_EINVAL;
+    if (blocks->rows == 0 || blocks->n == 0) return ISO_OK;
+    if (!grad || !grad_y || !workspace) return ISO_EINVAL;
+    if (!blocks->start_bits_dev || !blocks->clip_bits_dev || !blocks->row_nan_dev) return ISO_EINVAL;
+    if (((uintptr_t)workspace & 255u) != 0) return ISO_EINVAL;
+    const iso::Layout L = iso::make_layout(blocks->rows, blocks->n);
+    if (workspace_bytes < L.total) return ISO_EINVAL;
+    iso::VjpLaunch v{};
+    v.g = grad;
+    v.w = blocks->w_dev;
+    v.out = grad_y;
+    v.rows = blocks->rows;
+    v.n = blocks->n;
+    v.words = blocks->words;
+    v.dtype = blocks->dtype;
+    v.start_bits = blocks->start_bits_dev;
+    v.clip_bits = blocks->clip_bits_dev;
+    v.row_nan = blocks->row_nan_dev;
+    v.ws = (char*)workspace;
+    v.L = L;
+    v.stream = (hipStream_t)stream;
+    if (iso::launch_vjp(v) != hipSuccess) return ISO_EHIP;
+    return ISO_OK;
+}
+
+int iso_status(const void* workspace, void* stream) {
+    if (!workspace) return ISO_EINVAL;
+    unsigned long long last = 0;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        auto it = g_last_epoch.find(workspace);
+        if (it == g_last_epoch.end()) return ISO_OK;
+        last = it->second;
+    }
+    if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return ISO_EHIP;
+    unsigned long long word = 0;
+    if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return ISO_EHIP;
+    if ((word >> 8) == last) return -(int)(word & 0xff);
+    return ISO_OK;
+}
+
+const char* iso_strerror(int code) {
+    switch (code) {
+        case ISO_OK:
+            return "success";
+        case ISO_EINVAL:
+            return "invalid argument";
+        case ISO_EHIP:
+            return "HIP runtime error";
+        case ISO_EWEIGHT:
+            return "a weight is not strictly positive";
+        default:
+            return "unknown error";
+    }
+}
+
+}  // extern "C"

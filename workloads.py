@@ -128,8 +128,10 @@ def _weights(r, kind, shape, dtype):
     if kind == "uniform":
         return (r.random(shape) + 0.1).astype(dtype)
     if kind == "extreme":
-        # weights spanning e^-8 .. e^8
-        return np.exp(r.uniform(-8.0, 8.0, size=shape)).astype(dtype)
+        # weights spanning a ratio of e^8 (e^-4 .. e^4): the first page,
+        # Sec. 7.6, notes that with extreme weights a sum of 32 terms can be
+        # 32 e^8 times a single term
+        return np.exp(r.uniform(-4.0, 4.0, size=shape)).astype(dtype)
     raise ValueError(kind)
 
 
