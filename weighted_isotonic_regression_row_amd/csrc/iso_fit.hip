@@ -1,13 +1,14 @@
 // Forward kernels of the isotonic fit for gfx950.
 //
 // Page "Merge Hulls Without Copying Vertices: GPU Isotonic Regression":
-//   k_row_fit      rows of at most 8192 elements: one workgroup per row builds
+//   k_row_fit      rows of at most 6144 elements: one workgroup per row builds
 //                  the row's hull in LDS and writes the fit (Sec. 3: "a row that
 //                  fits in one chunk is finished at the second level").
-//   k_chunk_hull   longer rows: one workgroup per chunk of 4096 elements builds
-//                  the chunk's hull once, stores its vertices (chunk-relative
-//                  coordinates, Sec. 3.3), the chunk totals, and a tentative fit
-//                  from the chunk's own hull.
+//   k_chunk_hull   longer rows: one workgroup per chunk of 3584 elements builds
+//                  the chunk's hull once and stores it compactly (vertex bit
+//                  set, group starts, the coordinates of its end vertices),
+//                  the chunk totals, and a tentative fit from the chunk's own
+//                  hull.
 //   k_merge_tree   one workgroup per long row: double-double chunk starts
 //                  (exclusive scan of the chunk totals, Sec. 3.3 and App. B),
 //                  then every level of the merge tree on segment lists, at most
@@ -19,8 +20,8 @@
 //                  a chunk without a segment lies under one edge).
 #include <math.h>
 
-#include "iso_device.hpp"
 #include "iso_internal.hpp"
+#include "iso_tile.hpp"
 
 namespace iso {
 
@@ -37,6 +38,9 @@ struct RowArgs {
     int64_t words;
     unsigned long long* status;
     unsigned long long epoch;
+    int cap;             // vertices the LDS list holds (row kernel)
+    char* ovf;           // per-row vertex lists in global memory for rows whose lane hulls exceed cap
+    int64_t ovf_stride;  // bytes per row of ovf
 };
 
 // Every writer of one call stores the same value, so a plain exchange is
@@ -46,33 +50,8 @@ __device__ inline void report_weight_error(unsigned long long* status, unsigned 
     atomicExch(status, (epoch << 8) | 3ull);
 }
 
-// Expand (Sec. 3.4) over the workgroup's range: fit, block-start and clip bits.
 template <typename T>
-__device__ inline void wg_expand(int N, HullSmem s, T* out, int increasing, double lo, double hi,
-                                 uint64_t* sbits, uint64_t* cbits) {
-    const int lane = lane_id();
-    const int wid = threadIdx.x >> 6;
-    const int nw = blockDim.x >> 6;
-    const int G = hull_groups(N);
-    for (int g = wid; g < G; g += nw) {
-        uint64_t word;
-        const double sl = group_edge_slope(N, g, s, word);
-        const int i = g * kWave + lane;
-        bool clipped = false;
-        const double v = finish(sl, increasing, lo, hi, clipped);
-        if (i < N) out[i] = (T)v;
-        const uint64_t cb = __ballot(i < N && clipped);
-        if (sbits && lane == 0) {
-            const int cnt = N - g * kWave;
-            const uint64_t valid = (cnt >= 64) ? ~0ull : ((1ull << cnt) - 1ull);
-            sbits[g] = word & valid;
-            cbits[g] = cb;
-        }
-    }
-}
-
-template <typename T>
-__device__ inline void wg_write_nan_row(int64_t N, T* out, uint64_t* sbits, uint64_t* cbits) {
+__device__ inline void wg_write_nan(int64_t N, T* out, uint64_t* sbits, uint64_t* cbits) {
     for (int64_t i = threadIdx.x; i < N; i += blockDim.x) out[i] = (T)NAN;
     if (sbits) {
         const int64_t words = (N + 63) / 64;
@@ -83,37 +62,81 @@ __device__ inline void wg_write_nan_row(int64_t N, T* out, uint64_t* sbits, uint
     }
 }
 
+// Steps 1-2 of the tile pipeline (lane hulls, lane starts) on the elements at
+// y, w.  Returns the tile's flag (non-zero: a non-finite input or a bad
+// weight); nvert = the number of lane-hull vertices.  The lane's points stay
+// in xs, ys.
+template <typename T, int K>
+__device__ inline int tile_build(const Tile& t, const T* y, const T* w, int increasing, uint64_t& mask,
+                                 double (&xs)[K], double (&ys)[K], int& nvert) {
+    constexpr bool ABS = sizeof(T) == 4;
+    const int l = threadIdx.x;
+    const int cnt = min(max(t.N - l * K, 0), K);
+    int f = 0;
+    mask = lane_hull<T, K>(y + (int64_t)l * K, w ? w + (int64_t)l * K : nullptr, cnt, !increasing, xs, ys, f);
+    nvert = tile_lane_starts<!ABS>(t, make_double2(xs[K - 1], ys[K - 1]), f, __popcll(mask));
+    return t.flag[0];
+}
+
+// Step 4 and the stores: fit (and bits) of the tile's elements.  Overwrites
+// the list's coordinates with edge slopes.
+template <typename T, int K>
+__device__ inline void tile_finish(const Tile& t, uint64_t mask, int increasing, double lo, double hi, T* out,
+                                   uint64_t* sb, uint64_t* cb) {
+    constexpr bool ABS = sizeof(T) == 4;
+    tile_edge_slopes<K, ABS>(t);
+    double vals[K];
+    uint64_t clipm;
+    tile_expand<K>(t, mask, increasing, lo, hi, vals, clipm);
+    const int l = threadIdx.x;
+    const int cnt = min(max(t.N - l * K, 0), K);
+    store_lane<T, K>(out + (int64_t)l * K, cnt, vals);
+    if (sb) {
+        t.CM[l] = clipm;
+        __syncthreads();
+        tile_bits<K>(t, sb, cb);
+    }
+}
+
 // ---------------------------------------------------------------------------
 // one workgroup per row
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(512) void k_row_fit(RowArgs a) {
+template <typename T, int K>
+__global__ __launch_bounds__(384) void k_row_fit(RowArgs a) {
     extern __shared__ __align__(32) char smem[];
     const int64_t row = blockIdx.x;
     const int N = (int)a.n;
-    HullSmem s = hull_smem_carve(smem, N);
+    const Tile t = tile_carve(smem, blockDim.x, a.cap, K, N);
     const T* y = (const T*)a.y + row * a.n;
     const T* w = a.w ? (const T*)a.w + row * a.n : nullptr;
     T* out = (T*)a.fit + row * a.n;
     uint64_t* sb = a.start_bits ? a.start_bits + row * a.words : nullptr;
     uint64_t* cb = a.clip_bits ? a.clip_bits + row * a.words : nullptr;
-    if (threadIdx.x == 0) s.flag[0] = 0;
-    __syncthreads();
-    wg_load_prefix<T, 4>(y, w, N, a.increasing, s);
-    __syncthreads();
-    const int flag = s.flag[0];
+    uint64_t mask;
+    double xs[K], ys[K];
+    int nvert;
+    const int flag = tile_build<T, K>(t, y, w, a.increasing, mask, xs, ys, nvert);
     if (flag) {
-        wg_write_nan_row<T>(N, out, sb, cb);
+        wg_write_nan<T>(N, out, sb, cb);
         if (threadIdx.x == 0) {
             if (a.row_nan) a.row_nan[row] = 1u;
             if (flag == 2) report_weight_error(a.status, a.epoch);
         }
         return;
     }
-    wg_group_starts(N, s);
-    wg_group_hulls(N, s);
-    wg_group_merges(N, s);
-    wg_expand<T>(N, s, out, a.increasing, a.lo, a.hi, sb, cb);
+    constexpr bool ABS = sizeof(T) == 4;
+    if (nvert <= a.cap) {
+        tile_merges<K, ABS>(t, mask, xs, ys);
+        tile_finish<T, K>(t, mask, a.increasing, a.lo, a.hi, out, sb, cb);
+    } else {
+        // the vertex list goes to this row's area of global memory
+        Tile tg = t;
+        char* o = a.ovf + row * a.ovf_stride;
+        tg.VXY = (double2*)o;
+        tg.V = (unsigned short*)(o + 16 * (a.n + 1));
+        tile_merges<K, ABS>(tg, mask, xs, ys);
+        tile_finish<T, K>(tg, mask, a.increasing, a.lo, a.hi, out, sb, cb);
+    }
     if (a.row_nan && threadIdx.x == 0) a.row_nan[row] = 0u;
 }
 
@@ -122,32 +145,35 @@ __global__ __launch_bounds__(512) void k_row_fit(RowArgs a) {
 // ---------------------------------------------------------------------------
 struct ChunkArgs {
     RowArgs r;
-    int64_t m;  // chunks per row
-    double4* totals;  // chunk totals, double-double (xh, xl, yh, yl)
-    int* nv;
-    int* cflag;
-    double4* vxy;     // chunk hull vertices, chunk-relative double-double
-    int* vidx;
+    int64_t m;         // chunks per row
+    double4* tot;      // [rows*m] chunk totals (double-double x, y)
+    int* nv;           // [rows*m] vertices of the chunk hull
+    int* cflag;        // [rows*m]
+    uint64_t* cmask;   // [rows*m*kMaskWords]
+    int* cpre;         // [rows*m*kMaskWords]
+    double4* cgs;      // [rows*m*kGroups]
+    double4* cvx;      // [rows*m*kVMax]
+    int* cvi;          // [rows*m*kVMax]
 };
 
 template <typename T>
-__global__ __launch_bounds__(512) void k_chunk_hull(ChunkArgs a) {
+__global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
+    constexpr int K = kLaneK;
     extern __shared__ __align__(32) char smem[];
     const int64_t bid = blockIdx.x;
     const int64_t row = bid / a.m, c = bid % a.m;
     const int64_t e0 = c * kChunk;
     const int N = (int)((a.r.n - e0) < kChunk ? (a.r.n - e0) : kChunk);
-    HullSmem s = hull_smem_carve(smem, N);
+    const Tile t = tile_carve(smem, blockDim.x, kChunk, K, N);
     const T* y = (const T*)a.r.y + row * a.r.n + e0;
     const T* w = a.r.w ? (const T*)a.r.w + row * a.r.n + e0 : nullptr;
     T* out = (T*)a.r.fit + row * a.r.n + e0;
     uint64_t* sb = a.r.start_bits ? a.r.start_bits + row * a.r.words + e0 / 64 : nullptr;
     uint64_t* cb = a.r.clip_bits ? a.r.clip_bits + row * a.r.words + e0 / 64 : nullptr;
-    if (threadIdx.x == 0) s.flag[0] = 0;
-    __syncthreads();
-    wg_load_prefix<T, 4>(y, w, N, a.r.increasing, s);
-    __syncthreads();
-    const int flag = s.flag[0];
+    uint64_t mask;
+    double xs[K], ys[K];
+    int nvert;
+    const int flag = tile_build<T, K>(t, y, w, a.r.increasing, mask, xs, ys, nvert);
     if (flag) {
         // the whole row comes back NaN; k_fixup writes it
         if (threadIdx.x == 0) {
@@ -156,65 +182,152 @@ __global__ __launch_bounds__(512) void k_chunk_hull(ChunkArgs a) {
         }
         return;
     }
-    wg_group_starts(N, s);
-    wg_group_hulls(N, s);
-    wg_group_merges(N, s);
-
-    // vertex ranks: exclusive scan of the popcounts of the vertex words
-    const int nwords = hull_words(N);
-    const int lane = lane_id();
-    if ((threadIdx.x >> 6) == 0) {
-        const int k = (nwords + kWave - 1) / kWave;
-        int cnt = 0;
-        for (int j = 0; j < k; ++j) {
-            const int q = lane * k + j;
-            if (q < nwords) cnt += __popcll(s.Mk[q]);
-        }
-        const int incl = wave_incl_scan_int(cnt);
-        int ex = incl - cnt;
-        for (int j = 0; j < k; ++j) {
-            const int q = lane * k + j;
-            if (q < nwords) {
-                s.WO[q] = ex;
-                ex += __popcll(s.Mk[q]);
-            }
-        }
-        if (lane == kWave - 1) s.flag[1] = incl;
-    }
-    __syncthreads();
-    double4* V = a.vxy + bid * kVSlot;
-    int* VI = a.vidx + bid * kVSlot;
-    for (int k = threadIdx.x; k <= N; k += blockDim.x) {
-        const uint64_t word = s.Mk[k >> 6];
-        if ((word >> (k & 63)) & 1ull) {
-            const int rank = s.WO[k >> 6] + __popcll(word & ((1ull << (k & 63)) - 1ull));
-            V[rank] = pabs(s, k);
-            VI[rank] = k;
+    tile_merges<K, sizeof(T) == 4>(t, mask, xs, ys);  // the LDS list holds every point of a chunk
+    __syncthreads();  // every lane's final mask in M
+    const int l = threadIdx.x;
+    const int nv = t.flag[1];  // vertices of the chunk hull; rank r is list entry r
+    // explicit coordinates (relative to the chunk start) of the end windows,
+    // or of every vertex of a small hull
+    if (l < kVMax) {
+        const int r = (nv <= kVMax || l < kVMax / 2) ? l : nv - kVMax + l;
+        if (r < nv) {
+            const int p = t.V[r];
+            const double2 q = t.VXY[r];
+            a.cvi[bid * kVMax + l] = p;
+            a.cvx[bid * kVMax + l] = (sizeof(T) == 4) ? make_double4(q.x, 0.0, q.y, 0.0)
+                                                      : dd4_add_d(t.LS[lane_of<K>(p)], q);
         }
     }
-    if (threadIdx.x == 0) {
-        a.nv[bid] = s.flag[1];
+    // vertex bit set and the rank of each word's first vertex
+    constexpr int LPW = 64 / K;
+    if ((l % LPW) == 0 && l * K < N) {
+        uint64_t word = 0ull;
+#pragma unroll
+        for (int k = 0; k < LPW; ++k) word |= t.M[l + k] << (k * K);
+        a.cmask[bid * kMaskWords + l / LPW] = word;
+        a.cpre[bid * kMaskWords + l / LPW] = t.I[l];
+    }
+    // starts of the 256-element groups
+    constexpr int LPG = kGroup / K;
+    if ((l % LPG) == 0 && l * K < N) a.cgs[bid * kGroups + l / LPG] = t.LS[l];
+    if (l == 0) {
+        a.tot[bid] = t.LS[t.nl];
+        a.nv[bid] = nv;
         a.cflag[bid] = 0;
-        a.totals[bid] = pabs(s, N);
     }
     // tentative fit from the chunk's own hull; k_fixup corrects the elements
     // outside the chunk's surviving segment
-    wg_expand<T>(N, s, out, a.r.increasing, a.r.lo, a.r.hi, sb, cb);
+    tile_finish<T, K>(t, mask, a.r.increasing, a.r.lo, a.r.hi, out, sb, cb);
 }
 
 // ---------------------------------------------------------------------------
 // merge tree of one long row
 // ---------------------------------------------------------------------------
-struct MergeArgs {
-    int64_t m;
-    const double4* totals;
+
+// Read access to the stored chunk hulls of one row.
+struct HullView {
     const int* nv;
+    const double4* tot;
+    const uint64_t* mask;
+    const int* pre;
+    const double4* gs;
+    const double4* vx;
+    const int* vi;
+    const void* y;  // the row's elements
+    const void* w;
+    int negate;
+    int64_t n;
+};
+
+struct Vtx {
+    int p;      // chunk-local point
+    double4 v;  // coordinates relative to the chunk start (double-double x, y)
+};
+
+template <typename T>
+__device__ inline double2 elem_wt(const HullView& H, int64_t e) {
+    const double yv = (double)((const T*)H.y)[e];
+    const double wv = H.w ? (double)((const T*)H.w)[e] : 1.0;
+    double t = wv * yv;
+    if (H.negate) t = -t;
+    return make_double2(wv, t);
+}
+
+// Vertex of rank r of chunk c's hull.  The end windows are read directly;
+// any other vertex is found in the bit set (rank of each word's first vertex,
+// then the bit) and its coordinates are summed from the nearer end of its
+// 256-element group.
+template <typename T>
+__device__ inline Vtx vtx(const HullView& H, int c, int r) {
+    const int nv = H.nv[c];
+    int s = -1;
+    if (nv <= kVMax || r < kVMax / 2)
+        s = r;
+    else if (r >= nv - kVMax / 2)
+        s = r - nv + kVMax;
+    if (s >= 0) return Vtx{H.vi[c * kVMax + s], H.vx[c * kVMax + s]};
+    const int64_t e0 = (int64_t)c * kChunk;
+    const int Nc = (int)((H.n - e0) < kChunk ? (H.n - e0) : kChunk);
+    const int words = (Nc + 63) / 64;
+    const int* pre = H.pre + (int64_t)c * kMaskWords;
+    const uint64_t* mk = H.mask + (int64_t)c * kMaskWords;
+    int lo = 0, hi = words - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= r)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    uint64_t m = mk[lo];
+    for (int k = r - pre[lo]; k > 0 && m; --k) m &= m - 1ull;
+    const int p = m ? lo * 64 + lo_bit(m) + 1 : lo * 64 + 1;
+    const int G = (Nc + kGroup - 1) / kGroup;
+    int g = p / kGroup;
+    if (g > G - 1) g = G - 1;
+    const int gs0 = g * kGroup, ge = (gs0 + kGroup < Nc) ? gs0 + kGroup : Nc;
+    // compensated sums (two-sum), so that the partial sum adds no more than
+    // a unit of rounding of its own magnitude
+    double X = 0.0, Xe = 0.0, Y = 0.0, Ye = 0.0;
+    double4 v;
+    if (p - gs0 <= ge - p) {
+        for (int e = gs0; e < p; ++e) {
+            const double2 q = elem_wt<T>(H, e0 + e);
+            double se;
+            two_sum(X, q.x, X, se);
+            Xe += se;
+            two_sum(Y, q.y, Y, se);
+            Ye += se;
+        }
+        const double4 G0 = H.gs[(int64_t)c * kGroups + g];
+        v = dd4_add(G0, make_double4(X, Xe, Y, Ye));
+    } else {
+        for (int e = p; e < ge; ++e) {
+            const double2 q = elem_wt<T>(H, e0 + e);
+            double se;
+            two_sum(X, q.x, X, se);
+            Xe += se;
+            two_sum(Y, q.y, Y, se);
+            Ye += se;
+        }
+        const double4 B = (g + 1 < G) ? H.gs[(int64_t)c * kGroups + g + 1] : H.tot[c];
+        v = dd4_add(B, make_double4(-X, -Xe, -Y, -Ye));
+    }
+    return Vtx{p, v};
+}
+
+struct MergeArgs {
+    const void* y;
+    const void* w;
+    int64_t n, m;
+    int negate;
+    HullView H0;  // row 0's pointers; offset per row in the kernel
     const int* cflag;
-    const double4* vxy;
-    const int* vidx;
     double4* starts;
-    Desc* gdesc;
+    Desc* gd0;
+    Desc* gd1;
     int* gnc;
+    MRec* gmr;
     double* gso;
     Rec* rec;
     uint32_t* row_nan;
@@ -223,17 +336,17 @@ struct MergeArgs {
     int use_lds;
 };
 
-// a point of the row: chunk start + chunk-relative vertex, both double-double
+// a point of the row as one double-double pair (chunk start + chunk-relative
+// vertex, summed exactly), so that the difference of two points loses nothing
+// to the size of the chunk starts (first page, App. B, "Merge levels")
 struct PtD {
-    double4 c;  // chunk start (xh, xl, yh, yl)
-    double4 v;  // vertex relative to the chunk start
+    double4 a;
 };
 
 struct MCtx {
-    Desc* D;
-    int* NC;
+    const Desc* D;
     const double4* st;
-    const double4* V;
+    HullView H;
 };
 
 struct VR {
@@ -241,21 +354,26 @@ struct VR {
     int k;  // vertex rank in the chunk hull
 };
 
+template <typename T>
 __device__ __forceinline__ PtD ptd(const MCtx& X, int c, int k) {
     PtD p;
-    p.c = X.st[c];
-    p.v = X.V[(int64_t)c * kVSlot + k];
+    p.a = dd4_add(X.st[c], vtx<T>(X.H, c, k).v);
     return p;
 }
-__device__ __forceinline__ PtD ptv(const MCtx& X, VR v) { return ptd(X, X.D[v.s].c, v.k); }
+template <typename T>
+__device__ __forceinline__ PtD ptv(const MCtx& X, VR v) {
+    return ptd<T>(X, X.D[v.s].c, v.k);
+}
 
-// differences formed part by part (first page, App. B, "Merge levels": the
-// turn is computed from differences of the hi, lo and chunk-relative parts)
 __device__ __forceinline__ double pdx(const PtD& a, const PtD& b) {
-    return ((b.c.x - a.c.x) + (b.c.y - a.c.y)) + ((b.v.x - a.v.x) + (b.v.y - a.v.y));
+    double h, l;
+    dd_add(b.a.x, b.a.y, -a.a.x, -a.a.y, h, l);
+    return h + l;
 }
 __device__ __forceinline__ double pdy(const PtD& a, const PtD& b) {
-    return ((b.c.z - a.c.z) + (b.c.w - a.c.w)) + ((b.v.z - a.v.z) + (b.v.w - a.v.w));
+    double h, l;
+    dd_add(b.a.z, b.a.w, -a.a.z, -a.a.w, h, l);
+    return h + l;
 }
 __device__ __forceinline__ double turnD(const PtD& a, const PtD& b, const PtD& d) {
     return pdx(a, b) * pdy(a, d) - pdy(a, b) * pdx(a, d);
@@ -264,7 +382,7 @@ __device__ __forceinline__ double slopeD(const PtD& a, const PtD& b) { return pd
 
 // successor of v in the list whose last slot is s1
 __device__ __forceinline__ bool vsucc(const MCtx& X, VR v, int s1, VR& n) {
-    if (v.k < X.D[v.s].h) {
+    if (v.k < (int)X.D[v.s].h) {
         n.s = v.s;
         n.k = v.k + 1;
         return true;
@@ -278,7 +396,7 @@ __device__ __forceinline__ bool vsucc(const MCtx& X, VR v, int s1, VR& n) {
 }
 // predecessor of v in the list whose first slot is s0
 __device__ __forceinline__ bool vpred(const MCtx& X, VR v, int s0, VR& p) {
-    if (v.k > X.D[v.s].l) {
+    if (v.k > (int)X.D[v.s].l) {
         p.s = v.s;
         p.k = v.k - 1;
         return true;
@@ -300,15 +418,15 @@ __device__ inline VR first_true(const MCtx& X, int s0, int s1, int lastH, Pred p
     int lo = s0, hi = s1 + 1;
     while (lo < hi) {
         const int mid = (lo + hi) >> 1;
-        if (pred(VR{mid, X.D[mid].l}))
+        if (pred(VR{mid, (int)X.D[mid].l}))
             hi = mid;
         else
             lo = mid + 1;
     }
-    if (lo == s0) return VR{s0, X.D[s0].l};
+    if (lo == s0) return VR{s0, (int)X.D[s0].l};
     const int sg = lo - 1;
-    const int hv = (sg == s1) ? lastH : X.D[sg].h;
-    int rlo = X.D[sg].l + 1, rhi = hv + 1;
+    const int hv = (sg == s1) ? lastH : (int)X.D[sg].h;
+    int rlo = (int)X.D[sg].l + 1, rhi = hv + 1;
     while (rlo < rhi) {
         const int mid = (rlo + rhi) >> 1;
         if (pred(VR{sg, mid}))
@@ -320,27 +438,28 @@ __device__ inline VR first_true(const MCtx& X, int s0, int s1, int lastH, Pred p
     // only reached if rounding broke the predicate's guarantee at the view's
     // last vertex: stay inside the view
     if (lo > s1) return VR{s1, lastH};
-    return VR{lo, X.D[lo].l};
+    return VR{lo, (int)X.D[lo].l};
 }
 
 // Lower tangent from p (left of every vertex of B) to B = slots jB..sB1: the
 // vertex minimising the slope from p, the farthest one on ties.
+template <typename T>
 __device__ inline VR tangent_b(const MCtx& X, const PtD& p, int jB, int sB1) {
     return first_true(X, jB, sB1, X.D[sB1].h, [&](VR v) -> bool {
         VR nx;
         if (!vsucc(X, v, sB1, nx)) return true;
-        return turnD(p, ptv(X, v), ptv(X, nx)) > 0.0;
+        return turnD(p, ptv<T>(X, v), ptv<T>(X, nx)) > 0.0;
     });
 }
 
 constexpr int kWalkCap = 48;
 
-// Merge the node at j0 (slots j0..) with its right neighbour at jB (Sec. 3.3,
-// Lemma 4.2, Theorem 4.4).  The result overwrites the left node's slots.
-__device__ inline void merge_pair(const MCtx& X, int j0, int jB) {
-    Desc* D = X.D;
-    int cntA = X.NC[j0];
-    const int cntB = X.NC[jB];
+// Bridge of the node at j0 (cntA slots) and its right neighbour at jB (cntB
+// slots) (Sec. 3.3, Lemma 4.2, Theorem 4.4), as the rewrite of the merged
+// list.  Reads the descriptors only.
+template <typename T>
+__device__ inline MRec find_merge(const MCtx& X, int j0, int jB, int cntA, int cntB) {
+    const Desc* D = X.D;
     const int la = j0 + cntA - 1;
     const int sB1 = jB + cntB - 1;
     const Desc dA = D[la];
@@ -349,19 +468,23 @@ __device__ inline void merge_pair(const MCtx& X, int j0, int jB) {
     const VR sA{la, dA.h};
     const VR sB{jB, dB.l};
     VR pA, nB;
-    vpred(X, sA, j0, pA);  // A has at least two vertices
-    vsucc(X, sB, sB1, nB); // and so has B
-    PtD PA = ptv(X, pA), PS = ptv(X, sB), PB = ptv(X, nB);
+    vpred(X, sA, j0, pA);   // A has at least two vertices
+    vsucc(X, sB, sB1, nB);  // and so has B
+    PtD PA = ptv<T>(X, pA), PS = ptv<T>(X, sB), PB = ptv<T>(X, nB);
+    MRec r;
     if (turnD(PA, PS, PB) > 0.0) {
         // convex at s: keep s once, in B's first segment
-        if (dA.h - 1 < dA.l) {
-            cntA -= 1;
+        if ((int)dA.h - 1 < (int)dA.l) {
+            r.newA = cntA - 1;
+            r.alk = D[la - 1].h;
         } else {
-            D[la].h = dA.h - 1;
+            r.newA = cntA;
+            r.alk = (int)dA.h - 1;
         }
-        for (int i = 0; i < cntB; ++i) D[j0 + cntA + i] = D[jB + i];
-        X.NC[j0] = cntA + cntB;
-        return;
+        r.bs = jB;
+        r.nBk = cntB;
+        r.bek = dB.l;
+        return r;
     }
     // walk from the neighbours of s (Sec. 4, after Lemma 4.2), capped
     VR al = pA, be = nB;
@@ -370,8 +493,8 @@ __device__ inline void merge_pair(const MCtx& X, int j0, int jB) {
         VR pa, nb;
         const bool canA = vpred(X, al, j0, pa);
         const bool canB = vsucc(X, be, sB1, nb);
-        const PtD Pp = canA ? ptv(X, pa) : PA;
-        const PtD Pn = canB ? ptv(X, nb) : PB;
+        const PtD Pp = canA ? ptv<T>(X, pa) : PA;
+        const PtD Pn = canB ? ptv<T>(X, nb) : PB;
         const bool mA = canA && !(turnD(Pp, PA, PB) > 0.0);
         if (mA) {
             al = pa;
@@ -392,31 +515,42 @@ __device__ inline void merge_pair(const MCtx& X, int j0, int jB) {
         // against its tangent to B; a is left of the bridge while A's next
         // vertex lies strictly below the line from a to its tangent point.
         // Candidates end at the predecessor of s.
-        int aS1 = la, aLastH = dA.h - 1;
-        if (aLastH < dA.l) {
+        int aS1 = la, aLastH = (int)dA.h - 1;
+        if (aLastH < (int)dA.l) {
             aS1 = la - 1;
             aLastH = D[la - 1].h;
         }
         al = first_true(X, j0, aS1, aLastH, [&](VR a) -> bool {
             VR an;
             vsucc(X, a, la, an);
-            const PtD Pa = ptv(X, a);
-            const VR b = tangent_b(X, Pa, jB, sB1);
-            return !(turnD(Pa, ptv(X, an), ptv(X, b)) > 0.0);
+            const PtD Pa = ptv<T>(X, a);
+            const VR b = tangent_b<T>(X, Pa, jB, sB1);
+            return !(turnD(Pa, ptv<T>(X, an), ptv<T>(X, b)) > 0.0);
         });
-        be = tangent_b(X, ptv(X, al), jB, sB1);
+        be = tangent_b<T>(X, ptv<T>(X, al), jB, sB1);
     }
-    // cut A at alpha and B at beta, move B's tail down behind A's head
-    D[al.s].h = al.k;
-    const int newA = al.s - j0 + 1;
-    D[be.s].l = be.k;
-    const int nBk = sB1 - be.s + 1;
-    for (int i = 0; i < nBk; ++i) D[j0 + newA + i] = D[be.s + i];
-    X.NC[j0] = newA + nBk;
+    r.newA = al.s - j0 + 1;
+    r.alk = al.k;
+    r.bs = be.s;
+    r.nBk = sB1 - be.s + 1;
+    r.bek = be.k;
+    return r;
 }
 
 constexpr int kMergeThreads = 1024;
 
+__host__ __device__ inline size_t merge_union_bytes(int64_t m) {
+    const size_t scan = sizeof(double4) * kMergeThreads;
+    const size_t mr = sizeof(MRec) * (size_t)(m / 2 + 1);
+    return (scan > mr ? scan : mr);
+}
+__host__ __device__ inline size_t merge_smem_bytes(int64_t m, int use_lds) {
+    size_t b = merge_union_bytes(m) + 16;
+    if (use_lds) b += (2 * sizeof(Desc) + sizeof(int)) * (size_t)m;
+    return b;
+}
+
+template <typename T>
 __global__ __launch_bounds__(kMergeThreads) void k_merge_tree(MergeArgs a) {
     extern __shared__ __align__(32) char smem[];
     const int64_t row = blockIdx.x;
@@ -424,16 +558,25 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_tree(MergeArgs a) {
     const int tid = threadIdx.x;
     const int NT = blockDim.x;
     const int64_t base = row * a.m;
-    double4* sbuf = (double4*)smem;                     // [NT]
-    int* sflag = (int*)(smem + sizeof(double4) * NT);  // [4]
-    Desc* D;
+    char* p = smem;
+    double4* sbuf = (double4*)p;  // the scan's partial sums, then the merge records
+    MRec* MR = (MRec*)p;
+    p += merge_union_bytes(m);
+    int* sflag = (int*)p;
+    p += 16;
+    Desc *Dc, *Dn;
     int* NC;
     if (a.use_lds) {
-        D = (Desc*)(smem + sizeof(double4) * NT + 16);
-        NC = (int*)(smem + sizeof(double4) * NT + 16 + sizeof(Desc) * (size_t)m);
+        Dc = (Desc*)p;
+        p += sizeof(Desc) * (size_t)m;
+        Dn = (Desc*)p;
+        p += sizeof(Desc) * (size_t)m;
+        NC = (int*)p;
     } else {
-        D = a.gdesc + base;
+        Dc = a.gd0 + base;
+        Dn = a.gd1 + base;
         NC = a.gnc + base;
+        MR = a.gmr + base;
     }
     Rec* rec = a.rec + base;
 
@@ -458,11 +601,22 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_tree(MergeArgs a) {
         return;
     }
 
+    HullView H = a.H0;
+    H.nv += base;
+    H.tot += base;
+    H.mask += base * kMaskWords;
+    H.pre += base * kMaskWords;
+    H.gs += base * kGroups;
+    H.vx += base * kVMax;
+    H.vi += base * kVMax;
+    H.y = (const char*)a.y + row * a.n * (int64_t)sizeof(T);
+    H.w = a.w ? (const void*)((const char*)a.w + row * a.n * (int64_t)sizeof(T)) : nullptr;
+
     // 2. chunk starts: exclusive double-double scan of the chunk totals
     const int per = (m + NT - 1) / NT;
     const int c0 = min(m, tid * per), c1 = min(m, c0 + per);
     double4 loc = make_double4(0.0, 0.0, 0.0, 0.0);
-    for (int c = c0; c < c1; ++c) loc = dd4_add(loc, a.totals[base + c]);
+    for (int c = c0; c < c1; ++c) loc = dd4_add(loc, H.tot[c]);
     double4 v = loc;
     sbuf[tid] = v;
     __syncthreads();
@@ -478,64 +632,88 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_tree(MergeArgs a) {
     if (tid > 0) ex = sbuf[tid - 1];
     for (int c = c0; c < c1; ++c) {
         a.starts[base + c] = ex;
-        ex = dd4_add(ex, a.totals[base + c]);
+        ex = dd4_add(ex, H.tot[c]);
     }
     // 3. leaves: one segment per chunk, its whole hull
     for (int c = tid; c < m; c += NT) {
         Desc d;
         d.c = c;
         d.l = 0;
-        d.h = a.nv[base + c] - 1;
-        d.pad = 0;
-        D[c] = d;
+        d.h = (unsigned short)(H.nv[c] - 1);
+        Dc[c] = d;
         NC[c] = 1;
     }
-    __threadfence_block();
+    __threadfence();
     __syncthreads();
 
     MCtx X;
-    X.D = D;
-    X.NC = NC;
     X.st = a.starts + base;
-    X.V = a.vxy + base * kVSlot;
+    X.H = H;
 
-    // 4. merge levels
+    // 4. merge levels: the bridges of a level (one thread per merge), then
+    // every slot of the merged lists rewritten into the other buffer
     for (int h = 1; h < m; h <<= 1) {
         const int nm = (m - h + 2 * h - 1) / (2 * h);
+        X.D = Dc;
         for (int k = tid; k < nm; k += NT) {
             const int j0 = k * 2 * h;
-            merge_pair(X, j0, j0 + h);
+            MR[k] = find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h]);
         }
         __threadfence_block();
         __syncthreads();
+        for (int j = tid; j < m; j += NT) {
+            const int k = j / (2 * h);
+            if (k < nm) {
+                const int j0 = k * 2 * h;
+                const MRec r = MR[k];
+                const int pos = j - j0;
+                if (pos < r.newA) {
+                    Desc d = Dc[j0 + pos];
+                    if (pos == r.newA - 1) d.h = (unsigned short)r.alk;
+                    Dn[j] = d;
+                } else if (pos < r.newA + r.nBk) {
+                    Desc d = Dc[r.bs + pos - r.newA];
+                    if (pos == r.newA) d.l = (unsigned short)r.bek;
+                    Dn[j] = d;
+                }
+                if (pos == 0) NC[j0] = r.newA + r.nBk;
+            } else {
+                Dn[j] = Dc[j];
+            }
+        }
+        __threadfence_block();
+        __syncthreads();
+        Desc* tmp = Dc;
+        Dc = Dn;
+        Dn = tmp;
     }
+    X.D = Dc;
 
     // 5. per-chunk records of the root list
     const int K = NC[0];
     double* so = a.gso + base;
     for (int k = tid; k < K - 1; k += NT) {
-        const Desc d0 = D[k], d1 = D[k + 1];
-        so[k] = slopeD(ptd(X, d0.c, d0.h), ptd(X, d1.c, d1.l));
+        const Desc d0 = Dc[k], d1 = Dc[k + 1];
+        so[k] = slopeD(ptd<T>(X, d0.c, d0.h), ptd<T>(X, d1.c, d1.l));
     }
     __threadfence();
     __syncthreads();
-    const int* VI = a.vidx + base * kVSlot;
     for (int c = tid; c < m; c += NT) {
         // last root segment whose chunk is <= c
         int lo = 0, hi = K;
         while (hi - lo > 1) {
             const int mid = (lo + hi) >> 1;
-            if (D[mid].c <= c)
+            if (Dc[mid].c <= c)
                 lo = mid;
             else
                 hi = mid;
         }
-        const Desc d = D[lo];
+        const Desc d = Dc[lo];
         Rec r{};
         if (d.c == c) {
             r.mode = 0;
-            r.lo = VI[(int64_t)c * kVSlot + d.l];
-            r.hi = VI[(int64_t)c * kVSlot + d.h];
+            r.lo = vtx<T>(H, c, d.l).p;
+            r.hi = vtx<T>(H, c, d.h).p;
             r.sin = (lo > 0) ? so[lo - 1] : 0.0;
             r.sout = (lo < K - 1) ? so[lo] : 0.0;
         } else {
@@ -617,79 +795,124 @@ __global__ __launch_bounds__(256) void k_fixup(FixArgs a) {
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
-static int pick_threads(int N) {
-    const int G = hull_groups(N);
-    if (G >= 32) return 512;
-    if (G >= 8) return 256;
-    return 64 * ((G + 1) / 2 > 0 ? (G + 1) / 2 : 1);
+
+// Lanes and elements per lane for a row of N <= kSingleMax elements: a single
+// wave for short rows, else 16 elements per lane and ceil(N/16) lanes rounded
+// up to whole waves (at most 384).
+static void row_shape(int N, int& K, int& nl) {
+    if (N <= 128) {
+        K = 2;
+        nl = 64;
+    } else if (N <= 256) {
+        K = 4;
+        nl = 64;
+    } else if (N <= 512) {
+        K = 8;
+        nl = 64;
+    } else {
+        K = 16;
+        nl = ((N + 15) / 16 + 63) / 64 * 64;
+    }
+}
+
+// Vertices the LDS list of a row holds: enough for three workgroups per CU
+// when a quarter of the points or more fit (noisy rows keep about a fifth of
+// their points as lane-hull vertices); rows that need more use global memory.
+static int row_list_cap(int N, int nl, int K) {
+    const long fixed = (long)tile_smem_bytes(nl, 0, K);
+    const long room = (kRowLdsTarget - fixed) / 18;
+    long cap = room > N / 4 ? room : N / 4;
+    return (int)(cap < N ? cap : N);
+}
+
+template <typename T, int K>
+static hipError_t launch_row(const FitLaunch& a, RowArgs r, int nl) {
+    static bool attr_set = false;
+    if (!attr_set) {
+        (void)hipFuncSetAttribute((const void*)k_row_fit<T, K>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)tile_smem_bytes(K == 16 ? (int)(kSingleMax / 16) : 64,
+                                                       K == 16 ? (int)kSingleMax : 64 * K, K));
+        attr_set = true;
+    }
+    r.cap = row_list_cap((int)a.n, nl, K);
+    r.ovf = a.ws + a.L.ovf;
+    r.ovf_stride = (int64_t)a.L.ovf_stride;
+    hipLaunchKernelGGL((k_row_fit<T, K>), dim3((unsigned)a.rows), dim3(nl), tile_smem_bytes(nl, r.cap, K), a.stream,
+                       r);
+    return hipGetLastError();
 }
 
 template <typename T>
 static hipError_t launch_fit_t(const FitLaunch& a) {
     unsigned long long* status = (unsigned long long*)(a.ws + a.L.status);
+    const RowArgs r{a.y, a.w, a.fit, a.n, a.increasing, a.lo, a.hi, a.start_bits, a.clip_bits, a.row_nan,
+                    a.words, status, a.epoch, 0, nullptr, 0};
     if (a.n <= kSingleMax) {
-        RowArgs r{a.y, a.w, a.fit, a.n, a.increasing, a.lo, a.hi, a.start_bits, a.clip_bits, a.row_nan,
-                  a.words, status, a.epoch};
-        const int N = (int)a.n;
-        const size_t smem = hull_smem_bytes(N);
-        const int nt = pick_threads(N);
-        static bool attr_set = false;
-        if (!attr_set) {
-            (void)hipFuncSetAttribute((const void*)k_row_fit<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)hull_smem_bytes((int)kSingleMax));
-            attr_set = true;
+        int K, nl;
+        row_shape((int)a.n, K, nl);
+        switch (K) {
+            case 2:
+                return launch_row<T, 2>(a, r, nl);
+            case 4:
+                return launch_row<T, 4>(a, r, nl);
+            case 8:
+                return launch_row<T, 8>(a, r, nl);
+            default:
+                return launch_row<T, 16>(a, r, nl);
         }
-        hipLaunchKernelGGL(k_row_fit<T>, dim3((unsigned)a.rows), dim3(nt), smem, a.stream, r);
-        return hipGetLastError();
     }
     const int64_t m = a.L.m;
     ChunkArgs ca;
-    ca.r = RowArgs{a.y, a.w, a.fit, a.n, a.increasing, a.lo, a.hi, a.start_bits, a.clip_bits, a.row_nan,
-                   a.words, status, a.epoch};
+    ca.r = r;
     ca.m = m;
-    ca.totals = (double4*)(a.ws + a.L.totals);
+    ca.tot = (double4*)(a.ws + a.L.tot);
     ca.nv = (int*)(a.ws + a.L.nv);
     ca.cflag = (int*)(a.ws + a.L.cflag);
-    ca.vxy = (double4*)(a.ws + a.L.vxy);
-    ca.vidx = (int*)(a.ws + a.L.vidx);
+    ca.cmask = (uint64_t*)(a.ws + a.L.cmask);
+    ca.cpre = (int*)(a.ws + a.L.cpre);
+    ca.cgs = (double4*)(a.ws + a.L.cgs);
+    ca.cvx = (double4*)(a.ws + a.L.cvx);
+    ca.cvi = (int*)(a.ws + a.L.cvi);
     {
+        const size_t smem = tile_smem_bytes(kChunkLanes, kChunk, kLaneK);
         static bool attr_set = false;
         if (!attr_set) {
             (void)hipFuncSetAttribute((const void*)k_chunk_hull<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)hull_smem_bytes(kChunk));
+                                      (int)smem);
             attr_set = true;
         }
-        hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)(a.rows * m)), dim3(512), hull_smem_bytes(kChunk),
-                           a.stream, ca);
+        hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)(a.rows * m)), dim3(kChunkLanes), smem, a.stream, ca);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     MergeArgs ma;
+    ma.y = a.y;
+    ma.w = a.w;
+    ma.n = a.n;
     ma.m = m;
-    ma.totals = ca.totals;
-    ma.nv = ca.nv;
+    ma.negate = !a.increasing;
+    ma.H0 = HullView{ca.nv, ca.tot, ca.cmask, ca.cpre, ca.cgs, ca.cvx, ca.cvi, nullptr, nullptr, !a.increasing, a.n};
     ma.cflag = ca.cflag;
-    ma.vxy = ca.vxy;
-    ma.vidx = ca.vidx;
     ma.starts = (double4*)(a.ws + a.L.starts);
-    ma.gdesc = (Desc*)(a.ws + a.L.desc);
+    ma.gd0 = (Desc*)(a.ws + a.L.desc0);
+    ma.gd1 = (Desc*)(a.ws + a.L.desc1);
     ma.gnc = (int*)(a.ws + a.L.nc);
+    ma.gmr = (MRec*)(a.ws + a.L.mrec);
     ma.gso = (double*)(a.ws + a.L.so);
     ma.rec = (Rec*)(a.ws + a.L.rec);
     ma.row_nan = a.row_nan;
     ma.status = status;
     ma.epoch = a.epoch;
     ma.use_lds = (m <= kMergeLdsChunks) ? 1 : 0;
-    size_t msmem = sizeof(double4) * kMergeThreads + 16;
-    if (ma.use_lds) msmem += (sizeof(Desc) + sizeof(int)) * (size_t)m;
     {
         static bool attr_set = false;
         if (!attr_set) {
-            (void)hipFuncSetAttribute((const void*)k_merge_tree, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)(sizeof(double4) * kMergeThreads + 16 + (sizeof(Desc) + sizeof(int)) * kMergeLdsChunks));
+            (void)hipFuncSetAttribute((const void*)k_merge_tree<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)merge_smem_bytes(kMergeLdsChunks, 1));
             attr_set = true;
         }
-        hipLaunchKernelGGL(k_merge_tree, dim3((unsigned)a.rows), dim3(kMergeThreads), msmem, a.stream, ma);
+        hipLaunchKernelGGL(k_merge_tree<T>, dim3((unsigned)a.rows), dim3(kMergeThreads),
+                           merge_smem_bytes(m, ma.use_lds), a.stream, ma);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -8,29 +8,53 @@
 namespace iso {
 
 // Rows of at most this many elements are fitted by one workgroup each, the
-// whole row held in LDS (16 bytes per point: 8192 points = 128 KiB of the
-// 160 KiB of a gfx950 CU).
-constexpr int64_t kSingleMax = 8192;
+// whole row held in LDS (18 bytes per element plus 52 per lane of 16
+// elements: 6144 elements take 131 KiB of the 160 KiB of a gfx950 CU).
+constexpr int64_t kSingleMax = 6144;
 // Longer rows are cut into chunks of this many elements (first page, Sec. 3:
-// chunks of 1024 to 4096 points), whose hulls are merged as segment lists.
-constexpr int kChunk = 4096;
-// Vertex slot per chunk: C + 1 points (neighbouring chunks share one).
-constexpr int64_t kVSlot = kChunk + 1;
+// chunks of 1024 to 4096 points), one workgroup of 256 threads, 224 of them
+// holding 16 elements each (76 KiB of LDS, so that two chunks share a CU),
+// whose hulls are merged as segment lists.
+constexpr int kChunk = 3584;
+constexpr int kLaneK = 16;
+constexpr int kChunkLanes = 256;
+// Stored form of a chunk hull (written once by the chunk kernel):
+//   vertex bit set, bit p-1 <-> chunk point p (point 0 is always a vertex);
+constexpr int kMaskWords = kChunk / 64;
+//   starts of the 256-element groups relative to the chunk start
+//   (double-double), from which the merge tree recomputes a vertex's
+//   coordinates with at most 128 element reads;
+constexpr int kGroup = 256;
+constexpr int kGroups = kChunk / kGroup;
+//   the coordinates of the first and last kVMax/2 vertices (of all of them
+//   when the hull has at most kVMax), which cover the merges of dense hulls,
+//   whose bridges sit at or next to the shared points.
+constexpr int kVMax = 16;
+// LDS a row workgroup aims for (three per CU), and the vertex list of a row
+// that does not fit it lives in the workspace.
+constexpr long kRowLdsTarget = 54000;
 // Segment descriptors of a row are kept in LDS up to this many chunks.
 constexpr int64_t kMergeLdsChunks = 4096;
 // Elements per tile of the backward pass on long rows.
 constexpr int kVjpTile = 4096;
 
+// A segment of a node's hull: vertex ranks l..h of chunk c's hull (first
+// page, Sec. 3.3: a node's list lives in the descriptor slots of its chunks).
 struct Desc {
-    int c;  // chunk
-    int l;  // first vertex (rank in the chunk hull)
-    int h;  // last vertex
-    int pad;
+    int c;
+    unsigned short l, h;
+};
+
+// How one merge of a level rewrites its node's list: the left node keeps its
+// first newA descriptors (the last one ending at rank alk), the right node's
+// descriptors bs .. bs+nBk-1 follow (the first one starting at rank bek).
+struct MRec {
+    int newA, bs, nBk, alk, bek;
 };
 
 struct Rec {
-    int lo;    // chunk-local element where the chunk's surviving segment starts
-    int hi;    // chunk-local element where it ends
+    int lo;    // chunk-local point where the chunk's surviving segment starts
+    int hi;    // chunk-local point where it ends
     int mode;  // 0: has a segment; 1: lies under one edge; 2: NaN row
     int pad;
     double sin;   // slope of the edge entering the segment
@@ -41,18 +65,23 @@ struct Rec {
 struct Layout {
     int64_t rows, n, m;  // m = chunks per row (0 on the single-workgroup path)
     size_t status;       // u64 status word
-    size_t totals;       // double4 [rows*m] (double-double x, y)
-    size_t nv;           // int [rows*m]
+    size_t tot;          // double4 [rows*m] chunk totals (double-double x, y)
+    size_t nv;           // int [rows*m] vertices of each chunk hull
     size_t cflag;        // int [rows*m]
     size_t starts;       // double4 [rows*m]
     size_t rec;          // Rec [rows*m]
-    size_t desc;         // Desc [rows*m]
+    size_t desc0, desc1; // Desc [rows*m] (merge levels ping-pong between them)
     size_t nc;           // int [rows*m]
-    size_t seg;          // int [rows*m]
+    size_t mrec;         // MRec [rows*m]
     size_t so;           // double [rows*m]
-    size_t vxy;          // double4 [rows*m*kVSlot] (double-double x, y)
-    size_t vidx;         // int [rows*m*kVSlot]
-    size_t vjp;          // backward tile records (aliases the fit regions)
+    size_t cmask;        // u64 [rows*m*kMaskWords]
+    size_t cpre;         // int [rows*m*kMaskWords] rank of the first vertex >= each word
+    size_t cgs;          // double4 [rows*m*kGroups]
+    size_t cvx;          // double4 [rows*m*kVMax]
+    size_t cvi;          // int [rows*m*kVMax]
+    size_t ovf;          // single-workgroup rows: per-row vertex lists for rows whose lane hulls overflow LDS
+    size_t ovf_stride;   // bytes per row of ovf
+    size_t vjp;          // backward tile records (alias the fit regions)
     size_t total;
 };
 
@@ -65,31 +94,32 @@ inline Layout make_layout(int64_t rows, int64_t n) {
     L.m = (n > kSingleMax) ? (n + kChunk - 1) / kChunk : 0;
     const size_t rm = (size_t)rows * (size_t)L.m;
     size_t off = 0;
-    L.status = off;
-    off = align256(off + 8);
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align256(off + bytes);
+        return at;
+    };
+    L.status = take(8);
     L.vjp = off;  // the backward reuses everything after the status word
-    L.totals = off;
-    off = align256(off + 32 * rm);
-    L.nv = off;
-    off = align256(off + 4 * rm);
-    L.cflag = off;
-    off = align256(off + 4 * rm);
-    L.starts = off;
-    off = align256(off + 32 * rm);
-    L.rec = off;
-    off = align256(off + sizeof(Rec) * rm);
-    L.desc = off;
-    off = align256(off + sizeof(Desc) * rm);
-    L.nc = off;
-    off = align256(off + 4 * rm);
-    L.seg = off;
-    off = align256(off + 4 * rm);
-    L.so = off;
-    off = align256(off + 8 * rm);
-    L.vxy = off;
-    off = align256(off + 32 * rm * (size_t)kVSlot);
-    L.vidx = off;
-    off = align256(off + 4 * rm * (size_t)kVSlot);
+    L.tot = take(32 * rm);
+    L.nv = take(4 * rm);
+    L.cflag = take(4 * rm);
+    L.starts = take(32 * rm);
+    L.rec = take(sizeof(Rec) * rm);
+    L.desc0 = take(sizeof(Desc) * rm);
+    L.desc1 = take(sizeof(Desc) * rm);
+    L.nc = take(4 * rm);
+    L.mrec = take(sizeof(MRec) * rm);
+    L.so = take(8 * rm);
+    L.cmask = take(8 * rm * kMaskWords);
+    L.cpre = take(4 * rm * kMaskWords);
+    L.cgs = take(32 * rm * kGroups);
+    L.cvx = take(32 * rm * kVMax);
+    L.cvi = take(4 * rm * kVMax);
+    if (L.m == 0) {
+        L.ovf_stride = align256(16 * ((size_t)n + 1) + 2 * ((size_t)n + 1));
+        L.ovf = take(L.ovf_stride * (size_t)rows);
+    }
     // backward: per tile head, tail, carry, total (double2 each) + flag
     const size_t tiles = (n > kSingleMax) ? (size_t)rows * (size_t)((n + kVjpTile - 1) / kVjpTile) : 0;
     const size_t vjp_end = L.vjp + align256(tiles * (4 * 16 + 8));
@@ -132,6 +162,6 @@ struct VjpLaunch {
 
 // Launchers (iso_fit.hip, iso_vjp.hip).  Return hipSuccess or the launch error.
 hipError_t launch_fit(const FitLaunch& a);
-hipError_t launch_vjp(const VjpLaunch& a);
+hipError_t launch_vjp(const VjpLaunch& l);
 
 }  // namespace iso

@@ -1,0 +1,638 @@
+// One workgroup builds the lower convex hull of the cumulative sum diagram of
+// N consecutive elements (a "tile") and the slope of the hull edge above every
+// element (page "Merge Hulls Without Copying Vertices: GPU Isotonic
+// Regression", Sec. 2.1 Eq. (2)-(3), Sec. 3.1-3.2 and 3.4).
+//
+// Work split (gfx950, wave64):
+//   1. lane hull each lane (thread) owns K consecutive elements, i.e. the
+//                points lK+1 .. lK+K, reads them straight from global memory,
+//                and runs one monotone-chain pass over them in registers in
+//                float64: local prefix sums of (w, w*y) relative to the lane's
+//                start, and the lane's hull as a bit-mask stack whose top two
+//                entries are kept apart (the first page's lane hull, Sec. 3.1);
+//   2. starts    an exclusive scan of the lane totals gives each lane's start
+//                relative to the tile's first point (double-double for float64
+//                data);
+//   3. merges    ceil(log2(lanes)) rounds.  Before each, the current vertices
+//                are compacted into a sorted list in LDS (point index and
+//                coordinates); then neighbouring nodes of 2^r lanes are merged,
+//                a group of G threads per merge walking from the shared point
+//                to the bridge (Sec. 4, Lemma 4.2 and the walk after it) G
+//                candidates at a time, and the points strictly under the bridge
+//                are cleared from the lane masks;
+//   4. expand    every lane computes the slope of the hull edge above each of
+//                its elements (Sec. 3.4: the edge from the last vertex at or
+//                before the element's left point to the first vertex at or
+//                after its right point) and stores the fit.
+//
+// Coordinates.  For float64 data a point is its lane's start (double-double)
+// plus a local float64 sum of at most K terms, and differences are formed part
+// by part (the first page's Appendix B, "Merge levels").  For float32 data the
+// products w*y are exact in float64 and a float64 coordinate relative to the
+// tile's first point is accurate far beyond float32 output, so points carry
+// one float64 pair and differences are direct.  A turn of zero counts as
+// non-convex, so collinear middle points are dropped (Sec. 2.1 and Sec. 4).
+//
+// Point p of the tile (p = 0..N) is P_p; element i lies between P_i and
+// P_{i+1}.  Point 0 is always a vertex and belongs to no lane; point p >= 1
+// belongs to lane (p-1)/K as its local point p - lK, and is bit p-1-lK of that
+// lane's mask.
+#pragma once
+
+#include "iso_device.hpp"
+
+namespace iso {
+
+// LDS of a tile.  The workgroup has nl threads, a whole number of waves; lane
+// l holds the elements lK .. lK+K-1 that are < N <= cap (lanes past the end
+// hold none).
+struct Tile {
+    unsigned short* V;  // the current vertices, sorted (point indices): the tile's list, or one per wave
+    double2* VXY;       // their coordinates (local to the point's lane, or absolute)
+    double4* LS;        // [nl + 1] lane starts (double-double pairs), LS[nl] = tile total
+    uint64_t* M;        // [nl] final lane vertex masks
+    uint64_t* CM;       // [nl] lane clip masks
+    int* I;             // [nl] index in V of each lane's first vertex
+    int2* MR;           // [nl / 2 + 1] bridge (alpha, beta) points of the merges of a round
+    int* W;             // [16] per-wave partial sums
+    int* flag;          // [4]
+    int nl;             // lanes (= threads of the workgroup)
+    int N;              // elements
+};
+
+// List capacity: the tile's vertices plus point 0.
+__host__ __device__ inline size_t tile_list_len(int nl, int cap, int K) {
+    (void)nl;
+    (void)K;
+    return (size_t)cap + 1;
+}
+
+__host__ __device__ inline size_t tile_smem_bytes(int nl, int cap, int K) {
+    const size_t n = tile_list_len(nl, cap, K);
+    const size_t v = (2 * n + 15) & ~(size_t)15;
+    return v + 16 * n + 32 * (size_t)(nl + 1) + 16 * (size_t)nl + 4 * (size_t)nl + 8 * (size_t)(nl / 2 + 1) + 64 + 16 +
+           128;
+}
+
+__device__ inline Tile tile_carve(char* base, int nl, int cap, int K, int N) {
+    Tile t;
+    char* p = base;
+    const size_t n = tile_list_len(nl, cap, K);
+    t.VXY = (double2*)p;
+    p += 16 * n;
+    t.LS = (double4*)p;
+    p += 32 * (size_t)(nl + 1);
+    t.M = (uint64_t*)p;
+    p += 8 * (size_t)nl;
+    t.CM = (uint64_t*)p;
+    p += 8 * (size_t)nl;
+    t.MR = (int2*)p;
+    p += 8 * (size_t)(nl / 2 + 1);
+    t.I = (int*)p;
+    p += 4 * (size_t)nl;
+    t.W = (int*)p;
+    p += 64;
+    t.flag = (int*)p;
+    p += 16;
+    t.V = (unsigned short*)p;
+    t.nl = nl;
+    t.N = N;
+    return t;
+}
+
+template <int K>
+__device__ __forceinline__ int lane_of(int p) {
+    return p <= 0 ? 0 : (p - 1) / K;
+}
+
+// Coordinates of list entries i, j: P_j - P_i.
+template <int K, bool ABS>
+__device__ __forceinline__ double2 vdiff(const Tile& t, int i, int j) {
+    const double2 A = t.VXY[i], B = t.VXY[j];
+    if (ABS) return sub2(B, A);
+    const int li = lane_of<K>(t.V[i]), lj = lane_of<K>(t.V[j]);
+    if (li == lj) return sub2(B, A);
+    const double2 d = dd4_diff(t.LS[li], t.LS[lj]);
+    return make_double2(d.x + (B.x - A.x), d.y + (B.y - A.y));
+}
+
+template <int K, bool ABS>
+__device__ __forceinline__ double vturn(const Tile& t, int i, int j, int k) {
+    return cross2(vdiff<K, ABS>(t, i, j), vdiff<K, ABS>(t, i, k));
+}
+
+// ---------------------------------------------------------------------------
+// 1. lane hull, in registers
+// ---------------------------------------------------------------------------
+
+// K values of p[0..cnt) as float64 (0 past cnt); 16-byte vector loads when the
+// lane's elements are whole and aligned.
+template <typename T, int K>
+__device__ __forceinline__ void load_lane(const T* __restrict__ p, int cnt, double (&v)[K]) {
+    constexpr int VW = 16 / (int)sizeof(T);
+    if constexpr (K % VW == 0) {
+        if (cnt == K && (((uintptr_t)p) & 15) == 0) {
+            if constexpr (sizeof(T) == 4) {
+#pragma unroll
+                for (int q = 0; q < K / 4; ++q) {
+                    const float4 f = ((const float4*)p)[q];
+                    v[4 * q] = f.x;
+                    v[4 * q + 1] = f.y;
+                    v[4 * q + 2] = f.z;
+                    v[4 * q + 3] = f.w;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < K / 2; ++q) {
+                    const double2 d = ((const double2*)p)[q];
+                    v[2 * q] = d.x;
+                    v[2 * q + 1] = d.y;
+                }
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[j] = (j < cnt) ? (double)p[j] : 0.0;
+}
+
+template <typename T, int K>
+__device__ __forceinline__ void store_lane(T* __restrict__ p, int cnt, const double (&v)[K]) {
+    constexpr int VW = 16 / (int)sizeof(T);
+    if constexpr (K % VW == 0) {
+        if (cnt == K && (((uintptr_t)p) & 15) == 0) {
+            if constexpr (sizeof(T) == 4) {
+#pragma unroll
+                for (int q = 0; q < K / 4; ++q)
+                    ((float4*)p)[q] = make_float4((float)v[4 * q], (float)v[4 * q + 1], (float)v[4 * q + 2],
+                                                  (float)v[4 * q + 3]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < K / 2; ++q) ((double2*)p)[q] = make_double2(v[2 * q], v[2 * q + 1]);
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+        if (j < cnt) p[j] = (T)v[j];
+}
+
+// Loads the lane's elements, forms the local points (xs, ys)[j] = point j+1
+// relative to the lane's start, and returns the lane's hull as a mask (bit b
+// <-> local point b+1; point 0 is implicit).  f |= 1 for a non-finite input,
+// 2 for a weight <= 0.
+//
+// The hull is found by gift wrapping: from every local point j the next hull
+// vertex is the point k > j of least slope (the farthest one on ties, so
+// collinear middle points are dropped), compared by cross-multiplication;
+// the hull is the chain of these pointers from point 0.  All K(K+1)/2 pairs
+// are compared with compile-time indices: no divergence and no indexed access
+// to the lane's registers.
+template <typename T, int K>
+__device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restrict__ w, int cnt, int negate,
+                                     double (&xs)[K], double (&ys)[K], int& f) {
+    static_assert(K <= 16, "next-vertex offsets are packed in 4 bits");
+    double X = 0.0, Y = 0.0;
+    auto take = [&](int j, double yi, double wi) {
+        if (j < cnt) {
+            if (!isfinite(yi) || !isfinite(wi))
+                f |= 1;
+            else if (!(wi > 0.0))
+                f |= 2;
+            double ti = wi * yi;
+            if (negate) ti = -ti;
+            X += wi;
+            Y += ti;
+        }
+        xs[j] = X;
+        ys[j] = Y;
+    };
+    constexpr int VW = 16 / (int)sizeof(T);
+    bool done = false;
+    if constexpr (K % VW == 0) {
+        // whole, aligned lanes: 16-byte loads, each consumed at once
+        if (cnt == K && (((uintptr_t)y) & 15) == 0 && (w == nullptr || (((uintptr_t)w) & 15) == 0)) {
+#pragma unroll
+            for (int q = 0; q < K / VW; ++q) {
+                if constexpr (sizeof(T) == 4) {
+                    const float4 a = ((const float4*)y)[q];
+                    const float4 b = w ? ((const float4*)w)[q] : make_float4(1.f, 1.f, 1.f, 1.f);
+                    take(4 * q, a.x, b.x);
+                    take(4 * q + 1, a.y, b.y);
+                    take(4 * q + 2, a.z, b.z);
+                    take(4 * q + 3, a.w, b.w);
+                } else {
+                    const double2 a = ((const double2*)y)[q];
+                    const double2 b = w ? ((const double2*)w)[q] : make_double2(1.0, 1.0);
+                    take(2 * q, a.x, b.x);
+                    take(2 * q + 1, a.y, b.y);
+                }
+            }
+            done = true;
+        }
+    }
+    if (!done) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const double yi = (j < cnt) ? (double)y[j] : 0.0;
+            const double wi = (j < cnt) ? (w ? (double)w[j] : 1.0) : 0.0;
+            take(j, yi, wi);
+        }
+    }
+    // next-vertex pointers, as offsets nx - j - 1 in 4-bit fields
+    uint64_t nxp = 0ull;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const double xj = j ? xs[j - 1] : 0.0, yj = j ? ys[j - 1] : 0.0;
+        double bdx = xs[j] - xj, bdy = ys[j] - yj;
+        int bk = 0;
+#pragma unroll
+        for (int k = j + 2; k <= K; ++k) {
+            const double dx = xs[k - 1] - xj, dy = ys[k - 1] - yj;
+            const bool take = (k <= cnt) && (dy * bdx <= bdy * dx);
+            bdx = take ? dx : bdx;
+            bdy = take ? dy : bdy;
+            bk = take ? (k - j - 1) : bk;
+        }
+        nxp |= (uint64_t)bk << (4 * j);
+    }
+    uint64_t mask = 0ull;
+    int v = 0;
+    for (int s = 0; s < K && v < cnt; ++s) {
+        v += 1 + (int)((nxp >> (4 * v)) & 15ull);
+        mask |= 1ull << (v - 1);
+    }
+    return mask;
+}
+
+// ---------------------------------------------------------------------------
+// 2. lane starts: exclusive scan of the lane totals into LS[0..nl-1], LS[nl]
+// = the tile's total (double-double when DD, else plain float64 in .x/.z).
+// Also combines the lane flags into flag[0], and returns the number of lane
+// hull vertices of the tile (point 0 included).  Ends with a barrier.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double4 add4(bool dd, double4 a, double4 b) {
+    return dd ? dd4_add(a, b) : make_double4(a.x + b.x, 0.0, a.z + b.z, 0.0);
+}
+
+template <bool DD>
+__device__ inline int tile_lane_starts(const Tile& t, double2 total, int f, int pc) {
+    const int lane = lane_id(), wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    double4* wsum = (double4*)t.CM;  // nw <= 16 entries
+    const uint64_t b1 = __ballot(f & 1), b2 = __ballot(f & 2);
+    const int pcs = wave_incl_scan_int(pc);
+    if (threadIdx.x == 0) t.flag[0] = 0;
+    double4 v = make_double4(total.x, 0.0, total.y, 0.0);
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const double4 o = shfl_up4(v, d);
+        if (lane >= d) v = add4(DD, o, v);
+    }
+    if (lane == kWave - 1) {
+        wsum[wid] = v;
+        t.W[wid] = pcs;
+    }
+    __syncthreads();
+    if (lane == 0 && (b1 | b2)) atomicOr(t.flag, (b1 ? 1 : 0) | (b2 ? 2 : 0));
+    double4 acc = make_double4(0.0, 0.0, 0.0, 0.0), all = acc;
+    int nvert = 1;
+    for (int k = 0; k < nw; ++k) {
+        const double4 s = wsum[k];
+        if (k < wid) acc = add4(DD, acc, s);
+        all = add4(DD, all, s);
+        nvert += t.W[k];
+    }
+    double4 ex = shfl_up4(v, 1);
+    if (lane == 0) ex = make_double4(0.0, 0.0, 0.0, 0.0);
+    t.LS[threadIdx.x] = add4(DD, acc, ex);
+    if (threadIdx.x == 0) t.LS[t.nl] = all;
+    __syncthreads();
+    return nvert;
+}
+
+// ---------------------------------------------------------------------------
+// 3. compaction of the vertex set and the merge rounds
+// ---------------------------------------------------------------------------
+
+// the calling lane's group's bits of a wave ballot (G consecutive lanes)
+__device__ __forceinline__ uint64_t group_bits(uint64_t ballot, int G) {
+    if (G >= 64) return ballot;
+    return (ballot >> (lane_id() & ~(G - 1))) & ((1ull << G) - 1ull);
+}
+// number of consecutive set bits from bit 0
+__device__ __forceinline__ int trailing_ones(uint64_t m) { return (m == ~0ull) ? 64 : lo_bit(~m); }
+
+// Orders the calling wave's LDS accesses: writes by any of its lanes before
+// the call are seen by reads of any of its lanes after it.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
+// Block scope.  Writes the sorted vertex list of the whole tile: V[0] = point
+// 0, then every lane's vertices; I[l] = index of lane l's first vertex;
+// flag[1] = number of vertices.  The coordinates are local to the point's lane
+// (or absolute when ABS).  Ends with a barrier.
+template <int K, bool ABS>
+__device__ inline void tile_compact(const Tile& t, uint64_t mask, const double (&xs)[K], const double (&ys)[K]) {
+    const int l = threadIdx.x, lane = lane_id(), wid = l >> 6, nw = blockDim.x >> 6;
+    const int pc = __popcll(mask);
+    const int incl = wave_incl_scan_int(pc);
+    if (lane == kWave - 1) t.W[wid] = incl;
+    __syncthreads();
+    int r = 1;
+    for (int k = 0; k < wid; ++k) r += t.W[k];
+    r += incl - pc;
+    if (l == 0) {
+        int tot = 1;
+        for (int k = 0; k < nw; ++k) tot += t.W[k];
+        t.flag[1] = tot;
+        t.V[0] = 0;
+        t.VXY[0] = make_double2(0.0, 0.0);
+    }
+    t.I[l] = r;
+    double sx = 0.0, sy = 0.0;
+    if (ABS) {
+        const double4 s = t.LS[l];
+        sx = s.x;
+        sy = s.z;
+    }
+#pragma unroll
+    for (int b = 0; b < K; ++b) {
+        if ((mask >> b) & 1ull) {
+            t.V[r] = (unsigned short)(l * K + b + 1);
+            t.VXY[r] = ABS ? make_double2(sx + xs[b], sy + ys[b]) : make_double2(xs[b], ys[b]);
+            ++r;
+        }
+    }
+    __syncthreads();
+}
+
+// The bridge of two nodes that share one point, found by the calling group of
+// G lanes (g = 0..G-1): A = list entries [iA0, iS] and B = [jS, jB1], where
+// entries iS and jS hold the shared point (iS == jS when the two lists are
+// adjacent).  Returns the list indices (alpha in A, beta in B); (iS, jS) when
+// the chain is convex at the shared point.  From the neighbours of the shared
+// point the walk of the first page (Sec. 4, after Lemma 4.2) advances each
+// side to its tangent point against the other side's current end, G
+// candidates per step: a is passed over while it is not a strict vertex of
+// {pred(a), a, b}, and b while it is not one of {a, b, succ(b)}.
+template <int K, bool ABS>
+__device__ inline int2 group_bridge(const Tile& t, int iA0, int iS, int jS, int jB1, int g, int G) {
+    if (vturn<K, ABS>(t, iS - 1, iS, jS + 1) > 0.0) return make_int2(iS, jS);
+    int al = iS - 1, be = jS + 1;
+    for (;;) {
+        for (;;) {
+            const int i = al - g;
+            bool cont = false;
+            if (i > iA0) cont = !(vturn<K, ABS>(t, i - 1, i, be) > 0.0);
+            const int run = trailing_ones(group_bits(__ballot(cont), G));
+            const int step = run < G ? run : G;
+            al -= step;
+            if (step < G) break;
+        }
+        bool movedB = false;
+        for (;;) {
+            const int j = be + g;
+            bool cont = false;
+            if (j < jB1) cont = !(vturn<K, ABS>(t, al, j, j + 1) > 0.0);
+            const int run = trailing_ones(group_bits(__ballot(cont), G));
+            const int step = run < G ? run : G;
+            be += step;
+            if (step > 0) movedB = true;
+            if (step < G) break;
+        }
+        if (!movedB) break;
+    }
+    return make_int2(al, be);
+}
+
+// Writes the calling lane's vertices at list indices r, r+1, ...
+template <int K, bool ABS>
+__device__ __forceinline__ void write_vertices(const Tile& t, uint64_t mask, int r, const double (&xs)[K],
+                                               const double (&ys)[K]) {
+    double sx = 0.0, sy = 0.0;
+    if (ABS) {
+        const double4 s = t.LS[threadIdx.x];
+        sx = s.x;
+        sy = s.z;
+    }
+#pragma unroll
+    for (int b = 0; b < K; ++b) {
+        if ((mask >> b) & 1ull) {
+            t.V[r] = (unsigned short)(threadIdx.x * K + b + 1);
+            t.VXY[r] = ABS ? make_double2(sx + xs[b], sy + ys[b]) : make_double2(xs[b], ys[b]);
+            ++r;
+        }
+    }
+}
+
+// Clears the calling lane's vertices whose list indices (r0, r0+1, ... in bit
+// order) lie strictly between the bridge entries ab.x and ab.y.
+template <int K>
+__device__ __forceinline__ void clear_between(uint64_t& mask, int r0, int2 ab) {
+    uint64_t clr = 0ull;
+    int r = r0;
+#pragma unroll
+    for (int b = 0; b < K; ++b) {
+        if ((mask >> b) & 1ull) {
+            if (r > ab.x && r < ab.y) clr |= 1ull << b;
+            ++r;
+        }
+    }
+    mask &= ~clr;
+}
+
+// Steps 3a-3c: merges of the lane hulls into the tile's hull.  mask is the
+// calling lane's own mask; on return the final masks are in M and the sorted
+// vertex list of the whole tile in V, VXY, with I[l] the index of lane l's
+// first vertex.
+template <int K, bool ABS>
+__device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (&xs)[K], const double (&ys)[K]) {
+    const int used = (t.N + K - 1) / K;
+    const int l = threadIdx.x, lane = lane_id(), wid = l >> 6;
+    const int nwu = (used + kWave - 1) / kWave;  // waves holding elements
+    // 3a. one list of every lane hull's vertices; each wave's lanes occupy a
+    // contiguous region that starts with the wave's first point
+    tile_compact<K, ABS>(t, mask, xs, ys);
+    const int w0 = wid * kWave, wend = min(w0 + kWave, used);
+    int base = 0, end = 0;
+    if (w0 < used) {
+        base = t.I[w0] - 1;
+        end = (wend < used) ? t.I[wend] : t.flag[1];
+    }
+    __syncthreads();  // every lane has read the block-wide indices
+    // 3b. rounds inside each wave (nodes of up to 64 lanes): node ends and
+    // bridges pass between lanes by shuffles, the list is re-compacted inside
+    // the wave's region
+    int r0 = t.I[l];
+    for (int h = 1; h < kWave; h <<= 1) {
+        if (w0 + h >= wend) break;  // wave-uniform
+        if (h > 1) {
+            const int pc = __popcll(mask);
+            const int incl = wave_incl_scan_int(pc);
+            r0 = base + 1 + incl - pc;
+            end = base + 1 + __shfl(incl, kWave - 1, kWave);
+            wave_sync();
+            write_vertices<K, ABS>(t, mask, r0, xs, ys);
+            wave_sync();
+        }
+        const int nm = (wend - w0 - h + 2 * h - 1) / (2 * h);
+        int G = kWave;
+        while (G > 1 && G * nm > kWave) G >>= 1;
+        const int k = lane / G, g = lane & (G - 1);
+        const int kk = (k < nm) ? k : 0;
+        const int a = kk * 2 * h;  // lane offsets inside the wave
+        const int lb = min(a + 2 * h, wend - w0);
+        const int iA0 = __shfl(r0, a, kWave) - 1;
+        const int iS = __shfl(r0, a + h, kWave) - 1;
+        const int rB = __shfl(r0, lb < kWave ? lb : 0, kWave);
+        const int iB1 = (w0 + lb < wend) ? rB - 1 : end - 1;
+        int2 ab = make_int2(0, 0);
+        if (k < nm) ab = group_bridge<K, ABS>(t, iA0, iS, iS, iB1, g, G);
+        const int km = (l < wend) ? (lane / (2 * h)) : nm;
+        const int src = (km < nm) ? km * G : 0;
+        const int2 mine = make_int2(__shfl(ab.x, src, kWave), __shfl(ab.y, src, kWave));
+        if (km < nm) clear_between<K>(mask, r0, mine);
+        wave_sync();
+    }
+    // the wave's node, compacted in its region
+    if (w0 < used && wend - w0 > 1) {
+        const int pc = __popcll(mask);
+        const int incl = wave_incl_scan_int(pc);
+        r0 = base + 1 + incl - pc;
+        end = base + 1 + __shfl(incl, kWave - 1, kWave);
+        wave_sync();
+        write_vertices<K, ABS>(t, mask, r0, xs, ys);
+    }
+    t.M[l] = mask;
+    if (lane == 0) t.W[wid] = end;
+    __syncthreads();
+    // 3c. one wave merges the waves' nodes left to right: the surviving
+    // suffix of the right node is copied behind the surviving prefix of the
+    // left one, and the vertices under each bridge are cleared from the masks
+    if (wid == 0 && nwu > 1) {
+        int len = t.W[0];
+        for (int w = 1; w < nwu; ++w) {
+            const int jS = t.I[w * kWave] - 1;  // wave w's first point (as block-compacted)
+            const int jB1 = t.W[w] - 1;
+            const int2 ab = group_bridge<K, ABS>(t, 0, len - 1, jS, jB1, lane, kWave);
+            const int al = ab.x;
+            const int be = (ab.y == jS) ? jS + 1 : ab.y;
+            // clear the points strictly under the bridge: A's entries after al
+            // (the shared point among them when it goes) and B's before be
+            const int nA = len - 1 - al, nB = be - (jS + 1);
+            for (int q = lane; q < nA + nB; q += kWave) {
+                const int idx = (q < nA) ? al + 1 + q : jS + 1 + (q - nA);
+                const int p = t.V[idx];
+                const int ln = (p - 1) / K;
+                atomicAnd((unsigned long long*)&t.M[ln], ~(1ull << ((p - 1) - ln * K)));
+            }
+            // copy B's surviving entries behind al (destination never after
+            // source: read a block of 64, then write it)
+            const int cnt = jB1 - be + 1;
+            for (int off = 0; off < cnt; off += kWave) {
+                const int q = off + lane;
+                unsigned short pv = 0;
+                double2 xy = make_double2(0.0, 0.0);
+                if (q < cnt) {
+                    pv = t.V[be + q];
+                    xy = t.VXY[be + q];
+                }
+                wave_sync();
+                if (q < cnt) {
+                    t.V[al + 1 + q] = pv;
+                    t.VXY[al + 1 + q] = xy;
+                }
+                wave_sync();
+            }
+            len = al + 1 + cnt;
+        }
+    }
+    __syncthreads();
+    mask = t.M[l];
+    // the final vertex list
+    tile_compact<K, ABS>(t, mask, xs, ys);
+}
+
+// ---------------------------------------------------------------------------
+// 4. expand (Sec. 3.4).  First the slope of every edge of the tile's hull is
+// written over the list (VXY[i].x = slope of the edge from entry i to i+1);
+// then every element takes the slope of the edge that starts at the last
+// vertex at or before its left point: for element lK + j that is list entry
+// I[l] - 1 + (number of lane l's vertices among its local points 1..j).
+// ---------------------------------------------------------------------------
+template <int K, bool ABS>
+__device__ inline void tile_edge_slopes(const Tile& t) {
+    const int nv = t.flag[1];
+    double sv[K + 1];
+#pragma unroll
+    for (int k = 0; k <= K; ++k) {
+        const int i = threadIdx.x + k * t.nl;
+        sv[k] = 0.0;
+        if (i < nv - 1) {
+            const double2 d = vdiff<K, ABS>(t, i, i + 1);
+            sv[k] = d.y / d.x;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k <= K; ++k) {
+        const int i = threadIdx.x + k * t.nl;
+        if (i < nv - 1) t.VXY[i].x = sv[k];
+    }
+    __syncthreads();
+}
+
+// Slopes of the calling lane's elements, oriented and clipped, into
+// vals[0..cnt); clip flags into clipm (bit j <-> element lK + j).
+template <int K>
+__device__ inline void tile_expand(const Tile& t, uint64_t mask, int increasing, double clo, double chi,
+                                   double (&vals)[K], uint64_t& clipm) {
+    const int l = threadIdx.x;
+    const int cnt = min(max(t.N - l * K, 0), K);
+    const int i0 = t.I[l] - 1;
+    clipm = 0ull;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        vals[j] = 0.0;
+        if (j < cnt) {
+            const double sl = t.VXY[i0 + __popcll(mask & bits_upto(j - 1))].x;
+            bool c;
+            vals[j] = finish(sl, increasing, clo, chi, c);
+            if (c) clipm |= 1ull << j;
+        }
+    }
+}
+
+// Block-start and clip bit words of the tile's elements (the tile starts at
+// a multiple of 64 elements).  Element i >= 1 starts a block iff point i is a
+// vertex; element 0 always does.  Lane masks are K bits wide (K divides 64):
+// concatenated, bit lK + b stands for point lK + b + 1.  Needs M and CM
+// written and a barrier.
+template <int K>
+__device__ inline void tile_bits(const Tile& t, uint64_t* __restrict__ sbits, uint64_t* __restrict__ cbits) {
+    constexpr int LPW = 64 / K;  // lanes per word
+    const int words = (t.N + 63) / 64;
+    for (int q = threadIdx.x; q < words; q += blockDim.x) {
+        uint64_t cm = 0ull, vm = 0ull;
+#pragma unroll
+        for (int k = 0; k < LPW; ++k) {
+            const int l = q * LPW + k;
+            if (l < t.nl) {
+                vm |= (t.M[l] & bits_upto(K - 1)) << (k * K);
+                cm |= (t.CM[l] & bits_upto(K - 1)) << (k * K);
+            }
+        }
+        const uint64_t carry = (q == 0) ? 1ull : ((t.M[q * LPW - 1] >> (K - 1)) & 1ull);
+        const uint64_t s = (vm << 1) | carry;
+        const int cnt = t.N - q * 64;
+        const uint64_t valid = (cnt >= 64) ? ~0ull : ((1ull << cnt) - 1ull);
+        sbits[q] = s & valid;
+        cbits[q] = cm & valid;
+    }
+}
+
+}  // namespace iso
