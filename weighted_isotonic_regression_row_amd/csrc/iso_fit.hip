@@ -9,11 +9,13 @@
 //                  set, group starts, the coordinates of its end vertices),
 //                  the chunk totals, and a tentative fit from the chunk's own
 //                  hull.
-//   k_merge_tree   one workgroup per long row: double-double chunk starts
+//   k_merge_sub    the lower levels of the merge tree on segment lists, at
+//                  most one segment per chunk (Sec. 3.3, Theorem 4.4): one
+//                  workgroup per subtree of 64 chunks;
+//   k_merge_top    one workgroup per long row: double-double chunk starts
 //                  (exclusive scan of the chunk totals, Sec. 3.3 and App. B),
-//                  then every level of the merge tree on segment lists, at most
-//                  one segment per chunk (Sec. 3.3, Theorem 4.4), then per-chunk
-//                  records of the root list (Sec. 3.4).
+//                  the upper levels, then per-chunk records of the root list
+//                  (Sec. 3.4).
 //   k_fixup        per chunk, rewrites only the elements that lie outside the
 //                  chunk's surviving segment (the edge rule after Theorem 4.4:
 //                  they lie under the edge entering or leaving the segment, or
@@ -258,8 +260,7 @@ __device__ inline double2 elem_wt(const HullView& H, int64_t e) {
 // then the bit) and its coordinates are summed from the nearer end of its
 // 256-element group.
 template <typename T>
-__device__ inline Vtx vtx(const HullView& H, int c, int r) {
-    const int nv = H.nv[c];
+__device__ inline Vtx vtx_n(const HullView& H, int c, int r, int nv) {
     int s = -1;
     if (nv <= kVMax || r < kVMax / 2)
         s = r;
@@ -316,18 +317,27 @@ __device__ inline Vtx vtx(const HullView& H, int c, int r) {
     return Vtx{p, v};
 }
 
+template <typename T>
+__device__ inline Vtx vtx(const HullView& H, int c, int r) {
+    return vtx_n<T>(H, c, r, H.nv[c]);
+}
+
 struct MergeArgs {
     const void* y;
     const void* w;
     int64_t n, m;
+    int nsub;     // subtrees of kSub chunks per row
     int negate;
-    HullView H0;  // row 0's pointers; offset per row in the kernel
+    HullView H0;  // row 0's pointers; offset per row in the kernels
     const int* cflag;
     double4* starts;
-    Desc* gd0;
+    Desc* gsd;    // [rows*m] each subtree's hull as a list, in the slots of its chunks
+    int* gsn;     // [rows*nsub] their lengths
+    Desc* gd0;    // [rows*m] top levels' lists when they do not fit in LDS
     Desc* gd1;
     int* gnc;
     MRec* gmr;
+    int* gnv;     // unused slot kept for layout symmetry
     double* gso;
     Rec* rec;
     uint32_t* row_nan;
@@ -343,9 +353,16 @@ struct PtD {
     double4 a;
 };
 
+// What a merge reads: the descriptors of the current level, the chunk starts
+// in the merge's frame (st[c - st_off]; a subtree uses starts relative to its
+// first chunk, as the hull of a node does not change under translation), and
+// the vertex counts (nvc[c - nv_off]).
 struct MCtx {
     const Desc* D;
     const double4* st;
+    int st_off;
+    const int* nvc;
+    int nv_off;
     HullView H;
 };
 
@@ -357,7 +374,7 @@ struct VR {
 template <typename T>
 __device__ __forceinline__ PtD ptd(const MCtx& X, int c, int k) {
     PtD p;
-    p.a = dd4_add(X.st[c], vtx<T>(X.H, c, k).v);
+    p.a = dd4_add(X.st[c - X.st_off], vtx_n<T>(X.H, c, k, X.nvc[c - X.nv_off]).v);
     return p;
 }
 template <typename T>
@@ -408,6 +425,42 @@ __device__ __forceinline__ bool vpred(const MCtx& X, VR v, int s0, VR& p) {
     }
     return false;
 }
+// the vertex g places before v in the list whose first slot is s0
+__device__ inline bool step_back(const MCtx& X, VR v, int s0, int g, VR& out) {
+    int s = v.s, k = v.k;
+    while (g > 0) {
+        const int avail = k - (int)X.D[s].l;
+        if (g <= avail) {
+            k -= g;
+            g = 0;
+        } else {
+            if (s == s0) return false;
+            g -= avail + 1;
+            --s;
+            k = X.D[s].h;
+        }
+    }
+    out = VR{s, k};
+    return true;
+}
+// the vertex g places after v in the list whose last slot is s1
+__device__ inline bool step_fwd(const MCtx& X, VR v, int s1, int g, VR& out) {
+    int s = v.s, k = v.k;
+    while (g > 0) {
+        const int avail = (int)X.D[s].h - k;
+        if (g <= avail) {
+            k += g;
+            g = 0;
+        } else {
+            if (s == s1) return false;
+            g -= avail + 1;
+            ++s;
+            k = X.D[s].l;
+        }
+    }
+    out = VR{s, k};
+    return true;
+}
 
 // First vertex of the view (slots s0..s1, last slot ending at lastH) for which
 // a monotone predicate (false ... false true ... true) holds; the view's last
@@ -452,13 +505,40 @@ __device__ inline VR tangent_b(const MCtx& X, const PtD& p, int jB, int sB1) {
     });
 }
 
-constexpr int kWalkCap = 48;
-
-// Bridge of the node at j0 (cntA slots) and its right neighbour at jB (cntB
-// slots) (Sec. 3.3, Lemma 4.2, Theorem 4.4), as the rewrite of the merged
-// list.  Reads the descriptors only.
+// The bridge by nested bisection (Sec. 3.3, Thm. 5.2): a candidate a of A is
+// tested against its tangent to B; a is left of the bridge while A's next
+// vertex lies strictly below the line from a to its tangent point.
+// Candidates end at the predecessor of the shared point.
 template <typename T>
-__device__ inline MRec find_merge(const MCtx& X, int j0, int jB, int cntA, int cntB) {
+__device__ inline void bisect_bridge(const MCtx& X, int j0, int la, int jB, int sB1, VR& al, VR& be) {
+    const Desc dA = X.D[la];
+    int aS1 = la, aLastH = (int)dA.h - 1;
+    if (aLastH < (int)dA.l) {
+        aS1 = la - 1;
+        aLastH = X.D[la - 1].h;
+    }
+    al = first_true(X, j0, aS1, aLastH, [&](VR a) -> bool {
+        VR an;
+        vsucc(X, a, la, an);
+        const PtD Pa = ptv<T>(X, a);
+        const VR b = tangent_b<T>(X, Pa, jB, sB1);
+        return !(turnD(Pa, ptv<T>(X, an), ptv<T>(X, b)) > 0.0);
+    });
+    be = tangent_b<T>(X, ptv<T>(X, al), jB, sB1);
+}
+
+// Window steps a merge may take before it switches to bisection.
+constexpr int kWindowSteps = 16;
+
+// Merge of the node at slots j0.. (cntA descriptors) with its right neighbour
+// at jB.. (cntB) by a group of G lanes (g = 0..G-1, G a power of two <= 64)
+// (Sec. 3.3, Lemma 4.2, Theorem 4.4).  From the neighbours of the shared
+// point the walk of Sec. 4 advances each side to its tangent point against
+// the other side's current end, G candidates per step; a walk longer than
+// kWindowSteps steps is finished by nested bisection.  Returns the rewrite of
+// the merged list; reads the descriptors only.
+template <typename T>
+__device__ inline MRec find_merge(const MCtx& X, int j0, int jB, int cntA, int cntB, int g, int G) {
     const Desc* D = X.D;
     const int la = j0 + cntA - 1;
     const int sB1 = jB + cntB - 1;
@@ -470,9 +550,9 @@ __device__ inline MRec find_merge(const MCtx& X, int j0, int jB, int cntA, int c
     VR pA, nB;
     vpred(X, sA, j0, pA);   // A has at least two vertices
     vsucc(X, sB, sB1, nB);  // and so has B
-    PtD PA = ptv<T>(X, pA), PS = ptv<T>(X, sB), PB = ptv<T>(X, nB);
     MRec r;
-    if (turnD(PA, PS, PB) > 0.0) {
+    PtD Pbe = ptv<T>(X, nB);
+    if (turnD(ptv<T>(X, pA), ptv<T>(X, sB), Pbe) > 0.0) {
         // convex at s: keep s once, in B's first segment
         if ((int)dA.h - 1 < (int)dA.l) {
             r.newA = cntA - 1;
@@ -486,48 +566,71 @@ __device__ inline MRec find_merge(const MCtx& X, int j0, int jB, int cntA, int c
         r.bek = dB.l;
         return r;
     }
-    // walk from the neighbours of s (Sec. 4, after Lemma 4.2), capped
+    const int gb = lane_id() & ~(G - 1);
     VR al = pA, be = nB;
-    bool done = false;
-    for (int step = 0; step < kWalkCap; ++step) {
-        VR pa, nb;
-        const bool canA = vpred(X, al, j0, pa);
-        const bool canB = vsucc(X, be, sB1, nb);
-        const PtD Pp = canA ? ptv<T>(X, pa) : PA;
-        const PtD Pn = canB ? ptv<T>(X, nb) : PB;
-        const bool mA = canA && !(turnD(Pp, PA, PB) > 0.0);
-        if (mA) {
-            al = pa;
-            PA = Pp;
+    int steps = 0;
+    bool ok = true;
+    for (;;) {
+        // left side against be: pass over a while it is not a strict vertex
+        // of {pred(a), a, be}
+        for (;;) {
+            VR c0 = al, c1 = al;
+            const bool v0 = step_back(X, al, j0, g, c0);
+            const bool v1 = v0 && step_back(X, c0, j0, 1, c1);
+            bool cont = false;
+            if (v1) cont = !(turnD(ptv<T>(X, c1), ptv<T>(X, c0), Pbe) > 0.0);
+            const int run = trailing_ones(group_bits(__ballot(cont), G));
+            const int step = run < G ? run : G;
+            const int src = gb + (step < G ? step : G - 1);
+            const int ts = __shfl(step < G ? c0.s : c1.s, src, kWave);
+            const int tk = __shfl(step < G ? c0.k : c1.k, src, kWave);
+            if (step > 0) al = VR{ts, tk};
+            if (step < G) break;
+            if (++steps > kWindowSteps) {
+                ok = false;
+                break;
+            }
         }
-        const bool mB = canB && !(turnD(PA, PB, Pn) > 0.0);
-        if (mB) {
-            be = nb;
-            PB = Pn;
+        if (!ok) break;
+        // right side against the new al
+        const PtD Pal = ptv<T>(X, al);
+        bool movedB = false;
+        for (;;) {
+            VR c0 = be, c1 = be;
+            const bool v0 = step_fwd(X, be, sB1, g, c0);
+            const bool v1 = v0 && step_fwd(X, c0, sB1, 1, c1);
+            bool cont = false;
+            if (v1) cont = !(turnD(Pal, ptv<T>(X, c0), ptv<T>(X, c1)) > 0.0);
+            const int run = trailing_ones(group_bits(__ballot(cont), G));
+            const int step = run < G ? run : G;
+            const int src = gb + (step < G ? step : G - 1);
+            const int ts = __shfl(step < G ? c0.s : c1.s, src, kWave);
+            const int tk = __shfl(step < G ? c0.k : c1.k, src, kWave);
+            if (step > 0) {
+                be = VR{ts, tk};
+                movedB = true;
+            }
+            if (step < G) break;
+            if (++steps > kWindowSteps) {
+                ok = false;
+                break;
+            }
         }
-        if (!mA && !mB) {
-            done = true;
-            break;
-        }
+        if (!ok || !movedB) break;
+        Pbe = ptv<T>(X, be);
     }
-    if (!done) {
-        // nested bisection (Sec. 3.3, Thm. 5.2): a candidate a of A is tested
-        // against its tangent to B; a is left of the bridge while A's next
-        // vertex lies strictly below the line from a to its tangent point.
-        // Candidates end at the predecessor of s.
-        int aS1 = la, aLastH = (int)dA.h - 1;
-        if (aLastH < (int)dA.l) {
-            aS1 = la - 1;
-            aLastH = D[la - 1].h;
+    if (!ok) {
+        int as = 0, ak = 0, bs = 0, bk = 0;
+        if (g == 0) {
+            VR a2, b2;
+            bisect_bridge<T>(X, j0, la, jB, sB1, a2, b2);
+            as = a2.s;
+            ak = a2.k;
+            bs = b2.s;
+            bk = b2.k;
         }
-        al = first_true(X, j0, aS1, aLastH, [&](VR a) -> bool {
-            VR an;
-            vsucc(X, a, la, an);
-            const PtD Pa = ptv<T>(X, a);
-            const VR b = tangent_b<T>(X, Pa, jB, sB1);
-            return !(turnD(Pa, ptv<T>(X, an), ptv<T>(X, b)) > 0.0);
-        });
-        be = tangent_b<T>(X, ptv<T>(X, al), jB, sB1);
+        al = VR{__shfl(as, gb, kWave), __shfl(ak, gb, kWave)};
+        be = VR{__shfl(bs, gb, kWave), __shfl(bk, gb, kWave)};
     }
     r.newA = al.s - j0 + 1;
     r.alk = al.k;
@@ -537,21 +640,136 @@ __device__ inline MRec find_merge(const MCtx& X, int j0, int jB, int cntA, int c
     return r;
 }
 
-constexpr int kMergeThreads = 1024;
-
-__host__ __device__ inline size_t merge_union_bytes(int64_t m) {
-    const size_t scan = sizeof(double4) * kMergeThreads;
-    const size_t mr = sizeof(MRec) * (size_t)(m / 2 + 1);
-    return (scan > mr ? scan : mr);
+// Rewrites every slot of the merged lists of one level into Dn (one thread per
+// slot), and the node lengths in NC.
+__device__ inline void rewrite_level(const Desc* Dc, Desc* Dn, int* NC, const MRec* MR, int m, int h, int nm) {
+    for (int j = threadIdx.x; j < m; j += blockDim.x) {
+        const int k = j / (2 * h);
+        if (k < nm) {
+            const int j0 = k * 2 * h;
+            const MRec r = MR[k];
+            const int pos = j - j0;
+            if (pos < r.newA) {
+                Desc d = Dc[j0 + pos];
+                if (pos == r.newA - 1) d.h = (unsigned short)r.alk;
+                Dn[j] = d;
+            } else if (pos < r.newA + r.nBk) {
+                Desc d = Dc[r.bs + pos - r.newA];
+                if (pos == r.newA) d.l = (unsigned short)r.bek;
+                Dn[j] = d;
+            }
+            if (pos == 0) NC[j0] = r.newA + r.nBk;
+        } else {
+            Dn[j] = Dc[j];
+        }
+    }
 }
-__host__ __device__ inline size_t merge_smem_bytes(int64_t m, int use_lds) {
-    size_t b = merge_union_bytes(m) + 16;
-    if (use_lds) b += (2 * sizeof(Desc) + sizeof(int)) * (size_t)m;
+
+__device__ inline HullView row_view(const MergeArgs& a, int64_t row) {
+    const int64_t base = row * a.m;
+    HullView H = a.H0;
+    H.nv += base;
+    H.tot += base;
+    H.mask += base * kMaskWords;
+    H.pre += base * kMaskWords;
+    H.gs += base * kGroups;
+    H.vx += base * kVMax;
+    H.vi += base * kVMax;
+    return H;
+}
+
+constexpr int kMergeThreads = 512;
+
+// Lower levels of the merge tree: one workgroup per subtree of kSub chunks,
+// in coordinates relative to the subtree's first chunk.  Writes the
+// subtree's hull as a list of at most kSub segments.
+template <typename T>
+__global__ __launch_bounds__(kMergeThreads) void k_merge_sub(MergeArgs a) {
+    __shared__ Desc D0[kSub], D1[kSub];
+    __shared__ int NC[kSub], nvl[kSub];
+    __shared__ MRec MR[kSub / 2];
+    __shared__ double4 stl[kSub];
+    __shared__ int sflag;
+    const int64_t row = blockIdx.x / a.nsub;
+    const int sub = (int)(blockIdx.x % a.nsub);
+    const int m = (int)a.m;
+    const int c0 = sub * kSub, ms = min(kSub, m - c0);
+    const int64_t base = row * a.m;
+    const int tid = threadIdx.x;
+    if (tid == 0) sflag = 0;
+    __syncthreads();
+    if (tid < ms && a.cflag[base + c0 + tid]) atomicOr(&sflag, 1);
+    __syncthreads();
+    if (sflag) return;  // a NaN or a bad weight: k_merge_top writes the row's records
+    HullView H = row_view(a, row);
+    H.y = (const char*)a.y + row * a.n * (int64_t)sizeof(T);
+    H.w = a.w ? (const void*)((const char*)a.w + row * a.n * (int64_t)sizeof(T)) : nullptr;
+    if (tid < kWave) {
+        double4 v = (tid < ms) ? H.tot[c0 + tid] : make_double4(0.0, 0.0, 0.0, 0.0);
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const double4 o = shfl_up4(v, d);
+            if (tid >= d) v = dd4_add(o, v);
+        }
+        double4 ex = shfl_up4(v, 1);
+        if (tid == 0) ex = make_double4(0.0, 0.0, 0.0, 0.0);
+        if (tid < ms) {
+            const int nv = H.nv[c0 + tid];
+            stl[tid] = ex;
+            nvl[tid] = nv;
+            Desc dsc;
+            dsc.c = c0 + tid;
+            dsc.l = 0;
+            dsc.h = (unsigned short)(nv - 1);
+            D0[tid] = dsc;
+            NC[tid] = 1;
+        }
+    }
+    __syncthreads();
+    MCtx X;
+    X.st = stl;
+    X.st_off = c0;
+    X.nvc = nvl;
+    X.nv_off = c0;
+    X.H = H;
+    Desc* Dc = D0;
+    Desc* Dn = D1;
+    for (int h = 1; h < ms; h <<= 1) {
+        const int nm = (ms - h + 2 * h - 1) / (2 * h);
+        int G = kWave;
+        while (G > 1 && G * nm > (int)blockDim.x) G >>= 1;
+        const int k = tid / G, g = tid & (G - 1);
+        X.D = Dc;
+        if (k < nm) {
+            const int j0 = k * 2 * h;
+            const MRec r = find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h], g, G);
+            if (g == 0) MR[k] = r;
+        }
+        __syncthreads();
+        rewrite_level(Dc, Dn, NC, MR, ms, h, nm);
+        __syncthreads();
+        Desc* t = Dc;
+        Dc = Dn;
+        Dn = t;
+    }
+    const int cnt = NC[0];
+    for (int i = tid; i < cnt; i += blockDim.x) a.gsd[base + c0 + i] = Dc[i];
+    if (tid == 0) a.gsn[row * a.nsub + sub] = cnt;
+}
+
+__host__ __device__ inline size_t merge_top_smem_bytes(int64_t m, int use_lds) {
+    const size_t scan = sizeof(double4) * kMergeThreads;
+    const size_t mr = sizeof(MRec) * (size_t)(m / (2 * kSub) + 1);
+    size_t b = (scan > mr ? scan : mr) + 16;
+    if (use_lds) b += (2 * sizeof(Desc) + 2 * sizeof(int)) * (size_t)m;
     return b;
 }
 
+// Upper levels of the merge tree of one long row: double-double chunk starts
+// (exclusive scan of the chunk totals, Sec. 3.3 and App. B), the levels above
+// the subtrees, then per-chunk records of the root list (Sec. 3.4).
 template <typename T>
-__global__ __launch_bounds__(kMergeThreads) void k_merge_tree(MergeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void k_merge_top(MergeArgs a) {
     extern __shared__ __align__(32) char smem[];
     const int64_t row = blockIdx.x;
     const int m = (int)a.m;
@@ -561,22 +779,32 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_tree(MergeArgs a) {
     char* p = smem;
     double4* sbuf = (double4*)p;  // the scan's partial sums, then the merge records
     MRec* MR = (MRec*)p;
-    p += merge_union_bytes(m);
+    {
+        const size_t scan = sizeof(double4) * kMergeThreads;
+        const size_t mr = sizeof(MRec) * (size_t)(m / (2 * kSub) + 1);
+        p += (scan > mr ? scan : mr);
+    }
     int* sflag = (int*)p;
     p += 16;
+    HullView H = row_view(a, row);
+    H.y = (const char*)a.y + row * a.n * (int64_t)sizeof(T);
+    H.w = a.w ? (const void*)((const char*)a.w + row * a.n * (int64_t)sizeof(T)) : nullptr;
     Desc *Dc, *Dn;
-    int* NC;
+    int *NC, *nvl;
     if (a.use_lds) {
         Dc = (Desc*)p;
         p += sizeof(Desc) * (size_t)m;
         Dn = (Desc*)p;
         p += sizeof(Desc) * (size_t)m;
         NC = (int*)p;
+        p += sizeof(int) * (size_t)m;
+        nvl = (int*)p;
     } else {
         Dc = a.gd0 + base;
         Dn = a.gd1 + base;
         NC = a.gnc + base;
         MR = a.gmr + base;
+        nvl = nullptr;
     }
     Rec* rec = a.rec + base;
 
@@ -601,17 +829,6 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_tree(MergeArgs a) {
         return;
     }
 
-    HullView H = a.H0;
-    H.nv += base;
-    H.tot += base;
-    H.mask += base * kMaskWords;
-    H.pre += base * kMaskWords;
-    H.gs += base * kGroups;
-    H.vx += base * kVMax;
-    H.vi += base * kVMax;
-    H.y = (const char*)a.y + row * a.n * (int64_t)sizeof(T);
-    H.w = a.w ? (const void*)((const char*)a.w + row * a.n * (int64_t)sizeof(T)) : nullptr;
-
     // 2. chunk starts: exclusive double-double scan of the chunk totals
     const int per = (m + NT - 1) / NT;
     const int c0 = min(m, tid * per), c1 = min(m, c0 + per);
@@ -634,58 +851,42 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_tree(MergeArgs a) {
         a.starts[base + c] = ex;
         ex = dd4_add(ex, H.tot[c]);
     }
-    // 3. leaves: one segment per chunk, its whole hull
+    // 3. the subtrees' lists, one node per subtree at its first chunk's slot
     for (int c = tid; c < m; c += NT) {
-        Desc d;
-        d.c = c;
-        d.l = 0;
-        d.h = (unsigned short)(H.nv[c] - 1);
-        Dc[c] = d;
-        NC[c] = 1;
+        const int sub = c / kSub;
+        const int cnt = a.gsn[row * a.nsub + sub];
+        if (c - sub * kSub < cnt) Dc[c] = a.gsd[base + c];
+        if (c == sub * kSub) NC[c] = cnt;
+        if (nvl) nvl[c] = H.nv[c];
     }
     __threadfence();
     __syncthreads();
 
     MCtx X;
     X.st = a.starts + base;
+    X.st_off = 0;
+    X.nvc = nvl ? nvl : H.nv;
+    X.nv_off = 0;
     X.H = H;
 
-    // 4. merge levels: the bridges of a level (one thread per merge), then
-    // every slot of the merged lists rewritten into the other buffer
-    for (int h = 1; h < m; h <<= 1) {
+    // 4. the upper levels, one wave per merge
+    const int nw = NT / kWave, wid = tid / kWave, g = lane_id();
+    for (int h = kSub; h < m; h <<= 1) {
         const int nm = (m - h + 2 * h - 1) / (2 * h);
         X.D = Dc;
-        for (int k = tid; k < nm; k += NT) {
+        for (int k = wid; k < nm; k += nw) {
             const int j0 = k * 2 * h;
-            MR[k] = find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h]);
+            const MRec r = find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h], g, kWave);
+            if (g == 0) MR[k] = r;
         }
         __threadfence_block();
         __syncthreads();
-        for (int j = tid; j < m; j += NT) {
-            const int k = j / (2 * h);
-            if (k < nm) {
-                const int j0 = k * 2 * h;
-                const MRec r = MR[k];
-                const int pos = j - j0;
-                if (pos < r.newA) {
-                    Desc d = Dc[j0 + pos];
-                    if (pos == r.newA - 1) d.h = (unsigned short)r.alk;
-                    Dn[j] = d;
-                } else if (pos < r.newA + r.nBk) {
-                    Desc d = Dc[r.bs + pos - r.newA];
-                    if (pos == r.newA) d.l = (unsigned short)r.bek;
-                    Dn[j] = d;
-                }
-                if (pos == 0) NC[j0] = r.newA + r.nBk;
-            } else {
-                Dn[j] = Dc[j];
-            }
-        }
+        rewrite_level(Dc, Dn, NC, MR, m, h, nm);
         __threadfence_block();
         __syncthreads();
-        Desc* tmp = Dc;
+        Desc* t = Dc;
         Dc = Dn;
-        Dn = tmp;
+        Dn = t;
     }
     X.D = Dc;
 
@@ -711,9 +912,10 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_tree(MergeArgs a) {
         const Desc d = Dc[lo];
         Rec r{};
         if (d.c == c) {
+            const int nv = X.nvc[c];
             r.mode = 0;
-            r.lo = vtx<T>(H, c, d.l).p;
-            r.hi = vtx<T>(H, c, d.h).p;
+            r.lo = vtx_n<T>(H, c, d.l, nv).p;
+            r.hi = vtx_n<T>(H, c, d.h, nv).p;
             r.sin = (lo > 0) ? so[lo - 1] : 0.0;
             r.sout = (lo < K - 1) ? so[lo] : 0.0;
         } else {
@@ -890,29 +1092,38 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
     ma.w = a.w;
     ma.n = a.n;
     ma.m = m;
+    ma.nsub = (int)((m + kSub - 1) / kSub);
     ma.negate = !a.increasing;
     ma.H0 = HullView{ca.nv, ca.tot, ca.cmask, ca.cpre, ca.cgs, ca.cvx, ca.cvi, nullptr, nullptr, !a.increasing, a.n};
     ma.cflag = ca.cflag;
     ma.starts = (double4*)(a.ws + a.L.starts);
+    ma.gsd = (Desc*)(a.ws + a.L.gsd);
+    ma.gsn = (int*)(a.ws + a.L.gsn);
     ma.gd0 = (Desc*)(a.ws + a.L.desc0);
     ma.gd1 = (Desc*)(a.ws + a.L.desc1);
     ma.gnc = (int*)(a.ws + a.L.nc);
     ma.gmr = (MRec*)(a.ws + a.L.mrec);
+    ma.gnv = nullptr;
     ma.gso = (double*)(a.ws + a.L.so);
     ma.rec = (Rec*)(a.ws + a.L.rec);
     ma.row_nan = a.row_nan;
     ma.status = status;
     ma.epoch = a.epoch;
     ma.use_lds = (m <= kMergeLdsChunks) ? 1 : 0;
+    hipLaunchKernelGGL(k_merge_sub<T>, dim3((unsigned)(a.rows * ma.nsub)), dim3(kMergeThreads), 0, a.stream, ma);
+    {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     {
         static bool attr_set = false;
         if (!attr_set) {
-            (void)hipFuncSetAttribute((const void*)k_merge_tree<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      (int)merge_smem_bytes(kMergeLdsChunks, 1));
+            (void)hipFuncSetAttribute((const void*)k_merge_top<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)merge_top_smem_bytes(kMergeLdsChunks, 1));
             attr_set = true;
         }
-        hipLaunchKernelGGL(k_merge_tree<T>, dim3((unsigned)a.rows), dim3(kMergeThreads),
-                           merge_smem_bytes(m, ma.use_lds), a.stream, ma);
+        hipLaunchKernelGGL(k_merge_top<T>, dim3((unsigned)a.rows), dim3(kMergeThreads),
+                           merge_top_smem_bytes(m, ma.use_lds), a.stream, ma);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

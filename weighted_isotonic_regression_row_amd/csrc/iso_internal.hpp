@@ -27,12 +27,14 @@ constexpr int kMaskWords = kChunk / 64;
 constexpr int kGroup = 256;
 constexpr int kGroups = kChunk / kGroup;
 //   the coordinates of the first and last kVMax/2 vertices (of all of them
-//   when the hull has at most kVMax), which cover the merges of dense hulls,
-//   whose bridges sit at or next to the shared points.
-constexpr int kVMax = 16;
+//   when the hull has at most kVMax), which cover the walks of the merges,
+//   as those start at the shared points.
+constexpr int kVMax = 256;
 // LDS a row workgroup aims for (three per CU), and the vertex list of a row
 // that does not fit it lives in the workspace.
 constexpr long kRowLdsTarget = 54000;
+// The lower levels of the merge tree run on subtrees of this many chunks.
+constexpr int kSub = 64;
 // Segment descriptors of a row are kept in LDS up to this many chunks.
 constexpr int64_t kMergeLdsChunks = 4096;
 // Elements per tile of the backward pass on long rows.
@@ -70,7 +72,9 @@ struct Layout {
     size_t cflag;        // int [rows*m]
     size_t starts;       // double4 [rows*m]
     size_t rec;          // Rec [rows*m]
-    size_t desc0, desc1; // Desc [rows*m] (merge levels ping-pong between them)
+    size_t desc0, desc1; // Desc [rows*m] (upper merge levels ping-pong between them)
+    size_t gsd;          // Desc [rows*m] the subtrees' lists
+    size_t gsn;          // int [rows*ceil(m/kSub)]
     size_t nc;           // int [rows*m]
     size_t mrec;         // MRec [rows*m]
     size_t so;           // double [rows*m]
@@ -108,6 +112,8 @@ inline Layout make_layout(int64_t rows, int64_t n) {
     L.rec = take(sizeof(Rec) * rm);
     L.desc0 = take(sizeof(Desc) * rm);
     L.desc1 = take(sizeof(Desc) * rm);
+    L.gsd = take(sizeof(Desc) * rm);
+    L.gsn = take(4 * (size_t)rows * (size_t)((L.m + kSub - 1) / kSub));
     L.nc = take(4 * rm);
     L.mrec = take(sizeof(MRec) * rm);
     L.so = take(8 * rm);
