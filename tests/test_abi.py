@@ -59,9 +59,9 @@ def test_sizes(lib):
     assert lib.iso_workspace_bytes(1000, 5000, 0) >= 256
     small = lib.iso_workspace_bytes(1000, 5000, 0)
     big = lib.iso_workspace_bytes(32, 1 << 22, 1)
-    # chunk hulls of long rows live in the workspace, stored compactly: a few
-    # bytes per element, far below the 16-byte (x, y) of every point
-    assert 32 * (1 << 22) * 0.25 < big < 32 * (1 << 22) * 4
+    # chunk hulls of long rows live in the workspace: a vertex bit set, group
+    # starts and up to 1024 explicit vertices per chunk of 3584 elements
+    assert 32 * (1 << 22) * 0.25 < big < 32 * (1 << 22) * 12
     # single-workgroup rows: room for each row's vertex list in case its lane
     # hulls do not fit in LDS (18 bytes per point)
     assert 1000 * 5001 * 18 <= small < 1000 * 5001 * 19

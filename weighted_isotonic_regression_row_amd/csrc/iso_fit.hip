@@ -189,15 +189,15 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
     const int l = threadIdx.x;
     const int nv = t.flag[1];  // vertices of the chunk hull; rank r is list entry r
     // explicit coordinates (relative to the chunk start) of the end windows,
-    // or of every vertex of a small hull
-    if (l < kVMax) {
-        const int r = (nv <= kVMax || l < kVMax / 2) ? l : nv - kVMax + l;
+    // or of every vertex of a hull of at most kVMax vertices
+    for (int q = l; q < kVMax; q += blockDim.x) {
+        const int r = (nv <= kVMax || q < kVMax / 2) ? q : nv - kVMax + q;
         if (r < nv) {
             const int p = t.V[r];
-            const double2 q = t.VXY[r];
-            a.cvi[bid * kVMax + l] = p;
-            a.cvx[bid * kVMax + l] = (sizeof(T) == 4) ? make_double4(q.x, 0.0, q.y, 0.0)
-                                                      : dd4_add_d(t.LS[lane_of<K>(p)], q);
+            const double2 c = t.VXY[r];
+            a.cvi[bid * kVMax + q] = p;
+            a.cvx[bid * kVMax + q] = (sizeof(T) == 4) ? make_double4(c.x, 0.0, c.y, 0.0)
+                                                      : dd4_add_d(t.LS[lane_of<K>(p)], c);
         }
     }
     // vertex bit set and the rank of each word's first vertex
@@ -528,7 +528,7 @@ __device__ inline void bisect_bridge(const MCtx& X, int j0, int la, int jB, int 
 }
 
 // Window steps a merge may take before it switches to bisection.
-constexpr int kWindowSteps = 16;
+constexpr int kWindowSteps = 64;
 
 // Merge of the node at slots j0.. (cntA descriptors) with its right neighbour
 // at jB.. (cntB) by a group of G lanes (g = 0..G-1, G a power of two <= 64)
@@ -734,15 +734,13 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_sub(MergeArgs a) {
     X.H = H;
     Desc* Dc = D0;
     Desc* Dn = D1;
+    const int nwv = blockDim.x / kWave, wid = tid / kWave, g = lane_id();
     for (int h = 1; h < ms; h <<= 1) {
         const int nm = (ms - h + 2 * h - 1) / (2 * h);
-        int G = kWave;
-        while (G > 1 && G * nm > (int)blockDim.x) G >>= 1;
-        const int k = tid / G, g = tid & (G - 1);
         X.D = Dc;
-        if (k < nm) {
+        for (int k = wid; k < nm; k += nwv) {
             const int j0 = k * 2 * h;
-            const MRec r = find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h], g, G);
+            const MRec r = find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h], g, kWave);
             if (g == 0) MR[k] = r;
         }
         __syncthreads();

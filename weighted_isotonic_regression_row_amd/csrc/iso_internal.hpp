@@ -29,7 +29,7 @@ constexpr int kGroups = kChunk / kGroup;
 //   the coordinates of the first and last kVMax/2 vertices (of all of them
 //   when the hull has at most kVMax), which cover the walks of the merges,
 //   as those start at the shared points.
-constexpr int kVMax = 256;
+constexpr int kVMax = 1024;
 // LDS a row workgroup aims for (three per CU), and the vertex list of a row
 // that does not fit it lives in the workspace.
 constexpr long kRowLdsTarget = 54000;
