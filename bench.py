@@ -1,27 +1,35 @@
 """Benchmark of the batched weighted isotonic fit on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batch|dense|both]
-                    [--no-cpu] [--copy-probe]
+                    [--no-cpu] [--copy-probe] [--cpu-seconds S]
 
 A step is one whole fit (every kernel of the path) over one batch of
 synthetic input already resident in HBM:
 
-  batch: 1000 rows x 5000 float32, y ~ N(0,1), w ~ U(0.1, 1.1), non-increasing,
-         clipped to [0, 1] (the headline line: `value` is its elements/s);
+  batch (the headline line; `value` is its elements/s):
+         1000 rows x 5000 float32, y ~ N(0,1), w ~ U(0.1, 1.1), non-increasing,
+         clipped to [0, 1]; one launch of k_row_fit;
   dense: 32 rows x 2^22 float64, y_i = i/n with 1% of positions pushed down by
-         |N(0, 0.01)|, w ~ U(0.5, 1.5), increasing (reported in "dense").
+         |N(0, 0.01)|, w ~ U(0.5, 1.5), increasing; k_chunk_hull, k_merge_sub,
+         k_merge_top, k_fixup (reported in "dense").
 
-Prints ONE JSON line.  Algorithmic bytes are y + w read once and the fit
+Prints ONE JSON line.  Algorithmic bytes are y and w read once and the fit
 written once (12 B/element for the batch, 24 B/element for the dense rows);
 "% of HBM peak" divides them by the measured time and 8 TB/s.  The roofline
-object times the dominant kernel with HIP events on the launch stream.  The
-CPU baseline is the float64 oracle on the host cores, on a bounded sample.
+object times the batch's kernel with HIP events on the stream it is launched
+on.  Its `traffic` is the HBM bytes per launch that rocprofv3 counted
+(FETCH_SIZE and WRITE_SIZE, scaled against a plain copy of known size), read
+from the committed summary under profiles/ and reported only while the kernel
+sources are the ones that summary was taken from.  The CPU baseline is the
+float64 oracle on the host cores, on a bounded sample.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -32,10 +40,39 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+METRIC = "fit elements/s and % of HBM peak, 1000×5000 f32 and 32×2^22 f64 dense"
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_row_fit_1000x5000_f32.md")
+CSRC = os.path.join(ROOT, "weighted_isotonic_regression_row_amd", "csrc")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    """Hash of the HIP sources and the C ABI header (what the counters depend on)."""
+    h = hashlib.sha256()
+    files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp", ".cpp")))
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    with open(os.path.join(ROOT, "include", "iso.h"), "rb") as fh:
+        h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic():
+    """HBM bytes per launch of k_row_fit from the committed counter summary, if
+    it was taken from the current sources; else None."""
+    try:
+        text = open(TRAFFIC_SUMMARY).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"source hash:\s*([0-9a-f]+)", text)
+    m_bytes = re.search(r"traffic bytes per launch:\s*([0-9]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash():
+        return None
+    return int(m_bytes.group(1))
 
 
 def make_inputs(which):
@@ -46,7 +83,8 @@ def make_inputs(which):
 
 
 def time_gpu(wl, steps, warmup):
-    """Returns (ms_per_step from the wall clock, per-launch kernel ms from HIP events)."""
+    """Returns (ms_per_step from the wall clock, mean and median per-step ms from
+    HIP events recorded on the launch stream)."""
     import torch
     import weighted_isotonic_regression_row_amd as iso
     dev = torch.device("cuda:0")
@@ -54,12 +92,12 @@ def time_gpu(wl, steps, warmup):
     w = None if wl.w is None else torch.from_numpy(wl.w).to(dev)
     out = torch.empty_like(y)
     ws = iso.workspace(wl.rows, wl.n, y.dtype, dev)
-    # one correctness-free warm call with the status check (raises on bad weights)
+    # one call with the status check (raises on bad weights)
     iso.iso_fit(y, w, wl.increasing, wl.y_min, wl.y_max, out=out, ws=ws, blocks=False, check=True)
     for _ in range(warmup):
         iso.iso_fit(y, w, wl.increasing, wl.y_min, wl.y_max, out=out, ws=ws, blocks=False, check=False)
     torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
+    stream = torch.cuda.current_stream(dev)  # the library launches on this stream
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     t0 = time.perf_counter()
     for k in range(steps):
@@ -69,7 +107,7 @@ def time_gpu(wl, steps, warmup):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     per = [a.elapsed_time(b) for a, b in ev]
-    return (t1 - t0) * 1e3 / steps, float(np.mean(per)), float(np.median(per)), out
+    return (t1 - t0) * 1e3 / steps, float(np.mean(per)), float(np.median(per))
 
 
 def copy_probe(nbytes=256 << 20, reps=20):
@@ -96,13 +134,12 @@ def cpu_baseline(wl, seconds=10.0, max_rows=None):
     import oracle
     threads = min(os.cpu_count() or 1, 16)
     rows = wl.rows if max_rows is None else min(wl.rows, max_rows)
-    if wl.rows == 1:
-        threads = 1  # one row is sequential in pool adjacent violators
+    threads = min(threads, rows)  # rows are split over threads; one row is sequential
     y = wl.y[:rows].astype(np.float64)
     w = None if wl.w is None else wl.w[:rows].astype(np.float64)
     elems = 0
-    t0 = time.perf_counter()
     reps = 0
+    t0 = time.perf_counter()
     while True:
         oracle.fit(y, w, wl.increasing, wl.y_min, wl.y_max, threads=threads)
         elems += rows * wl.n
@@ -111,7 +148,8 @@ def cpu_baseline(wl, seconds=10.0, max_rows=None):
             break
     dt = time.perf_counter() - t0
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} of {wl.rows} rows x {wl.n}, float64 PAVA, {reps} repetitions in {dt:.1f} s"}
+            "sample": f"{rows} of {wl.rows} rows x {wl.n}, float64 pool adjacent violators, "
+                      f"{threads} threads, {reps} repetitions in {dt:.1f} s"}
 
 
 def main():
@@ -125,38 +163,40 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only: --gpus must be 1; rows shard trivially "
-                                   "across GPUs, see the design notes"}))
+        print(json.dumps({"error": "this build runs on one GPU only (--gpus 1); rows are independent and would "
+                                   "shard across GPUs with no exchange"}), flush=True)
         sys.exit(2)
 
     import torch
     if not torch.cuda.is_available():
-        print(json.dumps({"error": "no GPU visible"}))
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
         sys.exit(1)
     import weighted_isotonic_regression_row_amd as iso
     iso.load_library()
 
-    rec = {"metric": "fit elements/s and % of HBM peak (1000x5000 f32; 32x2^22 f64 dense)",
-           "value": None, "unit": "elements/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-           "ms_per_step": None, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-           "dtype": "f64", "data": "synthetic"}
+    rec = {"metric": METRIC, "value": None, "unit": "elements/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f64", "data": "synthetic"}
 
     if args.workload in ("batch", "both"):
         wl = make_inputs("batch")
         log(f"batch: {wl.name} {wl.y.shape}")
-        ms, kmean, kmed, _ = time_gpu(wl, args.steps, args.warmup)
+        ms, kmean, kmed = time_gpu(wl, args.steps, args.warmup)
         elems = wl.rows * wl.n
         algo = elems * (4 + 4 + 4)
         rec["value"] = elems / (ms * 1e-3)
         rec["ms_per_step"] = ms
-        rec["config"] = {"workload": "1000x5000 float32, N(0,1), w~U(0.1,1.1), non-increasing, clip [0,1]",
-                         "rows": wl.rows, "n": wl.n, "in_dtype": "f32", "accumulate": "f64",
-                         "algorithmic_bytes": algo, "hbm_frac_end_to_end": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        rec["config"] = {"workload": "1000 rows x 5000 float32, y~N(0,1), w~U(0.1,1.1), non-increasing, "
+                                     "clipped to [0,1]",
+                         "rows": wl.rows, "n": wl.n, "input_dtype": "f32", "accumulation": "f64",
+                         "algorithmic_bytes": algo,
+                         "hbm_frac_end_to_end": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         ach = algo / (kmean * 1e-3) / 1e9
-        rec["roofline"] = {"bound": "hbm", "kernel": "k_row_fit<float>", "achieved": ach, "peak": HBM_PEAK_GBS,
-                           "unit": "GB/s", "frac": ach / HBM_PEAK_GBS, "traffic": None,
-                           "kernel_ms_mean": kmean, "kernel_ms_median": kmed,
-                           "bytes_per_element": 12, "elements_per_launch": elems}
+        rec["roofline"] = {"bound": "hbm", "kernel": "k_row_fit<float,16>", "achieved": ach,
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                           "traffic": committed_traffic(), "kernel_ms_mean": kmean, "kernel_ms_median": kmed,
+                           "bytes_per_element": 12, "elements_per_launch": elems,
+                           "source_hash": source_hash()}
         if not args.no_cpu:
             log("cpu baseline (batch) ...")
             rec["cpu_baseline"] = cpu_baseline(wl, seconds=args.cpu_seconds)
@@ -165,12 +205,14 @@ def main():
     if args.workload in ("dense", "both"):
         wl = make_inputs("dense")
         log(f"dense: {wl.name} {wl.y.shape}")
-        steps = max(1, min(args.steps, 20))
-        ms, kmean, kmed, _ = time_gpu(wl, steps, min(args.warmup, 3))
+        steps = max(1, min(args.steps, 10))
+        ms, kmean, kmed = time_gpu(wl, steps, min(args.warmup, 2))
         elems = wl.rows * wl.n
         algo = elems * 24
-        dense = {"workload": "32x2^22 float64 dense hulls, w~U(0.5,1.5), increasing", "steps": steps,
-                 "ms_per_step": ms, "elements_per_s": elems / (ms * 1e-3), "algorithmic_bytes": algo,
+        dense = {"workload": "32 rows x 2^22 float64, y_i = i/n with 1% pushed down by |N(0,0.01)|, "
+                             "w~U(0.5,1.5), increasing",
+                 "steps": steps, "ms_per_step": ms, "fit_ms_events_mean": kmean,
+                 "elements_per_s": elems / (ms * 1e-3), "algorithmic_bytes": algo,
                  "hbm_frac_end_to_end": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         if not args.no_cpu:
             log("cpu baseline (dense, 2 rows) ...")
