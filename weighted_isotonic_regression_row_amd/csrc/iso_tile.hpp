@@ -54,7 +54,7 @@ struct Tile {
     uint64_t* CM;       // [nl] lane clip masks
     int* I;             // [nl] index in V of each lane's first vertex
     int2* MR;           // [nl / 2 + 1] bridge (alpha, beta) points of the merges of a round
-    int* W;             // [16] per-wave partial sums
+    int* W;             // [32] per-wave scratch
     int* flag;          // [4]
     int nl;             // lanes (= threads of the workgroup)
     int N;              // elements
@@ -70,8 +70,8 @@ __host__ __device__ inline size_t tile_list_len(int nl, int cap, int K) {
 __host__ __device__ inline size_t tile_smem_bytes(int nl, int cap, int K) {
     const size_t n = tile_list_len(nl, cap, K);
     const size_t v = (2 * n + 15) & ~(size_t)15;
-    return v + 16 * n + 32 * (size_t)(nl + 1) + 16 * (size_t)nl + 4 * (size_t)nl + 8 * (size_t)(nl / 2 + 1) + 64 + 16 +
-           128;
+    return v + 16 * n + 32 * (size_t)(nl + 1) + 16 * (size_t)nl + 4 * (size_t)nl + 8 * (size_t)(nl / 2 + 1) + 128 +
+           16 + 128;
 }
 
 __device__ inline Tile tile_carve(char* base, int nl, int cap, int K, int N) {
@@ -91,7 +91,7 @@ __device__ inline Tile tile_carve(char* base, int nl, int cap, int K, int N) {
     t.I = (int*)p;
     p += 4 * (size_t)nl;
     t.W = (int*)p;
-    p += 64;
+    p += 128;
     t.flag = (int*)p;
     p += 16;
     t.V = (unsigned short*)p;
@@ -409,152 +409,116 @@ __device__ inline int2 group_bridge(const Tile& t, int iA0, int iS, int jS, int 
     return make_int2(al, be);
 }
 
-// Writes the calling lane's vertices at list indices r, r+1, ...
+// Copies list entries [s0, s1] to d0.. (d0 <= s0) with the calling group of G
+// lanes, a block of G entries at a time, each block read before it is written
+// (a destination never lies after its source, so no unread entry is hit).
+__device__ inline void group_move(const Tile& t, int s0, int s1, int d0, int g, int G) {
+    const int cnt = s1 - s0 + 1;
+    if (d0 == s0 || cnt <= 0) return;  // uniform in the group
+    for (int off = 0; off < cnt; off += G) {
+        const int q = off + g;
+        unsigned short pv = 0;
+        double2 xy = make_double2(0.0, 0.0);
+        if (q < cnt) {
+            pv = t.V[s0 + q];
+            xy = t.VXY[s0 + q];
+        }
+        wave_sync();
+        if (q < cnt) {
+            t.V[d0 + q] = pv;
+            t.VXY[d0 + q] = xy;
+        }
+        wave_sync();
+    }
+}
+
+// Merges the nodes A = entries [a0, a1] and B = [b0, b1] (a1 and b0 hold the
+// same point) with the calling group: the bridge, then B's surviving suffix is
+// copied behind A's surviving prefix.  Returns the merged node's last index
+// (it starts at a0).
 template <int K, bool ABS>
-__device__ __forceinline__ void write_vertices(const Tile& t, uint64_t mask, int r, const double (&xs)[K],
-                                               const double (&ys)[K]) {
-    double sx = 0.0, sy = 0.0;
-    if (ABS) {
-        const double4 s = t.LS[threadIdx.x];
-        sx = s.x;
-        sy = s.z;
+__device__ inline int group_merge(const Tile& t, int a0, int a1, int b0, int b1, int g, int G) {
+    const int2 ab = group_bridge<K, ABS>(t, a0, a1, b0, b1, g, G);
+    int al = ab.x, be = ab.y;
+    if (be == b0) {
+        // convex at the shared point: keep A's copy of it
+        al = a1;
+        be = b0 + 1;
     }
-#pragma unroll
-    for (int b = 0; b < K; ++b) {
-        if ((mask >> b) & 1ull) {
-            t.V[r] = (unsigned short)(threadIdx.x * K + b + 1);
-            t.VXY[r] = ABS ? make_double2(sx + xs[b], sy + ys[b]) : make_double2(xs[b], ys[b]);
-            ++r;
-        }
-    }
+    group_move(t, be, b1, al + 1, g, G);
+    return al + 1 + (b1 - be);
 }
 
-// Clears the calling lane's vertices whose list indices (r0, r0+1, ... in bit
-// order) lie strictly between the bridge entries ab.x and ab.y.
-template <int K>
-__device__ __forceinline__ void clear_between(uint64_t& mask, int r0, int2 ab) {
-    uint64_t clr = 0ull;
-    int r = r0;
-#pragma unroll
-    for (int b = 0; b < K; ++b) {
-        if ((mask >> b) & 1ull) {
-            if (r > ab.x && r < ab.y) clr |= 1ull << b;
-            ++r;
-        }
-    }
-    mask &= ~clr;
-}
-
-// Steps 3a-3c: merges of the lane hulls into the tile's hull.  mask is the
-// calling lane's own mask; on return the final masks are in M and the sorted
-// vertex list of the whole tile in V, VXY, with I[l] the index of lane l's
-// first vertex.
+// Steps 3a-3d: merges of the lane hulls into the tile's hull.
+//   3a. one block-wide compaction writes the list of every lane hull's
+//       vertices in order (the lane's points xs, ys are not needed after it);
+//       each lane's node is the index range of its vertices and the point
+//       before them;
+//   3b. rounds inside each wave (nodes of up to 64 lanes) with node ranges
+//       passed between lanes by shuffles;
+//   3c. one wave merges the waves' nodes left to right;
+//   3d. the final lane masks are rebuilt from the list, and I[l] = index of
+//       lane l's first vertex.
+// On return the sorted vertex list of the whole tile is V, VXY [0, flag[1]).
 template <int K, bool ABS>
 __device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (&xs)[K], const double (&ys)[K]) {
     const int used = (t.N + K - 1) / K;
-    const int l = threadIdx.x, lane = lane_id(), wid = l >> 6;
+    const int l = threadIdx.x, lane = lane_id(), wid = l >> 6, nw = blockDim.x >> 6;
     const int nwu = (used + kWave - 1) / kWave;  // waves holding elements
-    // 3a. one list of every lane hull's vertices; each wave's lanes occupy a
-    // contiguous region that starts with the wave's first point
     tile_compact<K, ABS>(t, mask, xs, ys);
     const int w0 = wid * kWave, wend = min(w0 + kWave, used);
-    int base = 0, end = 0;
-    if (w0 < used) {
-        base = t.I[w0] - 1;
-        end = (wend < used) ? t.I[wend] : t.flag[1];
-    }
-    __syncthreads();  // every lane has read the block-wide indices
-    // 3b. rounds inside each wave (nodes of up to 64 lanes): node ends and
-    // bridges pass between lanes by shuffles, the list is re-compacted inside
-    // the wave's region
-    int r0 = t.I[l];
+    int ns = t.I[l] - 1;
+    int ne = (l + 1 < used) ? t.I[l + 1] - 1 : t.flag[1] - 1;
     for (int h = 1; h < kWave; h <<= 1) {
         if (w0 + h >= wend) break;  // wave-uniform
-        if (h > 1) {
-            const int pc = __popcll(mask);
-            const int incl = wave_incl_scan_int(pc);
-            r0 = base + 1 + incl - pc;
-            end = base + 1 + __shfl(incl, kWave - 1, kWave);
-            wave_sync();
-            write_vertices<K, ABS>(t, mask, r0, xs, ys);
-            wave_sync();
-        }
         const int nm = (wend - w0 - h + 2 * h - 1) / (2 * h);
         int G = kWave;
         while (G > 1 && G * nm > kWave) G >>= 1;
         const int k = lane / G, g = lane & (G - 1);
-        const int kk = (k < nm) ? k : 0;
-        const int a = kk * 2 * h;  // lane offsets inside the wave
-        const int lb = min(a + 2 * h, wend - w0);
-        const int iA0 = __shfl(r0, a, kWave) - 1;
-        const int iS = __shfl(r0, a + h, kWave) - 1;
-        const int rB = __shfl(r0, lb < kWave ? lb : 0, kWave);
-        const int iB1 = (w0 + lb < wend) ? rB - 1 : end - 1;
-        int2 ab = make_int2(0, 0);
-        if (k < nm) ab = group_bridge<K, ABS>(t, iA0, iS, iS, iB1, g, G);
+        const int la = ((k < nm) ? k : 0) * 2 * h;
+        const int a0 = __shfl(ns, la, kWave), a1 = __shfl(ne, la, kWave);
+        const int b0 = __shfl(ns, la + h, kWave), b1 = __shfl(ne, la + h, kWave);
+        int nend = 0;
+        if (k < nm) nend = group_merge<K, ABS>(t, a0, a1, b0, b1, g, G);
         const int km = (l < wend) ? (lane / (2 * h)) : nm;
         const int src = (km < nm) ? km * G : 0;
-        const int2 mine = make_int2(__shfl(ab.x, src, kWave), __shfl(ab.y, src, kWave));
-        if (km < nm) clear_between<K>(mask, r0, mine);
+        const int ns2 = __shfl(a0, src, kWave), ne2 = __shfl(nend, src, kWave);
+        if (km < nm) {
+            ns = ns2;
+            ne = ne2;
+        }
         wave_sync();
     }
-    // the wave's node, compacted in its region
-    if (w0 < used && wend - w0 > 1) {
-        const int pc = __popcll(mask);
-        const int incl = wave_incl_scan_int(pc);
-        r0 = base + 1 + incl - pc;
-        end = base + 1 + __shfl(incl, kWave - 1, kWave);
-        wave_sync();
-        write_vertices<K, ABS>(t, mask, r0, xs, ys);
+    if (lane == 0 && w0 < used) {
+        t.W[wid] = ns;
+        t.W[8 + wid] = ne;
     }
-    t.M[l] = mask;
-    if (lane == 0) t.W[wid] = end;
     __syncthreads();
-    // 3c. one wave merges the waves' nodes left to right: the surviving
-    // suffix of the right node is copied behind the surviving prefix of the
-    // left one, and the vertices under each bridge are cleared from the masks
-    if (wid == 0 && nwu > 1) {
-        int len = t.W[0];
-        for (int w = 1; w < nwu; ++w) {
-            const int jS = t.I[w * kWave] - 1;  // wave w's first point (as block-compacted)
-            const int jB1 = t.W[w] - 1;
-            const int2 ab = group_bridge<K, ABS>(t, 0, len - 1, jS, jB1, lane, kWave);
-            const int al = ab.x;
-            const int be = (ab.y == jS) ? jS + 1 : ab.y;
-            // clear the points strictly under the bridge: A's entries after al
-            // (the shared point among them when it goes) and B's before be
-            const int nA = len - 1 - al, nB = be - (jS + 1);
-            for (int q = lane; q < nA + nB; q += kWave) {
-                const int idx = (q < nA) ? al + 1 + q : jS + 1 + (q - nA);
-                const int p = t.V[idx];
-                const int ln = (p - 1) / K;
-                atomicAnd((unsigned long long*)&t.M[ln], ~(1ull << ((p - 1) - ln * K)));
-            }
-            // copy B's surviving entries behind al (destination never after
-            // source: read a block of 64, then write it)
-            const int cnt = jB1 - be + 1;
-            for (int off = 0; off < cnt; off += kWave) {
-                const int q = off + lane;
-                unsigned short pv = 0;
-                double2 xy = make_double2(0.0, 0.0);
-                if (q < cnt) {
-                    pv = t.V[be + q];
-                    xy = t.VXY[be + q];
-                }
-                wave_sync();
-                if (q < cnt) {
-                    t.V[al + 1 + q] = pv;
-                    t.VXY[al + 1 + q] = xy;
-                }
-                wave_sync();
-            }
-            len = al + 1 + cnt;
+    if (wid == 0) {
+        int last = t.W[8];  // wave 0's node starts at entry 0 (point 0)
+        for (int w = 1; w < nwu; ++w) last = group_merge<K, ABS>(t, 0, last, t.W[w], t.W[8 + w], lane, kWave);
+        if (lane == 0) t.flag[1] = last + 1;
+    }
+    t.M[l] = 0ull;
+    __syncthreads();
+    const int nv = t.flag[1];
+    for (int i = l; i < nv; i += blockDim.x) {
+        const int p = t.V[i];
+        if (p > 0) {
+            const int ln = (p - 1) / K;
+            atomicOr((unsigned long long*)&t.M[ln], 1ull << ((p - 1) - ln * K));
         }
     }
     __syncthreads();
     mask = t.M[l];
-    // the final vertex list
-    tile_compact<K, ABS>(t, mask, xs, ys);
+    const int pc = __popcll(mask);
+    const int incl = wave_incl_scan_int(pc);
+    if (lane == kWave - 1) t.W[16 + wid] = incl;
+    __syncthreads();
+    int r = 1;
+    for (int q = 0; q < wid; ++q) r += t.W[16 + q];
+    t.I[l] = r + incl - pc;
+    (void)nw;
 }
 
 // ---------------------------------------------------------------------------
