@@ -101,10 +101,12 @@ __device__ inline void tile_finish(const Tile& t, uint64_t mask, int increasing,
 }
 
 // ---------------------------------------------------------------------------
-// one workgroup per row
+// one workgroup per row.  The row's phases are latency-bound, so the register
+// budget is capped at 128 VGPRs (four waves per SIMD) even at the cost of a
+// few spilled values: measured faster than the uncapped 145-155 VGPRs.
 // ---------------------------------------------------------------------------
 template <typename T, int K>
-__global__ __launch_bounds__(384) void k_row_fit(RowArgs a) {
+__global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(4))) void k_row_fit(RowArgs a) {
     extern __shared__ __align__(32) char smem[];
     const int64_t row = blockIdx.x;
     const int N = (int)a.n;
