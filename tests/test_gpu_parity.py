@@ -87,6 +87,25 @@ def test_families(kind, n, dtype):
         check_fit(fit.cpu().numpy(), z, wl.y, dtype, True, f"{wl.name}")
 
 
+@pytest.mark.parametrize("n", [2500, 5000, 6144])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_rows_past_the_lds_list_mixed_with_others(n, dtype):
+    """One batch whose rows alternate between noise (a short vertex list, kept
+    in LDS) and increasing or sawtooth data (every point or most points a
+    lane-hull vertex, more than the LDS list holds: refitted with the list in
+    global memory), so both kernels of the single-workgroup path write rows of
+    the same launch."""
+    parts = [workloads.family("noise", 2, n, seed=7, dtype=dtype, weights="uniform"),
+             workloads.family("increasing", 2, n, seed=8, dtype=dtype, weights="uniform"),
+             workloads.family("sawtooth", 2, n, seed=9, dtype=dtype, weights="extreme")]
+    y = np.stack([parts[k % 3].y[k // 3] for k in range(6)])
+    w = np.stack([parts[k % 3].w[k // 3] for k in range(6)])
+    wl = workloads.Workload(f"mixed_6x{n}_{np.dtype(dtype).name}", y, w, True)
+    fit, *_ = gpu_fit(wl)
+    z, *_ = oracle_fit(wl)
+    check_fit(fit.cpu().numpy(), z, wl.y, dtype, True, wl.name)
+
+
 @pytest.mark.parametrize("n", [700, 5000, 30000])
 def test_block_starts_match_oracle_on_tie_free_data(n):
     wl = workloads.family("trend_noise", 4, n, seed=11, dtype=np.float64, weights="uniform")

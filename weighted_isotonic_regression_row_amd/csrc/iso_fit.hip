@@ -43,6 +43,7 @@ struct RowArgs {
     int cap;             // vertices the LDS list holds (row kernel)
     char* ovf;           // per-row vertex lists in global memory for rows whose lane hulls exceed cap
     int64_t ovf_stride;  // bytes per row of ovf
+    int* ovf_row;        // [rows] 1 where the row kernel left the row to k_row_ovf
 };
 
 // Every writer of one call stores the same value, so a plain exchange is
@@ -102,8 +103,10 @@ __device__ inline void tile_finish(const Tile& t, uint64_t mask, int increasing,
 
 // ---------------------------------------------------------------------------
 // one workgroup per row.  The row's phases are latency-bound, so the register
-// budget is capped at 128 VGPRs (four waves per SIMD) even at the cost of a
-// few spilled values: measured faster than the uncapped 145-155 VGPRs.
+// budget is capped at 128 VGPRs (four waves per SIMD).  The vertex list lives
+// in LDS; a row whose lane hulls hold more vertices than it has room for is
+// flagged and left to k_row_ovf, which keeps the list in global memory (one
+// code path per kernel keeps this one free of register spills).
 // ---------------------------------------------------------------------------
 template <typename T, int K>
 __global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(4))) void k_row_fit(RowArgs a) {
@@ -120,6 +123,8 @@ __global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(4))) void k
     double xs[K], ys[K];
     int nvert;
     const int flag = tile_build<T, K>(t, y, w, a.increasing, mask, xs, ys, nvert);
+    const bool over = !flag && nvert > a.cap + 1;  // the list holds point 0 and cap vertices; uniform
+    if (a.ovf_row && threadIdx.x == 0) a.ovf_row[row] = over ? 1 : 0;
     if (flag) {
         wg_write_nan<T>(N, out, sb, cb);
         if (threadIdx.x == 0) {
@@ -128,19 +133,38 @@ __global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(4))) void k
         }
         return;
     }
+    if (over) return;
     constexpr bool ABS = sizeof(T) == 4;
-    if (nvert <= a.cap) {
-        tile_merges<K, ABS>(t, mask, xs, ys);
-        tile_finish<T, K>(t, mask, a.increasing, a.lo, a.hi, out, sb, cb);
-    } else {
-        // the vertex list goes to this row's area of global memory
-        Tile tg = t;
-        char* o = a.ovf + row * a.ovf_stride;
-        tg.VXY = (double2*)o;
-        tg.V = (unsigned short*)(o + 16 * (a.n + 1));
-        tile_merges<K, ABS>(tg, mask, xs, ys);
-        tile_finish<T, K>(tg, mask, a.increasing, a.lo, a.hi, out, sb, cb);
-    }
+    tile_merges<K, ABS>(t, mask, xs, ys);
+    tile_finish<T, K>(t, mask, a.increasing, a.lo, a.hi, out, sb, cb);
+    if (a.row_nan && threadIdx.x == 0) a.row_nan[row] = 0u;
+}
+
+// The rows k_row_fit flagged: the same pipeline with the vertex list in the
+// row's area of the workspace (room for every point).  Other rows return at
+// once.
+template <typename T, int K>
+__global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(4))) void k_row_ovf(RowArgs a) {
+    extern __shared__ __align__(32) char smem[];
+    const int64_t row = blockIdx.x;
+    if (a.ovf_row[row] == 0) return;
+    const int N = (int)a.n;
+    Tile t = tile_carve(smem, blockDim.x, 0, K, N);
+    char* o = a.ovf + row * a.ovf_stride;
+    t.VXY = (double2*)o;
+    t.V = (unsigned short*)(o + 16 * (a.n + 1));
+    const T* y = (const T*)a.y + row * a.n;
+    const T* w = a.w ? (const T*)a.w + row * a.n : nullptr;
+    T* out = (T*)a.fit + row * a.n;
+    uint64_t* sb = a.start_bits ? a.start_bits + row * a.words : nullptr;
+    uint64_t* cb = a.clip_bits ? a.clip_bits + row * a.words : nullptr;
+    uint64_t mask;
+    double xs[K], ys[K];
+    int nvert;
+    (void)tile_build<T, K>(t, y, w, a.increasing, mask, xs, ys, nvert);  // inputs already checked
+    constexpr bool ABS = sizeof(T) == 4;
+    tile_merges<K, ABS>(t, mask, xs, ys);
+    tile_finish<T, K>(t, mask, a.increasing, a.lo, a.hi, out, sb, cb);
     if (a.row_nan && threadIdx.x == 0) a.row_nan[row] = 0u;
 }
 
@@ -1039,8 +1063,13 @@ static hipError_t launch_row(const FitLaunch& a, RowArgs r, int nl) {
     r.cap = row_list_cap((int)a.n, nl, K);
     r.ovf = a.ws + a.L.ovf;
     r.ovf_stride = (int64_t)a.L.ovf_stride;
+    const bool may_overflow = r.cap < a.n;
+    r.ovf_row = may_overflow ? (int*)(a.ws + a.L.ovfrow) : nullptr;
     hipLaunchKernelGGL((k_row_fit<T, K>), dim3((unsigned)a.rows), dim3(nl), tile_smem_bytes(nl, r.cap, K), a.stream,
                        r);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !may_overflow) return e;
+    hipLaunchKernelGGL((k_row_ovf<T, K>), dim3((unsigned)a.rows), dim3(nl), tile_smem_bytes(nl, 0, K), a.stream, r);
     return hipGetLastError();
 }
 
@@ -1048,7 +1077,7 @@ template <typename T>
 static hipError_t launch_fit_t(const FitLaunch& a) {
     unsigned long long* status = (unsigned long long*)(a.ws + a.L.status);
     const RowArgs r{a.y, a.w, a.fit, a.n, a.increasing, a.lo, a.hi, a.start_bits, a.clip_bits, a.row_nan,
-                    a.words, status, a.epoch, 0, nullptr, 0};
+                    a.words, status, a.epoch, 0, nullptr, 0, nullptr};
     if (a.n <= kSingleMax) {
         int K, nl;
         row_shape((int)a.n, K, nl);

@@ -85,6 +85,7 @@ struct Layout {
     size_t cvi;          // int [rows*m*kVMax]
     size_t ovf;          // single-workgroup rows: per-row vertex lists for rows whose lane hulls overflow LDS
     size_t ovf_stride;   // bytes per row of ovf
+    size_t ovfrow;       // int [rows] single-workgroup rows: 1 where the row's list went to ovf
     size_t vjp;          // backward tile records (alias the fit regions)
     size_t total;
 };
@@ -125,6 +126,7 @@ inline Layout make_layout(int64_t rows, int64_t n) {
     if (L.m == 0) {
         L.ovf_stride = align256(16 * ((size_t)n + 1) + 2 * ((size_t)n + 1));
         L.ovf = take(L.ovf_stride * (size_t)rows);
+        L.ovfrow = take(4 * (size_t)rows);
     }
     // backward: per tile head, tail, carry, total (double2 each) + flag
     const size_t tiles = (n > kSingleMax) ? (size_t)rows * (size_t)((n + kVjpTile - 1) / kVjpTile) : 0;

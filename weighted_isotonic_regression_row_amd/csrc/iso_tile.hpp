@@ -370,17 +370,82 @@ __device__ inline void tile_compact(const Tile& t, uint64_t mask, const double (
     __syncthreads();
 }
 
+// One test of the pairs nearest the shared point (points with absolute
+// coordinates).  The cells (i, j) of a D x D grid stand for a = iS - i in A
+// and b = jS + j in B; the group's lanes take PASSES cells each and evaluate
+//   t1(i, j): a is a strict vertex of {pred(a), a, b} (true at A's first entry),
+//   t3(i, j): b is a strict vertex of {a, b, succ(b)} (true at B's last entry).
+// Along each convex side these flip once, so the walk described below stops
+// exactly at the cell where t1 holds and fails one step nearer the shared
+// point on A, and t3 holds and fails one step nearer on B: the bridge (first
+// page, Sec. 4, Lemma 4.2), here checked at every cell at once.  All loads are
+// issued before any test (indices clamped into the nodes), so the whole grid
+// costs one LDS round trip.  Returns false when no cell qualifies (the bridge
+// lies farther out, or rounding broke the monotonicity); the caller walks.
+template <int PASSES>
+__device__ inline bool grid_bridge(const Tile& t, int iA0, int iS, int jS, int jB1, int g, int G, int2& ab) {
+    constexpr int D = 8;
+    double2 pa1[PASSES], pa[PASSES], pb[PASSES], pb1[PASSES];
+#pragma unroll
+    for (int m = 0; m < PASSES; ++m) {
+        const int c = m * G + g, i = c / D, j = c % D;
+        const int a = max(iS - i, iA0), b = min(jS + j, jB1);
+        pa1[m] = t.VXY[max(a - 1, 0)];
+        pa[m] = t.VXY[a];
+        pb[m] = t.VXY[b];
+        pb1[m] = t.VXY[min(b + 1, jB1)];
+    }
+    uint64_t T1 = 0ull, T3 = 0ull;
+#pragma unroll
+    for (int m = 0; m < PASSES; ++m) {
+        const int c = m * G + g, i = c / D, j = c % D;
+        const int a = iS - i, b = jS + j;
+        const bool in = (a >= iA0) && (b <= jB1);
+        const double u1 = cross2(sub2(pa[m], pa1[m]), sub2(pb[m], pa1[m]));
+        const double u3 = cross2(sub2(pb[m], pa[m]), sub2(pb1[m], pa[m]));
+        const bool t1 = in && j >= 1 && (a == iA0 || u1 > 0.0);
+        const bool t3 = in && i >= 1 && (b == jB1 || u3 > 0.0);
+        T1 |= group_bits(__ballot(t1), G) << (m * G);
+        T3 |= group_bits(__ballot(t3), G) << (m * G);
+    }
+    if ((T1 >> 1) & 1ull) {  // convex at the shared point
+        ab = make_int2(iS, jS);
+        return true;
+    }
+    const int imax = min(D - 1, iS - iA0), jmax = min(D - 1, jB1 - jS);
+    const uint64_t rows = (imax >= D - 1) ? ~0xFFull : (((1ull << (D * (imax + 1))) - 1ull) & ~0xFFull);
+    const uint64_t cols = ((1ull << (jmax + 1)) - 2ull) * 0x0101010101010101ull;  // j = 1 .. jmax in every row
+    const uint64_t cand = T1 & ~(T1 << D) & T3 & ~(T3 << 1) & rows & cols;
+    if (!cand) return false;
+    const int c = lo_bit(cand);
+    ab = make_int2(iS - c / D, jS + c % D);
+    return true;
+}
+
 // The bridge of two nodes that share one point, found by the calling group of
 // G lanes (g = 0..G-1): A = list entries [iA0, iS] and B = [jS, jB1], where
 // entries iS and jS hold the shared point (iS == jS when the two lists are
 // adjacent).  Returns the list indices (alpha in A, beta in B); (iS, jS) when
-// the chain is convex at the shared point.  From the neighbours of the shared
-// point the walk of the first page (Sec. 4, after Lemma 4.2) advances each
-// side to its tangent point against the other side's current end, G
-// candidates per step: a is passed over while it is not a strict vertex of
-// {pred(a), a, b}, and b while it is not one of {a, b, succ(b)}.
+// the chain is convex at the shared point.  With absolute coordinates, groups
+// of 16 or more lanes first test the 8 x 8 pairs nearest the shared point at
+// once.  Otherwise, and when
+// that test finds nothing, from the neighbours of the shared point the walk of
+// the first page (Sec. 4, after Lemma 4.2) advances each side to its tangent
+// point against the other side's current end, G candidates per step: a is
+// passed over while it is not a strict vertex of {pred(a), a, b}, and b while
+// it is not one of {a, b, succ(b)}.
 template <int K, bool ABS>
 __device__ inline int2 group_bridge(const Tile& t, int iA0, int iS, int jS, int jB1, int g, int G) {
+    if constexpr (ABS) {
+        int2 ab;
+        if (G == 64) {
+            if (grid_bridge<1>(t, iA0, iS, jS, jB1, g, G, ab)) return ab;
+        } else if (G == 32) {
+            if (grid_bridge<2>(t, iA0, iS, jS, jB1, g, G, ab)) return ab;
+        } else if (G == 16) {
+            if (grid_bridge<4>(t, iA0, iS, jS, jB1, g, G, ab)) return ab;
+        }
+    }
     if (vturn<K, ABS>(t, iS - 1, iS, jS + 1) > 0.0) return make_int2(iS, jS);
     int al = iS - 1, be = jS + 1;
     for (;;) {
@@ -410,8 +475,10 @@ __device__ inline int2 group_bridge(const Tile& t, int iA0, int iS, int jS, int 
 }
 
 // Copies list entries [s0, s1] to d0.. (d0 <= s0) with the calling group of G
-// lanes, a block of G entries at a time, each block read before it is written
-// (a destination never lies after its source, so no unread entry is hit).
+// lanes, a block of G entries at a time.  A block is read by all lanes before
+// any of it is written; a block's destination ends where the next block's
+// source starts (d0 <= s0), so no later source is overwritten.  The caller
+// orders the writes before its next reads of the list (wave_sync or barrier).
 __device__ inline void group_move(const Tile& t, int s0, int s1, int d0, int g, int G) {
     const int cnt = s1 - s0 + 1;
     if (d0 == s0 || cnt <= 0) return;  // uniform in the group
@@ -428,7 +495,6 @@ __device__ inline void group_move(const Tile& t, int s0, int s1, int d0, int g, 
             t.V[d0 + q] = pv;
             t.VXY[d0 + q] = xy;
         }
-        wave_sync();
     }
 }
 
@@ -456,7 +522,7 @@ __device__ inline int group_merge(const Tile& t, int a0, int a1, int b0, int b1,
 //       before them;
 //   3b. rounds inside each wave (nodes of up to 64 lanes) with node ranges
 //       passed between lanes by shuffles;
-//   3c. one wave merges the waves' nodes left to right;
+//   3c. the waves' nodes are merged in a tree, one wave per merge;
 //   3d. the final lane masks are rebuilt from the list, and I[l] = index of
 //       lane l's first vertex.
 // On return the sorted vertex list of the whole tile is V, VXY [0, flag[1]).
@@ -494,11 +560,17 @@ __device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (
         t.W[8 + wid] = ne;
     }
     __syncthreads();
-    if (wid == 0) {
-        int last = t.W[8];  // wave 0's node starts at entry 0 (point 0)
-        for (int w = 1; w < nwu; ++w) last = group_merge<K, ABS>(t, 0, last, t.W[w], t.W[8 + w], lane, kWave);
-        if (lane == 0) t.flag[1] = last + 1;
+    // 3c: a tree over the waves' nodes; at distance s, wave w (a multiple of
+    // 2s) merges its node with wave w + s's, all such merges at once (their
+    // list ranges are disjoint).
+    for (int s = 1; s < nwu; s <<= 1) {
+        if ((wid & (2 * s - 1)) == 0 && wid + s < nwu) {
+            const int e = group_merge<K, ABS>(t, t.W[wid], t.W[8 + wid], t.W[wid + s], t.W[8 + wid + s], lane, kWave);
+            if (lane == 0) t.W[8 + wid] = e;
+        }
+        __syncthreads();
     }
+    if (l == 0) t.flag[1] = t.W[8] + 1;  // wave 0's node starts at entry 0 (point 0)
     t.M[l] = 0ull;
     __syncthreads();
     const int nv = t.flag[1];
