@@ -109,7 +109,7 @@ __device__ inline void tile_finish(const Tile& t, uint64_t mask, int increasing,
 // code path per kernel keeps this one free of register spills).
 // ---------------------------------------------------------------------------
 template <typename T, int K>
-__global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(4))) void k_row_fit(RowArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_row_fit(RowArgs a) {
     extern __shared__ __align__(32) char smem[];
     const int64_t row = blockIdx.x;
     const int N = (int)a.n;
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(4))) void k
 // row's area of the workspace (room for every point).  Other rows return at
 // once.
 template <typename T, int K>
-__global__ __launch_bounds__(384) __attribute__((amdgpu_waves_per_eu(4))) void k_row_ovf(RowArgs a) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_row_ovf(RowArgs a) {
     extern __shared__ __align__(32) char smem[];
     const int64_t row = blockIdx.x;
     if (a.ovf_row[row] == 0) return;
@@ -1035,38 +1035,45 @@ static void row_shape(int N, int& K, int& nl) {
     } else if (N <= 512) {
         K = 8;
         nl = 64;
-    } else {
+    } else if (N <= 4096) {
         K = 16;
-        nl = ((N + 15) / 16 + 63) / 64 * 64;
+        nl = ((N + 15) / 16 + 63) / 64 * 64;  // at most four waves
+    } else {
+        K = 12;
+        nl = ((N + 11) / 12 + 63) / 64 * 64;  // five to eight waves
     }
 }
 
-// Vertices the LDS list of a row holds: enough for three workgroups per CU
-// when a quarter of the points or more fit (noisy rows keep about a fifth of
-// their points as lane-hull vertices); rows that need more use global memory.
+// Vertices the LDS list of a row holds.  A CU runs at most four waves per
+// SIMD at these kernels' register budget, and a workgroup of W waves places
+// ceil(W/4) of them on its busiest SIMD, so 4 / ceil(W/4) workgroups share a
+// CU; the list takes what their share of the 160 KiB leaves (at least a
+// quarter of the points).  Rows that need more go to k_row_ovf.
 static int row_list_cap(int N, int nl, int K) {
+    const int W = nl / 64;
+    const int per_simd = (W + 3) / 4;
+    const long wgs = per_simd >= 4 ? 1 : 4 / per_simd;
+    const long target = 163840 / wgs - 2048;
     const long fixed = (long)tile_smem_bytes(nl, 0, K);
-    const long room = (kRowLdsTarget - fixed) / 18;
-    long cap = room > N / 4 ? room : N / 4;
+    const long room = (target - fixed) / 18;
+    const long cap = room > N / 4 ? room : N / 4;
     return (int)(cap < N ? cap : N);
 }
 
 template <typename T, int K>
 static hipError_t launch_row(const FitLaunch& a, RowArgs r, int nl) {
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)k_row_fit<T, K>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)tile_smem_bytes(K == 16 ? (int)(kSingleMax / 16) : 64,
-                                                       K == 16 ? (int)kSingleMax : 64 * K, K));
-        attr_set = true;
-    }
     r.cap = row_list_cap((int)a.n, nl, K);
+    const size_t smem = tile_smem_bytes(nl, r.cap, K);
+    static size_t attr = 0;  // largest dynamic LDS requested so far for this instance
+    if (smem > attr) {
+        (void)hipFuncSetAttribute((const void*)k_row_fit<T, K>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+        attr = smem;
+    }
     r.ovf = a.ws + a.L.ovf;
     r.ovf_stride = (int64_t)a.L.ovf_stride;
     const bool may_overflow = r.cap < a.n;
     r.ovf_row = may_overflow ? (int*)(a.ws + a.L.ovfrow) : nullptr;
-    hipLaunchKernelGGL((k_row_fit<T, K>), dim3((unsigned)a.rows), dim3(nl), tile_smem_bytes(nl, r.cap, K), a.stream,
-                       r);
+    hipLaunchKernelGGL((k_row_fit<T, K>), dim3((unsigned)a.rows), dim3(nl), smem, a.stream, r);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !may_overflow) return e;
     hipLaunchKernelGGL((k_row_ovf<T, K>), dim3((unsigned)a.rows), dim3(nl), tile_smem_bytes(nl, 0, K), a.stream, r);
@@ -1088,6 +1095,8 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
                 return launch_row<T, 4>(a, r, nl);
             case 8:
                 return launch_row<T, 8>(a, r, nl);
+            case 12:
+                return launch_row<T, 12>(a, r, nl);
             default:
                 return launch_row<T, 16>(a, r, nl);
         }

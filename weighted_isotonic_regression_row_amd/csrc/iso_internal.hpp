@@ -8,8 +8,8 @@
 namespace iso {
 
 // Rows of at most this many elements are fitted by one workgroup each, the
-// whole row held in LDS (18 bytes per element plus 52 per lane of 16
-// elements: 6144 elements take 131 KiB of the 160 KiB of a gfx950 CU).
+// lane hulls' vertices listed in LDS (18 bytes per vertex plus about 60 per
+// lane; 512 lanes of 12 elements at most).
 constexpr int64_t kSingleMax = 6144;
 // Longer rows are cut into chunks of this many elements (first page, Sec. 3:
 // chunks of 1024 to 4096 points), one workgroup of 256 threads, 224 of them
@@ -30,9 +30,6 @@ constexpr int kGroups = kChunk / kGroup;
 //   when the hull has at most kVMax), which cover the walks of the merges,
 //   as those start at the shared points.
 constexpr int kVMax = 1024;
-// LDS a row workgroup aims for (three per CU), and the vertex list of a row
-// that does not fit it lives in the workspace.
-constexpr long kRowLdsTarget = 54000;
 // The lower levels of the merge tree run on subtrees of this many chunks.
 constexpr int kSub = 64;
 // Segment descriptors of a row are kept in LDS up to this many chunks.

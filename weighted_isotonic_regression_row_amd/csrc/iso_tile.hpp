@@ -650,21 +650,22 @@ __device__ inline void tile_expand(const Tile& t, uint64_t mask, int increasing,
 // written and a barrier.
 template <int K>
 __device__ inline void tile_bits(const Tile& t, uint64_t* __restrict__ sbits, uint64_t* __restrict__ cbits) {
-    constexpr int LPW = 64 / K;  // lanes per word
     const int words = (t.N + 63) / 64;
     for (int q = threadIdx.x; q < words; q += blockDim.x) {
-        uint64_t cm = 0ull, vm = 0ull;
-#pragma unroll
-        for (int k = 0; k < LPW; ++k) {
-            const int l = q * LPW + k;
-            if (l < t.nl) {
-                vm |= (t.M[l] & bits_upto(K - 1)) << (k * K);
-                cm |= (t.CM[l] & bits_upto(K - 1)) << (k * K);
-            }
+        uint64_t cm = 0ull, vm = 0ull;  // bit j <-> element 64q + j (vm: its right point is a vertex)
+        const int e0 = 64 * q;
+        const int l1 = min((e0 + 63) / K, t.nl - 1);
+        for (int l = e0 / K; l <= l1; ++l) {
+            const int off = l * K - e0;  // > -K
+            const uint64_t m = t.M[l] & bits_upto(K - 1), c = t.CM[l] & bits_upto(K - 1);
+            vm |= (off >= 0) ? (m << off) : (m >> -off);
+            cm |= (off >= 0) ? (c << off) : (c >> -off);
         }
-        const uint64_t carry = (q == 0) ? 1ull : ((t.M[q * LPW - 1] >> (K - 1)) & 1ull);
+        // element i starts a block when its left point P_i is a vertex: the
+        // right point of element i-1 (P_0 always)
+        const uint64_t carry = (q == 0) ? 1ull : ((t.M[(e0 - 1) / K] >> ((e0 - 1) % K)) & 1ull);
         const uint64_t s = (vm << 1) | carry;
-        const int cnt = t.N - q * 64;
+        const int cnt = t.N - e0;
         const uint64_t valid = (cnt >= 64) ? ~0ull : ((1ull << cnt) - 1ull);
         sbits[q] = s & valid;
         cbits[q] = cm & valid;
