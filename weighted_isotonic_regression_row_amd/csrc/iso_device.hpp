@@ -47,14 +47,51 @@ __device__ __forceinline__ double finish(double slope, int increasing, double lo
     return v;
 }
 
-__device__ __forceinline__ int wave_incl_scan_int(int v) {
-    const int lane = lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        int t = __shfl_up(v, d, kWave);
-        if (lane >= d) v += t;
-    }
+// Lane moves by DPP (data-parallel primitives of the gfx9 family: a VALU
+// operand read from another lane, no LDS round trip).  A lane whose source
+// falls outside the pattern, or whose row is masked off, reads 0.
+//   row_shr:n   from lane - n within each row of 16 lanes (0x110 + n)
+//   row_bcast15 lane 15 of each row to the next row (0x142; rows 1 and 3)
+//   row_bcast31 lane 31 to rows 2 and 3 (0x143)
+//   wave_shr1   from lane - 1 across the whole wave (0x138)
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int dpp_move(int v) {
+    return __builtin_amdgcn_update_dpp(0, v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_move(double v) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const unsigned lo = (unsigned)dpp_move<CTRL, ROWS>((int)(unsigned)b);
+    const unsigned hi = (unsigned)dpp_move<CTRL, ROWS>((int)(unsigned)(b >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double4 dpp_move(double4 v) {
+    return make_double4(dpp_move<CTRL, ROWS>(v.x), dpp_move<CTRL, ROWS>(v.y), dpp_move<CTRL, ROWS>(v.z),
+                        dpp_move<CTRL, ROWS>(v.w));
+}
+
+// Inclusive scan over the 64 lanes of the wave with op(earlier, later), whose
+// identity is the all-zero value: Hillis-Steele steps 1, 2, 4, 8 inside each
+// row of 16 lanes, then the rows' totals by two broadcasts.
+template <typename V, typename Op>
+__device__ __forceinline__ V wave_scan_incl(V v, Op op) {
+    v = op(dpp_move<0x111, 0xf>(v), v);
+    v = op(dpp_move<0x112, 0xf>(v), v);
+    v = op(dpp_move<0x114, 0xf>(v), v);
+    v = op(dpp_move<0x118, 0xf>(v), v);
+    v = op(dpp_move<0x142, 0xa>(v), v);
+    v = op(dpp_move<0x143, 0xc>(v), v);
     return v;
+}
+// The previous lane's value (0 in lane 0).
+template <typename V>
+__device__ __forceinline__ V wave_shift_up1(V v) {
+    return dpp_move<0x138, 0xf>(v);
+}
+
+__device__ __forceinline__ int wave_incl_scan_int(int v) {
+    return wave_scan_incl(v, [](int a, int b) { return a + b; });
 }
 
 // ---------------------------------------------------------------------------
@@ -92,10 +129,6 @@ __device__ __forceinline__ double4 dd4_add_d(double4 a, double2 b) {
     dd_add(a.x, a.y, b.x, 0.0, r.x, r.y);
     dd_add(a.z, a.w, b.y, 0.0, r.z, r.w);
     return r;
-}
-__device__ __forceinline__ double4 shfl_up4(double4 v, int d) {
-    return make_double4(__shfl_up(v.x, d, kWave), __shfl_up(v.y, d, kWave), __shfl_up(v.z, d, kWave),
-                        __shfl_up(v.w, d, kWave));
 }
 // B - A of two double-double pairs, rounded to a double pair (part by part)
 __device__ __forceinline__ double2 dd4_diff(double4 A, double4 B) {

@@ -732,13 +732,8 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_sub(MergeArgs a) {
     H.w = a.w ? (const void*)((const char*)a.w + row * a.n * (int64_t)sizeof(T)) : nullptr;
     if (tid < kWave) {
         double4 v = (tid < ms) ? H.tot[c0 + tid] : make_double4(0.0, 0.0, 0.0, 0.0);
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const double4 o = shfl_up4(v, d);
-            if (tid >= d) v = dd4_add(o, v);
-        }
-        double4 ex = shfl_up4(v, 1);
-        if (tid == 0) ex = make_double4(0.0, 0.0, 0.0, 0.0);
+        v = wave_scan_incl(v, [](double4 p, double4 q) { return dd4_add(p, q); });
+        const double4 ex = wave_shift_up1(v);
         if (tid < ms) {
             const int nv = H.nv[c0 + tid];
             stl[tid] = ex;

@@ -284,10 +284,11 @@ __device__ inline int tile_lane_starts(const Tile& t, double2 total, int f, int 
     const int pcs = wave_incl_scan_int(pc);
     if (threadIdx.x == 0) t.flag[0] = 0;
     double4 v = make_double4(total.x, 0.0, total.y, 0.0);
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const double4 o = shfl_up4(v, d);
-        if (lane >= d) v = add4(DD, o, v);
+    if constexpr (DD) {
+        v = wave_scan_incl(v, [](double4 a, double4 b) { return dd4_add(a, b); });
+    } else {
+        v.x = wave_scan_incl(v.x, [](double a, double b) { return a + b; });
+        v.z = wave_scan_incl(v.z, [](double a, double b) { return a + b; });
     }
     if (lane == kWave - 1) {
         wsum[wid] = v;
@@ -303,8 +304,7 @@ __device__ inline int tile_lane_starts(const Tile& t, double2 total, int f, int 
         all = add4(DD, all, s);
         nvert += t.W[k];
     }
-    double4 ex = shfl_up4(v, 1);
-    if (lane == 0) ex = make_double4(0.0, 0.0, 0.0, 0.0);
+    const double4 ex = wave_shift_up1(v);
     t.LS[threadIdx.x] = add4(DD, acc, ex);
     if (threadIdx.x == 0) t.LS[t.nl] = all;
     __syncthreads();
