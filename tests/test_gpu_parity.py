@@ -58,7 +58,7 @@ def test_config5_dense_full_sampled_rows():
     assert np.all(np.abs(lhs - rhs) <= 1e-9 * np.abs(wl.w * wl.y).sum(axis=1))
 
 
-SIZES = [1, 2, 3, 63, 64, 65, 127, 129, 257, 513, 1000, 3583, 3584, 3585, 4096, 4097, 4500, 6143, 6144, 6145, 7168, 7169,
+SIZES = [1, 2, 3, 63, 64, 65, 127, 129, 257, 513, 1000, 3583, 3584, 3585, 4096, 4097, 4500, 5120, 5121, 6143, 6144, 6145, 7168, 7169,
          8193, 12289, 20001, 65537]
 
 

@@ -1020,7 +1020,7 @@ __global__ __launch_bounds__(256) void k_fixup(FixArgs a) {
 // Lanes and elements per lane for a row of N <= kSingleMax elements: a single
 // wave for short rows, else 16 elements per lane and ceil(N/16) lanes rounded
 // up to whole waves (at most 384).
-static void row_shape(int N, int& K, int& nl) {
+static void row_shape(int N, bool f32, int& K, int& nl) {
     if (N <= 128) {
         K = 2;
         nl = 64;
@@ -1033,6 +1033,9 @@ static void row_shape(int N, int& K, int& nl) {
     } else if (N <= 4096) {
         K = 16;
         nl = ((N + 15) / 16 + 63) / 64 * 64;  // at most four waves
+    } else if (f32 && N <= 5120) {
+        K = 20;  // four waves (float64 rows would spill at this K)
+        nl = 256;
     } else {
         K = 12;
         nl = ((N + 11) / 12 + 63) / 64 * 64;  // five to eight waves
@@ -1082,7 +1085,7 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
                     a.words, status, a.epoch, 0, nullptr, 0, nullptr};
     if (a.n <= kSingleMax) {
         int K, nl;
-        row_shape((int)a.n, K, nl);
+        row_shape((int)a.n, sizeof(T) == 4, K, nl);
         switch (K) {
             case 2:
                 return launch_row<T, 2>(a, r, nl);
@@ -1092,6 +1095,8 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
                 return launch_row<T, 8>(a, r, nl);
             case 12:
                 return launch_row<T, 12>(a, r, nl);
+            case 20:
+                return launch_row<T, 20>(a, r, nl);
             default:
                 return launch_row<T, 16>(a, r, nl);
         }

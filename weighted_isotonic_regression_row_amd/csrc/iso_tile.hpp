@@ -192,7 +192,7 @@ __device__ __forceinline__ void store_lane(T* __restrict__ p, int cnt, const dou
 template <typename T, int K>
 __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restrict__ w, int cnt, int negate,
                                      double (&xs)[K], double (&ys)[K], int& f) {
-    static_assert(K <= 16, "next-vertex offsets are packed in 4 bits");
+    static_assert(K <= 24, "next-vertex offsets are packed in at most two words");
     double X = 0.0, Y = 0.0;
     auto take = [&](int j, double yi, double wi) {
         if (j < cnt) {
@@ -240,8 +240,11 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
             take(j, yi, wi);
         }
     }
-    // next-vertex pointers, as offsets nx - j - 1 in 4-bit fields
-    uint64_t nxp = 0ull;
+    // next-vertex pointers, as offsets nx - j - 1 in PB-bit fields, PE per word
+    constexpr int PB = (K <= 16) ? 4 : 5, PE = 64 / PB, PW = (K + PE - 1) / PE;
+    uint64_t nxp[PW];
+#pragma unroll
+    for (int q = 0; q < PW; ++q) nxp[q] = 0ull;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
         const double xj = j ? xs[j - 1] : 0.0, yj = j ? ys[j - 1] : 0.0;
@@ -255,12 +258,13 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
             bdy = take ? dy : bdy;
             bk = take ? (k - j - 1) : bk;
         }
-        nxp |= (uint64_t)bk << (4 * j);
+        nxp[j / PE] |= (uint64_t)bk << (PB * (j % PE));
     }
     uint64_t mask = 0ull;
     int v = 0;
     for (int s = 0; s < K && v < cnt; ++s) {
-        v += 1 + (int)((nxp >> (4 * v)) & 15ull);
+        const uint64_t word = (PW == 1 || v < PE) ? nxp[0] : nxp[PW - 1];
+        v += 1 + (int)((word >> (PB * (v % PE))) & ((1ull << PB) - 1ull));
         mask |= 1ull << (v - 1);
     }
     return mask;
