@@ -1096,7 +1096,8 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
             case 12:
                 return launch_row<T, 12>(a, r, nl);
             case 20:
-                return launch_row<T, 20>(a, r, nl);
+                if constexpr (sizeof(T) == 4) return launch_row<T, 20>(a, r, nl);
+                return hipErrorInvalidValue;  // row_shape gives float64 rows no K = 20
             default:
                 return launch_row<T, 16>(a, r, nl);
         }
