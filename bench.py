@@ -192,7 +192,7 @@ def main():
                          "algorithmic_bytes": algo,
                          "hbm_frac_end_to_end": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
         ach = algo / (kmean * 1e-3) / 1e9
-        rec["roofline"] = {"bound": "hbm", "kernel": "k_row_fit<float,16>", "achieved": ach,
+        rec["roofline"] = {"bound": "hbm", "kernel": "k_row_fit<float,20>", "achieved": ach,
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                            "traffic": committed_traffic(), "kernel_ms_mean": kmean, "kernel_ms_median": kmed,
                            "bytes_per_element": 12, "elements_per_launch": elems,

@@ -18,6 +18,14 @@ constexpr int kWave = 64;
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Orders the calling wave's LDS accesses: writes by any of its lanes before
+// the call are seen by reads of any of its lanes after it.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
+
 __device__ __forceinline__ int hi_bit(uint64_t m) { return 63 - __clzll((long long)m); }
 __device__ __forceinline__ int lo_bit(uint64_t m) { return __ffsll((long long)m) - 1; }
 

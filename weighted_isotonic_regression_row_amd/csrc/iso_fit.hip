@@ -44,6 +44,7 @@ struct RowArgs {
     char* ovf;           // per-row vertex lists in global memory for rows whose lane hulls exceed cap
     int64_t ovf_stride;  // bytes per row of ovf
     int* ovf_row;        // [rows] 1 where the row kernel left the row to k_row_ovf
+    int stage;           // row kernel: read the inputs through LDS (lane_load_staged)
 };
 
 // Every writer of one call stores the same value, so a plain exchange is
@@ -69,14 +70,23 @@ __device__ inline void wg_write_nan(int64_t N, T* out, uint64_t* sbits, uint64_t
 // y, w.  Returns the tile's flag (non-zero: a non-finite input or a bad
 // weight); nvert = the number of lane-hull vertices.  The lane's points stay
 // in xs, ys.
+// With stage set, the inputs pass through the still unused vertex list (each
+// wave K * 64 elements of it).
 template <typename T, int K>
 __device__ inline int tile_build(const Tile& t, const T* y, const T* w, int increasing, uint64_t& mask,
-                                 double (&xs)[K], double (&ys)[K], int& nvert) {
+                                 double (&xs)[K], double (&ys)[K], int& nvert, bool stage = false) {
     constexpr bool ABS = sizeof(T) == 4;
     const int l = threadIdx.x;
     const int cnt = min(max(t.N - l * K, 0), K);
     int f = 0;
-    mask = lane_hull<T, K>(y + (int64_t)l * K, w ? w + (int64_t)l * K : nullptr, cnt, !increasing, xs, ys, f);
+    if (stage) {
+        const int e0 = (l & ~(kWave - 1)) * K;  // the wave's first element
+        T* st = (T*)t.VXY + e0;
+        mask = lane_hull<T, K>(y + e0, w ? w + e0 : nullptr, cnt, !increasing, xs, ys, f, st,
+                               min(max(t.N - e0, 0), K * kWave));
+    } else {
+        mask = lane_hull<T, K>(y + (int64_t)l * K, w ? w + (int64_t)l * K : nullptr, cnt, !increasing, xs, ys, f);
+    }
     nvert = tile_lane_starts<!ABS>(t, make_double2(xs[K - 1], ys[K - 1]), f, __popcll(mask));
     return t.flag[0];
 }
@@ -122,7 +132,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     uint64_t mask;
     double xs[K], ys[K];
     int nvert;
-    const int flag = tile_build<T, K>(t, y, w, a.increasing, mask, xs, ys, nvert);
+    const int flag = tile_build<T, K>(t, y, w, a.increasing, mask, xs, ys, nvert, a.stage != 0);
     const bool over = !flag && nvert > a.cap + 1;  // the list holds point 0 and cap vertices; uniform
     if (a.ovf_row && threadIdx.x == 0) a.ovf_row[row] = over ? 1 : 0;
     if (flag) {
@@ -1069,6 +1079,10 @@ static hipError_t launch_row(const FitLaunch& a, RowArgs r, int nl) {
     }
     r.ovf = a.ws + a.L.ovf;
     r.ovf_stride = (int64_t)a.L.ovf_stride;
+    // stage the inputs through LDS when a lane's K elements are not whole
+    // 64-byte segments and the list has room for every wave's span
+    r.stage = ((K * (int)sizeof(T)) % 64 != 0) && ((K * (int)sizeof(T)) % 16 == 0) &&
+              ((size_t)nl * K * sizeof(T) <= tile_list_len(nl, r.cap, K) * 16);
     const bool may_overflow = r.cap < a.n;
     r.ovf_row = may_overflow ? (int*)(a.ws + a.L.ovfrow) : nullptr;
     hipLaunchKernelGGL((k_row_fit<T, K>), dim3((unsigned)a.rows), dim3(nl), smem, a.stream, r);
@@ -1082,7 +1096,7 @@ template <typename T>
 static hipError_t launch_fit_t(const FitLaunch& a) {
     unsigned long long* status = (unsigned long long*)(a.ws + a.L.status);
     const RowArgs r{a.y, a.w, a.fit, a.n, a.increasing, a.lo, a.hi, a.start_bits, a.clip_bits, a.row_nan,
-                    a.words, status, a.epoch, 0, nullptr, 0, nullptr};
+                    a.words, status, a.epoch, 0, nullptr, 0, nullptr, 0};
     if (a.n <= kSingleMax) {
         int K, nl;
         row_shape((int)a.n, sizeof(T) == 4, K, nl);

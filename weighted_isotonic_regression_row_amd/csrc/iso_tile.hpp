@@ -178,10 +178,51 @@ __device__ __forceinline__ void store_lane(T* __restrict__ p, int cnt, const dou
         if (j < cnt) p[j] = (T)v[j];
 }
 
+// The wave's K * 64 elements of one input through LDS, for lanes whose K
+// elements are not a whole number of 64-byte segments (per-lane 16-byte loads
+// then touch each segment from several lanes and instructions, and HBM serves
+// some segments more than once): consecutive lanes read consecutive 16-byte
+// pieces (one contiguous KiB per load instruction) into the wave's stage, and
+// each lane then reads its own K values.  avail = elements of the span that
+// exist; the rest read as 0.
+template <typename T, int K>
+__device__ __forceinline__ void lane_load_staged(const T* __restrict__ base, int avail, T* stage, T (&v)[K]) {
+    constexpr int VW = 16 / (int)sizeof(T);
+    constexpr int NV = K * kWave / VW;
+    static_assert((K * (int)sizeof(T)) % 16 == 0, "a lane's values are read back as 16-byte pieces");
+    const int lane = lane_id();
+    if ((((uintptr_t)base) & 15) == 0) {
+#pragma unroll
+        for (int q = 0; q < NV / kWave; ++q) {
+            const int e = (q * kWave + lane) * VW;
+            if (e + VW <= avail) {
+                *(uint4*)(stage + e) = *(const uint4*)(base + e);
+            } else {
+#pragma unroll
+                for (int r = 0; r < VW; ++r) stage[e + r] = (e + r < avail) ? base[e + r] : (T)0;
+            }
+        }
+    } else {
+        for (int e = lane; e < K * kWave; e += kWave) stage[e] = (e < avail) ? base[e] : (T)0;
+    }
+    wave_sync();
+#pragma unroll
+    for (int q = 0; q < K / VW; ++q) {
+        const uint4 u = *(const uint4*)(stage + lane * K + q * VW);
+        const T* pu = (const T*)&u;
+#pragma unroll
+        for (int r = 0; r < VW; ++r) v[q * VW + r] = pu[r];
+    }
+    wave_sync();  // every lane has its values before the stage is reused
+}
+
 // Loads the lane's elements, forms the local points (xs, ys)[j] = point j+1
 // relative to the lane's start, and returns the lane's hull as a mask (bit b
 // <-> local point b+1; point 0 is implicit).  f |= 1 for a non-finite input,
-// 2 for a weight <= 0.
+// 2 for a weight <= 0.  With a stage (LDS, K * 64 elements for the calling
+// wave), the inputs come through lane_load_staged from the wave's span
+// starting at y, w with avail elements; otherwise each lane reads its own
+// elements at y, w.
 //
 // The hull is found by gift wrapping: from every local point j the next hull
 // vertex is the point k > j of least slope (the farthest one on ties, so
@@ -191,7 +232,8 @@ __device__ __forceinline__ void store_lane(T* __restrict__ p, int cnt, const dou
 // to the lane's registers.
 template <typename T, int K>
 __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restrict__ w, int cnt, int negate,
-                                     double (&xs)[K], double (&ys)[K], int& f) {
+                                     double (&xs)[K], double (&ys)[K], int& f, T* stage = nullptr,
+                                     int avail = 0) {
     static_assert(K <= 24, "next-vertex offsets are packed in at most two words");
     double X = 0.0, Y = 0.0;
     auto take = [&](int j, double yi, double wi) {
@@ -210,9 +252,24 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
     };
     constexpr int VW = 16 / (int)sizeof(T);
     bool done = false;
+    if constexpr ((K * (int)sizeof(T)) % 16 == 0) {
+        if (stage) {
+            T yv[K], wv[K];
+            lane_load_staged<T, K>(y, avail, stage, yv);
+            if (w) {
+                lane_load_staged<T, K>(w, avail, stage, wv);
+            } else {
+#pragma unroll
+                for (int j = 0; j < K; ++j) wv[j] = (T)1;
+            }
+#pragma unroll
+            for (int j = 0; j < K; ++j) take(j, (double)yv[j], (double)wv[j]);
+            done = true;
+        }
+    }
     if constexpr (K % VW == 0) {
         // whole, aligned lanes: 16-byte loads, each consumed at once
-        if (cnt == K && (((uintptr_t)y) & 15) == 0 && (w == nullptr || (((uintptr_t)w) & 15) == 0)) {
+        if (!done && cnt == K && (((uintptr_t)y) & 15) == 0 && (w == nullptr || (((uintptr_t)w) & 15) == 0)) {
 #pragma unroll
             for (int q = 0; q < K / VW; ++q) {
                 if constexpr (sizeof(T) == 4) {
@@ -327,13 +384,6 @@ __device__ __forceinline__ uint64_t group_bits(uint64_t ballot, int G) {
 // number of consecutive set bits from bit 0
 __device__ __forceinline__ int trailing_ones(uint64_t m) { return (m == ~0ull) ? 64 : lo_bit(~m); }
 
-// Orders the calling wave's LDS accesses: writes by any of its lanes before
-// the call are seen by reads of any of its lanes after it.
-__device__ __forceinline__ void wave_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-}
 
 // Block scope.  Writes the sorted vertex list of the whole tile: V[0] = point
 // 0, then every lane's vertices; I[l] = index of lane l's first vertex;
