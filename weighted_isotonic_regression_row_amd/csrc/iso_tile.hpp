@@ -5,21 +5,21 @@
 //
 // Work split (gfx950, wave64):
 //   1. lane hull each lane (thread) owns K consecutive elements, i.e. the
-//                points lK+1 .. lK+K, reads them straight from global memory,
-//                and runs one monotone-chain pass over them in registers in
-//                float64: local prefix sums of (w, w*y) relative to the lane's
-//                start, and the lane's hull as a bit-mask stack whose top two
-//                entries are kept apart (the first page's lane hull, Sec. 3.1);
-//   2. starts    an exclusive scan of the lane totals gives each lane's start
-//                relative to the tile's first point (double-double for float64
-//                data);
-//   3. merges    ceil(log2(lanes)) rounds.  Before each, the current vertices
-//                are compacted into a sorted list in LDS (point index and
-//                coordinates); then neighbouring nodes of 2^r lanes are merged,
-//                a group of G threads per merge walking from the shared point
-//                to the bridge (Sec. 4, Lemma 4.2 and the walk after it) G
-//                candidates at a time, and the points strictly under the bridge
-//                are cleared from the lane masks;
+//                points lK+1 .. lK+K, reads them from global memory (through
+//                LDS when K elements are not whole 64-byte segments), forms
+//                their float64 prefix sums of (w, w*y) relative to the lane's
+//                start, and builds its hull by gift wrapping with compile-time
+//                register indices (the first page's lane hull, Sec. 3.1);
+//   2. starts    an exclusive DPP scan of the lane totals gives each lane's
+//                start relative to the tile's first point (double-double for
+//                float64 data);
+//   3. merges    the lane-hull vertices are compacted once into a sorted list
+//                in LDS; a lane's node is an index range of it.  Rounds inside
+//                each wave merge neighbouring nodes, a group of G lanes per
+//                merge finding the bridge (Sec. 4, Lemma 4.2 and the walk
+//                after it) and moving the right node's surviving suffix
+//                behind the left node's surviving prefix; then a tree over
+//                the waves' nodes;
 //   4. expand    every lane computes the slope of the hull edge above each of
 //                its elements (Sec. 3.4: the edge from the last vertex at or
 //                before the element's left point to the first vertex at or
