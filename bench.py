@@ -49,15 +49,24 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed (a comment
+    edit does not change the kernels the counters describe)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_hash() -> str:
-    """Hash of the HIP sources and the C ABI header (what the counters depend on)."""
+    """Hash of the HIP sources and the C ABI header, comments and whitespace
+    aside (what the counters depend on)."""
     h = hashlib.sha256()
     files = sorted(f for f in os.listdir(CSRC) if f.endswith((".hip", ".hpp", ".cpp")))
     for f in files:
-        with open(os.path.join(CSRC, f), "rb") as fh:
-            h.update(f.encode() + b"\0" + fh.read())
-    with open(os.path.join(ROOT, "include", "iso.h"), "rb") as fh:
-        h.update(fh.read())
+        with open(os.path.join(CSRC, f), encoding="utf-8") as fh:
+            h.update(f.encode() + b"\0" + _code_only(fh.read()).encode())
+    with open(os.path.join(ROOT, "include", "iso.h"), encoding="utf-8") as fh:
+        h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 
