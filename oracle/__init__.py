@@ -55,6 +55,8 @@ def _load():
         ]
         lib.iso_oracle_vjp.restype = ctypes.c_int
         lib.iso_oracle_vjp.argtypes = [dp, bp, bp, bp, dp, ctypes.c_int64, ctypes.c_int64, dp]
+        lib.iso_oracle_vjp_w.restype = ctypes.c_int
+        lib.iso_oracle_vjp_w.argtypes = [dp, dp, bp, bp, bp, dp, ctypes.c_int64, ctypes.c_int64, dp]
         _lib = lib
     return _lib
 
@@ -114,6 +116,25 @@ def vjp(g, block_start, clipped=None, row_nan=None, w=None):
     w2 = None if w is None else _as2d(w)
     out = np.empty((rows, n), dtype=np.float64)
     st = lib.iso_oracle_vjp(_dptr(g2), _bptr(bs), _bptr(cl), _bptr(rn), _dptr(w2), rows, n, _dptr(out))
+    if st != OK:
+        raise ValueError("invalid arguments")
+    return out
+
+
+def vjp_w(g, y, block_start, clipped=None, row_nan=None, w=None):
+    """grad_w = (sum_{i in B(j)} g_i [not clipped_i]) * (y_j - mean_B) / W_B over the given partition
+    (page "torchisotonic", "Semantics": the fit is differentiable in the weights)."""
+    lib = _load()
+    g2 = _as2d(g)
+    rows, n = g2.shape
+    y2 = _as2d(y)
+    bs = np.ascontiguousarray(np.asarray(block_start, dtype=np.uint8).reshape(rows, n))
+    cl = None if clipped is None else np.ascontiguousarray(np.asarray(clipped, dtype=np.uint8).reshape(rows, n))
+    rn = None if row_nan is None else np.ascontiguousarray(np.asarray(row_nan, dtype=np.uint8).reshape(rows))
+    w2 = None if w is None else _as2d(w)
+    out = np.empty((rows, n), dtype=np.float64)
+    st = lib.iso_oracle_vjp_w(_dptr(g2), _dptr(y2), _bptr(bs), _bptr(cl), _bptr(rn), _dptr(w2), rows, n,
+                              _dptr(out))
     if st != OK:
         raise ValueError("invalid arguments")
     return out

@@ -307,3 +307,49 @@ int iso_oracle_vjp(const double* g, const uint8_t* block_start, const uint8_t* c
     }
     return ORACLE_OK;
 }
+
+/*
+ * Vector-Jacobian product of the (clipped) fit with respect to the weights
+ * (the PyPI page, "Semantics": the fit is differentiable in y and in the
+ * weights), for the partition given by block_start and the clip flags.  A
+ * block B takes the value mean_B = sum_B w y / sum_B w, whose derivative in
+ * w_j (j in B) is (y_j - mean_B) / sum_B w; so
+ *     grad_w[j] = (sum_{i in B, not clipped} g_i) * (y_j - mean_B) / sum_B w.
+ * The same formula holds for the non-increasing fit (its blocks' values are
+ * the same weighted means).  g, y, w, out: [rows, n] float64; w may be NULL
+ * (unit weights).  row_nan may be NULL; rows flagged there come back NaN.
+ */
+int iso_oracle_vjp_w(const double* g, const double* y, const uint8_t* block_start, const uint8_t* clipped,
+                     const uint8_t* row_nan, const double* w, int64_t rows, int64_t n, double* out) {
+    if (rows < 0 || n < 0) return ORACLE_EINVAL;
+    if (rows == 0 || n == 0) return ORACLE_OK;
+    if (!g || !y || !block_start || !out) return ORACLE_EINVAL;
+    for (int64_t r = 0; r < rows; ++r) {
+        const double* gr = g + r * n;
+        const double* yr = y + r * n;
+        const uint8_t* bs = block_start + r * n;
+        const uint8_t* cl = clipped ? clipped + r * n : NULL;
+        const double* wr = w ? w + r * n : NULL;
+        double* o = out + r * n;
+        if (row_nan && row_nan[r]) {
+            for (int64_t i = 0; i < n; ++i) o[i] = NAN;
+            continue;
+        }
+        int64_t lo = 0;
+        while (lo < n) {
+            int64_t hi = lo + 1;
+            while (hi < n && !bs[hi]) ++hi;
+            acc_t sg = {0.0, 0.0}, sw = {0.0, 0.0}, sy = {0.0, 0.0};
+            for (int64_t i = lo; i < hi; ++i) {
+                const double wi = wr ? wr[i] : 1.0;
+                if (!(cl && cl[i])) acc_add(&sg, gr[i]);
+                acc_add(&sw, wi);
+                acc_add(&sy, wi * yr[i]);
+            }
+            const double G = acc_value(&sg), W = acc_value(&sw), mean = acc_value(&sy) / W;
+            for (int64_t i = lo; i < hi; ++i) o[i] = G * (yr[i] - mean) / W;
+            lo = hi;
+        }
+    }
+    return ORACLE_OK;
+}

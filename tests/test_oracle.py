@@ -320,3 +320,69 @@ def test_oracle_vjp_unit_weight_block_mean():
     assert list(bs[0]) == [1, 0, 0, 1, 0]
     v = oracle.vjp(g, bs, cl, rn)[0]
     np.testing.assert_allclose(v, [3.0, 3.0, 3.0, 1.0, 1.0], rtol=0, atol=1e-15)
+
+
+# ------------------------------------------------------------ VJP in w
+# The fit is differentiable in y and in the weights (page "torchisotonic",
+# "Semantics").  Pins: central finite differences in w, a hand case derived
+# from the block mean's quotient rule, and the invariance of the fit under a
+# common scale of the weights (so sum_j w_j dL/dw_j = 0 on every row).
+
+@pytest.mark.parametrize("seed", range(8))
+def test_oracle_vjp_w_finite_differences(seed):
+    r = workloads.rng(7000 + seed)
+    n = int(r.integers(2, 60))
+    y = r.standard_normal(n)
+    w = r.random(n) + 0.2
+    inc = bool(seed % 2)
+    lo, hi = (-0.5, 0.5) if seed % 3 == 0 else (None, None)
+    g = r.standard_normal(n)
+    z, bs, cl, rn, _ = oracle.fit(y, w, inc, lo, hi)
+    starts = np.nonzero(bs[0])[0]
+    zu = oracle.fit(y, w, inc)[0][0]
+    if (len(starts) > 1 and np.min(np.abs(np.diff(zu[starts]))) < 1e-3) or \
+            (lo is not None and np.min(np.minimum(np.abs(zu - lo), np.abs(zu - hi))) < 1e-3):
+        pytest.skip("near a kink")
+    v = oracle.vjp_w(g, y, bs, cl, rn, w)[0]
+    h = 1e-6
+    fd = np.empty(n)
+    for j in range(n):
+        wp, wm = w.copy(), w.copy()
+        wp[j] += h
+        wm[j] -= h
+        fd[j] = (g @ oracle.fit(y, wp, inc, lo, hi)[0][0] - g @ oracle.fit(y, wm, inc, lo, hi)[0][0]) / (2 * h)
+    np.testing.assert_allclose(v, fd, rtol=1e-6, atol=1e-7)
+
+
+def test_oracle_vjp_w_hand_cases():
+    # blocks {3, 1, 2} (mean 2) and {5, 4} (mean 4.5), unit weights:
+    # dL/dw_j = (sum of g over the block) * (y_j - mean) / (block weight)
+    y = np.array([3.0, 1.0, 2.0, 5.0, 4.0])
+    g = np.array([1.0, 2.0, 6.0, -1.0, 3.0])
+    z, bs, cl, rn, _ = oracle.fit(y)
+    np.testing.assert_allclose(oracle.vjp_w(g, y, bs, cl, rn)[0], [3.0, -3.0, 0.0, 0.5, -0.5], rtol=0,
+                               atol=1e-15)
+    # one pooled block f = (w1 y1 + w2 y2) / (w1 + w2) = 1.5 for y = (3, 1),
+    # w = (1, 3): df/dw1 = (y1 - f) / W = 0.375, df/dw2 = -0.125; L = 2 f + 5 f
+    y = np.array([3.0, 1.0])
+    w = np.array([1.0, 3.0])
+    g = np.array([2.0, 5.0])
+    z, bs, cl, rn, _ = oracle.fit(y, w)
+    np.testing.assert_allclose(oracle.vjp_w(g, y, bs, cl, rn, w)[0], [2.625, -0.875], rtol=0, atol=1e-15)
+    # a clipped block contributes nothing
+    z, bs, cl, rn, _ = oracle.fit(y, w, True, 2.0, 3.0)
+    assert cl[0].all()
+    np.testing.assert_array_equal(oracle.vjp_w(g, y, bs, cl, rn, w)[0], [0.0, 0.0])
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_oracle_vjp_w_scale_invariance(seed):
+    r = workloads.rng(7100 + seed)
+    y = r.standard_normal((5, 300))
+    w = r.random((5, 300)) * 3 + 0.1
+    g = r.standard_normal((5, 300))
+    inc = bool(seed % 2)
+    z, bs, cl, rn, _ = oracle.fit(y, w, inc, -0.3 if seed >= 2 else None, 0.4 if seed >= 2 else None)
+    v = oracle.vjp_w(g, y, bs, cl, rn, w)
+    s = np.sum(w * v, axis=1)
+    assert np.max(np.abs(s)) <= 1e-12 * max(1.0, np.abs(w * v).sum(axis=1).max())
