@@ -131,6 +131,32 @@ int iso_vjp(const void* grad_dev, const iso_blocks* blocks, void* grad_y_dev, vo
             size_t workspace_bytes, void* stream);
 
 /*
+ * Vector-Jacobian products of the fit with respect to y and to the weights
+ * (page "torchisotonic", "Semantics": the fit is differentiable in y and in
+ * the weights).  A block B takes the value mean_B = sum_B w y / sum_B w, so
+ * for j in B, with G_B = sum_{i in B, clip inactive at i} grad[i] and
+ * W_B = sum_B w:
+ *     grad_y[j] = w_j * G_B / W_B                 (as iso_vjp),
+ *     grad_w[j] = G_B * (y_j - mean_B) / W_B.
+ * The non-increasing fit has the same form over its own blocks.  Unit weights
+ * (blocks->w_dev == NULL) give the derivative in weights that are all 1.
+ * Rows that came back NaN give NaN in both.
+ *
+ *   grad_dev      [rows, n] of blocks->dtype, read only.
+ *   blocks        handle filled by iso_fit (host struct).
+ *   y_dev         the y that iso_fit was given ([rows, n] of blocks->dtype,
+ *                 read only); required when grad_w_dev is not NULL.
+ *   grad_y_dev    [rows, n] of blocks->dtype, written, or NULL.
+ *   grad_w_dev    [rows, n] of blocks->dtype, written, or NULL.
+ *   workspace_dev iso_workspace_bytes(rows, n, dtype) bytes (may be the fit's).
+ *
+ * Both outputs NULL, or grad_w_dev without y_dev, is ISO_EINVAL (unless rows
+ * or n is 0: then nothing is queued and ISO_OK is returned).
+ */
+int iso_vjp_yw(const void* grad_dev, const iso_blocks* blocks, const void* y_dev, void* grad_y_dev,
+               void* grad_w_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
  * Synchronises `stream` and returns the data error of the most recent iso_fit
  * that used this workspace: ISO_OK or ISO_EWEIGHT (ISO_EHIP if the read fails,
  * ISO_EINVAL for a NULL workspace).

@@ -36,7 +36,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     fns = declared_functions()
-    assert fns == sorted(["iso_blocks_bytes", "iso_fit", "iso_status", "iso_strerror", "iso_vjp",
+    assert fns == sorted(["iso_blocks_bytes", "iso_fit", "iso_status", "iso_strerror", "iso_vjp", "iso_vjp_yw",
                           "iso_workspace_bytes"])
 
 
@@ -122,8 +122,26 @@ def test_vjp_rejects_bad_arguments_on_host(lib):
     bc.start_bits_dev, bc.clip_bits_dev, bc.row_nan_dev = 8192, 8192 + 256, 8192 + 512
     assert lib.iso_vjp(None, ctypes.byref(bc), 512, 4096, 1 << 20, None) == iso.ISO_EINVAL
     assert lib.iso_vjp(256, ctypes.byref(bc), 512, 4096, 1, None) == iso.ISO_EINVAL
+    assert lib.iso_vjp(256, ctypes.byref(bc), None, 4096, 1 << 20, None) == iso.ISO_EINVAL  # no output
     bc.dtype = 5
     assert lib.iso_vjp(256, ctypes.byref(bc), 512, 4096, 1 << 20, None) == iso.ISO_EINVAL
+
+
+def test_vjp_yw_rejects_bad_arguments_on_host(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    E = iso.ISO_EINVAL
+    bc = iso.IsoBlocksC()
+    assert lib.iso_vjp_yw(256, ctypes.byref(bc), 128, 512, 640, 4096, 1 << 20, None) == E  # invalid handle
+    bc.valid = 1
+    bc.rows, bc.n, bc.words, bc.dtype = 2, 3, 1, 0
+    bc.start_bits_dev, bc.clip_bits_dev, bc.row_nan_dev = 8192, 8192 + 256, 8192 + 512
+    assert lib.iso_vjp_yw(256, ctypes.byref(bc), 128, None, None, 4096, 1 << 20, None) == E  # no output
+    assert lib.iso_vjp_yw(256, ctypes.byref(bc), None, 512, 640, 4096, 1 << 20, None) == E   # grad_w without y
+    assert lib.iso_vjp_yw(None, ctypes.byref(bc), 128, 512, 640, 4096, 1 << 20, None) == E
+    assert lib.iso_vjp_yw(256, ctypes.byref(bc), 128, 512, 640, 4096 + 8, 1 << 20, None) == E  # misaligned
+    assert lib.iso_vjp_yw(256, ctypes.byref(bc), 128, 512, 640, 4096, 1, None) == E  # workspace too small
+    bc.rows = 0
+    assert lib.iso_vjp_yw(None, ctypes.byref(bc), None, None, None, None, 0, None) == iso.ISO_OK  # empty
 
 
 def test_status_without_calls(lib):

@@ -155,6 +155,54 @@ def test_vjp_matches_oracle(n, dtype):
     assert np.max(np.abs(gy - ref)) <= tol
 
 
+@pytest.mark.parametrize("n", [1, 63, 700, 5000, 6144, 6145, 20001])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+@pytest.mark.parametrize("weighted", [True, False])
+def test_vjp_w_matches_oracle(n, dtype, weighted):
+    """grad_w = G_B (y_j - mean_B) / W_B (page "torchisotonic", "Semantics": the
+    fit is differentiable in the weights) against the oracle on the GPU's own
+    partition; single-tile and multi-tile rows, clipped, both orientations."""
+    import weighted_isotonic_regression_row_amd as iso
+    wl = workloads.family("trend_noise", 3, n, seed=n % 83, dtype=dtype, weights="uniform" if weighted else "unit",
+                          increasing=(n % 2 == 1))
+    if not weighted:
+        wl.w = None
+    wl.y_min, wl.y_max = 0.1, 0.8
+    r = workloads.rng(321)
+    g = r.standard_normal(wl.y.shape).astype(dtype)
+    fit, b, y, w = gpu_fit(wl)
+    gy, gw = iso.iso_vjp_yw(to_dev(g), b, y)
+    gy_only = iso.iso_vjp(to_dev(g), b)
+    np.testing.assert_array_equal(gy.cpu().numpy(), gy_only.cpu().numpy())
+    gs, gc, grn = gpu_blocks(b)
+    w64 = None if wl.w is None else wl.w.astype(np.float64)
+    ref_w = oracle.vjp_w(g.astype(np.float64), wl.y.astype(np.float64), gs, gc, grn, w64)
+    ref_y = oracle.vjp(g.astype(np.float64), gs, gc, grn, w64)
+    tol = 1e-12 if dtype == np.float64 else 2e-6
+    gwn = gw.cpu().numpy().astype(np.float64)
+    gyn = gy.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(gwn - ref_w)) <= tol * max(1.0, np.abs(ref_w).max()), f"grad_w n={n}"
+    assert np.max(np.abs(gyn - ref_y)) <= tol * max(1.0, np.abs(ref_y).max()), f"grad_y n={n}"
+    # the fit does not change when all weights are scaled: sum_j w_j grad_w_j = 0 per row
+    wv = np.ones_like(gwn) if wl.w is None else wl.w.astype(np.float64)
+    assert np.max(np.abs(np.sum(wv * gwn, axis=1))) <= 50 * tol * max(1.0, np.abs(wv * gwn).sum(axis=1).max())
+
+
+@pytest.mark.parametrize("n", [300, 20000])
+def test_vjp_w_nan_rows(n):
+    import weighted_isotonic_regression_row_amd as iso
+    r = workloads.rng(8)
+    y = r.standard_normal((3, n))
+    w = r.random((3, n)) + 0.1
+    y[1, n // 2] = np.nan
+    wl = workloads.Workload("nan", y, w, True)
+    fit, b, yd, wd = gpu_fit(wl)
+    gy, gw = iso.iso_vjp_yw(to_dev(r.standard_normal((3, n))), b, yd, want_y=False)
+    assert gy is None
+    gwn = gw.cpu().numpy()
+    assert np.isnan(gwn[1]).all() and np.isfinite(gwn[[0, 2]]).all()
+
+
 def test_config3_soft_rank_forward_backward():
     import weighted_isotonic_regression_row_amd as iso
     wl = workloads.cfg3_soft_rank()

@@ -8,6 +8,7 @@ library (or without a GPU) the calls raise.
 
     fit, blocks = iso_fit(y, w, increasing=True, y_min=None, y_max=None)
     grad_y = iso_vjp(grad, blocks)
+    grad_y, grad_w = iso_vjp_yw(grad, blocks, y)
 
 The fit of each row is the weighted least-squares monotone sequence (page
 "Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Eq. (1)),
@@ -31,7 +32,8 @@ ISO_EINVAL = -1
 ISO_EHIP = -2
 ISO_EWEIGHT = -3
 
-SYMBOLS = ("iso_workspace_bytes", "iso_blocks_bytes", "iso_fit", "iso_vjp", "iso_status", "iso_strerror")
+SYMBOLS = ("iso_workspace_bytes", "iso_blocks_bytes", "iso_fit", "iso_vjp", "iso_vjp_yw", "iso_status",
+           "iso_strerror")
 
 
 class IsoBlocksC(ctypes.Structure):
@@ -78,6 +80,8 @@ def load_library(path: str | None = None):
                             ctypes.POINTER(IsoBlocksC), vp, vp, c_size, vp]
     lib.iso_vjp.restype = c_int
     lib.iso_vjp.argtypes = [vp, ctypes.POINTER(IsoBlocksC), vp, vp, c_size, vp]
+    lib.iso_vjp_yw.restype = c_int
+    lib.iso_vjp_yw.argtypes = [vp, ctypes.POINTER(IsoBlocksC), vp, vp, vp, vp, c_size, vp]
     lib.iso_status.restype = c_int
     lib.iso_status.argtypes = [vp, vp]
     lib.iso_strerror.restype = ctypes.c_char_p
@@ -218,9 +222,34 @@ def iso_vjp(grad: torch.Tensor, blocks: Blocks, *, out: torch.Tensor | None = No
     return out.view(blocks.shape)
 
 
+def iso_vjp_yw(grad: torch.Tensor, blocks: Blocks, y: torch.Tensor, *, want_y: bool = True,
+               ws: torch.Tensor | None = None):
+    """(grad_y or None, grad_w): grad_w = G_B (y_j - mean_B) / W_B over the fit's blocks, where y is the
+    tensor the fit was computed from (page "torchisotonic", "Semantics": differentiable in y and in w)."""
+    lib = load_library()
+    g2 = _as_rows(grad)
+    y2 = _as_rows(y)
+    rows, n = blocks.c.rows, blocks.c.n
+    for t, name in ((g2, "grad"), (y2, "y")):
+        if tuple(t.shape) != (rows, n) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous tensor of the fit's shape")
+        if _dtype_code(t) != blocks.c.dtype:
+            raise ValueError(f"{name} must have the fit's dtype")
+    gy = torch.empty_like(g2) if want_y else None
+    gw = torch.empty_like(g2)
+    if ws is None:
+        ws = workspace(rows, n, g2.dtype, g2.device)
+    code = lib.iso_vjp_yw(g2.data_ptr(), ctypes.byref(blocks.c), y2.data_ptr(),
+                          None if gy is None else gy.data_ptr(), gw.data_ptr(), ws.data_ptr(), ws.numel(),
+                          _stream_ptr(g2.device))
+    if code != ISO_OK:
+        raise IsoError(code, "iso_vjp_yw")
+    return (None if gy is None else gy.view(blocks.shape)), gw.view(blocks.shape)
+
+
 def iso_status(ws: torch.Tensor) -> int:
     return int(load_library().iso_status(ws.data_ptr(), _stream_ptr(ws.device)))
 
 
-__all__ = ["iso_fit", "iso_vjp", "iso_status", "iso_workspace_bytes", "iso_blocks_bytes", "workspace",
+__all__ = ["iso_fit", "iso_vjp", "iso_vjp_yw", "iso_status", "iso_workspace_bytes", "iso_blocks_bytes", "workspace",
            "Blocks", "IsoError", "load_library", "SYMBOLS"]

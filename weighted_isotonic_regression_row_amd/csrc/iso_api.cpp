@@ -112,12 +112,14 @@ int iso_fit(const void* y, const void* w, int64_t rows, int64_t n, int increasin
     return ISO_OK;
 }
 
-int iso_vjp(const void* grad, const iso_blocks* blocks, void* grad_y, void* workspace, size_t workspace_bytes,
-            void* stream) {
+int iso_vjp_yw(const void* grad, const iso_blocks* blocks, const void* y, void* grad_y, void* grad_w,
+               void* workspace, size_t workspace_bytes, void* stream) {
     if (!blocks || !blocks->valid) return ISO_EINVAL;
     if (blocks->rows < 0 || blocks->n < 0 || !valid_dtype(blocks->dtype)) return ISO_EINVAL;
     if (blocks->rows == 0 || blocks->n == 0) return ISO_OK;
-    if (!grad || !grad_y || !workspace) return ISO_EINVAL;
+    if (!grad || !workspace) return ISO_EINVAL;
+    if (!grad_y && !grad_w) return ISO_EINVAL;
+    if (grad_w && !y) return ISO_EINVAL;
     if (!blocks->start_bits_dev || !blocks->clip_bits_dev || !blocks->row_nan_dev) return ISO_EINVAL;
     if (((uintptr_t)workspace & 255u) != 0) return ISO_EINVAL;
     const iso::Layout L = iso::make_layout(blocks->rows, blocks->n);
@@ -125,7 +127,9 @@ int iso_vjp(const void* grad, const iso_blocks* blocks, void* grad_y, void* work
     iso::VjpLaunch v{};
     v.g = grad;
     v.w = blocks->w_dev;
+    v.y = y;
     v.out = grad_y;
+    v.out_w = grad_w;
     v.rows = blocks->rows;
     v.n = blocks->n;
     v.words = blocks->words;
@@ -138,6 +142,11 @@ int iso_vjp(const void* grad, const iso_blocks* blocks, void* grad_y, void* work
     v.stream = (hipStream_t)stream;
     if (iso::launch_vjp(v) != hipSuccess) return ISO_EHIP;
     return ISO_OK;
+}
+
+int iso_vjp(const void* grad, const iso_blocks* blocks, void* grad_y, void* workspace, size_t workspace_bytes,
+            void* stream) {
+    return iso_vjp_yw(grad, blocks, nullptr, grad_y, nullptr, workspace, workspace_bytes, stream);
 }
 
 int iso_status(const void* workspace, void* stream) {

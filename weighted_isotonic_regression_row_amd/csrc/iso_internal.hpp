@@ -125,9 +125,9 @@ inline Layout make_layout(int64_t rows, int64_t n) {
         L.ovf = take(L.ovf_stride * (size_t)rows);
         L.ovfrow = take(4 * (size_t)rows);
     }
-    // backward: per tile head, tail, carry, total (double2 each) + flag
+    // backward: per tile head, tail, carry, total (up to three doubles each) + flag
     const size_t tiles = (n > kSingleMax) ? (size_t)rows * (size_t)((n + kVjpTile - 1) / kVjpTile) : 0;
-    const size_t vjp_end = L.vjp + align256(tiles * (4 * 16 + 8));
+    const size_t vjp_end = L.vjp + align256(tiles * (4 * 24 + 8));
     L.total = (off > vjp_end ? off : vjp_end);
     if (L.total < 256) L.total = 256;
     return L;
@@ -154,7 +154,9 @@ struct FitLaunch {
 struct VjpLaunch {
     const void* g;
     const void* w;
-    void* out;
+    const void* y;  // needed for out_w
+    void* out;      // grad_y or nullptr
+    void* out_w;    // grad_w or nullptr
     int64_t rows, n, words;
     int dtype;
     const uint64_t* start_bits;

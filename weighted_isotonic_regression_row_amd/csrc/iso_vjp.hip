@@ -1,18 +1,23 @@
-// Backward kernels: vector-Jacobian product of the fit with respect to y.
+// Backward kernels: vector-Jacobian products of the fit with respect to y
+// and to the weights.
 //
 // Page "Merge Hulls Without Copying Vertices: GPU Isotonic Regression",
 // Appendix C: the product of the isotonic step is A g, A averaging over the
-// solver's blocks (and Sec. 7.8 for its cost).  With weights, differentiating
-// a block's value sum_B w y / sum_B w gives, for j in block B,
-//     grad_y[j] = w_j * sum_{i in B} g'_i / sum_{i in B} w_i,
-// where g'_i = g_i unless the clip was active at i (then 0).  The partition is
-// the forward pass's own (its block-start bits), as the page's tests require.
+// solver's blocks (and Sec. 7.8 for its cost).  With weights, a block B takes
+// the value mean_B = sum_B w y / sum_B w; differentiating it gives, for j in B,
+//     grad_y[j] = w_j * G_B / W_B,
+//     grad_w[j] = G_B * (y_j - mean_B) / W_B        (page "torchisotonic",
+//                 "Semantics": the fit is differentiable in y and in w),
+// where G_B = sum_{i in B} g'_i, g'_i = g_i unless the clip was active at i
+// (then 0), and W_B = sum_B w.  The partition is the forward pass's own (its
+// block-start bits), as the page's tests require.
 //
 // A tile of up to 8192 elements is one workgroup: a segmented inclusive scan
-// of (g', w) inside each 64-element group (wave64 shuffles), a carry across
-// groups, then every element reads its block's total at the block's last
-// element.  Rows longer than one tile go through three launches: per-tile
-// partial sums, a per-row carry pass, and the tile pass with those carries.
+// of (g', w) -- and w y when the weight product is asked for -- inside each
+// 64-element group (wave64 shuffles), a carry across groups, then every
+// element reads its block's totals at the block's last element.  Rows longer
+// than one tile go through three launches: per-tile partial sums, a per-row
+// carry pass, and the tile pass with those carries.
 #include <math.h>
 
 #include "iso_device.hpp"
@@ -20,31 +25,55 @@
 
 namespace iso {
 
+// Running block sums: (g', w) or (g', w, w y).
+template <int NF>
+struct Acc {
+    double v[NF];
+};
+template <int NF>
+__host__ __device__ __forceinline__ Acc<NF> acc_zero() {
+    Acc<NF> r;
+#pragma unroll
+    for (int k = 0; k < NF; ++k) r.v[k] = 0.0;
+    return r;
+}
+template <int NF>
+__device__ __forceinline__ Acc<NF> acc_sum(const Acc<NF>& a, const Acc<NF>& b) {
+    Acc<NF> r;
+#pragma unroll
+    for (int k = 0; k < NF; ++k) r.v[k] = a.v[k] + b.v[k];
+    return r;
+}
+
 struct VjpArgs {
     const void* g;
     const void* w;
-    void* out;
+    const void* y;  // the fit's input, for the weight product
+    void* out;      // grad_y, or nullptr
+    void* out_w;    // grad_w, or nullptr
     int64_t n, words;
     int T;       // elements per tile
     int ntiles;  // tiles per row
     const uint64_t* sb;
     const uint64_t* cb;
     const uint32_t* row_nan;
-    double2* head;   // [rows * ntiles] sum from the tile start to its first block start
-    double2* tail;   // [rows * ntiles] sum from the tile's last block start to its end
-    int* has;        // [rows * ntiles] tile holds a block start
-    double2* carry;  // [rows * ntiles] open block's sum before the tile
-    double2* tot;    // [rows * ntiles] total of the block open at the tile's end
-    int mode;        // 0: whole row in one tile; 1: partial sums; 2: tile pass of a long row
+    void* head;   // Acc [rows * ntiles] sums from the tile start to its first block start
+    void* tail;   // Acc [rows * ntiles] sums from the tile's last block start to its end
+    int* has;     // [rows * ntiles] tile holds a block start
+    void* carry;  // Acc [rows * ntiles] open block's sums before the tile
+    void* tot;    // Acc [rows * ntiles] totals of the block open at the tile's end
+    int mode;     // 0: whole row in one tile; 1: partial sums; 2: tile pass of a long row
 };
 
+template <int NF>
 __host__ __device__ inline size_t vjp_smem_bytes(int T) {
     const int G = (T + 63) / 64;
-    return sizeof(double2) * (size_t)T + (size_t)G * (sizeof(double2) * 2 + sizeof(int) * 3) + 64;
+    return sizeof(Acc<NF>) * (size_t)T + (size_t)G * (sizeof(Acc<NF>) * 2 + sizeof(int) * 3) + 64;
 }
 
-template <typename T>
+template <typename T, int NF>
 __global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
+    using A = Acc<NF>;
     extern __shared__ __align__(32) char smem[];
     const int64_t bid = blockIdx.x;
     const int64_t row = bid / a.ntiles;
@@ -52,26 +81,37 @@ __global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
     const int64_t t0 = (int64_t)tile * a.T;
     const int N = (int)((a.n - t0) < a.T ? (a.n - t0) : a.T);
     const int G = (N + 63) / 64;
-    double2* F = (double2*)smem;
-    double2* gtail = F + a.T;
-    double2* gcarry = gtail + G;
+    A* F = (A*)smem;
+    A* gtail = F + a.T;
+    A* gcarry = gtail + G;
     int* ghas = (int*)(gcarry + G);
     int* gfirst = ghas + G;
     int* gnext = gfirst + G;
 
     const T* g = (const T*)a.g + row * a.n + t0;
     const T* w = a.w ? (const T*)a.w + row * a.n + t0 : nullptr;
-    T* out = (T*)a.out + row * a.n + t0;
+    const T* y = (NF == 3) ? (const T*)a.y + row * a.n + t0 : nullptr;
+    T* out = a.out ? (T*)a.out + row * a.n + t0 : nullptr;
+    T* out_w = (NF == 3) ? (T*)a.out_w + row * a.n + t0 : nullptr;
     const uint64_t* sb = a.sb + row * a.words + t0 / 64;
     const uint64_t* cb = a.cb + row * a.words + t0 / 64;
     const int64_t ti = row * a.ntiles + tile;
+    A* head = (A*)a.head;
+    A* tail = (A*)a.tail;
+    A* carry = (A*)a.carry;
+    A* tot_open = (A*)a.tot;
 
     if (a.row_nan[row]) {
-        if (a.mode != 1)
-            for (int i = threadIdx.x; i < N; i += blockDim.x) out[i] = (T)NAN;
-        else if (threadIdx.x == 0) {
-            a.head[ti] = make_double2(0.0, 1.0);
-            a.tail[ti] = make_double2(0.0, 1.0);
+        if (a.mode != 1) {
+            for (int i = threadIdx.x; i < N; i += blockDim.x) {
+                if (out) out[i] = (T)NAN;
+                if (NF == 3) out_w[i] = (T)NAN;
+            }
+        } else if (threadIdx.x == 0) {
+            A u = acc_zero<NF>();
+            u.v[1] = 1.0;
+            head[ti] = u;
+            tail[ti] = u;
             a.has[ti] = 1;
         }
         return;
@@ -87,28 +127,27 @@ __global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
         const uint64_t vmask = (N - q * 64 >= 64) ? ~0ull : ((1ull << (N - q * 64)) - 1ull);
         const uint64_t sw = sb[q] & vmask;
         const uint64_t cw = cb[q];
-        double gv = 0.0, wv = 0.0;
+        A v = acc_zero<NF>();
         if (valid) {
-            gv = ((cw >> lane) & 1ull) ? 0.0 : (double)g[e];
-            wv = w ? (double)w[e] : 1.0;
+            v.v[0] = ((cw >> lane) & 1ull) ? 0.0 : (double)g[e];
+            v.v[1] = w ? (double)w[e] : 1.0;
+            if (NF == 3) v.v[NF - 1] = v.v[1] * (double)y[e];
         }
         int fl = (int)((sw >> lane) & 1ull);
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
-            const double og = __shfl_up(gv, d, 64);
-            const double ow = __shfl_up(wv, d, 64);
+            A o;
+#pragma unroll
+            for (int k = 0; k < NF; ++k) o.v[k] = __shfl_up(v.v[k], d, 64);
             const int of = __shfl_up(fl, d, 64);
             if (lane >= d) {
-                if (!fl) {
-                    gv = og + gv;
-                    wv = ow + wv;
-                }
+                if (!fl) v = acc_sum(o, v);
                 fl |= of;
             }
         }
-        if (valid) F[e] = make_double2(gv, wv);
+        if (valid) F[e] = v;
         if (lane == 63) {
-            gtail[q] = make_double2(gv, wv);
+            gtail[q] = v;
             ghas[q] = sw != 0ull;
             gfirst[q] = sw ? lo_bit(sw) : 64;
         }
@@ -116,11 +155,11 @@ __global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
     __syncthreads();
     // phase 2: carries across groups and the next block start after each group
     if (threadIdx.x == 0) {
-        double2 c = (a.mode == 2) ? a.carry[ti] : make_double2(0.0, 0.0);
+        A c = (a.mode == 2) ? carry[ti] : acc_zero<NF>();
         for (int q = 0; q < G; ++q) {
             gcarry[q] = c;
-            const double2 t = gtail[q];
-            c = ghas[q] ? t : make_double2(c.x + t.x, c.y + t.y);
+            const A t = gtail[q];
+            c = ghas[q] ? t : acc_sum(c, t);
         }
         int nx = N;
         for (int q = G - 1; q >= 0; --q) {
@@ -130,10 +169,10 @@ __global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
         if (a.mode == 1) {
             // tail: the open block at the tile's end (no carry in this pass);
             // the head is read after the carries are added below
-            a.tail[ti] = c;
+            tail[ti] = c;
             a.has[ti] = (nx < N) ? 1 : 0;
-            if (nx >= N) a.head[ti] = c;  // no start: the whole tile
-            gfirst[0] = nx;               // group 0's first start is no longer needed
+            if (nx >= N) head[ti] = c;  // no start: the whole tile
+            gfirst[0] = nx;             // group 0's first start is no longer needed
         }
     }
     __syncthreads();
@@ -142,11 +181,7 @@ __global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
         const int e = q * 64 + lane;
         if (e < N) {
             const uint64_t sw = sb[q];
-            if ((sw & bits_upto(lane)) == 0ull) {
-                const double2 c = gcarry[q];
-                const double2 v = F[e];
-                F[e] = make_double2(v.x + c.x, v.y + c.y);
-            }
+            if ((sw & bits_upto(lane)) == 0ull) F[e] = acc_sum(F[e], gcarry[q]);
         }
     }
     __syncthreads();
@@ -154,57 +189,68 @@ __global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
         // head: the tile's prefix before its first block start
         if (threadIdx.x == 0) {
             const int nx = gfirst[0];
-            if (nx < N) a.head[ti] = (nx > 0) ? F[nx - 1] : make_double2(0.0, 0.0);
+            if (nx < N) head[ti] = (nx > 0) ? F[nx - 1] : acc_zero<NF>();
         }
         return;
     }
-    // phase 4: every element takes its block's total, found at the block's end
-    const double2 open_total = (a.mode == 2) ? a.tot[ti] : make_double2(0.0, 0.0);
+    // phase 4: every element takes its block's totals, found at the block's end
+    const A open_total = (a.mode == 2) ? tot_open[ti] : acc_zero<NF>();
     for (int q = wid; q < G; q += nw) {
         const int e = q * 64 + lane;
         if (e < N) {
             const uint64_t vmask = (N - q * 64 >= 64) ? ~0ull : ((1ull << (N - q * 64)) - 1ull);
             const uint64_t later = sb[q] & vmask & bits_from(lane + 1);
             const int nxt = later ? q * 64 + lo_bit(later) : gnext[q];
-            double2 tot;
+            A tb;
             if (nxt < N)
-                tot = F[nxt - 1];
+                tb = F[nxt - 1];
             else
-                tot = (a.mode == 2) ? open_total : F[N - 1];
-            const double wv = w ? (double)w[e] : 1.0;
-            out[e] = (T)(wv * (tot.x / tot.y));
+                tb = (a.mode == 2) ? open_total : F[N - 1];
+            const double gw = tb.v[0] / tb.v[1];  // G_B / W_B
+            if (out) {
+                const double wv = w ? (double)w[e] : 1.0;
+                out[e] = (T)(wv * gw);
+            }
+            if (NF == 3) {
+                const double mean = tb.v[NF - 1] / tb.v[1];
+                out_w[e] = (T)(gw * ((double)y[e] - mean));
+            }
         }
     }
 }
 
 // per-row carries across tiles (one thread per row)
+template <int NF>
 __global__ void k_vjp_carry(VjpArgs a, int64_t rows) {
+    using A = Acc<NF>;
     const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= rows) return;
+    A* head = (A*)a.head;
+    A* tail = (A*)a.tail;
+    A* carry = (A*)a.carry;
+    A* tot = (A*)a.tot;
     const int64_t b = row * a.ntiles;
-    double2 c = make_double2(0.0, 0.0);
+    A c = acc_zero<NF>();
     for (int t = 0; t < a.ntiles; ++t) {
-        a.carry[b + t] = c;
-        const double2 hd = a.head[b + t], tl = a.tail[b + t];
-        c = a.has[b + t] ? tl : make_double2(c.x + hd.x, c.y + hd.y);
+        carry[b + t] = c;
+        c = a.has[b + t] ? tail[b + t] : acc_sum(c, head[b + t]);
     }
-    double2 after = c;
-    a.tot[b + a.ntiles - 1] = after;
+    A after = c;
+    tot[b + a.ntiles - 1] = after;
     for (int t = a.ntiles - 2; t >= 0; --t) {
-        if (a.has[b + t + 1]) {
-            const double2 ci = a.carry[b + t + 1], hd = a.head[b + t + 1];
-            after = make_double2(ci.x + hd.x, ci.y + hd.y);
-        }
-        a.tot[b + t] = after;
+        if (a.has[b + t + 1]) after = acc_sum(carry[b + t + 1], head[b + t + 1]);
+        tot[b + t] = after;
     }
 }
 
-template <typename T>
+template <typename T, int NF>
 static hipError_t launch_vjp_t(const VjpLaunch& l) {
     VjpArgs a{};
     a.g = l.g;
     a.w = l.w;
+    a.y = l.y;
     a.out = l.out;
+    a.out_w = l.out_w;
     a.n = l.n;
     a.words = l.words;
     a.sb = l.start_bits;
@@ -212,8 +258,8 @@ static hipError_t launch_vjp_t(const VjpLaunch& l) {
     a.row_nan = l.row_nan;
     static bool attr_set = false;
     if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)k_vjp_tile<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            (int)vjp_smem_bytes((int)kSingleMax));
+        (void)hipFuncSetAttribute((const void*)k_vjp_tile<T, NF>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  (int)vjp_smem_bytes<NF>((int)kSingleMax));
         attr_set = true;
     }
     if (l.n <= kSingleMax) {
@@ -222,33 +268,34 @@ static hipError_t launch_vjp_t(const VjpLaunch& l) {
         a.mode = 0;
         const int G = (a.T + 63) / 64;
         const int nt = G >= 32 ? 512 : (G >= 8 ? 256 : 64);
-        hipLaunchKernelGGL(k_vjp_tile<T>, dim3((unsigned)l.rows), dim3(nt), vjp_smem_bytes(a.T), l.stream, a);
+        hipLaunchKernelGGL((k_vjp_tile<T, NF>), dim3((unsigned)l.rows), dim3(nt), vjp_smem_bytes<NF>(a.T), l.stream,
+                           a);
         return hipGetLastError();
     }
     a.T = kVjpTile;
     a.ntiles = (int)((l.n + kVjpTile - 1) / kVjpTile);
     const size_t tiles = (size_t)l.rows * (size_t)a.ntiles;
-    char* p = l.ws + l.L.vjp;
-    a.head = (double2*)p;
-    a.tail = a.head + tiles;
-    a.carry = a.tail + tiles;
-    a.tot = a.carry + tiles;
-    a.has = (int*)(a.tot + tiles);
+    Acc<NF>* p = (Acc<NF>*)(l.ws + l.L.vjp);
+    a.head = p;
+    a.tail = p + tiles;
+    a.carry = p + 2 * tiles;
+    a.tot = p + 3 * tiles;
+    a.has = (int*)(p + 4 * tiles);
     a.mode = 1;
-    hipLaunchKernelGGL(k_vjp_tile<T>, dim3((unsigned)tiles), dim3(512), vjp_smem_bytes(a.T), l.stream, a);
+    hipLaunchKernelGGL((k_vjp_tile<T, NF>), dim3((unsigned)tiles), dim3(512), vjp_smem_bytes<NF>(a.T), l.stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_vjp_carry, dim3((unsigned)((l.rows + 63) / 64)), dim3(64), 0, l.stream, a, l.rows);
+    hipLaunchKernelGGL(k_vjp_carry<NF>, dim3((unsigned)((l.rows + 63) / 64)), dim3(64), 0, l.stream, a, l.rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.mode = 2;
-    hipLaunchKernelGGL(k_vjp_tile<T>, dim3((unsigned)tiles), dim3(512), vjp_smem_bytes(a.T), l.stream, a);
+    hipLaunchKernelGGL((k_vjp_tile<T, NF>), dim3((unsigned)tiles), dim3(512), vjp_smem_bytes<NF>(a.T), l.stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_vjp(const VjpLaunch& l) {
-    if (l.dtype == 0) return launch_vjp_t<float>(l);
-    return launch_vjp_t<double>(l);
+    if (l.out_w) return (l.dtype == 0) ? launch_vjp_t<float, 3>(l) : launch_vjp_t<double, 3>(l);
+    return (l.dtype == 0) ? launch_vjp_t<float, 2>(l) : launch_vjp_t<double, 2>(l);
 }
 
 }  // namespace iso
