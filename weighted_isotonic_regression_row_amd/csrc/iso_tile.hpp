@@ -529,25 +529,36 @@ __device__ inline int2 group_bridge(const Tile& t, int iA0, int iS, int jS, int 
 }
 
 // Copies list entries [s0, s1] to d0.. (d0 <= s0) with the calling group of G
-// lanes, a block of G entries at a time.  A block is read by all lanes before
-// any of it is written; a block's destination ends where the next block's
-// source starts (d0 <= s0), so no later source is overwritten.  The caller
-// orders the writes before its next reads of the list (wave_sync or barrier).
+// lanes, four blocks of G entries per step.  A step's blocks are read by all
+// lanes before any of them is written; a step's destinations end where the
+// next step's sources start (d0 <= s0), so no later source is overwritten.
+// The caller orders the writes before its next reads of the list (wave_sync
+// or barrier).
 __device__ inline void group_move(const Tile& t, int s0, int s1, int d0, int g, int G) {
+    constexpr int kB = 4;
     const int cnt = s1 - s0 + 1;
     if (d0 == s0 || cnt <= 0) return;  // uniform in the group
-    for (int off = 0; off < cnt; off += G) {
-        const int q = off + g;
-        unsigned short pv = 0;
-        double2 xy = make_double2(0.0, 0.0);
-        if (q < cnt) {
-            pv = t.V[s0 + q];
-            xy = t.VXY[s0 + q];
+    for (int off = 0; off < cnt; off += kB * G) {
+        unsigned short pv[kB];
+        double2 xy[kB];
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            const int q = off + b * G + g;
+            pv[b] = 0;
+            xy[b] = make_double2(0.0, 0.0);
+            if (q < cnt) {
+                pv[b] = t.V[s0 + q];
+                xy[b] = t.VXY[s0 + q];
+            }
         }
         wave_sync();
-        if (q < cnt) {
-            t.V[d0 + q] = pv;
-            t.VXY[d0 + q] = xy;
+#pragma unroll
+        for (int b = 0; b < kB; ++b) {
+            const int q = off + b * G + g;
+            if (q < cnt) {
+                t.V[d0 + q] = pv[b];
+                t.VXY[d0 + q] = xy[b];
+            }
         }
     }
 }
