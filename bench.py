@@ -4,7 +4,8 @@
                     [--no-cpu] [--copy-probe] [--cpu-seconds S]
 
 A step is one whole fit (every kernel of the path) over one batch of
-synthetic input already resident in HBM:
+synthetic input already resident in HBM (the backward products of the batch
+are timed separately and reported in "backward"):
 
   batch (the headline line; `value` is its elements/s):
          1000 rows x 5000 float32, y ~ N(0,1), w ~ U(0.1, 1.1), non-increasing,
@@ -119,6 +120,44 @@ def time_gpu(wl, steps, warmup):
     return (t1 - t0) * 1e3 / steps, float(np.mean(per)), float(np.median(per))
 
 
+def time_backward(wl, steps):
+    """Event-timed products of the fit (inputs and blocks resident): grad_y
+    alone, and grad_y with grad_w.  Returns a dict."""
+    import torch
+    import weighted_isotonic_regression_row_amd as iso
+    dev = torch.device("cuda:0")
+    y = torch.from_numpy(wl.y).to(dev)
+    w = None if wl.w is None else torch.from_numpy(wl.w).to(dev)
+    ws = iso.workspace(wl.rows, wl.n, y.dtype, dev)
+    _, blocks = iso.iso_fit(y, w, wl.increasing, wl.y_min, wl.y_max, ws=ws, blocks=True, check=True)
+    g = torch.randn_like(y)
+    gy = torch.empty_like(y)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    ms_y = run(lambda: iso.iso_vjp(g, blocks, out=gy, ws=ws))
+    ms_yw = run(lambda: iso.iso_vjp_yw(g, blocks, y, ws=ws))
+    elems = wl.rows * wl.n
+    es = wl.y.dtype.itemsize
+    wb = 0 if wl.w is None else es
+    by = elems * (2 * es + wb)          # g read, w read, grad_y written
+    byw = elems * (4 * es + wb)         # g, y, w read, grad_y and grad_w written
+    return {"vjp_ms": ms_y, "vjp_algorithmic_bytes": by, "vjp_hbm_frac": by / (ms_y * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "vjp_yw_ms": ms_yw, "vjp_yw_algorithmic_bytes": byw,
+            "vjp_yw_hbm_frac": byw / (ms_yw * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
 def copy_probe(nbytes=256 << 20, reps=20):
     """Device-to-device copy bandwidth of a plain copy of known size (read + write)."""
     import torch
@@ -206,6 +245,7 @@ def main():
                            "traffic": committed_traffic(), "kernel_ms_mean": kmean, "kernel_ms_median": kmed,
                            "bytes_per_element": 12, "elements_per_launch": elems,
                            "source_hash": source_hash()}
+        rec["backward"] = time_backward(wl, args.steps)
         if not args.no_cpu:
             log("cpu baseline (batch) ...")
             rec["cpu_baseline"] = cpu_baseline(wl, seconds=args.cpu_seconds)

@@ -106,6 +106,44 @@ def test_rows_past_the_lds_list_mixed_with_others(n, dtype):
     check_fit(fit.cpu().numpy(), z, wl.y, dtype, True, wl.name)
 
 
+@pytest.mark.parametrize("n", [1, 2, 5, 15, 16])
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_short_rows_one_per_lane(n, dtype):
+    """Rows of at most 16 elements are fitted one row per lane (the first
+    page, Sec. 3.5: short rows packed several to a warp): many rows of several
+    families, both orientations, clipped and not, with block bits and both
+    backward products."""
+    import weighted_isotonic_regression_row_amd as iso
+    r = workloads.rng(900 + n)
+    rows = 3000
+    parts = []
+    for kind, weights in (("noise", "uniform"), ("trend_noise", "extreme"), ("ties", "unit"), ("increasing", "unit"),
+                          ("constant", "uniform"), ("sawtooth", "uniform")):
+        parts.append(workloads.family(kind, rows // 6, n, seed=n, dtype=dtype, weights=weights))
+    y = np.concatenate([p.y for p in parts])
+    w = np.concatenate([p.w if p.w is not None else np.ones_like(p.y) for p in parts])
+    for inc, clip in ((True, None), (False, (-0.3, 0.4))):
+        wl = workloads.Workload(f"short_{rows}x{n}_{np.dtype(dtype).name}", y, w, inc)
+        if clip:
+            wl.y_min, wl.y_max = clip
+        fit, b, yd, wd = gpu_fit(wl)
+        z, bs, cl, rn, _ = oracle_fit(wl)
+        check_fit(fit.cpu().numpy(), z, wl.y, dtype, inc, wl.name)
+        gs, gc, grn = gpu_blocks(b)
+        assert not grn.any()
+        # the partition is unique away from exact ties; on tie data compare the fit only
+        g = r.standard_normal(y.shape).astype(dtype)
+        gy, gw = iso.iso_vjp_yw(to_dev(g), b, yd)
+        ref_y = oracle.vjp(g.astype(np.float64), gs, gc, grn, w.astype(np.float64))
+        ref_w = oracle.vjp_w(g.astype(np.float64), y.astype(np.float64), gs, gc, grn, w.astype(np.float64))
+        tol = 1e-12 if dtype == np.float64 else 2e-6
+        assert np.max(np.abs(gy.cpu().numpy().astype(np.float64) - ref_y)) <= tol * max(1.0, np.abs(ref_y).max())
+        assert np.max(np.abs(gw.cpu().numpy().astype(np.float64) - ref_w)) <= tol * max(1.0, np.abs(ref_w).max())
+        # block starts agree with the oracle's on the tie-free noise rows
+        k = rows // 6
+        np.testing.assert_array_equal(gs[:k], bs[:k])
+
+
 @pytest.mark.parametrize("n", [700, 5000, 30000])
 def test_block_starts_match_oracle_on_tie_free_data(n):
     wl = workloads.family("trend_noise", 4, n, seed=11, dtype=np.float64, weights="uniform")
@@ -218,7 +256,7 @@ def test_config3_soft_rank_forward_backward():
     np.testing.assert_array_equal(gs, bs)
 
 
-@pytest.mark.parametrize("n", [300, 20000])
+@pytest.mark.parametrize("n", [16, 300, 20000])
 def test_nan_rows_and_weight_errors(n):
     import weighted_isotonic_regression_row_amd as iso
     r = workloads.rng(7)

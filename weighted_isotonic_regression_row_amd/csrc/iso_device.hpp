@@ -102,6 +102,59 @@ __device__ __forceinline__ int wave_incl_scan_int(int v) {
     return wave_scan_incl(v, [](int a, int b) { return a + b; });
 }
 
+// K values of p[0..cnt) as float64 (0 past cnt); 16-byte vector loads when the
+// lane's elements are whole and aligned.
+template <typename T, int K>
+__device__ __forceinline__ void load_lane(const T* __restrict__ p, int cnt, double (&v)[K]) {
+    constexpr int VW = 16 / (int)sizeof(T);
+    if constexpr (K % VW == 0) {
+        if (cnt == K && (((uintptr_t)p) & 15) == 0) {
+            if constexpr (sizeof(T) == 4) {
+#pragma unroll
+                for (int q = 0; q < K / 4; ++q) {
+                    const float4 f = ((const float4*)p)[q];
+                    v[4 * q] = f.x;
+                    v[4 * q + 1] = f.y;
+                    v[4 * q + 2] = f.z;
+                    v[4 * q + 3] = f.w;
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < K / 2; ++q) {
+                    const double2 d = ((const double2*)p)[q];
+                    v[2 * q] = d.x;
+                    v[2 * q + 1] = d.y;
+                }
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j) v[j] = (j < cnt) ? (double)p[j] : 0.0;
+}
+
+template <typename T, int K>
+__device__ __forceinline__ void store_lane(T* __restrict__ p, int cnt, const double (&v)[K]) {
+    constexpr int VW = 16 / (int)sizeof(T);
+    if constexpr (K % VW == 0) {
+        if (cnt == K && (((uintptr_t)p) & 15) == 0) {
+            if constexpr (sizeof(T) == 4) {
+#pragma unroll
+                for (int q = 0; q < K / 4; ++q)
+                    ((float4*)p)[q] = make_float4((float)v[4 * q], (float)v[4 * q + 1], (float)v[4 * q + 2],
+                                                  (float)v[4 * q + 3]);
+            } else {
+#pragma unroll
+                for (int q = 0; q < K / 2; ++q) ((double2*)p)[q] = make_double2(v[2 * q], v[2 * q + 1]);
+            }
+            return;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < K; ++j)
+        if (j < cnt) p[j] = (T)v[j];
+}
+
 // ---------------------------------------------------------------------------
 // double-double arithmetic (error-free transformations; additions only, so no
 // contraction into fused multiply-adds can change them)

@@ -179,6 +179,69 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
 }
 
 // ---------------------------------------------------------------------------
+// rows of at most kLaneRow elements, one row per lane (first page, Sec. 3.5:
+// short rows are packed several to a warp; here each lane holds a whole row).
+// The lane's hull is the row's hull, so there is nothing to merge: a forward
+// pass over the points gives the slope of each hull edge at its end vertex,
+// and a backward pass hands every element the slope of the first vertex at or
+// after its right point.  No LDS, no barriers.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void k_rows_lane(RowArgs a, int64_t rows) {
+    constexpr int K = kLaneRow;
+    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= rows) return;
+    const int N = (int)a.n;
+    const T* y = (const T*)a.y + row * a.n;
+    const T* w = a.w ? (const T*)a.w + row * a.n : nullptr;
+    T* out = (T*)a.fit + row * a.n;
+    uint64_t* sb = a.start_bits ? a.start_bits + row * a.words : nullptr;  // one word: n <= 64
+    uint64_t* cb = a.clip_bits ? a.clip_bits + row * a.words : nullptr;
+    double xs[K], ys[K];
+    int f = 0;
+    const uint64_t mask = lane_hull<T, K>(y, w, N, !a.increasing, xs, ys, f);
+    if (f) {
+        for (int j = 0; j < N; ++j) out[j] = (T)NAN;
+        if (sb) {
+            *sb = 0ull;
+            *cb = 0ull;
+        }
+        if (a.row_nan) a.row_nan[row] = 1u;
+        if (f == 2) report_weight_error(a.status, a.epoch);
+        return;
+    }
+    // E[b] = slope of the hull edge ending at point b + 1 (where that point is
+    // a vertex); the edge starts at the previous vertex (px, py)
+    double E[K];
+    double px = 0.0, py = 0.0;
+#pragma unroll
+    for (int b = 0; b < K; ++b) {
+        E[b] = 0.0;
+        if (b < N && ((mask >> b) & 1ull)) {
+            E[b] = (ys[b] - py) / (xs[b] - px);
+            px = xs[b];
+            py = ys[b];
+        }
+    }
+    double vals[K];
+    uint64_t clipm = 0ull;
+    double cur = 0.0;
+#pragma unroll
+    for (int b = K - 1; b >= 0; --b) {
+        if (b < N && ((mask >> b) & 1ull)) cur = E[b];  // point N is always a vertex
+        bool c = false;
+        vals[b] = finish(cur, a.increasing, a.lo, a.hi, c);
+        if (b < N && c) clipm |= 1ull << b;
+    }
+    store_lane<T, K>(out, N, vals);
+    if (sb) {
+        *sb = ((mask << 1) | 1ull) & bits_upto(N - 1);  // element j starts a block iff point j is a vertex
+        *cb = clipm;
+    }
+    if (a.row_nan) a.row_nan[row] = 0u;
+}
+
+// ---------------------------------------------------------------------------
 // chunk hulls of long rows
 // ---------------------------------------------------------------------------
 struct ChunkArgs {
@@ -1097,6 +1160,11 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
     unsigned long long* status = (unsigned long long*)(a.ws + a.L.status);
     const RowArgs r{a.y, a.w, a.fit, a.n, a.increasing, a.lo, a.hi, a.start_bits, a.clip_bits, a.row_nan,
                     a.words, status, a.epoch, 0, nullptr, 0, nullptr, 0};
+    if (a.n <= kLaneRow) {
+        const unsigned grid = (unsigned)((a.rows + 255) / 256);
+        hipLaunchKernelGGL(k_rows_lane<T>, dim3(grid), dim3(256), 0, a.stream, r, (int64_t)a.rows);
+        return hipGetLastError();
+    }
     if (a.n <= kSingleMax) {
         int K, nl;
         row_shape((int)a.n, sizeof(T) == 4, K, nl);

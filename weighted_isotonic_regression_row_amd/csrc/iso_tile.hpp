@@ -125,59 +125,6 @@ __device__ __forceinline__ double vturn(const Tile& t, int i, int j, int k) {
 // 1. lane hull, in registers
 // ---------------------------------------------------------------------------
 
-// K values of p[0..cnt) as float64 (0 past cnt); 16-byte vector loads when the
-// lane's elements are whole and aligned.
-template <typename T, int K>
-__device__ __forceinline__ void load_lane(const T* __restrict__ p, int cnt, double (&v)[K]) {
-    constexpr int VW = 16 / (int)sizeof(T);
-    if constexpr (K % VW == 0) {
-        if (cnt == K && (((uintptr_t)p) & 15) == 0) {
-            if constexpr (sizeof(T) == 4) {
-#pragma unroll
-                for (int q = 0; q < K / 4; ++q) {
-                    const float4 f = ((const float4*)p)[q];
-                    v[4 * q] = f.x;
-                    v[4 * q + 1] = f.y;
-                    v[4 * q + 2] = f.z;
-                    v[4 * q + 3] = f.w;
-                }
-            } else {
-#pragma unroll
-                for (int q = 0; q < K / 2; ++q) {
-                    const double2 d = ((const double2*)p)[q];
-                    v[2 * q] = d.x;
-                    v[2 * q + 1] = d.y;
-                }
-            }
-            return;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < K; ++j) v[j] = (j < cnt) ? (double)p[j] : 0.0;
-}
-
-template <typename T, int K>
-__device__ __forceinline__ void store_lane(T* __restrict__ p, int cnt, const double (&v)[K]) {
-    constexpr int VW = 16 / (int)sizeof(T);
-    if constexpr (K % VW == 0) {
-        if (cnt == K && (((uintptr_t)p) & 15) == 0) {
-            if constexpr (sizeof(T) == 4) {
-#pragma unroll
-                for (int q = 0; q < K / 4; ++q)
-                    ((float4*)p)[q] = make_float4((float)v[4 * q], (float)v[4 * q + 1], (float)v[4 * q + 2],
-                                                  (float)v[4 * q + 3]);
-            } else {
-#pragma unroll
-                for (int q = 0; q < K / 2; ++q) ((double2*)p)[q] = make_double2(v[2 * q], v[2 * q + 1]);
-            }
-            return;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < K; ++j)
-        if (j < cnt) p[j] = (T)v[j];
-}
-
 // The wave's K * 64 elements of one input through LDS, for lanes whose K
 // elements are not a whole number of 64-byte segments (per-lane 16-byte loads
 // then touch each segment from several lanes and instructions, and HBM serves
@@ -710,9 +657,9 @@ __device__ inline void tile_expand(const Tile& t, uint64_t mask, int increasing,
 
 // Block-start and clip bit words of the tile's elements (the tile starts at
 // a multiple of 64 elements).  Element i >= 1 starts a block iff point i is a
-// vertex; element 0 always does.  Lane masks are K bits wide (K divides 64):
-// concatenated, bit lK + b stands for point lK + b + 1.  Needs M and CM
-// written and a barrier.
+// vertex; element 0 always does.  Lane masks are K bits wide: concatenated,
+// bit lK + b stands for point lK + b + 1.  Needs M and CM written and a
+// barrier.
 template <int K>
 __device__ inline void tile_bits(const Tile& t, uint64_t* __restrict__ sbits, uint64_t* __restrict__ cbits) {
     const int words = (t.N + 63) / 64;

@@ -44,6 +44,14 @@ __device__ __forceinline__ Acc<NF> acc_sum(const Acc<NF>& a, const Acc<NF>& b) {
     for (int k = 0; k < NF; ++k) r.v[k] = a.v[k] + b.v[k];
     return r;
 }
+// p ? a : b field by field (a select of whole structs would go through memory)
+template <int NF>
+__device__ __forceinline__ Acc<NF> acc_pick(bool p, const Acc<NF>& a, const Acc<NF>& b) {
+    Acc<NF> r;
+#pragma unroll
+    for (int k = 0; k < NF; ++k) r.v[k] = p ? a.v[k] : b.v[k];
+    return r;
+}
 
 struct VjpArgs {
     const void* g;
@@ -155,11 +163,12 @@ __global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
     __syncthreads();
     // phase 2: carries across groups and the next block start after each group
     if (threadIdx.x == 0) {
-        A c = (a.mode == 2) ? carry[ti] : acc_zero<NF>();
+        A c = acc_zero<NF>();
+        if (a.mode == 2) c = carry[ti];
         for (int q = 0; q < G; ++q) {
             gcarry[q] = c;
             const A t = gtail[q];
-            c = ghas[q] ? t : acc_sum(c, t);
+            c = acc_pick(ghas[q] != 0, t, acc_sum(c, t));
         }
         int nx = N;
         for (int q = G - 1; q >= 0; --q) {
@@ -189,23 +198,20 @@ __global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
         // head: the tile's prefix before its first block start
         if (threadIdx.x == 0) {
             const int nx = gfirst[0];
-            if (nx < N) head[ti] = (nx > 0) ? F[nx - 1] : acc_zero<NF>();
+            if (nx < N) head[ti] = acc_pick(nx > 0, F[max(nx, 1) - 1], acc_zero<NF>());
         }
         return;
     }
     // phase 4: every element takes its block's totals, found at the block's end
-    const A open_total = (a.mode == 2) ? tot_open[ti] : acc_zero<NF>();
+    A open_total = acc_zero<NF>();
+    if (a.mode == 2) open_total = tot_open[ti];
     for (int q = wid; q < G; q += nw) {
         const int e = q * 64 + lane;
         if (e < N) {
             const uint64_t vmask = (N - q * 64 >= 64) ? ~0ull : ((1ull << (N - q * 64)) - 1ull);
             const uint64_t later = sb[q] & vmask & bits_from(lane + 1);
             const int nxt = later ? q * 64 + lo_bit(later) : gnext[q];
-            A tb;
-            if (nxt < N)
-                tb = F[nxt - 1];
-            else
-                tb = (a.mode == 2) ? open_total : F[N - 1];
+            const A tb = acc_pick(nxt < N, F[min(nxt, N) - 1], acc_pick(a.mode == 2, open_total, F[N - 1]));
             const double gw = tb.v[0] / tb.v[1];  // G_B / W_B
             if (out) {
                 const double wv = w ? (double)w[e] : 1.0;
@@ -233,13 +239,85 @@ __global__ void k_vjp_carry(VjpArgs a, int64_t rows) {
     A c = acc_zero<NF>();
     for (int t = 0; t < a.ntiles; ++t) {
         carry[b + t] = c;
-        c = a.has[b + t] ? tail[b + t] : acc_sum(c, head[b + t]);
+        c = acc_pick(a.has[b + t] != 0, tail[b + t], acc_sum(c, head[b + t]));
     }
     A after = c;
     tot[b + a.ntiles - 1] = after;
     for (int t = a.ntiles - 2; t >= 0; --t) {
         if (a.has[b + t + 1]) after = acc_sum(carry[b + t + 1], head[b + t + 1]);
         tot[b + t] = after;
+    }
+}
+
+// Rows of at most kLaneRow elements, one row per lane: running block sums
+// forward, then each block's totals handed back to its elements.  Whole,
+// aligned rows are read and written with 16-byte accesses.
+template <typename T, int NF>
+__global__ __launch_bounds__(256) void k_vjp_lane(VjpArgs a, int64_t rows) {
+    using A = Acc<NF>;
+    constexpr int K = kLaneRow;
+    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= rows) return;
+    const int N = (int)a.n;
+    const T* g = (const T*)a.g + row * a.n;
+    const T* w = a.w ? (const T*)a.w + row * a.n : nullptr;
+    const T* y = (NF == 3) ? (const T*)a.y + row * a.n : nullptr;
+    T* out = a.out ? (T*)a.out + row * a.n : nullptr;
+    T* out_w = (NF == 3) ? (T*)a.out_w + row * a.n : nullptr;
+    if (a.row_nan[row]) {
+        for (int j = 0; j < N; ++j) {
+            if (out) out[j] = (T)NAN;
+            if (NF == 3) out_w[j] = (T)NAN;
+        }
+        return;
+    }
+    const uint64_t sw = a.sb[row * a.words], cw = a.cb[row * a.words];
+    A run[K];
+    {
+        double gv[K], wv[K], yv[K];
+        load_lane<T, K>(g, N, gv);
+        if (w) {
+            load_lane<T, K>(w, N, wv);
+        } else {
+#pragma unroll
+            for (int j = 0; j < K; ++j) wv[j] = 1.0;
+        }
+        if (NF == 3) load_lane<T, K>(y, N, yv);
+        A c = acc_zero<NF>();
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            if (j < N) {
+                if ((sw >> j) & 1ull) c = acc_zero<NF>();
+                c.v[0] += ((cw >> j) & 1ull) ? 0.0 : gv[j];
+                c.v[1] += wv[j];
+                if (NF == 3) c.v[NF - 1] += wv[j] * yv[j];
+            }
+            run[j] = c;
+        }
+    }
+    double gw[K];  // G_B / W_B of each element's block, then the products
+    double mean[K];
+    A tot = acc_zero<NF>();
+#pragma unroll
+    for (int j = K - 1; j >= 0; --j) {
+        // element j closes its block when it is the last or the next starts one
+        if (j < N && (j == N - 1 || ((sw >> (j + 1)) & 1ull))) tot = run[j];
+        gw[j] = tot.v[0] / tot.v[1];
+        mean[j] = (NF == 3) ? tot.v[NF - 1] / tot.v[1] : 0.0;
+    }
+    if (out) {
+        double v[K];
+        if (w) load_lane<T, K>(w, N, v);
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = (w ? v[j] : 1.0) * gw[j];
+        store_lane<T, K>(out, N, v);
+    }
+    if (NF == 3) {
+        double v[K];
+        load_lane<T, K>(y, N, v);
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = gw[j] * (v[j] - mean[j]);
+        store_lane<T, K>(out_w, N, v);
     }
 }
 
@@ -256,6 +334,11 @@ static hipError_t launch_vjp_t(const VjpLaunch& l) {
     a.sb = l.start_bits;
     a.cb = l.clip_bits;
     a.row_nan = l.row_nan;
+    if (l.n <= kLaneRow) {
+        hipLaunchKernelGGL((k_vjp_lane<T, NF>), dim3((unsigned)((l.rows + 255) / 256)), dim3(256), 0, l.stream, a,
+                           l.rows);
+        return hipGetLastError();
+    }
     static bool attr_set = false;
     if (!attr_set) {
         (void)hipFuncSetAttribute((const void*)k_vjp_tile<T, NF>, hipFuncAttributeMaxDynamicSharedMemorySize,
