@@ -1116,15 +1116,16 @@ static void row_shape(int N, bool f32, int& K, int& nl) {
 }
 
 // Vertices the LDS list of a row holds.  A CU runs at most four waves per
-// SIMD at these kernels' register budget, and a workgroup of W waves places
-// ceil(W/4) of them on its busiest SIMD, so 4 / ceil(W/4) workgroups share a
-// CU; the list takes what their share of the 160 KiB leaves (at least a
+// SIMD at these kernels' register budget.  A workgroup of W <= 4 waves puts
+// one wave on each of W SIMDs, so 16 / W of them share a CU; one of W > 4
+// waves puts ceil(W/4) of them on its busiest SIMD, so 4 / ceil(W/4) share
+// it.  The list takes what their share of the 160 KiB leaves (at least a
 // quarter of the points).  Rows that need more go to k_row_ovf.
 static int row_list_cap(int N, int nl, int K) {
     const int W = nl / 64;
     const int per_simd = (W + 3) / 4;
-    const long wgs = per_simd >= 4 ? 1 : 4 / per_simd;
-    const long target = 163840 / wgs - 2048;
+    const long wgs = (W <= 4) ? 16 / W : (per_simd >= 4 ? 1 : 4 / per_simd);
+    const long target = 163840 / wgs - 512;
     const long fixed = (long)tile_smem_bytes(nl, 0, K);
     const long room = (target - fixed) / 18;
     const long cap = room > N / 4 ? room : N / 4;
