@@ -1136,11 +1136,8 @@ template <typename T, int K>
 static hipError_t launch_row(const FitLaunch& a, RowArgs r, int nl) {
     r.cap = row_list_cap((int)a.n, nl, K);
     const size_t smem = tile_smem_bytes(nl, r.cap, K);
-    static size_t attr = 0;  // largest dynamic LDS requested so far for this instance
-    if (smem > attr) {
-        (void)hipFuncSetAttribute((const void*)k_row_fit<T, K>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-        attr = smem;
-    }
+    static size_t seen[kMaxDevices] = {};
+    (void)ensure_lds((const void*)k_row_fit<T, K>, smem, seen);
     r.ovf = a.ws + a.L.ovf;
     r.ovf_stride = (int64_t)a.L.ovf_stride;
     // stage the inputs through LDS when a lane's K elements are not whole
@@ -1199,12 +1196,8 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
     ca.cvi = (int*)(a.ws + a.L.cvi);
     {
         const size_t smem = tile_smem_bytes(kChunkLanes, kChunk, kLaneK);
-        static bool attr_set = false;
-        if (!attr_set) {
-            (void)hipFuncSetAttribute((const void*)k_chunk_hull<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      (int)smem);
-            attr_set = true;
-        }
+        static size_t seen[kMaxDevices] = {};
+        (void)ensure_lds((const void*)k_chunk_hull<T>, smem, seen);
         hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)(a.rows * m)), dim3(kChunkLanes), smem, a.stream, ca);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -1238,12 +1231,8 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
         if (e != hipSuccess) return e;
     }
     {
-        static bool attr_set = false;
-        if (!attr_set) {
-            (void)hipFuncSetAttribute((const void*)k_merge_top<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      (int)merge_top_smem_bytes(kMergeLdsChunks, 1));
-            attr_set = true;
-        }
+        static size_t seen[kMaxDevices] = {};
+        (void)ensure_lds((const void*)k_merge_top<T>, merge_top_smem_bytes(kMergeLdsChunks, 1), seen);
         hipLaunchKernelGGL(k_merge_top<T>, dim3((unsigned)a.rows), dim3(kMergeThreads),
                            merge_top_smem_bytes(m, ma.use_lds), a.stream, ma);
         hipError_t e = hipGetLastError();

@@ -170,6 +170,21 @@ struct VjpLaunch {
     hipStream_t stream;
 };
 
+// Raises a kernel's dynamic-LDS limit to at least `bytes` on the current
+// device.  The attribute belongs to the device, so `seen` (the call site's
+// static table, one entry per device id) records what each device was given;
+// concurrent first calls may both set it, which is harmless.
+constexpr int kMaxDevices = 64;
+inline hipError_t ensure_lds(const void* fn, size_t bytes, size_t (&seen)[kMaxDevices]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (seen[dev] >= bytes) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) seen[dev] = bytes;
+    return e;
+}
+
 // Launchers (iso_fit.hip, iso_vjp.hip).  Return hipSuccess or the launch error.
 hipError_t launch_fit(const FitLaunch& a);
 hipError_t launch_vjp(const VjpLaunch& l);

@@ -339,12 +339,8 @@ static hipError_t launch_vjp_t(const VjpLaunch& l) {
                            l.rows);
         return hipGetLastError();
     }
-    static bool attr_set = false;
-    if (!attr_set) {
-        (void)hipFuncSetAttribute((const void*)k_vjp_tile<T, NF>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                  (int)vjp_smem_bytes<NF>((int)kSingleMax));
-        attr_set = true;
-    }
+    static size_t seen[kMaxDevices] = {};
+    (void)ensure_lds((const void*)k_vjp_tile<T, NF>, vjp_smem_bytes<NF>((int)kSingleMax), seen);
     if (l.n <= kSingleMax) {
         a.T = (int)l.n;
         a.ntiles = 1;
