@@ -321,6 +321,201 @@ __global__ __launch_bounds__(256) void k_vjp_lane(VjpArgs a, int64_t rows) {
     }
 }
 
+// Rows of kLaneRow < n <= kSingleMax elements, one workgroup per row, all
+// sums in registers (kVjpK elements per lane):
+//   1. each lane forms the segmented prefix sums of its elements (reset at
+//      every block start);
+//   2. a segmented scan over the lanes (DPP inside each wave, the waves'
+//      aggregates through LDS) gives every lane the sums of the block that is
+//      open when the lane begins, and a max-scan gives, for the block open at
+//      each lane's end, the lane where that block began;
+//   3. the lane where a block that began in an earlier lane ends writes the
+//      block's totals to that lane's LDS slot; after one barrier the lanes
+//      that the block spans read them;
+//   4. a backward pass over each lane's elements hands every element its
+//      block's totals and writes the products.
+constexpr int kVjpK = 8;
+
+template <int NF>
+struct SegSum {
+    int f;  // a block starts inside the span
+    Acc<NF> a;
+};
+// (earlier, later): the later span's sums restart if a block starts in it
+template <int NF>
+__device__ __forceinline__ SegSum<NF> seg_op(const SegSum<NF>& x, const SegSum<NF>& y) {
+    SegSum<NF> r;
+    r.f = x.f | y.f;
+#pragma unroll
+    for (int k = 0; k < NF; ++k) r.a.v[k] = y.f ? y.a.v[k] : x.a.v[k] + y.a.v[k];
+    return r;
+}
+template <int CTRL, int ROWS, int NF>
+__device__ __forceinline__ SegSum<NF> seg_move(const SegSum<NF>& x) {
+    SegSum<NF> r;
+    r.f = dpp_move<CTRL, ROWS>(x.f);
+#pragma unroll
+    for (int k = 0; k < NF; ++k) r.a.v[k] = dpp_move<CTRL, ROWS>(x.a.v[k]);
+    return r;
+}
+template <int NF>
+__device__ __forceinline__ SegSum<NF> seg_scan_wave(SegSum<NF> x) {
+    x = seg_op(seg_move<0x111, 0xf>(x), x);
+    x = seg_op(seg_move<0x112, 0xf>(x), x);
+    x = seg_op(seg_move<0x114, 0xf>(x), x);
+    x = seg_op(seg_move<0x118, 0xf>(x), x);
+    x = seg_op(seg_move<0x142, 0xa>(x), x);
+    x = seg_op(seg_move<0x143, 0xc>(x), x);
+    return x;
+}
+__device__ __forceinline__ int max_scan_wave(int v) {
+    return wave_scan_incl(v, [](int a, int b) { return a > b ? a : b; });
+}
+
+template <int NF>
+__host__ __device__ inline size_t vjp_row_smem_bytes(int nl) {
+    // slots [nl] + per wave (flag, sums) and max-scan values
+    return sizeof(Acc<NF>) * (size_t)nl + 16 * (sizeof(Acc<NF>) + 2 * sizeof(int)) + 64;
+}
+
+template <typename T, int NF>
+__global__ __launch_bounds__(1024) void k_vjp_row(VjpArgs a) {
+    using A = Acc<NF>;
+    constexpr int K = kVjpK;
+    extern __shared__ __align__(32) char smem[];
+    const int64_t row = blockIdx.x;
+    const int N = (int)a.n;
+    const int l = threadIdx.x, lane = lane_id(), wid = l >> 6, nw = blockDim.x >> 6;
+    A* slot = (A*)smem;
+    A* wsum = slot + blockDim.x;
+    int* wflag = (int*)(wsum + 16);
+    int* wmax = wflag + 16;
+    const T* g = (const T*)a.g + row * a.n;
+    const T* w = a.w ? (const T*)a.w + row * a.n : nullptr;
+    const T* y = (NF == 3) ? (const T*)a.y + row * a.n : nullptr;
+    T* out = a.out ? (T*)a.out + row * a.n : nullptr;
+    T* out_w = (NF == 3) ? (T*)a.out_w + row * a.n : nullptr;
+    if (a.row_nan[row]) {  // uniform: before any barrier
+        for (int i = l; i < N; i += blockDim.x) {
+            if (out) out[i] = (T)NAN;
+            if (NF == 3) out_w[i] = (T)NAN;
+        }
+        return;
+    }
+    const int e0 = l * K;
+    const int cnt = min(max(N - e0, 0), K);
+    const int words = (N + 63) / 64;
+    // start bits of elements e0 .. e0 + K (one past the lane), clip bits of the lane's
+    uint32_t sbit = 0, cbit = 0;
+    if (cnt > 0) {
+        const int q = e0 >> 6, off = e0 & 63;
+        const uint64_t* sb = a.sb + row * a.words;
+        const uint64_t* cb = a.cb + row * a.words;
+        const uint64_t s0 = sb[q], s1 = (q + 1 < words) ? sb[q + 1] : 0ull;
+        const uint64_t win = (s0 >> off) | (off ? (s1 << (64 - off)) : 0ull);
+        sbit = (uint32_t)(win & ((1ull << (K + 1)) - 1ull));
+        cbit = (uint32_t)((cb[q] >> off) & ((1ull << K) - 1ull));
+    }
+    // 1. in-lane segmented prefix sums
+    double gv[K], wv[K], yv[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) gv[j] = wv[j] = yv[j] = 0.0;
+    if (cnt > 0) {
+        load_lane<T, K>(g + e0, cnt, gv);
+        if (w) {
+            load_lane<T, K>(w + e0, cnt, wv);
+        } else {
+#pragma unroll
+            for (int j = 0; j < K; ++j) wv[j] = 1.0;
+        }
+        if (NF == 3) load_lane<T, K>(y + e0, cnt, yv);
+    }
+    A P[K];
+    {
+        A c = acc_zero<NF>();
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            if ((sbit >> j) & 1u) c = acc_zero<NF>();
+            if (j < cnt) {
+                c.v[0] += ((cbit >> j) & 1u) ? 0.0 : gv[j];
+                c.v[1] += wv[j];
+                if (NF == 3) c.v[NF - 1] += wv[j] * yv[j];
+            }
+            P[j] = c;
+        }
+    }
+    const uint32_t own = sbit & ((1u << K) - 1u) & ((cnt >= K) ? 0xFFFFFFFFu : ((1u << cnt) - 1u));
+    // 2. carries: segmented scan of (block starts in the lane, sums since its last start)
+    SegSum<NF> me;
+    me.f = own ? 1 : 0;
+    me.a = P[K - 1];
+    SegSum<NF> inc = seg_scan_wave(me);
+    int mx = max_scan_wave(own ? l + 1 : 0);
+    if (lane == kWave - 1) {
+        wsum[wid] = inc.a;
+        wflag[wid] = inc.f;
+        wmax[wid] = mx;
+    }
+    __syncthreads();
+    SegSum<NF> pre;
+    pre.f = 0;
+    pre.a = acc_zero<NF>();
+    int pmax = 0;
+    for (int k = 0; k < wid; ++k) {
+        SegSum<NF> o;
+        o.f = wflag[k];
+        o.a = wsum[k];
+        pre = seg_op(pre, o);
+        pmax = max(pmax, wmax[k]);
+    }
+    SegSum<NF> ex;  // exclusive within the wave
+    ex.f = dpp_move<0x138, 0xf>(inc.f);
+#pragma unroll
+    for (int k = 0; k < NF; ++k) ex.a.v[k] = dpp_move<0x138, 0xf>(inc.a.v[k]);
+    const SegSum<NF> cin = seg_op(pre, ex);  // sums of the block open when the lane begins
+    // lanes (+1) where blocks began: the last one before the lane holds the
+    // block open at its start, the last one up to it the block open at its end
+    const int begin_open = max(pmax, dpp_move<0x138, 0xf>(mx)) - 1;
+    const int end_open = max(pmax, mx) - 1;
+    // the carry reaches the elements before the lane's first start
+    const int first = own ? (__ffs((int)own) - 1) : K;
+#pragma unroll
+    for (int j = 0; j < K; ++j) P[j] = acc_pick(j < first, acc_sum(cin.a, P[j]), P[j]);
+    // 3. a block that began in an earlier lane and ends here: totals to its slot
+    //    (element j ends a block when it is the row's last or j + 1 starts one)
+    int last_end = -1, first_end = K;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const bool end = (j < cnt) && ((e0 + j == N - 1) || ((sbit >> (j + 1)) & 1u));
+        if (end) {
+            last_end = j;
+            if (first_end == K) first_end = j;
+        }
+    }
+    if (first_end < K && first_end < first && begin_open >= 0) {
+        A v = acc_zero<NF>();
+#pragma unroll
+        for (int j = 0; j < K; ++j) v = acc_pick(j == first_end, P[j], v);  // no indexed access to registers
+        slot[begin_open] = v;
+    }
+    __syncthreads();
+    // 4. totals per element, backward; elements after the lane's last block end
+    //    belong to the block open at its end
+    A tot = acc_zero<NF>();
+    if (cnt > 0 && last_end < cnt - 1) tot = slot[end_open];
+#pragma unroll
+    for (int j = K - 1; j >= 0; --j) {
+        tot = acc_pick(j == last_end || (j < last_end && ((sbit >> (j + 1)) & 1u)), P[j], tot);
+        const double gw = tot.v[0] / tot.v[1];
+        gv[j] = wv[j] * gw;
+        if (NF == 3) yv[j] = gw * (yv[j] - tot.v[NF - 1] / tot.v[1]);
+    }
+    if (cnt > 0) {
+        if (out) store_lane<T, K>(out + e0, cnt, gv);
+        if (NF == 3) store_lane<T, K>(out_w + e0, cnt, yv);
+    }
+}
+
 template <typename T, int NF>
 static hipError_t launch_vjp_t(const VjpLaunch& l) {
     VjpArgs a{};
@@ -342,12 +537,8 @@ static hipError_t launch_vjp_t(const VjpLaunch& l) {
     static size_t seen[kMaxDevices] = {};
     (void)ensure_lds((const void*)k_vjp_tile<T, NF>, vjp_smem_bytes<NF>((int)kSingleMax), seen);
     if (l.n <= kSingleMax) {
-        a.T = (int)l.n;
-        a.ntiles = 1;
-        a.mode = 0;
-        const int G = (a.T + 63) / 64;
-        const int nt = G >= 32 ? 512 : (G >= 8 ? 256 : 64);
-        hipLaunchKernelGGL((k_vjp_tile<T, NF>), dim3((unsigned)l.rows), dim3(nt), vjp_smem_bytes<NF>(a.T), l.stream,
+        const int nl = (int)(((l.n + kVjpK - 1) / kVjpK + 63) / 64 * 64);
+        hipLaunchKernelGGL((k_vjp_row<T, NF>), dim3((unsigned)l.rows), dim3(nl), vjp_row_smem_bytes<NF>(nl), l.stream,
                            a);
         return hipGetLastError();
     }
