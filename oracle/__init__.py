@@ -138,3 +138,38 @@ def vjp_w(g, y, block_start, clipped=None, row_nan=None, w=None):
     if st != OK:
         raise ValueError("invalid arguments")
     return out
+
+
+def soft_rank(x, eps=1.0):
+    """Soft rank with quadratic regularization (first page, Sec. 7.9): theta = x / eps is sorted in
+    decreasing order into s, the non-increasing fit v of z = s - (n, n-1, ..., 1) is computed with unit
+    weights, and the rank of the element at sorted position i is s_i - v_i, put back in the original order.
+
+    The order of theta is the order of x (eps > 0), so x itself is sorted; equal values keep their index
+    order (any order gives the same ranks: equal s_i pool into one block).  Returns
+    (r, perm, block_start, row_nan): perm[r, i] is the index of the element at sorted position i, and
+    block_start / row_nan describe the fit's partition over the sorted positions.  A row holding a NaN
+    comes back NaN.
+    """
+    x2 = _as2d(x)
+    rows, n = x2.shape
+    if not (eps > 0 and np.isfinite(eps)):
+        raise ValueError("eps must be positive and finite")
+    perm = np.argsort(-x2, axis=1, kind="stable")
+    s = np.take_along_axis(x2, perm, axis=1) / eps
+    z = s - np.arange(n, 0, -1, dtype=np.float64)[None, :]
+    v, bs, _cl, rn, _st = fit(z, None, increasing=False)
+    r = np.empty_like(x2)
+    np.put_along_axis(r, perm, s - v, axis=1)
+    return r, perm, bs, rn
+
+
+def soft_rank_vjp(g, eps, perm, block_start, row_nan=None):
+    """Vector-Jacobian product of soft_rank in x: with g_s the upstream gradient in sorted order and A the
+    block averaging of the fit (unit weights), d/dx = P^T (g_s - A g_s) / eps, P the sorting permutation."""
+    g2 = _as2d(g)
+    gs = np.take_along_axis(g2, perm, axis=1)
+    ags = vjp(gs, block_start, None, row_nan)
+    out = np.empty_like(g2)
+    np.put_along_axis(out, perm, (gs - ags) / eps, axis=1)
+    return out

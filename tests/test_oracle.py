@@ -386,3 +386,125 @@ def test_oracle_vjp_w_scale_invariance(seed):
     v = oracle.vjp_w(g, y, bs, cl, rn, w)
     s = np.sum(w * v, axis=1)
     assert np.max(np.abs(s)) <= 1e-12 * max(1.0, np.abs(w * v).sum(axis=1).max())
+
+
+# ---------------------------------------------------------------- soft rank (first page, Sec. 7.9)
+
+def hard_ranks(x):
+    """1 for the smallest value of a row, n for the largest (distinct values)."""
+    return (np.argsort(np.argsort(x, axis=-1, kind="stable"), axis=-1, kind="stable") + 1).astype(np.float64)
+
+
+@pytest.mark.parametrize("n", [1, 2, 7, 64, 513])
+def test_soft_rank_one_block_closed_form(n):
+    """Sorted gaps below 1 make z = s - (n..1) strictly increasing, so the non-increasing fit pools the whole
+    row into its mean and r = theta - mean(theta) + (n + 1) / 2."""
+    r = workloads.rng(n)
+    for eps in (1.0, 2.5):
+        x = r.random((3, n)) * 0.99 * eps
+        got, perm, bs, rn = oracle.soft_rank(x, eps)
+        theta = x / eps
+        want = theta - theta.mean(axis=1, keepdims=True) + (n + 1) / 2.0
+        np.testing.assert_allclose(got, want, rtol=0, atol=1e-12 * n)
+        assert bs[:, 0].all() and not bs[:, 1:].any() and not rn.any()
+
+
+@pytest.mark.parametrize("n", [2, 5, 40, 300])
+def test_soft_rank_hard_rank_regime(n):
+    """Sorted gaps of at least 1 make z non-increasing already: the fit is z itself and the soft ranks are
+    the hard ranks (n for the largest value)."""
+    r = workloads.rng(100 + n)
+    x = r.permutation(n)[None, :] * 3.0 + r.random((1, n)) * 0.5
+    got, _, bs, _ = oracle.soft_rank(x, 1.0)
+    np.testing.assert_allclose(got, hard_ranks(x), rtol=0, atol=1e-12 * n)
+    assert bs.all()
+    y = r.standard_normal((4, n))
+    gap = np.min(np.diff(np.sort(y, axis=1), axis=1))
+    got, *_ = oracle.soft_rank(y, gap / 2)
+    np.testing.assert_allclose(got, hard_ranks(y), rtol=0, atol=1e-9 * n)
+
+
+def permutahedron_projection(theta):
+    """Euclidean projection of theta onto the convex hull of the permutations of (1..n), solved as a
+    quadratic programme over Rado's description of that hull: the sum over any subset S is at most the
+    sum of the |S| largest of (1..n), with equality for the full set."""
+    from scipy.optimize import minimize
+    n = len(theta)
+    top = np.cumsum(np.arange(n, 0, -1, dtype=np.float64))
+    cons = [{"type": "eq", "fun": lambda r: np.sum(r) - top[-1]}]
+    for k in range(1, n):
+        for S in itertools.combinations(range(n), k):
+            idx = np.array(S)
+            cons.append({"type": "ineq", "fun": lambda r, idx=idx, b=top[k - 1]: b - np.sum(r[idx])})
+    x0 = np.full(n, (n + 1) / 2.0)
+    res = minimize(lambda r: 0.5 * np.sum((r - theta) ** 2), x0, jac=lambda r: r - theta,
+                   constraints=cons, method="SLSQP", options={"ftol": 1e-14, "maxiter": 500})
+    assert res.success, res.message
+    return res.x
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_soft_rank_is_the_permutahedron_projection(seed):
+    """The soft rank of Sec. 7.9 is the projection of theta onto the permutahedron (Blondel et al.), which
+    is computed here by a generic solver that shares nothing with pool adjacent violators."""
+    r = workloads.rng(200 + seed)
+    n = 2 + seed % 4
+    eps = [0.3, 1.0, 2.0][seed % 3]
+    x = r.standard_normal(n) * 1.5
+    got, *_ = oracle.soft_rank(x, eps)
+    want = permutahedron_projection(x / eps)
+    np.testing.assert_allclose(got[0], want, rtol=0, atol=2e-6)
+
+
+def test_soft_rank_invariances():
+    """Shifts of theta along (1..1) do not move the projection; a permutation of x permutes the ranks;
+    the ranks sum to n(n+1)/2, keep the order of x, and tied values get equal ranks."""
+    r = workloads.rng(9)
+    x = r.standard_normal((5, 50))
+    base, *_ = oracle.soft_rank(x, 0.7)
+    shifted, *_ = oracle.soft_rank(x + 3.25, 0.7)
+    np.testing.assert_allclose(shifted, base, rtol=0, atol=1e-10)
+    p = r.permutation(50)
+    permuted, *_ = oracle.soft_rank(x[:, p], 0.7)
+    np.testing.assert_allclose(permuted, base[:, p], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(base.sum(axis=1), 50 * 51 / 2, rtol=1e-14)
+    order = np.argsort(x, axis=1)
+    assert (np.diff(np.take_along_axis(base, order, axis=1), axis=1) >= -1e-12).all()
+    t = x.copy()
+    t[:, 7] = t[:, 3]
+    t[:, 20] = t[:, 3]
+    tied, *_ = oracle.soft_rank(t, 0.05)
+    assert np.all(tied[:, 7] == tied[:, 3]) and np.all(tied[:, 20] == tied[:, 3])
+
+
+def test_soft_rank_nan_rows():
+    x = workloads.rng(4).standard_normal((3, 9))
+    x[1, 4] = np.nan
+    got, perm, bs, rn = oracle.soft_rank(x, 1.0)
+    assert np.isnan(got[1]).all() and not np.isnan(got[[0, 2]]).any()
+    assert list(rn) == [0, 1, 0]
+    g = np.ones_like(x)
+    d = oracle.soft_rank_vjp(g, 1.0, perm, bs, rn)
+    assert np.isnan(d[1]).all() and not np.isnan(d[[0, 2]]).any()
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_soft_rank_vjp_finite_differences(seed):
+    """The product of soft_rank_vjp against central differences of soft_rank in float64 (Appendix B,
+    "Tests": gradients against finite differences on the CPU)."""
+    r = workloads.rng(300 + seed)
+    n = [3, 8, 17, 40][seed % 4]
+    eps = [0.2, 1.0][seed % 2]
+    x = r.standard_normal((2, n))
+    g = r.standard_normal((2, n))
+    _, perm, bs, rn = oracle.soft_rank(x, eps)
+    got = oracle.soft_rank_vjp(g, eps, perm, bs, rn)
+    h = 1e-6
+    num = np.zeros_like(x)
+    for k in range(n):
+        e = np.zeros_like(x)
+        e[:, k] = h
+        fp, *_ = oracle.soft_rank(x + e, eps)
+        fm, *_ = oracle.soft_rank(x - e, eps)
+        num[:, k] = np.sum(g * (fp - fm), axis=1) / (2 * h)
+    np.testing.assert_allclose(got, num, rtol=0, atol=1e-6)
