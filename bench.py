@@ -12,7 +12,10 @@ are timed separately and reported in "backward"):
          clipped to [0, 1]; one launch of k_row_fit;
   dense: 32 rows x 2^22 float64, y_i = i/n with 1% of positions pushed down by
          |N(0, 0.01)|, w ~ U(0.5, 1.5), increasing; k_chunk_hull, k_merge_sub,
-         k_merge_top, k_fixup (reported in "dense").
+         k_merge_top, k_fixup (reported in "dense");
+  soft rank: 4096 x 512 float32 standard normal scores, forward and backward
+         of the first page's Sec. 7.9 composition at eps = 1 and 1/n
+         (reported in "soft_rank").
 
 Prints ONE JSON line.  Algorithmic bytes are y and w read once and the fit
 written once (12 B/element for the batch, 24 B/element for the dense rows);
@@ -158,6 +161,45 @@ def time_backward(wl, steps):
             "vjp_yw_hbm_frac": byw / (ms_yw * 1e-3) / 1e9 / HBM_PEAK_GBS}
 
 
+def time_soft_rank(steps, rows=4096, n=512):
+    """Event-timed soft rank (first page, Sec. 7.9) of standard normal scores, forward and backward, at
+    eps = 1 and eps = 1/n.  Algorithmic bytes: x read, ranks and the permutation written (12 B/element)
+    forward; the gradient and the permutation read, the gradient in x written (12 B/element) backward."""
+    import torch
+    import weighted_isotonic_regression_row_amd as iso
+    import workloads
+    dev = torch.device("cuda:0")
+    x, g = workloads.soft_rank_input(rows, n)
+    x, g = torch.from_numpy(x).to(dev), torch.from_numpy(g).to(dev)
+    ws = iso.soft_rank_workspace(rows, n, x.dtype, dev)
+    r = torch.empty_like(x)
+    d = torch.empty_like(x)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    out = {"workload": f"{rows} rows x {n} float32, x~N(0,1), g~N(0,1)"}
+    elems = rows * n
+    for name, eps in (("eps_1", 1.0), ("eps_1_over_n", 1.0 / n)):
+        _, st = iso.soft_rank(x, eps, out=r, ws=ws)
+        fwd = run(lambda: iso.soft_rank(x, eps, out=r, ws=ws))
+        bwd = run(lambda: iso.soft_rank_vjp(g, st, out=d, ws=ws))
+        out[name] = {"forward_ms": fwd, "backward_ms": bwd, "elements_per_s_fwd_bwd": elems / ((fwd + bwd) * 1e-3),
+                     "forward_hbm_frac": 12 * elems / (fwd * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "backward_hbm_frac": 12 * elems / (bwd * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    return out
+
+
 def copy_probe(nbytes=256 << 20, reps=20):
     """Device-to-device copy bandwidth of a plain copy of known size (read + write)."""
     import torch
@@ -246,6 +288,7 @@ def main():
                            "bytes_per_element": 12, "elements_per_launch": elems,
                            "source_hash": source_hash()}
         rec["backward"] = time_backward(wl, args.steps)
+        rec["soft_rank"] = time_soft_rank(args.steps)
         if not args.no_cpu:
             log("cpu baseline (batch) ...")
             rec["cpu_baseline"] = cpu_baseline(wl, seconds=args.cpu_seconds)

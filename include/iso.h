@@ -157,6 +157,74 @@ int iso_vjp_yw(const void* grad_dev, const iso_blocks* blocks, const void* y_dev
                void* grad_w_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
+ * Soft rank with quadratic regularization of strength eps (first page,
+ * Sec. 7.9, after Blondel et al.): for each row, theta = x / eps is sorted in
+ * decreasing order into s, the non-increasing fit v of z = s - (n, n-1, ..., 1)
+ * is computed with unit weights by the same solver as iso_fit, and the element
+ * at sorted position i gets the rank s_i - v_i.  This is the Euclidean
+ * projection of theta onto the permutahedron of (1, ..., n): ranks sum to
+ * n(n+1)/2, keep the order of x, are the hard ranks (n for the largest value)
+ * when eps is small enough, and tied values share one rank.  Equal values are
+ * sorted in index order.  A row holding a NaN comes back NaN.
+ *
+ * Rows of at most ISO_SOFT_RANK_MAX_N elements (one workgroup sorts a row).
+ * The state keeps what the backward pass needs: the sorting permutation, its
+ * inverse, and the fit's partition over the sorted positions.
+ *   blocks     partition of the fit of z in sorted order (w_dev is NULL, no
+ *              clipping);
+ *   perm_dev   [rows, n] int32: perm[r * n + i] = index of the element at
+ *              sorted position i of row r;
+ *   rank_dev   [rows, n] int32: the inverse of perm within each row;
+ *   eps        the strength the ranks were computed with.
+ */
+#define ISO_SOFT_RANK_MAX_N 8192
+
+typedef struct iso_soft_rank_state {
+    iso_blocks blocks;
+    int32_t* perm_dev;
+    int32_t* rank_dev;
+    double eps;
+    int valid;
+} iso_soft_rank_state;
+
+/* Bytes of device memory backing an iso_soft_rank_state for rows x n. */
+size_t iso_soft_rank_state_bytes(int64_t rows, int64_t n);
+
+/* Bytes of device workspace iso_soft_rank and iso_soft_rank_vjp need
+ * (256-byte aligned; 0 for invalid sizes or n > ISO_SOFT_RANK_MAX_N). */
+size_t iso_soft_rank_workspace_bytes(int64_t rows, int64_t n, int dtype);
+
+/*
+ * Soft ranks of every row.
+ *   x_dev          [rows, n] of dtype, read only.
+ *   eps            regularization strength, finite and > 0.
+ *   r_dev          [rows, n] of dtype, written.  May not alias x.
+ *   state_out      host struct filled with the backward state (required).
+ *   state_mem_dev  iso_soft_rank_state_bytes(rows, n) bytes, 256-aligned.
+ *   workspace_dev  iso_soft_rank_workspace_bytes(rows, n, dtype) bytes,
+ *                  256-aligned; one call in flight per workspace.
+ * ISO_EINVAL for n > ISO_SOFT_RANK_MAX_N, a bad eps or dtype, NULL pointers,
+ * misaligned or short buffers.  rows == 0 or n == 0 queues nothing.
+ */
+int iso_soft_rank(const void* x_dev, int64_t rows, int64_t n, double eps, int dtype, void* r_dev,
+                  iso_soft_rank_state* state_out, void* state_mem_dev, void* workspace_dev,
+                  size_t workspace_bytes, void* stream);
+
+/*
+ * Vector-Jacobian product of the soft ranks in x: with g_s the upstream
+ * gradient in sorted order and A the block averaging of the fit,
+ *     grad_x[perm[i]] = (g_s[i] - (A g_s)[i]) / eps.
+ * Rows that came back NaN give NaN.
+ *   grad_dev       [rows, n] of the forward's dtype, read only.
+ *   state          filled by iso_soft_rank (its memory still alive).
+ *   grad_x_dev     [rows, n] of that dtype, written.
+ *   workspace_dev  iso_soft_rank_workspace_bytes(rows, n, dtype) bytes (may be
+ *                  the forward's once it has completed in stream order).
+ */
+int iso_soft_rank_vjp(const void* grad_dev, const iso_soft_rank_state* state, void* grad_x_dev,
+                      void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
  * Synchronises `stream` and returns the data error of the most recent iso_fit
  * that used this workspace: ISO_OK or ISO_EWEIGHT (ISO_EHIP if the read fails,
  * ISO_EINVAL for a NULL workspace).

@@ -37,7 +37,8 @@ def lib():
 def test_header_declares_the_boundary():
     fns = declared_functions()
     assert fns == sorted(["iso_blocks_bytes", "iso_fit", "iso_status", "iso_strerror", "iso_vjp", "iso_vjp_yw",
-                          "iso_workspace_bytes"])
+                          "iso_workspace_bytes", "iso_soft_rank", "iso_soft_rank_vjp", "iso_soft_rank_state_bytes",
+                          "iso_soft_rank_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -142,6 +143,64 @@ def test_vjp_yw_rejects_bad_arguments_on_host(lib):
     assert lib.iso_vjp_yw(256, ctypes.byref(bc), 128, 512, 640, 4096, 1, None) == E  # workspace too small
     bc.rows = 0
     assert lib.iso_vjp_yw(None, ctypes.byref(bc), None, None, None, None, 0, None) == iso.ISO_OK  # empty
+
+
+def test_soft_rank_sizes(lib):
+    assert lib.iso_soft_rank_workspace_bytes(4096, 512, 0) >= 2 * 4096 * 512 * 4
+    assert lib.iso_soft_rank_workspace_bytes(4, 8193, 0) == 0      # longer than one workgroup sorts
+    assert lib.iso_soft_rank_workspace_bytes(4, 8192, 1) >= 2 * 4 * 8192 * 8
+    assert lib.iso_soft_rank_workspace_bytes(-1, 5, 0) == 0
+    assert lib.iso_soft_rank_workspace_bytes(2, 5, 3) == 0
+    # the permutation, its inverse and the block bits
+    assert lib.iso_soft_rank_state_bytes(4096, 512) >= 2 * 4 * 4096 * 512 + lib.iso_blocks_bytes(4096, 512)
+    assert lib.iso_soft_rank_state_bytes(-1, 5) == 0
+
+
+def _sr(lib, x=256, rows=2, n=3, eps=1.0, dt=0, r=512, st=True, mem=8192, ws=1 << 16, wsb=1 << 20):
+    import weighted_isotonic_regression_row_amd as iso
+    sc = iso.IsoSoftRankStateC()
+    code = lib.iso_soft_rank(x, rows, n, eps, dt, r, ctypes.byref(sc) if st else None, mem, ws, wsb, None)
+    return code, sc
+
+
+def test_soft_rank_rejects_bad_arguments_on_host(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    E = iso.ISO_EINVAL
+    for kw in ({"rows": -1}, {"n": -1}, {"n": 8193}, {"dt": 2}, {"eps": 0.0}, {"eps": -1.0}, {"eps": math.inf},
+               {"eps": math.nan}, {"st": False}, {"mem": None}, {"mem": 8192 + 8}, {"x": None}, {"r": None},
+               {"ws": None}, {"ws": (1 << 16) + 8}, {"wsb": 8}, {"r": 256 + 4}):
+        assert _sr(lib, **kw)[0] == E, kw
+
+
+def test_soft_rank_empty_is_a_noop(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    code, sc = _sr(lib, rows=0, x=None, r=None, ws=None)
+    assert code == iso.ISO_OK and sc.valid == 1 and sc.blocks.valid == 1
+    assert lib.iso_soft_rank_vjp(None, ctypes.byref(sc), None, None, 0, None) == iso.ISO_OK
+
+
+def test_soft_rank_vjp_rejects_bad_arguments_on_host(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    E = iso.ISO_EINVAL
+    sc = iso.IsoSoftRankStateC()
+    assert lib.iso_soft_rank_vjp(256, ctypes.byref(sc), 512, 1 << 16, 1 << 20, None) == E  # invalid state
+    assert lib.iso_soft_rank_vjp(256, None, 512, 1 << 16, 1 << 20, None) == E
+    code, sc = _sr(lib, x=None)   # fails, leaves the state invalid
+    assert code == E and sc.valid == 0
+    assert lib.iso_soft_rank_vjp(256, ctypes.byref(sc), 512, 1 << 16, 1 << 20, None) == E
+    sc.valid = 1
+    sc.blocks.valid = 1
+    sc.blocks.rows, sc.blocks.n, sc.blocks.words, sc.blocks.dtype = 2, 3, 1, 0
+    sc.blocks.start_bits_dev, sc.blocks.clip_bits_dev, sc.blocks.row_nan_dev = 8192, 8192 + 256, 8192 + 512
+    sc.perm_dev, sc.rank_dev, sc.eps = 8192 + 1024, 8192 + 2048, 1.0
+    assert lib.iso_soft_rank_vjp(None, ctypes.byref(sc), 512, 1 << 16, 1 << 20, None) == E
+    assert lib.iso_soft_rank_vjp(256, ctypes.byref(sc), None, 1 << 16, 1 << 20, None) == E
+    assert lib.iso_soft_rank_vjp(256, ctypes.byref(sc), 512, (1 << 16) + 8, 1 << 20, None) == E
+    assert lib.iso_soft_rank_vjp(256, ctypes.byref(sc), 512, 1 << 16, 8, None) == E
+    sc.eps = 0.0
+    assert lib.iso_soft_rank_vjp(256, ctypes.byref(sc), 512, 1 << 16, 1 << 20, None) == E
+    sc.eps, sc.perm_dev = 1.0, None
+    assert lib.iso_soft_rank_vjp(256, ctypes.byref(sc), 512, 1 << 16, 1 << 20, None) == E
 
 
 def test_status_without_calls(lib):

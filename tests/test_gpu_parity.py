@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_helpers import (check_fit, gpu_blocks, gpu_fit, oracle_fit, scale_of, to_dev)
+from gpu_helpers import (TOL_F32, TOL_F64, check_fit, gpu_blocks, gpu_fit, oracle_fit, scale_of, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -309,3 +309,103 @@ def test_empty_inputs():
         assert f.shape == shape
         g = iso.iso_vjp(torch.empty(shape, dtype=torch.float64, device="cuda:0"), b)
         assert g.shape == shape
+
+
+# ---------------------------------------------------------------- soft rank (first page, Sec. 7.9)
+
+SR_SIZES = [1, 2, 63, 65, 100, 512, 1000, 4096, 5000, 6144, 6145, 8192]
+
+
+def _soft_rank_case(x, eps, dtype, what, check_partition=None):
+    import torch
+    import weighted_isotonic_regression_row_amd as iso
+    rows, n = x.shape
+    r_gpu, st = iso.soft_rank(to_dev(x), eps)
+    torch.cuda.synchronize()
+    r_ref, perm, bs, rn = oracle.soft_rank(x.astype(np.float64), eps)
+    # the sorting permutation is index work: bit-exact, ties in index order.  A row holding a NaN comes
+    # back all NaN whatever its order, so there it only has to be a permutation.
+    finite = np.isfinite(x).all(axis=1)
+    gperm = st.perm().cpu().numpy()
+    np.testing.assert_array_equal(gperm[finite], perm[finite], err_msg=what)
+    np.testing.assert_array_equal(np.sort(gperm, axis=1), np.broadcast_to(np.arange(n), (rows, n)))
+    rank = st.rank().cpu().numpy()
+    np.testing.assert_array_equal(np.take_along_axis(rank, gperm, axis=1), np.broadcast_to(np.arange(n), (rows, n)))
+    perm = np.where(finite[:, None], perm, gperm)
+    # ranks: within the fit's tolerance of the scale of z = s - (n..1)
+    scale = (float(np.abs(x[finite].astype(np.float64)).max()) / eps if finite.any() else 0.0) + n
+    rg = r_gpu.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(rg), np.isnan(r_ref)), what
+    ok = ~np.isnan(r_ref)
+    if ok.any():
+        err = float(np.max(np.abs(rg[ok] - r_ref[ok])))
+        tol = (TOL_F64 if dtype == np.float64 else TOL_F32) * scale
+        assert err <= tol, f"{what}: ranks off by {err:.3e} > {tol:.3e}"
+        # in sorted order the ranks do not increase, up to rounding of the scale
+        srt = np.take_along_axis(rg, perm, axis=1)[finite]
+        up = float(np.max(np.diff(srt, axis=1), initial=0.0))
+        slack = (1e-12 if dtype == np.float64 else 4 * float(np.spacing(np.float32(scale))))
+        assert up <= slack, f"{what}: ranks out of order by {up:.3e}"
+    gsb, gcb, grn = gpu_blocks(st.blocks)
+    np.testing.assert_array_equal(grn.astype(bool), rn.astype(bool))
+    if check_partition:
+        np.testing.assert_array_equal(gsb[finite], bs[finite])
+    return st, perm, (gsb, grn), r_ref
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n", SR_SIZES)
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_soft_rank_matches_oracle(n, dtype):
+    """Soft ranks and their product against the oracle: both strengths of the first page's Sec. 7.9
+    (eps = 1, where rows pool into few blocks, and eps = 1/n, near the hard ranks); rows of one wave,
+    of several waves, and beyond one workgroup's fit (6145 and more: chunked fit)."""
+    import weighted_isotonic_regression_row_amd as iso
+    rows = 3 if n > 1000 else 17
+    x, g = workloads.soft_rank_input(rows, n, seed=n % 97, dtype=dtype)
+    for eps in (1.0, 1.0 / n):
+        st, perm, (gsb, grn), _ = _soft_rank_case(x, eps, dtype, f"n={n} eps={eps}",
+                                                   check_partition=(dtype == np.float64))
+        d = iso.soft_rank_vjp(to_dev(g), st).cpu().numpy().astype(np.float64)
+        # the product on the GPU's own partition (exact ties of block means may split either way)
+        ref = oracle.soft_rank_vjp(g.astype(np.float64), eps, perm, gsb, grn)
+        tol = (1e-12 if dtype == np.float64 else 2e-6) * max(1.0, float(np.abs(ref).max()))
+        err = float(np.max(np.abs(d - ref)))
+        assert err <= tol, f"n={n} eps={eps}: product off by {err:.3e} > {tol:.3e}"
+
+
+@pytest.mark.gpu
+def test_soft_rank_config3_shape():
+    """4096 x 512 float32 standard normal scores, eps = 1 and 1/512, forward and backward (the soft-rank
+    shape of the first page's Table 6, at the size of the batch it is measured on here)."""
+    import weighted_isotonic_regression_row_amd as iso
+    x, g = workloads.soft_rank_input()
+    for eps in (1.0, 1.0 / 512):
+        st, perm, (gsb, grn), _ = _soft_rank_case(x, eps, np.float32, f"4096x512 eps={eps}")
+        d = iso.soft_rank_vjp(to_dev(g), st).cpu().numpy().astype(np.float64)
+        ref = oracle.soft_rank_vjp(g.astype(np.float64), eps, perm, gsb, grn)
+        assert float(np.max(np.abs(d - ref))) <= 2e-6 * max(1.0, float(np.abs(ref).max()))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_soft_rank_ties_signed_zeros_and_nan_rows(dtype):
+    """Equal values (and -0 against +0) sort in index order and share one rank; a row holding a NaN comes
+    back NaN, forward and backward, without disturbing the other rows."""
+    import weighted_isotonic_regression_row_amd as iso
+    r = workloads.rng(11)
+    x = r.integers(-3, 4, size=(6, 300)).astype(dtype)
+    x[0, ::7] = -0.0
+    x[0, 3::7] = 0.0
+    x[2, 150] = np.nan
+    x[4, 0] = np.nan
+    for eps in (1.0, 0.01):
+        st, perm, (gsb, grn), r_ref = _soft_rank_case(x, eps, dtype, f"ties eps={eps}")
+        rg = iso.soft_rank(to_dev(x), eps)[0].cpu().numpy()
+        for row in (0, 1, 3, 5):
+            for v in np.unique(x[row]):
+                vals = rg[row][x[row] == v]
+                assert np.all(vals == vals[0])
+        g = np.ones_like(x)
+        d = iso.soft_rank_vjp(to_dev(g), st).cpu().numpy()
+        assert np.isnan(d[[2, 4]]).all() and not np.isnan(d[[0, 1, 3, 5]]).any()

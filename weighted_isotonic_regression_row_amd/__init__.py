@@ -9,10 +9,14 @@ library (or without a GPU) the calls raise.
     fit, blocks = iso_fit(y, w, increasing=True, y_min=None, y_max=None)
     grad_y = iso_vjp(grad, blocks)
     grad_y, grad_w = iso_vjp_yw(grad, blocks, y)
+    ranks, state = soft_rank(x, eps)
+    grad_x = soft_rank_vjp(grad, state)
 
 The fit of each row is the weighted least-squares monotone sequence (page
 "Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Eq. (1)),
-with the semantics of the "torchisotonic" PyPI page ("Semantics").
+with the semantics of the "torchisotonic" PyPI page ("Semantics").  The soft rank is the composition of the first page's
+Sec. 7.9: a per-row sort, the non-increasing fit of s - (n..1), and s minus
+that fit in the original order.
 """
 from __future__ import annotations
 
@@ -32,8 +36,9 @@ ISO_EINVAL = -1
 ISO_EHIP = -2
 ISO_EWEIGHT = -3
 
-SYMBOLS = ("iso_workspace_bytes", "iso_blocks_bytes", "iso_fit", "iso_vjp", "iso_vjp_yw", "iso_status",
-           "iso_strerror")
+SYMBOLS = ("iso_workspace_bytes", "iso_blocks_bytes", "iso_fit", "iso_vjp", "iso_vjp_yw", "iso_soft_rank_state_bytes",
+           "iso_soft_rank_workspace_bytes", "iso_soft_rank", "iso_soft_rank_vjp", "iso_status", "iso_strerror")
+SOFT_RANK_MAX_N = 8192
 
 
 class IsoBlocksC(ctypes.Structure):
@@ -48,6 +53,18 @@ class IsoBlocksC(ctypes.Structure):
         ("n", ctypes.c_int64),
         ("words", ctypes.c_int64),
         ("dtype", ctypes.c_int),
+        ("valid", ctypes.c_int),
+    ]
+
+
+class IsoSoftRankStateC(ctypes.Structure):
+    """Mirror of struct iso_soft_rank_state (include/iso.h)."""
+
+    _fields_ = [
+        ("blocks", IsoBlocksC),
+        ("perm_dev", ctypes.c_void_p),
+        ("rank_dev", ctypes.c_void_p),
+        ("eps", ctypes.c_double),
         ("valid", ctypes.c_int),
     ]
 
@@ -82,6 +99,15 @@ def load_library(path: str | None = None):
     lib.iso_vjp.argtypes = [vp, ctypes.POINTER(IsoBlocksC), vp, vp, c_size, vp]
     lib.iso_vjp_yw.restype = c_int
     lib.iso_vjp_yw.argtypes = [vp, ctypes.POINTER(IsoBlocksC), vp, vp, vp, vp, c_size, vp]
+    lib.iso_soft_rank_state_bytes.restype = c_size
+    lib.iso_soft_rank_state_bytes.argtypes = [i64, i64]
+    lib.iso_soft_rank_workspace_bytes.restype = c_size
+    lib.iso_soft_rank_workspace_bytes.argtypes = [i64, i64, c_int]
+    lib.iso_soft_rank.restype = c_int
+    lib.iso_soft_rank.argtypes = [vp, i64, i64, c_double, c_int, vp, ctypes.POINTER(IsoSoftRankStateC), vp, vp,
+                                  c_size, vp]
+    lib.iso_soft_rank_vjp.restype = c_int
+    lib.iso_soft_rank_vjp.argtypes = [vp, ctypes.POINTER(IsoSoftRankStateC), vp, vp, c_size, vp]
     lib.iso_status.restype = c_int
     lib.iso_status.argtypes = [vp, vp]
     lib.iso_strerror.restype = ctypes.c_char_p
@@ -247,9 +273,87 @@ def iso_vjp_yw(grad: torch.Tensor, blocks: Blocks, y: torch.Tensor, *, want_y: b
     return (None if gy is None else gy.view(blocks.shape)), gw.view(blocks.shape)
 
 
+class SoftRankState:
+    """Backward state of soft_rank (struct iso_soft_rank_state plus the memory behind it)."""
+
+    def __init__(self, c: IsoSoftRankStateC, mem: torch.Tensor, shape):
+        self.c = c
+        self.mem = mem
+        self.shape = shape
+        self.blocks = Blocks(c.blocks, mem, None, shape)
+
+    def perm(self) -> torch.Tensor:
+        """[rows, n] int32 view: index of the element at each sorted position."""
+        rows, n = self.c.blocks.rows, self.c.blocks.n
+        off = self.c.perm_dev - self.mem.data_ptr()
+        return self.mem[off:off + 4 * rows * n].view(torch.int32).view(rows, n)
+
+    def rank(self) -> torch.Tensor:
+        """[rows, n] int32 view: sorted position of each element (the inverse of perm)."""
+        rows, n = self.c.blocks.rows, self.c.blocks.n
+        off = self.c.rank_dev - self.mem.data_ptr()
+        return self.mem[off:off + 4 * rows * n].view(torch.int32).view(rows, n)
+
+
+def soft_rank_workspace(rows: int, n: int, dtype: torch.dtype, device) -> torch.Tensor:
+    code = ISO_F32 if dtype == torch.float32 else ISO_F64
+    nb = int(load_library().iso_soft_rank_workspace_bytes(rows, n, code))
+    if nb == 0:
+        raise ValueError(f"soft rank needs rows of at most {SOFT_RANK_MAX_N} elements")
+    return torch.empty(nb, dtype=torch.uint8, device=device)
+
+
+def soft_rank(x: torch.Tensor, eps: float = 1.0, *, out: torch.Tensor | None = None,
+              ws: torch.Tensor | None = None):
+    """Soft ranks of every row of x (first page, Sec. 7.9): the projection of x / eps onto the
+    permutahedron of (1..n).  Returns (ranks, state); rows of at most SOFT_RANK_MAX_N elements."""
+    if not x.is_cuda:
+        raise ValueError("soft_rank runs on the GPU: x must be a device tensor")
+    lib = load_library()
+    shape = x.shape
+    x2 = _as_rows(x)
+    if not x2.is_contiguous():
+        raise ValueError("x must be contiguous")
+    rows, n = x2.shape
+    dt = _dtype_code(x2)
+    if out is None:
+        out = torch.empty_like(x2)
+    if ws is None:
+        ws = soft_rank_workspace(rows, n, x2.dtype, x2.device)
+    mem = torch.empty(max(int(lib.iso_soft_rank_state_bytes(rows, n)), 256), dtype=torch.uint8, device=x2.device)
+    st = IsoSoftRankStateC()
+    code = lib.iso_soft_rank(x2.data_ptr(), rows, n, float(eps), dt, out.data_ptr(), ctypes.byref(st), mem.data_ptr(),
+                             ws.data_ptr(), ws.numel(), _stream_ptr(x2.device))
+    if code != ISO_OK:
+        raise IsoError(code, "iso_soft_rank")
+    return out.view(shape), SoftRankState(st, mem, shape)
+
+
+def soft_rank_vjp(grad: torch.Tensor, state: SoftRankState, *, out: torch.Tensor | None = None,
+                  ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Gradient in x of <grad, soft_rank(x, eps)>: P^T (g_s - A g_s) / eps over the fit's blocks."""
+    lib = load_library()
+    g2 = _as_rows(grad)
+    rows, n = state.c.blocks.rows, state.c.blocks.n
+    if tuple(g2.shape) != (rows, n) or not g2.is_contiguous():
+        raise ValueError("grad must be a contiguous tensor of the ranks' shape")
+    if _dtype_code(g2) != state.c.blocks.dtype:
+        raise ValueError("grad must have the ranks' dtype")
+    if out is None:
+        out = torch.empty_like(g2)
+    if ws is None:
+        ws = soft_rank_workspace(rows, n, g2.dtype, g2.device)
+    code = lib.iso_soft_rank_vjp(g2.data_ptr(), ctypes.byref(state.c), out.data_ptr(), ws.data_ptr(), ws.numel(),
+                                 _stream_ptr(g2.device))
+    if code != ISO_OK:
+        raise IsoError(code, "iso_soft_rank_vjp")
+    return out.view(state.shape)
+
+
 def iso_status(ws: torch.Tensor) -> int:
     return int(load_library().iso_status(ws.data_ptr(), _stream_ptr(ws.device)))
 
 
-__all__ = ["iso_fit", "iso_vjp", "iso_vjp_yw", "iso_status", "iso_workspace_bytes", "iso_blocks_bytes", "workspace",
+__all__ = ["iso_fit", "iso_vjp", "iso_vjp_yw", "soft_rank", "soft_rank_vjp", "SoftRankState", "soft_rank_workspace",
+           "SOFT_RANK_MAX_N", "iso_status", "iso_workspace_bytes", "iso_blocks_bytes", "workspace",
            "Blocks", "IsoError", "load_library", "SYMBOLS"]

@@ -149,6 +149,110 @@ int iso_vjp(const void* grad, const iso_blocks* blocks, void* grad_y, void* work
     return iso_vjp_yw(grad, blocks, nullptr, grad_y, nullptr, workspace, workspace_bytes, stream);
 }
 
+size_t iso_soft_rank_state_bytes(int64_t rows, int64_t n) {
+    if (rows < 0 || n < 0) return 0;
+    const size_t idx = iso::align256(4 * (size_t)rows * (size_t)n);
+    return iso::align256(iso_blocks_bytes(rows, n)) + 2 * idx;
+}
+
+size_t iso_soft_rank_workspace_bytes(int64_t rows, int64_t n, int dtype) {
+    if (rows < 0 || n < 0 || n > iso::kRankMaxN || !valid_dtype(dtype)) return 0;
+    const size_t esz = dtype == ISO_F32 ? 4 : 8;
+    return iso::align256(iso::make_layout(rows, n).total) + 2 * iso::align256(esz * (size_t)rows * (size_t)n);
+}
+
+namespace {
+
+iso::RankLaunch rank_launch(const iso_soft_rank_state* st, void* workspace) {
+    iso::RankLaunch l{};
+    const int64_t rows = st->blocks.rows, n = st->blocks.n;
+    const size_t esz = st->blocks.dtype == ISO_F32 ? 4 : 8;
+    l.rows = rows;
+    l.n = n;
+    l.words = st->blocks.words;
+    l.dtype = st->blocks.dtype;
+    l.eps = st->eps;
+    l.perm = st->perm_dev;
+    l.rank = st->rank_dev;
+    l.start_bits = st->blocks.start_bits_dev;
+    l.clip_bits = st->blocks.clip_bits_dev;
+    l.row_nan = st->blocks.row_nan_dev;
+    l.ws = (char*)workspace;
+    l.L = iso::make_layout(rows, n);
+    l.zoff = iso::align256(l.L.total);
+    l.voff = l.zoff + iso::align256(esz * (size_t)rows * (size_t)n);
+    return l;
+}
+
+}  // namespace
+
+int iso_soft_rank(const void* x, int64_t rows, int64_t n, double eps, int dtype, void* r,
+                  iso_soft_rank_state* state_out, void* state_mem, void* workspace, size_t workspace_bytes,
+                  void* stream) {
+    if (rows < 0 || n < 0 || !valid_dtype(dtype)) return ISO_EINVAL;
+    if (n > iso::kRankMaxN || rows > (int64_t)INT32_MAX) return ISO_EINVAL;
+    if (!(eps > 0.0) || !isfinite(eps)) return ISO_EINVAL;
+    if (!state_out || !state_mem) return ISO_EINVAL;
+    if (((uintptr_t)state_mem & 255u) != 0) return ISO_EINVAL;
+    memset(state_out, 0, sizeof(*state_out));
+    const int64_t words = (n + 63) / 64;
+    char* sm = (char*)state_mem;
+    const size_t bits = iso::align256(8 * (size_t)words * (size_t)rows);
+    const size_t bb = iso::align256(iso_blocks_bytes(rows, n));
+    const size_t idx = iso::align256(4 * (size_t)rows * (size_t)n);
+    iso_blocks* b = &state_out->blocks;
+    b->start_bits_dev = (uint64_t*)sm;
+    b->clip_bits_dev = (uint64_t*)(sm + bits);
+    b->row_nan_dev = (uint32_t*)(sm + 2 * bits);
+    b->w_dev = nullptr;
+    b->rows = rows;
+    b->n = n;
+    b->words = words;
+    b->dtype = dtype;
+    b->valid = 1;
+    state_out->perm_dev = (int32_t*)(sm + bb);
+    state_out->rank_dev = (int32_t*)(sm + bb + idx);
+    state_out->eps = eps;
+    if (rows == 0 || n == 0) {
+        state_out->valid = 1;
+        return ISO_OK;
+    }
+    if (!x || !r || !workspace) return ISO_EINVAL;
+    if (((uintptr_t)workspace & 255u) != 0) return ISO_EINVAL;
+    if (workspace_bytes < iso_soft_rank_workspace_bytes(rows, n, dtype)) return ISO_EINVAL;
+    const size_t bytes = (size_t)rows * (size_t)n * (dtype == ISO_F32 ? 4 : 8);
+    const char* rb = (const char*)r;
+    const char* xb = (const char*)x;
+    if (xb < rb + bytes && rb < xb + bytes) return ISO_EINVAL;
+    iso::RankLaunch l = rank_launch(state_out, workspace);
+    l.in = x;
+    l.out = r;
+    l.stream = (hipStream_t)stream;
+    if (iso::launch_soft_rank(l) != hipSuccess) return ISO_EHIP;
+    state_out->valid = 1;
+    return ISO_OK;
+}
+
+int iso_soft_rank_vjp(const void* grad, const iso_soft_rank_state* state, void* grad_x, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+    if (!state || !state->valid || !state->blocks.valid) return ISO_EINVAL;
+    const int64_t rows = state->blocks.rows, n = state->blocks.n;
+    if (rows < 0 || n < 0 || n > iso::kRankMaxN || !valid_dtype(state->blocks.dtype)) return ISO_EINVAL;
+    if (rows == 0 || n == 0) return ISO_OK;
+    if (!grad || !grad_x || !workspace || !state->perm_dev || !state->rank_dev) return ISO_EINVAL;
+    if (!state->blocks.start_bits_dev || !state->blocks.clip_bits_dev || !state->blocks.row_nan_dev)
+        return ISO_EINVAL;
+    if (!(state->eps > 0.0) || !isfinite(state->eps)) return ISO_EINVAL;
+    if (((uintptr_t)workspace & 255u) != 0) return ISO_EINVAL;
+    if (workspace_bytes < iso_soft_rank_workspace_bytes(rows, n, state->blocks.dtype)) return ISO_EINVAL;
+    iso::RankLaunch l = rank_launch(state, workspace);
+    l.in = grad;
+    l.out = grad_x;
+    l.stream = (hipStream_t)stream;
+    if (iso::launch_soft_rank_vjp(l) != hipSuccess) return ISO_EHIP;
+    return ISO_OK;
+}
+
 int iso_status(const void* workspace, void* stream) {
     if (!workspace) return ISO_EINVAL;
     unsigned long long last = 0;

@@ -185,8 +185,36 @@ inline hipError_t ensure_lds(const void* fn, size_t bytes, size_t (&seen)[kMaxDe
     return e;
 }
 
-// Launchers (iso_fit.hip, iso_vjp.hip).  Return hipSuccess or the launch error.
+// Soft rank (first page, Sec. 7.9): rows of at most this many elements are
+// sorted by one workgroup in LDS (12 bytes per entry for float64).
+constexpr int64_t kRankMaxN = 8192;
+
+// Soft rank and its backward: `in` is x (forward) or the upstream gradient
+// (backward), `out` the ranks or the gradient in x.  The workspace holds the
+// solver's layout L from offset 0, then two [rows, n] arrays of the data type
+// at zoff and voff (z and its fit; the sorted gradient and its block averages).
+struct RankLaunch {
+    const void* in;
+    void* out;
+    int64_t rows, n, words;
+    int dtype;
+    double eps;
+    int32_t* perm;
+    int32_t* rank;
+    uint64_t* start_bits;
+    uint64_t* clip_bits;
+    uint32_t* row_nan;
+    char* ws;
+    Layout L;
+    size_t zoff, voff;
+    hipStream_t stream;
+};
+
+// Launchers (iso_fit.hip, iso_vjp.hip, iso_rank.hip).  Return hipSuccess or
+// the launch error.
 hipError_t launch_fit(const FitLaunch& a);
 hipError_t launch_vjp(const VjpLaunch& l);
+hipError_t launch_soft_rank(const RankLaunch& l);
+hipError_t launch_soft_rank_vjp(const RankLaunch& l);
 
 }  // namespace iso

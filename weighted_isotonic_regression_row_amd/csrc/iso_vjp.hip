@@ -385,7 +385,7 @@ __global__ __launch_bounds__(1024) void k_vjp_row(VjpArgs a) {
     extern __shared__ __align__(32) char smem[];
     const int64_t row = blockIdx.x;
     const int N = (int)a.n;
-    const int l = threadIdx.x, lane = lane_id(), wid = l >> 6, nw = blockDim.x >> 6;
+    const int l = threadIdx.x, lane = lane_id(), wid = l >> 6;
     A* slot = (A*)smem;
     A* wsum = slot + blockDim.x;
     int* wflag = (int*)(wsum + 16);

@@ -83,6 +83,15 @@ def cfg3_soft_rank(rows=4096, n=512, seed=3) -> Workload:
     return Workload("cfg3_4096x512_f32_softrank_fwd_bwd", y, None, True, g=g)
 
 
+def soft_rank_input(rows=4096, n=512, seed=3, dtype=np.float32):
+    """Input of the soft-rank composition (first page, Sec. 7.9): standard normal
+    scores x and a standard normal upstream gradient g, [rows, n]."""
+    r = rng(seed)
+    x = r.standard_normal((rows, n)).astype(dtype)
+    g = r.standard_normal((rows, n)).astype(dtype)
+    return x, g
+
+
 def cfg4_calibration(n=6_500_000, seed=4) -> Workload:
     """Calibration-shaped single row, float64: sorted scores s ~ N(0,1),
     integer counts c ~ 1 + Poisson(2) as weights, y = Binomial(c, sigmoid(1.5 s - 3)) / c,
