@@ -150,19 +150,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     if (a.row_nan && threadIdx.x == 0) a.row_nan[row] = 0u;
 }
 
-// The rows k_row_fit flagged: the same pipeline with the vertex list in the
-// row's area of the workspace (room for every point).  Other rows return at
-// once.
+// The rows k_row_fit flagged: the same pipeline with room for every point in
+// the vertex list, in LDS when a.cap == N (one-wave rows: 13 KiB at most) or
+// else in the row's area of the workspace.  Other rows return at once.
 template <typename T, int K>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_row_ovf(RowArgs a) {
     extern __shared__ __align__(32) char smem[];
     const int64_t row = blockIdx.x;
     if (a.ovf_row[row] == 0) return;
     const int N = (int)a.n;
-    Tile t = tile_carve(smem, blockDim.x, 0, K, N);
-    char* o = a.ovf + row * a.ovf_stride;
-    t.VXY = (double2*)o;
-    t.V = (unsigned short*)(o + 16 * (a.n + 1));
+    const bool in_lds = a.cap >= N;
+    Tile t = tile_carve(smem, blockDim.x, in_lds ? N : 0, K, N);
+    if (!in_lds) {
+        char* o = a.ovf + row * a.ovf_stride;
+        t.VXY = (double2*)o;
+        t.V = (unsigned short*)(o + 16 * (a.n + 1));
+    }
     const T* y = (const T*)a.y + row * a.n;
     const T* w = a.w ? (const T*)a.w + row * a.n : nullptr;
     T* out = (T*)a.fit + row * a.n;
@@ -1125,7 +1128,7 @@ static int row_list_cap(int N, int nl, int K) {
     const int W = nl / 64;
     const int per_simd = (W + 3) / 4;
     const long wgs = (W <= 4) ? 16 / W : (per_simd >= 4 ? 1 : 4 / per_simd);
-    const long target = 163840 / wgs - 512;
+    const long target = kLdsBytes / wgs - 512;
     const long fixed = (long)tile_smem_bytes(nl, 0, K);
     const long room = (target - fixed) / 18;
     const long cap = room > N / 4 ? room : N / 4;
@@ -1149,7 +1152,14 @@ static hipError_t launch_row(const FitLaunch& a, RowArgs r, int nl) {
     hipLaunchKernelGGL((k_row_fit<T, K>), dim3((unsigned)a.rows), dim3(nl), smem, a.stream, r);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || !may_overflow) return e;
-    hipLaunchKernelGGL((k_row_ovf<T, K>), dim3((unsigned)a.rows), dim3(nl), tile_smem_bytes(nl, 0, K), a.stream, r);
+    // the flagged rows again: one-wave rows keep the whole list in LDS (a
+    // dozen rows still share a CU), wider rows keep it in the workspace
+    RowArgs o = r;
+    o.cap = nl == 64 ? (int)a.n : 0;
+    const size_t osmem = tile_smem_bytes(nl, o.cap, K);
+    static size_t oseen[kMaxDevices] = {};
+    (void)ensure_lds((const void*)k_row_ovf<T, K>, osmem, oseen);
+    hipLaunchKernelGGL((k_row_ovf<T, K>), dim3((unsigned)a.rows), dim3(nl), osmem, a.stream, o);
     return hipGetLastError();
 }
 

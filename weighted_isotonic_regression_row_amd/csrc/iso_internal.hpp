@@ -10,6 +10,8 @@ namespace iso {
 // Rows of at most this many elements are fitted one per lane (the whole row's
 // hull in registers); the backward pass handles them the same way.
 constexpr int kLaneRow = 16;
+// LDS of one CU (bytes).
+constexpr int kLdsBytes = 163840;
 // Rows of at most this many elements are fitted by one workgroup each, the
 // lane hulls' vertices listed in LDS (18 bytes per vertex plus about 60 per
 // lane; 512 lanes of 12 elements at most).

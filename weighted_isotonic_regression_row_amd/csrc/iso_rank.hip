@@ -47,90 +47,237 @@ struct SortArgs {
     int32_t* rank;
     void* z;
     int n;
-    int P;  // power of two >= n, at least 64
+    int P;  // power of two >= n, at least 64; P / E threads
     double eps;
 };
 
-// One compare-exchange stage of the network at distance j inside blocks of
-// size k; a block with (i & k) == 0 is put in decreasing order.  A float32
-// entry packs (key << 32) | ~index, so that one unsigned comparison orders by
-// key and then by the lower index; padding entries are 0 and sort last.
+// A sort entry.  A float32 entry packs (key << 32) | ~index into k, so that one
+// unsigned comparison orders by key and then by the lower index; a float64
+// entry keeps the index in i.  Padding entries (k = 0, index all ones) come
+// after every element.
+struct Ent {
+    uint64_t k;
+    uint32_t i;
+};
+
 template <typename T>
-__device__ __forceinline__ void sort_stage(uint64_t* K, uint32_t* I, int half, int k, int j) {
-    for (int q = threadIdx.x; q < half; q += blockDim.x) {
-        const int i = 2 * q - (q & (j - 1));
-        const int l = i + j;
-        const bool dec = (i & k) == 0;
-        const uint64_t u = K[i], v = K[l];
-        if constexpr (sizeof(T) == 4) {
-            if (dec ? (v > u) : (u > v)) {
-                K[i] = v;
-                K[l] = u;
-            }
-        } else {
-            const uint32_t a = I[i], b = I[l];
-            const bool l_first = v > u || (v == u && b < a);  // the entry at l comes first
-            if (dec == l_first) {
-                K[i] = v;
-                K[l] = u;
-                I[i] = b;
-                I[l] = a;
-            }
-        }
-    }
+__device__ __forceinline__ bool before(const Ent& a, const Ent& b) {
+    if constexpr (sizeof(T) == 4)
+        return a.k > b.k;
+    else
+        return a.k > b.k || (a.k == b.k && a.i < b.i);
 }
 
 template <typename T>
-__global__ __launch_bounds__(1024) void k_rank_sort(SortArgs a) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int n = a.n, P = a.P;
-    const int64_t row0 = (int64_t)blockIdx.x * n;
-    const T* x = (const T*)a.x + row0;
-    uint64_t* K = (uint64_t*)smem;
-    uint32_t* I = (uint32_t*)(smem + 8 * (size_t)P);
-    for (int i = threadIdx.x; i < P; i += blockDim.x) {
-        if constexpr (sizeof(T) == 4) {
-            K[i] = i < n ? (((uint64_t)sort_key(x[i]) << 32) | (uint32_t)~(uint32_t)i) : 0ull;
-        } else {
-            K[i] = i < n ? sort_key(x[i]) : 0ull;
-            I[i] = i < n ? (uint32_t)i : 0xffffffffu;
-        }
+__device__ __forceinline__ Ent shfl_xor_ent(const Ent& a, int m) {
+    Ent r;
+    const int lo = __shfl_xor((int)(uint32_t)a.k, m), hi = __shfl_xor((int)(uint32_t)(a.k >> 32), m);
+    r.k = ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+    r.i = sizeof(T) == 4 ? 0u : (uint32_t)__shfl_xor((int)a.i, m);
+    return r;
+}
+
+// The entry of lane (this lane ^ M) for the masks DPP reaches inside a row of
+// 16 lanes (quad permutations, the row and half-row mirrors, a rotation by 8;
+// xor 4 is the half-row mirror followed by the quad reversal); M == 0 takes
+// any mask m through the LDS crossbar.
+template <typename T, int CTRL>
+__device__ __forceinline__ Ent dpp_ent(const Ent& a) {
+    Ent r;
+    const unsigned lo = (unsigned)dpp_move<CTRL, 0xf>((int)(uint32_t)a.k);
+    const unsigned hi = (unsigned)dpp_move<CTRL, 0xf>((int)(uint32_t)(a.k >> 32));
+    r.k = ((uint64_t)hi << 32) | lo;
+    r.i = sizeof(T) == 4 ? 0u : (uint32_t)dpp_move<CTRL, 0xf>((int)a.i);
+    return r;
+}
+
+template <typename T, int M>
+__device__ __forceinline__ Ent lanes_xor(const Ent& a, int m) {
+    if constexpr (M == 1) return dpp_ent<T, 0xB1>(a);  // quad_perm [1,0,3,2]
+    if constexpr (M == 2) return dpp_ent<T, 0x4E>(a);  // quad_perm [2,3,0,1]
+    if constexpr (M == 3) return dpp_ent<T, 0x1B>(a);  // quad_perm [3,2,1,0]
+    if constexpr (M == 4) return dpp_ent<T, 0x1B>(dpp_ent<T, 0x141>(a));
+    if constexpr (M == 7) return dpp_ent<T, 0x141>(a);   // row_half_mirror
+    if constexpr (M == 8) return dpp_ent<T, 0x128>(a);   // row_ror:8
+    if constexpr (M == 15) return dpp_ent<T, 0x140>(a);  // row_mirror
+    if constexpr (M == 0) return shfl_xor_ent<T>(a, m);
+    return a;
+}
+
+template <typename T>
+__device__ __forceinline__ Ent sel(bool c, const Ent& a, const Ent& b) {
+    Ent r;
+    r.k = c ? a.k : b.k;
+    r.i = sizeof(T) == 4 ? 0u : (c ? a.i : b.i);
+    return r;
+}
+
+// The network sorts P entries in decreasing order, every comparison in the
+// same direction: phase k (k = 2, 4, ..., P) first compares position p with
+// its mirror p ^ (k-1) inside its block of k, then p with p ^ j for
+// j = k/4, ..., 1; of each pair the lower position keeps the entry that comes
+// first.  Thread t holds positions tE .. tE+E-1, so distances below E stay in
+// the thread, partners up to 64E away are lanes of the same wave (shuffles; a
+// mirror partner holds the entries in reverse), farther ones go through LDS.
+template <typename T, int E>
+__device__ __forceinline__ void cas(Ent (&v)[E], int a, int b) {
+    const bool sw = before<T>(v[b], v[a]);
+    const Ent x = v[a], y = v[b];
+    v[a] = sel<T>(sw, y, x);
+    v[b] = sel<T>(sw, x, y);
+}
+
+template <typename T, int E, int KK>
+__device__ __forceinline__ void mirror_in_thread(Ent (&v)[E]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (!(e & (KK / 2))) cas<T, E>(v, e, e ^ (KK - 1));
+}
+
+template <typename T, int E, int J>
+__device__ __forceinline__ void half_in_thread(Ent (&v)[E]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (!(e & J)) cas<T, E>(v, e, e | J);
+}
+
+// partner lane t ^ mask; `bit` (>= E) of the position says whether this lane
+// holds the lower positions of its pairs
+template <typename T, int E, bool MIRROR, int M>
+__device__ __forceinline__ void stage_in_wave_m(Ent (&v)[E], bool first, int mask) {
+    Ent o[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) o[e] = lanes_xor<T, M>(v[MIRROR ? E - 1 - e : e], mask);
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = sel<T>(first == before<T>(o[e], v[e]), o[e], v[e]);
+}
+
+template <typename T, int E, bool MIRROR>
+__device__ __forceinline__ void stage_in_wave(Ent (&v)[E], int t, int mask, int bit) {
+    const bool first = ((t * E) & bit) == 0;
+    switch (mask) {
+        case 1:
+            stage_in_wave_m<T, E, MIRROR, 1>(v, first, mask);
+            break;
+        case 2:
+            stage_in_wave_m<T, E, MIRROR, 2>(v, first, mask);
+            break;
+        case 3:
+            stage_in_wave_m<T, E, MIRROR, 3>(v, first, mask);
+            break;
+        case 4:
+            stage_in_wave_m<T, E, MIRROR, 4>(v, first, mask);
+            break;
+        case 7:
+            stage_in_wave_m<T, E, MIRROR, 7>(v, first, mask);
+            break;
+        case 8:
+            stage_in_wave_m<T, E, MIRROR, 8>(v, first, mask);
+            break;
+        case 15:
+            stage_in_wave_m<T, E, MIRROR, 15>(v, first, mask);
+            break;
+        default:
+            stage_in_wave_m<T, E, MIRROR, 0>(v, first, mask);
     }
-    // Stages at distance <= 64 keep every wave inside its own 128 entries (the
-    // pairs of a wave are 64 consecutive q), so between two such stages a wave
-    // only waits for itself; any stage at a larger distance, before or after,
-    // needs the whole workgroup.
-    const int half = P / 2;
-    int jprev = P;
-    for (int k = 2; k <= P; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            if (j >= 128 || jprev >= 128)
-                __syncthreads();
-            else
-                wave_sync();
-            jprev = j;
-            sort_stage<T>(K, I, half, k, j);
-        }
+}
+
+// partner position p ^ xr through LDS (K, I: P entries)
+template <typename T, int E>
+__device__ __forceinline__ void stage_in_lds(Ent (&v)[E], int t, int xr, int bit, uint64_t* K, uint32_t* I) {
+    const int p = t * E;
+    const bool first = (p & bit) == 0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        K[p + e] = v[e].k;
+        if constexpr (sizeof(T) == 8) I[p + e] = v[e].i;
     }
     __syncthreads();
-    T* z = (T*)a.z + row0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        Ent o;
+        o.k = K[(p + e) ^ xr];
+        o.i = sizeof(T) == 4 ? 0u : I[(p + e) ^ xr];
+        v[e] = sel<T>(first == before<T>(o, v[e]), o, v[e]);
+    }
+    __syncthreads();
+}
+
+template <typename T, int E>
+__global__ __launch_bounds__(1024) void k_rank_sort(SortArgs a) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int n = a.n, P = a.P, t = threadIdx.x;
+    const int64_t row0 = (int64_t)blockIdx.x * n;
+    const int p0 = t * E;
+    const int cnt = min(max(n - p0, 0), E);
+    double xv[E];
+    load_lane<T, E>((const T*)a.x + row0 + p0, cnt, xv);
+    Ent v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const bool real = e < cnt;
+        const T x = (T)xv[e];
+        if constexpr (sizeof(T) == 4) {
+            v[e].k = real ? (((uint64_t)sort_key(x) << 32) | (uint32_t)~(uint32_t)(p0 + e)) : 0ull;
+            v[e].i = 0u;
+        } else {
+            v[e].k = real ? sort_key(x) : 0ull;
+            v[e].i = real ? (uint32_t)(p0 + e) : 0xffffffffu;
+        }
+    }
+    uint64_t* K = (uint64_t*)smem;
+    uint32_t* I = (uint32_t*)(smem + 8 * (size_t)P);
+    for (int k = 2; k <= P; k <<= 1) {
+        if (k <= E) {
+            if constexpr (E >= 2)
+                if (k == 2) mirror_in_thread<T, E, 2>(v);
+            if constexpr (E >= 4)
+                if (k == 4) mirror_in_thread<T, E, 4>(v);
+            if constexpr (E >= 8)
+                if (k == 8) mirror_in_thread<T, E, 8>(v);
+        } else if (k <= 64 * E) {
+            stage_in_wave<T, E, true>(v, t, k / E - 1, k >> 1);
+        } else {
+            stage_in_lds<T, E>(v, t, k - 1, k >> 1, K, I);
+        }
+        for (int j = k >> 2; j > 0; j >>= 1) {
+            if (j >= 64 * E) {
+                stage_in_lds<T, E>(v, t, j, j, K, I);
+            } else if (j >= E) {
+                stage_in_wave<T, E, false>(v, t, j / E, j);
+            } else {
+                if constexpr (E >= 8)
+                    if (j == 4) half_in_thread<T, E, 4>(v);
+                if constexpr (E >= 4)
+                    if (j == 2) half_in_thread<T, E, 2>(v);
+                if constexpr (E >= 2)
+                    if (j == 1) half_in_thread<T, E, 1>(v);
+            }
+        }
+    }
+    // thread t now holds sorted positions p0 .. p0+E-1; padding sorts last,
+    // so every position below n holds an element of the row
     int32_t* perm = a.perm + row0;
     int32_t* rank = a.rank + row0;
-    for (int i = threadIdx.x; i < n; i += blockDim.x) {
-        const uint64_t e = K[i];
-        int p;
-        double xv;
+    double zv[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        int idx;
+        double x;
         if constexpr (sizeof(T) == 4) {
-            p = (int)~(uint32_t)e;
-            xv = (double)key_value((uint32_t)(e >> 32));
+            idx = (int)~(uint32_t)v[e].k;
+            x = (double)key_value((uint32_t)(v[e].k >> 32));
         } else {
-            p = (int)I[i];
-            xv = key_value(e);
+            idx = (int)v[e].i;
+            x = key_value(v[e].k);
         }
-        perm[i] = p;
-        if ((unsigned)p < (unsigned)n) rank[p] = i;  // always true once sorted: padding sorts last
-        z[i] = (T)(xv / a.eps - (double)(n - i));
+        zv[e] = x / a.eps - (double)(n - (p0 + e));
+        if (e < cnt) {
+            perm[p0 + e] = idx;
+            if ((unsigned)idx < (unsigned)n) rank[idx] = p0 + e;
+        }
     }
+    store_lane<T, E>((T*)a.z + row0 + p0, cnt, zv);
 }
 
 // Element-wise passes over rows x n, grid-stride; `narrow` says that every
@@ -205,24 +352,46 @@ unsigned ew_grid(int64_t total) {
     return (unsigned)(b < 65536 ? b : 65536);
 }
 
+// Entries per thread of the sort: one wave of E entries each up to 512, then
+// eight per thread (at most 1024 threads for 8192 entries).
+template <typename T, int E>
+hipError_t launch_sort(const SortArgs& s, int64_t rows, hipStream_t stream) {
+    const int nt = s.P / E;
+    const size_t lds = nt > 64 ? (size_t)s.P * (sizeof(T) == 4 ? 8 : 12) : 0;
+    static size_t seen[kMaxDevices];
+    if (lds > 0) {
+        const hipError_t e = ensure_lds((const void*)k_rank_sort<T, E>, lds, seen);
+        if (e != hipSuccess) return e;
+    }
+    k_rank_sort<T, E><<<dim3((unsigned)rows), dim3(nt), lds, stream>>>(s);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t soft_rank_t(const RankLaunch& l) {
-    const int P = sort_width(l.n);
-    const int nt = P / 2 < 64 ? 64 : (P / 2 > 1024 ? 1024 : P / 2);
-    const size_t lds = (size_t)P * (sizeof(T) == 4 ? 8 : 12);
-    static size_t seen[kMaxDevices];
-    hipError_t e = ensure_lds((const void*)k_rank_sort<T>, lds, seen);
-    if (e != hipSuccess) return e;
     SortArgs s{};
     s.x = l.in;
     s.perm = l.perm;
     s.rank = l.rank;
     s.z = l.ws + l.zoff;
     s.n = (int)l.n;
-    s.P = P;
+    s.P = sort_width(l.n);
     s.eps = l.eps;
-    k_rank_sort<T><<<dim3((unsigned)l.rows), dim3(nt), lds, l.stream>>>(s);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipError_t e;
+    switch (s.P) {
+        case 64:
+            e = launch_sort<T, 1>(s, l.rows, l.stream);
+            break;
+        case 128:
+            e = launch_sort<T, 2>(s, l.rows, l.stream);
+            break;
+        case 256:
+            e = launch_sort<T, 4>(s, l.rows, l.stream);
+            break;
+        default:
+            e = launch_sort<T, 8>(s, l.rows, l.stream);
+    }
+    if (e != hipSuccess) return e;
 
     FitLaunch f{};
     f.y = l.ws + l.zoff;
