@@ -173,3 +173,55 @@ def soft_rank_vjp(g, eps, perm, block_start, row_nan=None):
     out = np.empty_like(g2)
     np.put_along_axis(out, perm, (gs - ags) / eps, axis=1)
     return out
+
+
+def calibration_fit(scores, labels):
+    """Calibration curve of each row (first page, Sec. 7.7; "torchisotonic" PyPI page, "What it is for":
+    scikit-learn's IsotonicRegression curve): the scores are sorted, equal scores are pooled (their labels
+    summed and counted), and the non-decreasing fit of the pooled means is computed with the counts as
+    weights.  Returns (xs, fit, m): xs and fit [rows, n] float64 hold the m[r] distinct scores of row r in
+    increasing order and the curve's values there (the rest NaN).  A row holding a NaN (score or label) has
+    no curve: m = 0."""
+    s2 = _as2d(scores)
+    l2 = _as2d(labels)
+    if s2.shape != l2.shape:
+        raise ValueError("labels must have the shape of scores")
+    rows, n = s2.shape
+    xs = np.full((rows, n), np.nan)
+    fv = np.full((rows, n), np.nan)
+    m = np.zeros(rows, dtype=np.int64)
+    for r in range(rows):
+        s, lab = s2[r], l2[r]
+        if n == 0 or np.isnan(s).any() or np.isnan(lab).any():
+            continue
+        order = np.argsort(s, kind="stable")
+        u, inv, cnt = np.unique(s[order], return_inverse=True, return_counts=True)
+        sums = np.zeros(len(u))
+        np.add.at(sums, inv, lab[order])
+        z, *_ = fit(sums / cnt, cnt.astype(np.float64), increasing=True)
+        k = len(u)
+        xs[r, :k] = u
+        fv[r, :k] = z[0]
+        m[r] = k
+    return xs, fv, m
+
+
+def calibrate(q, xs, fv, m):
+    """Calibrated values of the queries q [rows, k] on each row's curve ("torchisotonic" PyPI page, "What it
+    is for"): linear between the curve's points, constant beyond them; a NaN query, or a row without a curve,
+    gives NaN."""
+    q2 = _as2d(q)
+    out = np.full(q2.shape, np.nan)
+    for r in range(q2.shape[0]):
+        k = int(m[r])
+        if k == 0:
+            continue
+        x, f = xs[r, :k], fv[r, :k]
+        if k == 1:
+            out[r] = f[0]
+        else:
+            i = np.clip(np.searchsorted(x, q2[r], side="left"), 1, k - 1)
+            t = np.clip((q2[r] - x[i - 1]) / (x[i] - x[i - 1]), 0.0, 1.0)
+            out[r] = f[i - 1] + t * (f[i] - f[i - 1])
+        out[r, np.isnan(q2[r])] = np.nan
+    return out

@@ -508,3 +508,85 @@ def test_soft_rank_vjp_finite_differences(seed):
         fm, *_ = oracle.soft_rank(x - e, eps)
         num[:, k] = np.sum(g * (fp - fm), axis=1) / (2 * h)
     np.testing.assert_allclose(got, num, rtol=0, atol=1e-6)
+
+
+# ---------------------------------------------------------------- calibration (first page, Sec. 7.7; PyPI usage)
+
+def test_calibration_hand_cases():
+    """Worked by hand: equal scores pool before the fit, and the curve interpolates linearly between its
+    points and is constant beyond them."""
+    xs, fv, m = oracle.calibration_fit([[1.0, 2.0, 1.0]], [[0.0, 0.0, 1.0]])
+    # pooled: x = (1, 2), y = (1/2, 0), weights (2, 1); the violation pools both: (2*(1/2) + 0)/3 = 1/3
+    assert m[0] == 2 and list(xs[0, :2]) == [1.0, 2.0]
+    np.testing.assert_allclose(fv[0, :2], [1 / 3, 1 / 3], rtol=0, atol=1e-15)
+    xs, fv, m = oracle.calibration_fit([[0.0, 1.0, 2.0, 1.0]], [[0.0, 1.0, 1.0, 0.0]])
+    assert m[0] == 3
+    np.testing.assert_allclose(fv[0, :3], [0.0, 0.5, 1.0], rtol=0, atol=1e-15)
+    out = oracle.calibrate([[0.5, -1.0, 5.0, 1.5, 1.0, np.nan]], xs, fv, m)
+    np.testing.assert_allclose(out[0, :5], [0.25, 0.0, 1.0, 0.75, 0.5], rtol=0, atol=1e-15)
+    assert np.isnan(out[0, 5])
+    xs, fv, m = oracle.calibration_fit([[3.0, 3.0]], [[1.0, 0.0]])
+    assert m[0] == 1 and oracle.calibrate([[-7.0, 9.0]], xs, fv, m).tolist() == [[0.5, 0.5]]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_calibration_matches_sklearn(seed):
+    """scikit-learn's IsotonicRegression (out_of_bounds="clip") pools equal scores, fits, and interpolates
+    linearly: the curve's predictions must agree, ties included."""
+    from sklearn.isotonic import IsotonicRegression
+    r = workloads.rng(400 + seed)
+    n = [20, 200, 3000][seed % 3]
+    s = np.round(r.standard_normal(n), 1 + seed % 3)  # coarse scores: many ties
+    p = 1.0 / (1.0 + np.exp(-(1.5 * s - 1.0)))
+    y = (r.random(n) < p).astype(np.float64) if seed % 2 == 0 else p + 0.3 * r.standard_normal(n)
+    q = np.concatenate([np.linspace(s.min() - 1, s.max() + 1, 101), s[:50]])
+    xs, fv, m = oracle.calibration_fit(s, y)
+    got = oracle.calibrate(q, xs, fv, m)[0]
+    want = IsotonicRegression(increasing=True, out_of_bounds="clip").fit(s, y).predict(q)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+    assert m[0] == len(np.unique(s))
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_calibration_without_ties_is_the_fit_of_the_sorted_labels(seed):
+    """With distinct scores there is nothing to pool: the curve at the sorted scores is the plain isotonic
+    fit of the labels in score order (scipy)."""
+    from scipy.optimize import isotonic_regression
+    r = workloads.rng(500 + seed)
+    s = r.permutation(300) + r.random(300) * 0.5
+    y = r.standard_normal(300)
+    xs, fv, m = oracle.calibration_fit(s, y)
+    order = np.argsort(s)
+    assert m[0] == 300 and np.array_equal(xs[0], s[order])
+    np.testing.assert_allclose(fv[0], isotonic_regression(y[order]).x, rtol=0, atol=1e-12)
+
+
+def test_calibration_equals_fit_with_tied_labels_replaced_by_their_mean():
+    """A property of Eq. (1): equal neighbouring values always get equal fits, so pooling equal scores is
+    the same as replacing their labels by the group mean and fitting every sample with unit weight."""
+    from scipy.optimize import isotonic_regression
+    r = workloads.rng(17)
+    s = np.round(r.standard_normal(2000), 1)
+    y = r.standard_normal(2000)
+    xs, fv, m = oracle.calibration_fit(s, y)
+    order = np.argsort(s, kind="stable")
+    ss, yy = s[order], y[order].copy()
+    u, inv = np.unique(ss, return_inverse=True)
+    means = np.bincount(inv, yy) / np.bincount(inv)
+    full = isotonic_regression(means[inv]).x
+    np.testing.assert_allclose(full, fv[0, :m[0]][inv], rtol=0, atol=1e-12)
+
+
+def test_calibration_nan_rows_and_rows():
+    r = workloads.rng(23)
+    s = np.round(r.standard_normal((4, 50)), 1)
+    y = r.random((4, 50))
+    s[1, 3] = np.nan
+    y[2, 7] = np.nan
+    xs, fv, m = oracle.calibration_fit(s, y)
+    assert m[1] == 0 and m[2] == 0 and m[0] > 0 and m[3] > 0
+    assert np.isnan(oracle.calibrate(s, xs, fv, m)[[1, 2]]).all()
+    for row in (0, 3):
+        xr, fr, mr = oracle.calibration_fit(s[row], y[row])
+        np.testing.assert_array_equal(xr[0], xs[row])
+        np.testing.assert_allclose(fr[0], fv[row], rtol=0, atol=0)
