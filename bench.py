@@ -1,6 +1,6 @@
 """Benchmark of the batched weighted isotonic fit on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batch|dense|soft_rank|all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batch|dense|soft_rank|calibration|all]
                     [--no-cpu] [--copy-probe] [--cpu-seconds S]
 
 A step is one whole fit (every kernel of the path) over one batch of
@@ -15,7 +15,10 @@ are timed separately and reported in "backward"):
          k_merge_top, k_fixup (reported in "dense");
   soft rank: 4096 x 512 float32 standard normal scores, forward and backward
          of the first page's Sec. 7.9 composition at eps = 1 and 1/n
-         (reported in "soft_rank").
+         (reported in "soft_rank");
+  calibration: one curve over 6.5e6 float64 scores (the first page's Sec. 7.7
+         day), sort, pooling and fit, then 100001 queries (reported in
+         "calibration").
 
 Prints ONE JSON line.  Algorithmic bytes are y and w read once and the fit
 written once (12 B/element for the batch, 24 B/element for the dense rows);
@@ -201,6 +204,46 @@ def time_soft_rank(steps, rows=4096, n=512):
     return out
 
 
+def time_calibration(steps):
+    """Event-timed calibration curve (first page, Sec. 7.7; PyPI usage) of 6.5 million float64 scores on a 1e-5
+    grid with click labels: sort, pooling of equal scores, weighted fit; then 100001 queries on the curve.
+    Algorithmic bytes: scores and labels read, distinct scores and the curve written (at most 32 B/element)."""
+    import torch
+    import weighted_isotonic_regression_row_amd as iso
+    import workloads
+    dev = torch.device("cuda:0")
+    s, y, q = workloads.calibration_input()
+    s, y, q = torch.from_numpy(s).to(dev), torch.from_numpy(y).to(dev), torch.from_numpy(q).to(dev)
+    rows, n = s.shape
+    ws = iso.calibration_workspace(rows, n, s.dtype, dev)
+    xs, fit, m = iso.calibration_fit(s, y, ws=ws)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+
+    def run(fn, k):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(k):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / k
+
+    k = max(1, min(steps, 10))
+    fit_ms = run(lambda: iso.calibration_fit(s, y, ws=ws), k)
+    pred_ms = run(lambda: iso.calibrate(q, xs, fit, m, out=out), k)
+    distinct = int(m[0].item())
+    algo = n * 16 + distinct * 16
+    return {"workload": "1 curve over 6.5e6 float64 scores (N(0,1) on a 1e-5 grid), Bernoulli(sigmoid(1.5 s - 3)) "
+                        "labels; 100001 queries",
+            "distinct_scores": distinct, "fit_ms": fit_ms, "scores_per_s": n / (fit_ms * 1e-3),
+            "fit_hbm_frac": algo / (fit_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "predict_ms": pred_ms,
+            "queries_per_s": q.numel() / (pred_ms * 1e-3)}
+
+
 def copy_probe(nbytes=256 << 20, reps=20):
     """Device-to-device copy bandwidth of a plain copy of known size (read + write)."""
     import torch
@@ -248,7 +291,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["batch", "dense", "soft_rank", "all", "both"], default="all")
+    ap.add_argument("--workload", choices=["batch", "dense", "soft_rank", "calibration", "all", "both"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true", help="also time a plain device copy")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -321,6 +364,10 @@ def main():
     if args.workload in ("soft_rank", "all"):
         log("soft rank 4096 x 512 ...")
         rec["soft_rank"] = time_soft_rank(args.steps)
+
+    if args.workload in ("calibration", "all"):
+        log("calibration 6.5e6 ...")
+        rec["calibration"] = time_calibration(args.steps)
 
     if args.copy_probe:
         gbs, nb = copy_probe()

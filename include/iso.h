@@ -225,6 +225,45 @@ int iso_soft_rank_vjp(const void* grad_dev, const iso_soft_rank_state* state, vo
                       void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
+ * Calibration curve of every row (first page, Sec. 7.7; page "torchisotonic",
+ * "What it is for": scikit-learn's IsotonicRegression curve).  The row's
+ * scores are sorted in increasing order, equal scores are pooled (their labels
+ * summed and counted), and the curve is the non-decreasing fit of the pooled
+ * means with the counts as weights, computed by the same solver as iso_fit.
+ *   scores_dev, labels_dev  [rows, n] of dtype, read only.
+ *   xs_dev         [rows, n] of dtype, written: the m[r] distinct scores of
+ *                  row r in increasing order (-0 and +0 are one score, kept as
+ *                  +0); entries past m[r] are NaN.
+ *   fit_dev        [rows, n] of dtype, written: the curve at xs (entries past
+ *                  m[r] are unspecified).
+ *   m_dev          [rows] int32, written: the number of distinct scores, 0 for
+ *                  a row holding a NaN score or label (which has no curve).
+ *   workspace_dev  iso_calibration_workspace_bytes(rows, n, dtype) bytes,
+ *                  256-aligned; one call in flight per workspace.
+ * Scores and labels must be finite apart from NaN.  ISO_EINVAL for a bad
+ * dtype, NULL pointers, misaligned or short buffers, n above INT32_MAX.
+ * rows == 0 or n == 0 queues nothing.
+ */
+size_t iso_calibration_workspace_bytes(int64_t rows, int64_t n, int dtype);
+
+int iso_calibration_fit(const void* scores_dev, const void* labels_dev, int64_t rows, int64_t n, int dtype,
+                        void* xs_dev, void* fit_dev, int32_t* m_dev, void* workspace_dev, size_t workspace_bytes,
+                        void* stream);
+
+/*
+ * Calibrated values (page "torchisotonic", "What it is for"): each query of
+ * row r is placed on row r's curve, linearly between its points (the first
+ * point at or above the query and the one before it) and constant beyond the
+ * first and last points.  A NaN query, or a row without a curve (m = 0),
+ * gives NaN.
+ *   xs_dev, fit_dev, m_dev  as written by iso_calibration_fit ([rows, n],
+ *                  [rows, n], [rows]).
+ *   q_dev          [rows, k] of dtype, read only; out_dev [rows, k], written.
+ */
+int iso_calibrate(const void* xs_dev, const void* fit_dev, const int32_t* m_dev, int64_t rows, int64_t n,
+                  const void* q_dev, int64_t k, int dtype, void* out_dev, void* stream);
+
+/*
  * Synchronises `stream` and returns the data error of the most recent iso_fit
  * that used this workspace: ISO_OK or ISO_EWEIGHT (ISO_EHIP if the read fails,
  * ISO_EINVAL for a NULL workspace).

@@ -38,7 +38,8 @@ def test_header_declares_the_boundary():
     fns = declared_functions()
     assert fns == sorted(["iso_blocks_bytes", "iso_fit", "iso_status", "iso_strerror", "iso_vjp", "iso_vjp_yw",
                           "iso_workspace_bytes", "iso_soft_rank", "iso_soft_rank_vjp", "iso_soft_rank_state_bytes",
-                          "iso_soft_rank_workspace_bytes"])
+                          "iso_soft_rank_workspace_bytes", "iso_calibration_workspace_bytes", "iso_calibration_fit",
+                          "iso_calibrate"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -201,6 +202,36 @@ def test_soft_rank_vjp_rejects_bad_arguments_on_host(lib):
     assert lib.iso_soft_rank_vjp(256, ctypes.byref(sc), 512, 1 << 16, 1 << 20, None) == E
     sc.eps, sc.perm_dev = 1.0, None
     assert lib.iso_soft_rank_vjp(256, ctypes.byref(sc), 512, 1 << 16, 1 << 20, None) == E
+
+
+def test_calibration_sizes(lib):
+    # sorted (key, index) entries twice, run starts and label prefixes, pooled means and weights
+    assert lib.iso_calibration_workspace_bytes(1, 6_500_000, 1) >= 6_500_000 * (2 * 12 + 4 + 16 + 16)
+    assert lib.iso_calibration_workspace_bytes(-1, 5, 0) == 0
+    assert lib.iso_calibration_workspace_bytes(2, 5, 4) == 0
+    assert lib.iso_calibration_workspace_bytes(1, 1 << 31, 0) == 0
+
+
+def _cal(lib, s=256, y=512, rows=2, n=3, dt=0, xs=1024, fit=2048, m=4096, ws=1 << 16, wsb=1 << 24):
+    return lib.iso_calibration_fit(s, y, rows, n, dt, xs, fit, m, ws, wsb, None)
+
+
+def test_calibration_rejects_bad_arguments_on_host(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    E = iso.ISO_EINVAL
+    for kw in ({"rows": -1}, {"n": -1}, {"dt": 2}, {"s": None}, {"y": None}, {"xs": None}, {"fit": None},
+               {"m": None}, {"ws": None}, {"ws": (1 << 16) + 8}, {"wsb": 8}, {"xs": 2048}, {"xs": 256 + 4},
+               {"fit": 512}):
+        assert _cal(lib, **kw) == E, kw
+    assert _cal(lib, rows=0, s=None, y=None, xs=None, fit=None, m=None, ws=None) == iso.ISO_OK
+    assert _cal(lib, n=0, s=None, y=None, xs=None, fit=None, m=None, ws=None) == iso.ISO_OK
+    # evaluation
+    assert lib.iso_calibrate(256, 512, 1024, 2, 3, 2048, 5, 2, 4096, None) == E       # dtype
+    assert lib.iso_calibrate(None, 512, 1024, 2, 3, 2048, 5, 0, 4096, None) == E
+    assert lib.iso_calibrate(256, 512, None, 2, 3, 2048, 5, 0, 4096, None) == E
+    assert lib.iso_calibrate(256, 512, 1024, 2, 3, 2048, 5, 0, None, None) == E
+    assert lib.iso_calibrate(256, 512, 1024, 2, 3, 2048, -1, 0, 4096, None) == E
+    assert lib.iso_calibrate(None, None, None, 2, 3, None, 0, 0, None, None) == iso.ISO_OK  # no queries
 
 
 def test_status_without_calls(lib):

@@ -409,3 +409,88 @@ def test_soft_rank_ties_signed_zeros_and_nan_rows(dtype):
         g = np.ones_like(x)
         d = iso.soft_rank_vjp(to_dev(g), st).cpu().numpy()
         assert np.isnan(d[[2, 4]]).all() and not np.isnan(d[[0, 1, 3, 5]]).any()
+
+
+# ---------------------------------------------------------------- calibration (first page, Sec. 7.7; PyPI usage)
+
+def _calibration_case(s, y, q, what):
+    import torch
+    import weighted_isotonic_regression_row_amd as iso
+    dtype = s.dtype
+    xs, fit, m = iso.calibration_fit(to_dev(s), to_dev(y))
+    p = iso.calibrate(to_dev(q), xs, fit, m)
+    torch.cuda.synchronize()
+    rx, rf, rm = oracle.calibration_fit(s.astype(np.float64), y.astype(np.float64))
+    gm = m.cpu().numpy()
+    np.testing.assert_array_equal(gm, rm, err_msg=what)           # the number of distinct scores: exact
+    gx = xs.cpu().numpy().astype(np.float64)
+    gf = fit.cpu().numpy().astype(np.float64)
+    finite = np.isfinite(y)
+    scale = float(np.abs(y[finite]).max()) if finite.any() else 1.0
+    tol = (TOL_F64 if dtype == np.float64 else TOL_F32) * max(scale, 1e-300)
+    for r in range(s.shape[0]):
+        k = int(rm[r])
+        if k == 0:
+            continue
+        assert np.array_equal(gx[r, :k], rx[r, :k]), f"{what}: distinct scores of row {r}"
+        assert np.isnan(gx[r, k:]).all(), f"{what}: xs past m in row {r}"
+        err = float(np.max(np.abs(gf[r, :k] - rf[r, :k])))
+        assert err <= tol, f"{what}: curve of row {r} off by {err:.3e} > {tol:.3e}"
+        assert (np.diff(gf[r, :k]) >= -MONO_SLACK[np.dtype(dtype)] * scale).all(), f"{what}: curve of row {r} decreases"
+    ref = oracle.calibrate(q.astype(np.float64), rx, rf, rm)
+    gp = p.cpu().numpy().astype(np.float64)
+    assert np.array_equal(np.isnan(gp), np.isnan(ref)), f"{what}: NaN pattern of the predictions"
+    ok = ~np.isnan(ref)
+    if ok.any():
+        err = float(np.max(np.abs(gp[ok] - ref[ok])))
+        assert err <= 2 * tol, f"{what}: predictions off by {err:.3e}"
+
+
+MONO_SLACK = {np.dtype(np.float64): 1e-12, np.dtype(np.float32): 4 * 2.0 ** -23}
+CAL_SIZES = [1, 2, 100, 2048, 2049, 8192, 8193, 20000, 70001]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n", CAL_SIZES)
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_calibration_matches_oracle(n, dtype):
+    """Curves and predictions against the oracle: one pool tile and ragged ones, one sort tile and several
+    merged (8193 and more), coarse scores (many ties), Bernoulli and continuous labels, several rows."""
+    r = workloads.rng(600 + n % 101)
+    rows = 3 if n <= 20000 else 1
+    s = np.round(r.standard_normal((rows, n)), 2).astype(dtype)
+    p = 1.0 / (1.0 + np.exp(-(1.5 * s.astype(np.float64) - 1.0)))
+    y = (r.random((rows, n)) < p).astype(dtype)
+    if rows > 1:
+        y[1] = (p[1] + 0.2 * r.standard_normal(n)).astype(dtype)
+    q = np.concatenate([np.linspace(-5, 5, 257)[None, :].repeat(rows, 0), s[:, :64]], axis=1).astype(dtype)
+    _calibration_case(s, y, q, f"n={n}")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_calibration_edge_rows(dtype):
+    """All scores equal (one point: a constant curve), -0 against +0 (one score), distinct scores (nothing to
+    pool), and rows holding a NaN score or label (no curve: m = 0, NaN predictions)."""
+    r = workloads.rng(31)
+    n = 3000
+    s = r.standard_normal((6, n))
+    s[0] = 0.25
+    s[1, ::2] = -0.0
+    s[1, 1::2] = 0.0
+    s[2] = r.permutation(n)
+    s[3, 17] = np.nan
+    y = r.random((6, n))
+    y[4, 5] = np.nan
+    s, y = s.astype(dtype), y.astype(dtype)
+    q = np.concatenate([np.linspace(-3, 3, 101)[None, :].repeat(6, 0), s[:, :20]], axis=1).astype(dtype)
+    q[5, 3] = np.nan
+    _calibration_case(s, y, q, "edge rows")
+
+
+@pytest.mark.gpu
+def test_calibration_day_of_scores():
+    """6.5 million float64 scores of one curve (the first page's Sec. 7.7 day, synthetic): scores on a grid
+    of 1e-5 (pooled runs of equal scores), click labels from a logistic curve."""
+    s, y, q = workloads.calibration_input()
+    _calibration_case(s, y, q, "6.5e6 scores")

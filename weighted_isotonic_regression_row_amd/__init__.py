@@ -11,12 +11,17 @@ library (or without a GPU) the calls raise.
     grad_y, grad_w = iso_vjp_yw(grad, blocks, y)
     ranks, state = soft_rank(x, eps)
     grad_x = soft_rank_vjp(grad, state)
+    xs, curve, m = calibration_fit(scores, labels)
+    p = calibrate(new_scores, xs, curve, m)
 
 The fit of each row is the weighted least-squares monotone sequence (page
 "Merge Hulls Without Copying Vertices: GPU Isotonic Regression", Eq. (1)),
 with the semantics of the "torchisotonic" PyPI page ("Semantics").  The soft rank is the composition of the first page's
 Sec. 7.9: a per-row sort, the non-increasing fit of s - (n..1), and s minus
-that fit in the original order.
+that fit in the original order.  The calibration curve is that of Sec. 7.7
+and of the PyPI page's usage: scores sorted, equal scores pooled, the
+weighted non-decreasing fit of the pooled means, evaluated by linear
+interpolation.
 """
 from __future__ import annotations
 
@@ -37,7 +42,8 @@ ISO_EHIP = -2
 ISO_EWEIGHT = -3
 
 SYMBOLS = ("iso_workspace_bytes", "iso_blocks_bytes", "iso_fit", "iso_vjp", "iso_vjp_yw", "iso_soft_rank_state_bytes",
-           "iso_soft_rank_workspace_bytes", "iso_soft_rank", "iso_soft_rank_vjp", "iso_status", "iso_strerror")
+           "iso_soft_rank_workspace_bytes", "iso_soft_rank", "iso_soft_rank_vjp", "iso_calibration_workspace_bytes",
+           "iso_calibration_fit", "iso_calibrate", "iso_status", "iso_strerror")
 SOFT_RANK_MAX_N = 8192
 
 
@@ -108,6 +114,12 @@ def load_library(path: str | None = None):
                                   c_size, vp]
     lib.iso_soft_rank_vjp.restype = c_int
     lib.iso_soft_rank_vjp.argtypes = [vp, ctypes.POINTER(IsoSoftRankStateC), vp, vp, c_size, vp]
+    lib.iso_calibration_workspace_bytes.restype = c_size
+    lib.iso_calibration_workspace_bytes.argtypes = [i64, i64, c_int]
+    lib.iso_calibration_fit.restype = c_int
+    lib.iso_calibration_fit.argtypes = [vp, vp, i64, i64, c_int, vp, vp, vp, vp, c_size, vp]
+    lib.iso_calibrate.restype = c_int
+    lib.iso_calibrate.argtypes = [vp, vp, vp, i64, i64, vp, i64, c_int, vp, vp]
     lib.iso_status.restype = c_int
     lib.iso_status.argtypes = [vp, vp]
     lib.iso_strerror.restype = ctypes.c_char_p
@@ -350,10 +362,63 @@ def soft_rank_vjp(grad: torch.Tensor, state: SoftRankState, *, out: torch.Tensor
     return out.view(state.shape)
 
 
+def calibration_workspace(rows: int, n: int, dtype: torch.dtype, device) -> torch.Tensor:
+    code = ISO_F32 if dtype == torch.float32 else ISO_F64
+    return torch.empty(max(int(load_library().iso_calibration_workspace_bytes(rows, n, code)), 256), dtype=torch.uint8,
+                       device=device)
+
+
+def calibration_fit(scores: torch.Tensor, labels: torch.Tensor, *, ws: torch.Tensor | None = None):
+    """Calibration curve of every row (first page, Sec. 7.7; PyPI page, "What it is for"): returns (xs, fit, m),
+    the m[r] distinct scores of row r in increasing order and the curve there (entries past m[r] unspecified)."""
+    if not scores.is_cuda:
+        raise ValueError("calibration_fit runs on the GPU: scores must be a device tensor")
+    lib = load_library()
+    s2 = _as_rows(scores)
+    l2 = _as_rows(labels)
+    if s2.shape != l2.shape or s2.dtype != l2.dtype or s2.device != l2.device:
+        raise ValueError("labels must have the shape, dtype and device of scores")
+    if not s2.is_contiguous() or not l2.is_contiguous():
+        raise ValueError("scores and labels must be contiguous")
+    rows, n = s2.shape
+    dt = _dtype_code(s2)
+    xs = torch.empty_like(s2)
+    fit = torch.empty_like(s2)
+    m = torch.empty(rows, dtype=torch.int32, device=s2.device)
+    if ws is None:
+        ws = calibration_workspace(rows, n, s2.dtype, s2.device)
+    code = lib.iso_calibration_fit(s2.data_ptr(), l2.data_ptr(), rows, n, dt, xs.data_ptr(), fit.data_ptr(),
+                                   m.data_ptr(), ws.data_ptr(), ws.numel(), _stream_ptr(s2.device))
+    if code != ISO_OK:
+        raise IsoError(code, "iso_calibration_fit")
+    return xs, fit, m
+
+
+def calibrate(q: torch.Tensor, xs: torch.Tensor, fit: torch.Tensor, m: torch.Tensor, *,
+              out: torch.Tensor | None = None) -> torch.Tensor:
+    """Calibrated values of the queries q [rows, k] on the curves (linear between points, constant beyond)."""
+    lib = load_library()
+    shape = q.shape
+    q2 = _as_rows(q)
+    if not q2.is_contiguous() or q2.dtype != xs.dtype or xs.shape != fit.shape or q2.shape[0] != xs.shape[0]:
+        raise ValueError("q must be contiguous, of the curve's dtype, one row per curve")
+    if m.dtype != torch.int32 or m.numel() != xs.shape[0]:
+        raise ValueError("m must be the int32 counts of calibration_fit")
+    rows, k = q2.shape
+    if out is None:
+        out = torch.empty_like(q2)
+    code = lib.iso_calibrate(xs.data_ptr(), fit.data_ptr(), m.data_ptr(), rows, xs.shape[1], q2.data_ptr(), k,
+                             _dtype_code(q2), out.data_ptr(), _stream_ptr(q2.device))
+    if code != ISO_OK:
+        raise IsoError(code, "iso_calibrate")
+    return out.view(shape)
+
+
 def iso_status(ws: torch.Tensor) -> int:
     return int(load_library().iso_status(ws.data_ptr(), _stream_ptr(ws.device)))
 
 
 __all__ = ["iso_fit", "iso_vjp", "iso_vjp_yw", "soft_rank", "soft_rank_vjp", "SoftRankState", "soft_rank_workspace",
+           "calibration_fit", "calibrate", "calibration_workspace",
            "SOFT_RANK_MAX_N", "iso_status", "iso_workspace_bytes", "iso_blocks_bytes", "workspace",
            "Blocks", "IsoError", "load_library", "SYMBOLS"]

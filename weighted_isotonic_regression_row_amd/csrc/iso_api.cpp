@@ -253,6 +253,66 @@ int iso_soft_rank_vjp(const void* grad, const iso_soft_rank_state* state, void* 
     return ISO_OK;
 }
 
+size_t iso_calibration_workspace_bytes(int64_t rows, int64_t n, int dtype) {
+    if (rows < 0 || n < 0 || n > (int64_t)INT32_MAX || !valid_dtype(dtype)) return 0;
+    return iso::make_cal_layout(rows, n, dtype == ISO_F32 ? 4 : 8).total;
+}
+
+int iso_calibration_fit(const void* scores, const void* labels, int64_t rows, int64_t n, int dtype, void* xs,
+                        void* fit, int32_t* m, void* workspace, size_t workspace_bytes, void* stream) {
+    if (rows < 0 || n < 0 || !valid_dtype(dtype) || n > (int64_t)INT32_MAX) return ISO_EINVAL;
+    if (rows == 0 || n == 0) return ISO_OK;
+    if (!scores || !labels || !xs || !fit || !m || !workspace) return ISO_EINVAL;
+    if (((uintptr_t)workspace & 255u) != 0) return ISO_EINVAL;
+    const size_t esz = dtype == ISO_F32 ? 4 : 8;
+    const iso::CalLayout C = iso::make_cal_layout(rows, n, esz);
+    if (workspace_bytes < C.total) return ISO_EINVAL;
+    if (rows * ((n + 8191) / 8192) > (int64_t)UINT32_MAX) return ISO_EINVAL;
+    const size_t bytes = (size_t)rows * (size_t)n * esz;
+    auto overlap = [&](const void* p, const void* q) {
+        const char* a = (const char*)p;
+        const char* b = (const char*)q;
+        return a < b + bytes && b < a + bytes;
+    };
+    if (overlap(xs, fit) || overlap(xs, scores) || overlap(xs, labels) || overlap(fit, scores) ||
+        overlap(fit, labels))
+        return ISO_EINVAL;
+    iso::CalLaunch l{};
+    l.scores = scores;
+    l.labels = labels;
+    l.rows = rows;
+    l.n = n;
+    l.dtype = dtype;
+    l.xs = xs;
+    l.fit = fit;
+    l.m = m;
+    l.ws = (char*)workspace;
+    l.C = C;
+    l.stream = (hipStream_t)stream;
+    if (iso::launch_calibration_fit(l) != hipSuccess) return ISO_EHIP;
+    return ISO_OK;
+}
+
+int iso_calibrate(const void* xs, const void* fit, const int32_t* m, int64_t rows, int64_t n, const void* q,
+                  int64_t k, int dtype, void* out, void* stream) {
+    if (rows < 0 || n < 0 || k < 0 || !valid_dtype(dtype)) return ISO_EINVAL;
+    if (rows == 0 || k == 0) return ISO_OK;
+    if (n == 0 || !xs || !fit || !m || !q || !out) return ISO_EINVAL;
+    iso::CalPredictLaunch l{};
+    l.xs = xs;
+    l.fit = fit;
+    l.m = m;
+    l.q = q;
+    l.out = out;
+    l.rows = rows;
+    l.n = n;
+    l.k = k;
+    l.dtype = dtype;
+    l.stream = (hipStream_t)stream;
+    if (iso::launch_calibrate(l) != hipSuccess) return ISO_EHIP;
+    return ISO_OK;
+}
+
 int iso_status(const void* workspace, void* stream) {
     if (!workspace) return ISO_EINVAL;
     unsigned long long last = 0;

@@ -92,6 +92,19 @@ def soft_rank_input(rows=4096, n=512, seed=3, dtype=np.float32):
     return x, g
 
 
+def calibration_input(n=6_500_000, seed=4, dtype=np.float64):
+    """Raw input of the calibration composition (first page, Sec. 7.7: one curve
+    over a day of 6.5 million click-model scores; synthetic): scores N(0,1) on a
+    grid of 1e-5, so that equal scores pool into runs; click labels
+    Bernoulli(sigmoid(1.5 s - 3)); queries spanning and beyond the scores."""
+    r = rng(seed)
+    s = np.round(r.standard_normal(n), 5)
+    p = 1.0 / (1.0 + np.exp(-(1.5 * s - 3.0)))
+    y = (r.random(n) < p).astype(dtype)
+    q = np.linspace(-6.0, 6.0, 100_001)
+    return s.astype(dtype)[None, :], y[None, :], q.astype(dtype)[None, :]
+
+
 def cfg4_calibration(n=6_500_000, seed=4) -> Workload:
     """Calibration-shaped single row, float64: sorted scores s ~ N(0,1),
     integer counts c ~ 1 + Poisson(2) as weights, y = Binomial(c, sigmoid(1.5 s - 3)) / c,
