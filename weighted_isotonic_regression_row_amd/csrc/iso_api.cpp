@@ -9,6 +9,7 @@
 #include <unordered_map>
 
 #include "../../include/iso.h"
+#include "iso_compose.hpp"
 #include "iso_internal.hpp"
 
 namespace {

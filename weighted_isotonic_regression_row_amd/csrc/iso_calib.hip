@@ -25,6 +25,7 @@
 #include <math.h>
 
 #include "iso_device.hpp"
+#include "iso_compose.hpp"
 #include "iso_internal.hpp"
 #include "iso_sort.hpp"
 
