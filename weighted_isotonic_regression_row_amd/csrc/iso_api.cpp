@@ -268,7 +268,7 @@ int iso_calibration_fit(const void* scores, const void* labels, int64_t rows, in
     const size_t esz = dtype == ISO_F32 ? 4 : 8;
     const iso::CalLayout C = iso::make_cal_layout(rows, n, esz);
     if (workspace_bytes < C.total) return ISO_EINVAL;
-    if (rows * ((n + 8191) / 8192) > (int64_t)UINT32_MAX) return ISO_EINVAL;
+    if (rows * ((n + 2047) / 2048) > (int64_t)UINT32_MAX) return ISO_EINVAL;  // merge and pooling grids
     const size_t bytes = (size_t)rows * (size_t)n * esz;
     auto overlap = [&](const void* p, const void* q) {
         const char* a = (const char*)p;

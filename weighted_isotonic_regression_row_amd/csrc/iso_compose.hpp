@@ -16,6 +16,7 @@ struct CalLayout {
     size_t trec, tmax, tnan;      // [rows * ceil(n / 2048)]: double4, double, int
     size_t rtot, rnan;            // [rows]: double4, int
     size_t start, pst;            // [rows * n]: int32, double2
+    size_t ys;                    // [rows * n] of the data type: labels in score order
     size_t yp, wp;                // [rows * n] of the data type
     size_t total;
 };
@@ -42,6 +43,7 @@ inline CalLayout make_cal_layout(int64_t rows, int64_t n, size_t esz) {
     C.rnan = take(4 * (size_t)rows);
     C.start = take(4 * rn);
     C.pst = take(16 * rn);
+    C.ys = take(esz * rn);
     C.yp = take(esz * rn);
     C.wp = take(esz * rn);
     C.total = off;
