@@ -189,9 +189,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
 // and a backward pass hands every element the slope of the first vertex at or
 // after its right point.  No LDS, no barriers.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int K>
 __global__ __launch_bounds__(256) void k_rows_lane(RowArgs a, int64_t rows) {
-    constexpr int K = kLaneRow;
     const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= rows) return;
     const int N = (int)a.n;
@@ -1170,7 +1169,10 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
                     a.words, status, a.epoch, 0, nullptr, 0, nullptr, 0};
     if (a.n <= kLaneRow) {
         const unsigned grid = (unsigned)((a.rows + 255) / 256);
-        hipLaunchKernelGGL(k_rows_lane<T>, dim3(grid), dim3(256), 0, a.stream, r, (int64_t)a.rows);
+        if (a.n <= 16)
+            hipLaunchKernelGGL((k_rows_lane<T, 16>), dim3(grid), dim3(256), 0, a.stream, r, (int64_t)a.rows);
+        else
+            hipLaunchKernelGGL((k_rows_lane<T, 32>), dim3(grid), dim3(256), 0, a.stream, r, (int64_t)a.rows);
         return hipGetLastError();
     }
     if (a.n <= kSingleMax) {

@@ -8,8 +8,9 @@
 namespace iso {
 
 // Rows of at most this many elements are fitted one per lane (the whole row's
-// hull in registers); the backward pass handles them the same way.
-constexpr int kLaneRow = 16;
+// hull in registers: 16 points per lane up to 16 elements, else 32); the
+// backward pass handles them the same way.
+constexpr int kLaneRow = 32;
 // LDS of one CU (bytes).
 constexpr int kLdsBytes = 163840;
 // Rows of at most this many elements are fitted by one workgroup each, the

@@ -181,7 +181,7 @@ template <typename T, int K>
 __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restrict__ w, int cnt, int negate,
                                      double (&xs)[K], double (&ys)[K], int& f, T* stage = nullptr,
                                      int avail = 0) {
-    static_assert(K <= 24, "next-vertex offsets are packed in at most two words");
+    static_assert(K <= 32, "next-vertex offsets are packed in at most three words");
     double X = 0.0, Y = 0.0;
     auto take = [&](int j, double yi, double wi) {
         if (j < cnt) {
@@ -267,7 +267,9 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
     uint64_t mask = 0ull;
     int v = 0;
     for (int s = 0; s < K && v < cnt; ++s) {
-        const uint64_t word = (PW == 1 || v < PE) ? nxp[0] : nxp[PW - 1];
+        uint64_t word = nxp[0];
+#pragma unroll
+        for (int q = 1; q < PW; ++q) word = v >= q * PE ? nxp[q] : word;
         v += 1 + (int)((word >> (PB * (v % PE))) & ((1ull << PB) - 1ull));
         mask |= 1ull << (v - 1);
     }

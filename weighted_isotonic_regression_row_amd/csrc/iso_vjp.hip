@@ -252,10 +252,9 @@ __global__ void k_vjp_carry(VjpArgs a, int64_t rows) {
 // Rows of at most kLaneRow elements, one row per lane: running block sums
 // forward, then each block's totals handed back to its elements.  Whole,
 // aligned rows are read and written with 16-byte accesses.
-template <typename T, int NF>
+template <typename T, int NF, int K>
 __global__ __launch_bounds__(256) void k_vjp_lane(VjpArgs a, int64_t rows) {
     using A = Acc<NF>;
-    constexpr int K = kLaneRow;
     const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= rows) return;
     const int N = (int)a.n;
@@ -530,8 +529,11 @@ static hipError_t launch_vjp_t(const VjpLaunch& l) {
     a.cb = l.clip_bits;
     a.row_nan = l.row_nan;
     if (l.n <= kLaneRow) {
-        hipLaunchKernelGGL((k_vjp_lane<T, NF>), dim3((unsigned)((l.rows + 255) / 256)), dim3(256), 0, l.stream, a,
-                           l.rows);
+        const dim3 grid((unsigned)((l.rows + 255) / 256));
+        if (l.n <= 16)
+            hipLaunchKernelGGL((k_vjp_lane<T, NF, 16>), grid, dim3(256), 0, l.stream, a, l.rows);
+        else
+            hipLaunchKernelGGL((k_vjp_lane<T, NF, 32>), grid, dim3(256), 0, l.stream, a, l.rows);
         return hipGetLastError();
     }
     static size_t seen[kMaxDevices] = {};
