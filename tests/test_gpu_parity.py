@@ -495,3 +495,38 @@ def test_calibration_day_of_scores():
     of 1e-5 (pooled runs of equal scores), click labels from a logistic curve."""
     s, y, q = workloads.calibration_input()
     _calibration_case(s, y, q, "6.5e6 scores")
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("n", [5000, 300, 24, 20000])
+def test_fit_replayed_from_a_hip_graph(n):
+    """The fit call captured in a HIP graph (it records kernel launches only, no memset) gives the eager
+    result bit for bit on every replay, with eager work and synchronisations between the replays;
+    one-workgroup rows, one-wave rows, one-row-per-lane rows and chunked rows (several launches)."""
+    import torch
+    import weighted_isotonic_regression_row_amd as iso
+    rows = 64 if n <= 5000 else 4
+    wl = workloads.family("noise", rows, n, seed=n, dtype=np.float32, weights="uniform", increasing=False)
+    wl.y_min, wl.y_max = 0.0, 1.0
+    y, w = to_dev(wl.y), to_dev(wl.w)
+    ws = iso.workspace(rows, n, y.dtype, y.device)
+    eager = iso.iso_fit(y, w, False, 0.0, 1.0, ws=ws, blocks=False, check=True)[0].clone()
+    out = torch.empty_like(y)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # a first call on the capture stream sets any launch attributes
+        iso.iso_fit(y, w, False, 0.0, 1.0, out=out, ws=ws, blocks=False, check=False)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        iso.iso_fit(y, w, False, 0.0, 1.0, out=out, ws=ws, blocks=False, check=False)
+    for k in range(3):
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {k}"
+        other = iso.iso_fit(y * 0.5, w, True, ws=iso.workspace(rows, n, y.dtype, y.device), blocks=False,
+                            check=False)[0]
+        torch.cuda.synchronize()
+        del other
