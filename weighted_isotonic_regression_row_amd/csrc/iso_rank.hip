@@ -3,8 +3,9 @@
 //
 // Forward, per row: theta = x / eps is sorted in decreasing order into s;
 // z = s - (n, n-1, ..., 1) is fitted non-increasing with unit weights by the
-// library's own solver (launch_fit), and the element at sorted position i gets
-// the rank s_i - v_i, written back in the original order.
+// library's own solver, and the element at sorted position i gets the rank
+// s_i - v_i, written back in the original order.  Rows of 65 to 512 elements
+// run all of it in one kernel (k_rank_fused); other rows take these steps:
 //   k_rank_sort    one workgroup per row: a bitonic network over (key, index)
 //                  pairs in LDS, where key is an order-preserving unsigned image
 //                  of x (theta has the order of x as eps > 0), ties broken by the
@@ -18,9 +19,12 @@
 //   k_rank_gather      g_s[i] = g[perm[i]];
 //   launch_vjp         A g_s over the fit's blocks;
 //   k_rank_vjp_finish  grad[k] = (g[k] - (A g_s)[rank[k]]) / eps.
+#include <math.h>
+
 #include "iso_device.hpp"
 #include "iso_internal.hpp"
 #include "iso_sort.hpp"
+#include "iso_tile.hpp"
 
 namespace iso {
 namespace {
@@ -37,7 +41,7 @@ struct SortArgs {
 
 template <typename T, int E>
 __global__ __launch_bounds__(1024) void k_rank_sort(SortArgs a) {
-    extern __shared__ __align__(16) unsigned char smem[];
+    extern __shared__ __align__(32) char smem[];
     const int n = a.n, P = a.P, t = threadIdx.x;
     const int64_t row0 = (int64_t)blockIdx.x * n;
     const int p0 = t * E;
@@ -81,6 +85,104 @@ __global__ __launch_bounds__(1024) void k_rank_sort(SortArgs a) {
         }
     }
     store_lane<T, E>((T*)a.z + row0 + p0, cnt, zv);
+}
+
+// Rows of 65 to 512 elements in one kernel, one wave per row.  After the
+// sort, lane l holds sorted positions lE .. lE+E-1, which is the layout of
+// the one-wave fit tile with E points per lane: z = s - (n..1) goes from the
+// sort's registers into the lane hulls, the tile keeps every vertex in LDS
+// (no overflow pass), and each element's rank s - v is stored straight to its
+// original position.
+struct FusedArgs {
+    const void* x;
+    void* r;
+    int32_t* perm;
+    int32_t* rank;
+    uint64_t* start_bits;
+    uint64_t* clip_bits;
+    uint32_t* row_nan;
+    int64_t words;
+    int n;
+    double eps;
+};
+
+template <typename T, int E>
+__global__ __launch_bounds__(64) void k_rank_fused(FusedArgs a) {
+    extern __shared__ __align__(32) char smem[];
+    const int n = a.n, t = threadIdx.x, p0 = t * E;
+    const int64_t row = blockIdx.x;
+    const int64_t row0 = row * n;
+    const int cnt = min(max(n - p0, 0), E);
+    double xv[E];
+    load_lane<T, E>((const T*)a.x + row0 + p0, cnt, xv);
+    Ent v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const bool real = e < cnt;
+        const T x = (T)xv[e];
+        if constexpr (sizeof(T) == 4) {
+            v[e].k = real ? (((uint64_t)sort_key(x) << 32) | (uint32_t)~(uint32_t)(p0 + e)) : 0ull;
+            v[e].i = 0u;
+        } else {
+            v[e].k = real ? sort_key(x) : 0ull;
+            v[e].i = real ? (uint32_t)(p0 + e) : 0xffffffffu;
+        }
+    }
+    sort_entries<T, E>(v, t, 64 * E, nullptr, nullptr);  // every partner is inside the wave
+    int idx[E];
+    double sv[E], z[E];
+    int32_t* perm = a.perm + row0;
+    int32_t* rank = a.rank + row0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        double x;
+        if constexpr (sizeof(T) == 4) {
+            idx[e] = (int)~(uint32_t)v[e].k;
+            x = (double)key_value((uint32_t)(v[e].k >> 32));
+        } else {
+            idx[e] = (int)v[e].i;
+            x = key_value(v[e].k);
+        }
+        sv[e] = x / a.eps;
+        z[e] = sv[e] - (double)(n - (p0 + e));
+        if (e < cnt) {
+            perm[p0 + e] = idx[e];
+            if ((unsigned)idx[e] < (unsigned)n) rank[idx[e]] = p0 + e;
+        }
+    }
+    // the non-increasing fit of z over the sorted positions (tile pipeline)
+    constexpr bool ABS = sizeof(T) == 4;
+    const Tile tl = tile_carve(smem, 64, n, E, n);
+    double xs[E], ys[E];
+    int f = 0;
+    uint64_t mask = lane_hull_vals<E>(z, cnt, 1, xs, ys, f);
+    (void)tile_lane_starts<!ABS>(tl, make_double2(xs[E - 1], ys[E - 1]), f, __popcll(mask));
+    uint64_t* sb = a.start_bits + row * a.words;
+    uint64_t* cb = a.clip_bits + row * a.words;
+    T* r = (T*)a.r + row0;
+    if (tl.flag[0]) {  // a NaN in the row
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+            if (e < cnt && (unsigned)idx[e] < (unsigned)n) r[idx[e]] = (T)NAN;
+        for (int q = t; q < (int)a.words; q += 64) {
+            sb[q] = 0ull;
+            cb[q] = 0ull;
+        }
+        if (t == 0) a.row_nan[row] = 1u;
+        return;
+    }
+    tile_merges<E, ABS>(tl, mask, xs, ys);
+    tile_edge_slopes<E, ABS>(tl);
+    double vals[E];
+    uint64_t clipm;
+    tile_expand<E>(tl, mask, 0, -INFINITY, INFINITY, vals, clipm);
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+        if (e < cnt && (unsigned)idx[e] < (unsigned)n) r[idx[e]] = (T)(sv[e] - vals[e]);
+    tl.CM[t] = clipm;
+    __syncthreads();
+    tile_bits<E>(tl, sb, cb);
+    if (t == 0) a.row_nan[row] = 0u;
 }
 
 // Element-wise passes over rows x n, grid-stride; `narrow` says that every
@@ -170,8 +272,30 @@ hipError_t launch_sort(const SortArgs& s, int64_t rows, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <typename T, int E>
+hipError_t launch_fused(const RankLaunch& l) {
+    FusedArgs f{};
+    f.x = l.in;
+    f.r = l.out;
+    f.perm = l.perm;
+    f.rank = l.rank;
+    f.start_bits = l.start_bits;
+    f.clip_bits = l.clip_bits;
+    f.row_nan = l.row_nan;
+    f.words = l.words;
+    f.n = (int)l.n;
+    f.eps = l.eps;
+    k_rank_fused<T, E><<<dim3((unsigned)l.rows), dim3(64), tile_smem_bytes(64, (int)l.n, E), l.stream>>>(f);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t soft_rank_t(const RankLaunch& l) {
+    if (l.n > 64 && l.n <= 512) {
+        if (l.n <= 128) return launch_fused<T, 2>(l);
+        if (l.n <= 256) return launch_fused<T, 4>(l);
+        return launch_fused<T, 8>(l);
+    }
     SortArgs s{};
     s.x = l.in;
     s.perm = l.perm;

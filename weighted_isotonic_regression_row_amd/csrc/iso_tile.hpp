@@ -123,6 +123,43 @@ __device__ __forceinline__ double vturn(const Tile& t, int i, int j, int k) {
 
 // ---------------------------------------------------------------------------
 // 1. lane hull, in registers
+// Gift wrapping over the lane's points (xs, ys)[0..cnt) (point j+1 of the
+// lane at index j; the lane's start is the origin): the bit mask of the hull's
+// vertices, bit j for point j+1.
+template <int K>
+__device__ __forceinline__ uint64_t lane_gift_wrap(const double (&xs)[K], const double (&ys)[K], int cnt) {
+    // next-vertex pointers, as offsets nx - j - 1 in PB-bit fields, PE per word
+    constexpr int PB = (K <= 16) ? 4 : 5, PE = 64 / PB, PW = (K + PE - 1) / PE;
+    uint64_t nxp[PW];
+#pragma unroll
+    for (int q = 0; q < PW; ++q) nxp[q] = 0ull;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const double xj = j ? xs[j - 1] : 0.0, yj = j ? ys[j - 1] : 0.0;
+        double bdx = xs[j] - xj, bdy = ys[j] - yj;
+        int bk = 0;
+#pragma unroll
+        for (int k = j + 2; k <= K; ++k) {
+            const double dx = xs[k - 1] - xj, dy = ys[k - 1] - yj;
+            const bool take = (k <= cnt) && (dy * bdx <= bdy * dx);
+            bdx = take ? dx : bdx;
+            bdy = take ? dy : bdy;
+            bk = take ? (k - j - 1) : bk;
+        }
+        nxp[j / PE] |= (uint64_t)bk << (PB * (j % PE));
+    }
+    uint64_t mask = 0ull;
+    int v = 0;
+    for (int s = 0; s < K && v < cnt; ++s) {
+        uint64_t word = nxp[0];
+#pragma unroll
+        for (int q = 1; q < PW; ++q) word = v >= q * PE ? nxp[q] : word;
+        v += 1 + (int)((word >> (PB * (v % PE))) & ((1ull << PB) - 1ull));
+        mask |= 1ull << (v - 1);
+    }
+    return mask;
+}
+
 // ---------------------------------------------------------------------------
 
 // The wave's K * 64 elements of one input through LDS, for lanes whose K
@@ -244,36 +281,26 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
             take(j, yi, wi);
         }
     }
-    // next-vertex pointers, as offsets nx - j - 1 in PB-bit fields, PE per word
-    constexpr int PB = (K <= 16) ? 4 : 5, PE = 64 / PB, PW = (K + PE - 1) / PE;
-    uint64_t nxp[PW];
-#pragma unroll
-    for (int q = 0; q < PW; ++q) nxp[q] = 0ull;
+    return lane_gift_wrap<K>(xs, ys, cnt);
+}
+
+// The same on values already in registers, with unit weights: yv[j] for
+// j < cnt (f as in lane_hull; a non-finite value sets bit 1).
+template <int K>
+__device__ inline uint64_t lane_hull_vals(const double (&yv)[K], int cnt, int negate, double (&xs)[K],
+                                          double (&ys)[K], int& f) {
+    double X = 0.0, Y = 0.0;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
-        const double xj = j ? xs[j - 1] : 0.0, yj = j ? ys[j - 1] : 0.0;
-        double bdx = xs[j] - xj, bdy = ys[j] - yj;
-        int bk = 0;
-#pragma unroll
-        for (int k = j + 2; k <= K; ++k) {
-            const double dx = xs[k - 1] - xj, dy = ys[k - 1] - yj;
-            const bool take = (k <= cnt) && (dy * bdx <= bdy * dx);
-            bdx = take ? dx : bdx;
-            bdy = take ? dy : bdy;
-            bk = take ? (k - j - 1) : bk;
+        if (j < cnt) {
+            if (!isfinite(yv[j])) f |= 1;
+            X += 1.0;
+            Y += negate ? -yv[j] : yv[j];
         }
-        nxp[j / PE] |= (uint64_t)bk << (PB * (j % PE));
+        xs[j] = X;
+        ys[j] = Y;
     }
-    uint64_t mask = 0ull;
-    int v = 0;
-    for (int s = 0; s < K && v < cnt; ++s) {
-        uint64_t word = nxp[0];
-#pragma unroll
-        for (int q = 1; q < PW; ++q) word = v >= q * PE ? nxp[q] : word;
-        v += 1 + (int)((word >> (PB * (v % PE))) & ((1ull << PB) - 1ull));
-        mask |= 1ull << (v - 1);
-    }
-    return mask;
+    return lane_gift_wrap<K>(xs, ys, cnt);
 }
 
 // ---------------------------------------------------------------------------
