@@ -299,7 +299,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", choices=["batch", "dense", "soft_rank", "calibration", "all", "both"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg (profiling runs)")
-    ap.add_argument("--copy-probe", action="store_true", help="also time a plain device copy")
+    ap.add_argument("--copy-probe", action="store_true", help="time a plain device copy (also done by default runs)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -375,7 +375,7 @@ def main():
         log("calibration 6.5e6 ...")
         rec["calibration"] = time_calibration(args.steps)
 
-    if args.copy_probe:
+    if args.copy_probe or args.workload == "all":
         gbs, nb = copy_probe()
         rec["copy_probe"] = {"bytes_moved_per_copy": 2 * nb, "GB_per_s": gbs, "frac_of_peak": gbs / HBM_PEAK_GBS}
 
