@@ -106,14 +106,14 @@ def test_rows_past_the_lds_list_mixed_with_others(n, dtype):
     check_fit(fit.cpu().numpy(), z, wl.y, dtype, True, wl.name)
 
 
-@pytest.mark.parametrize("n", [1, 2, 5, 15, 16, 17, 24, 31, 32, 33])
+@pytest.mark.parametrize("n", [1, 2, 5, 15, 16, 17, 24, 31, 32, 33, 40, 48, 64, 65])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 def test_short_rows_one_per_lane(n, dtype):
-    """Rows of at most 32 elements are fitted one row per lane (the first
-    page, Sec. 3.5: short rows packed several to a warp; 16 or 32 points per
-    lane), 33 goes to the one-wave tile: many rows of several families, both
-    orientations, clipped and not, with block bits and both backward
-    products."""
+    """Rows of at most 32 elements are fitted one row per lane, rows of 33 to
+    64 on two lanes whose hulls are merged across point 32 (the first page,
+    Sec. 3.5: short rows packed several to a warp), 65 goes to the one-wave
+    tile: many rows of several families, both orientations, clipped and not,
+    with block bits and both backward products."""
     import weighted_isotonic_regression_row_amd as iso
     r = workloads.rng(900 + n)
     rows = 3000

@@ -320,6 +320,108 @@ __global__ __launch_bounds__(256) void k_vjp_lane(VjpArgs a, int64_t rows) {
     }
 }
 
+// Rows of 33 to 64 elements, two lanes per row (as the fit): each lane runs
+// the block sums of its 32 elements; the block open at the end of the left
+// lane carries its sums into the right lane's elements before the right lane's
+// first block start, and the right lane's first block total flows back to the
+// left lane's last block when that block continues across element 32.
+template <int NF>
+__device__ __forceinline__ Acc<NF> shfl_xor_acc(const Acc<NF>& a, int m) {
+    Acc<NF> r;
+#pragma unroll
+    for (int k = 0; k < NF; ++k) r.v[k] = __shfl_xor(a.v[k], m);
+    return r;
+}
+
+template <typename T, int NF>
+__global__ __launch_bounds__(64) void k_vjp_pair(VjpArgs a, int64_t rows) {
+    using A = Acc<NF>;
+    constexpr int K = 32;
+    const int h = threadIdx.x & 1;
+    const int64_t row = ((int64_t)blockIdx.x * 64 + threadIdx.x) >> 1;
+    if (row >= rows) return;  // both lanes of a pair leave together
+    const int N = (int)a.n;   // 33 .. 64
+    const int cnt = h ? N - K : K;
+    const int64_t e0 = row * a.n + h * K;
+    const T* g = (const T*)a.g + e0;
+    const T* w = a.w ? (const T*)a.w + e0 : nullptr;
+    const T* y = (NF == 3) ? (const T*)a.y + e0 : nullptr;
+    T* out = a.out ? (T*)a.out + e0 : nullptr;
+    T* out_w = (NF == 3) ? (T*)a.out_w + e0 : nullptr;
+    if (a.row_nan[row]) {
+        for (int j = 0; j < cnt; ++j) {
+            if (out) out[j] = (T)NAN;
+            if (NF == 3) out_w[j] = (T)NAN;
+        }
+        return;
+    }
+    const uint64_t swr = a.sb[row * a.words], cwr = a.cb[row * a.words];
+    const uint64_t sw = h ? (swr >> K) : swr;  // bit j <-> element hK + j (the left lane also sees element 32's)
+    const uint64_t cw = h ? (cwr >> K) : cwr;
+    const bool cont = !((swr >> K) & 1ull);  // the block open at element 31 continues into element 32
+    A run[K];
+    {
+        double gv[K], wv[K], yv[K];
+        load_lane<T, K>(g, cnt, gv);
+        if (w) {
+            load_lane<T, K>(w, cnt, wv);
+        } else {
+#pragma unroll
+            for (int j = 0; j < K; ++j) wv[j] = 1.0;
+        }
+        if (NF == 3) load_lane<T, K>(y, cnt, yv);
+        A c = acc_zero<NF>();
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            if (j < cnt) {
+                if ((sw >> j) & 1ull) c = acc_zero<NF>();
+                c.v[0] += ((cw >> j) & 1ull) ? 0.0 : gv[j];
+                c.v[1] += wv[j];
+                if (NF == 3) c.v[NF - 1] += wv[j] * yv[j];
+            }
+            run[j] = c;
+        }
+    }
+    // the left lane's open block into the right lane, up to its first start
+    const A end0 = shfl_xor_acc<NF>(run[K - 1], 1);
+    if (h == 1 && cont) {
+        const int fs = sw ? lo_bit(sw) : K;
+#pragma unroll
+        for (int j = 0; j < K; ++j) run[j] = acc_pick(j < fs, acc_sum(end0, run[j]), run[j]);
+    }
+    // the right lane's first block total back to the left lane
+    const uint64_t ends = (h ? bits_upto(cnt - 1) & ((sw >> 1) | (1ull << (cnt - 1))) : 0ull);
+    const int jf = h ? lo_bit(ends) : 0;
+    A first = acc_zero<NF>();
+#pragma unroll
+    for (int j = 0; j < K; ++j) first = acc_pick(j == jf, run[j], first);
+    const A from1 = shfl_xor_acc<NF>(first, 1);
+    double gw[K];
+    double mean[K];
+    A tot = (h == 0 && cont) ? from1 : acc_zero<NF>();
+#pragma unroll
+    for (int j = K - 1; j >= 0; --j) {
+        // element j closes its block when the next element starts one (or it is the row's last)
+        if (j < cnt && ((h == 1 && j == cnt - 1) || ((sw >> (j + 1)) & 1ull))) tot = run[j];
+        gw[j] = tot.v[0] / tot.v[1];
+        mean[j] = (NF == 3) ? tot.v[NF - 1] / tot.v[1] : 0.0;
+    }
+    if (out) {
+        double v[K];
+        if (w) load_lane<T, K>(w, cnt, v);
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = (w ? v[j] : 1.0) * gw[j];
+        store_lane<T, K>(out, cnt, v);
+    }
+    if (NF == 3) {
+        double v[K];
+        load_lane<T, K>(y, cnt, v);
+#pragma unroll
+        for (int j = 0; j < K; ++j) v[j] = gw[j] * (v[j] - mean[j]);
+        store_lane<T, K>(out_w, cnt, v);
+    }
+}
+
 // Rows of kLaneRow < n <= kSingleMax elements, one workgroup per row, all
 // sums in registers (kVjpK elements per lane):
 //   1. each lane forms the segmented prefix sums of its elements (reset at
@@ -534,6 +636,11 @@ static hipError_t launch_vjp_t(const VjpLaunch& l) {
             hipLaunchKernelGGL((k_vjp_lane<T, NF, 16>), grid, dim3(256), 0, l.stream, a, l.rows);
         else
             hipLaunchKernelGGL((k_vjp_lane<T, NF, 32>), grid, dim3(256), 0, l.stream, a, l.rows);
+        return hipGetLastError();
+    }
+    if (l.n <= 2 * kLaneRow) {
+        hipLaunchKernelGGL((k_vjp_pair<T, NF>), dim3((unsigned)((2 * l.rows + 63) / 64)), dim3(64), 0, l.stream, a,
+                           l.rows);
         return hipGetLastError();
     }
     static size_t seen[kMaxDevices] = {};
