@@ -255,21 +255,20 @@ __global__ __launch_bounds__(256) void k_rows_lane(RowArgs a, int64_t rows) {
 // takes the slope of the merged hull's edge above it.  One wave of 32 rows per
 // workgroup.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int K>
 __global__ __launch_bounds__(64) void k_rows_pair(RowArgs a, int64_t rows) {
-    constexpr int K = 32;
     __shared__ double2 Pt[32][2 * K + 1];  // per row: its points 0 .. n, absolute
     const int rl = threadIdx.x >> 1, h = threadIdx.x & 1;
     const int64_t row = (int64_t)blockIdx.x * 32 + rl;
     if (row >= rows) return;  // both lanes of a pair leave together
-    const int N = (int)a.n;   // 33 .. 64
+    const int N = (int)a.n;   // K + 1 .. 2K
     const int cnt = h ? N - K : K;
     const int64_t e0 = row * a.n + h * K;
     double xs[K], ys[K];
     int f = 0;
     const uint64_t mask = lane_hull<T, K>((const T*)a.y + e0, a.w ? (const T*)a.w + e0 : nullptr, cnt, !a.increasing,
                                           xs, ys, f);
-    // the right lane's points are relative to point 32, the left lane's total
+    // the right lane's points are relative to point K, the left lane's total
     const double X0 = __shfl_xor(xs[K - 1], 1), Y0 = __shfl_xor(ys[K - 1], 1);
     const double ox = h ? X0 : 0.0, oy = h ? Y0 : 0.0;
     if (h == 0) Pt[rl][0] = make_double2(0.0, 0.0);
@@ -280,7 +279,7 @@ __global__ __launch_bounds__(64) void k_rows_pair(RowArgs a, int64_t rows) {
     const uint64_t mo = __shfl_xor(mask, 1);
     wave_sync();
     T* out = (T*)a.fit + e0;
-    uint64_t* sb = a.start_bits ? a.start_bits + row * a.words : nullptr;  // one word: n <= 64
+    uint64_t* sb = a.start_bits ? a.start_bits + row * a.words : nullptr;  // one word: n <= 2K <= 64
     uint64_t* cb = a.clip_bits ? a.clip_bits + row * a.words : nullptr;
     if (fr) {
         for (int j = 0; j < cnt; ++j) out[j] = (T)NAN;
@@ -294,8 +293,8 @@ __global__ __launch_bounds__(64) void k_rows_pair(RowArgs a, int64_t rows) {
         }
         return;
     }
-    // vertex sets: left hull over points 0..32 (bit p), right hull over
-    // points 32..N (bit p - 32); both lanes compute the same bridge
+    // vertex sets: left hull over points 0..K (bit p), right hull over
+    // points K..N (bit p - K); both lanes compute the same bridge
     const uint64_t VA = 1ull | ((h ? mo : mask) << 1);
     const uint64_t VB = 1ull | ((h ? mask : mo) << 1);
     auto turn = [&](int i, int j, int k) {
@@ -1304,7 +1303,7 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
     }
     if (a.n <= 2 * kLaneRow) {
         const unsigned grid = (unsigned)((a.rows + 31) / 32);
-        hipLaunchKernelGGL(k_rows_pair<T>, dim3(grid), dim3(64), 0, a.stream, r, (int64_t)a.rows);
+        hipLaunchKernelGGL((k_rows_pair<T, 32>), dim3(grid), dim3(64), 0, a.stream, r, (int64_t)a.rows);
         return hipGetLastError();
     }
     if (a.n <= kSingleMax) {

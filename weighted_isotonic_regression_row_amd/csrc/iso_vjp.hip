@@ -320,8 +320,9 @@ __global__ __launch_bounds__(256) void k_vjp_lane(VjpArgs a, int64_t rows) {
     }
 }
 
-// Rows of 33 to 64 elements, two lanes per row (as the fit): each lane runs
-// the block sums of its 32 elements; the block open at the end of the left
+// Rows of 17 to 64 elements, two lanes of K = 16 or 32 elements per row (the
+// fit takes one lane up to 32 and two above; the block bits are the same
+// word): each lane runs the block sums of its elements; the block open at the end of the left
 // lane carries its sums into the right lane's elements before the right lane's
 // first block start, and the right lane's first block total flows back to the
 // left lane's last block when that block continues across element 32.
@@ -333,14 +334,13 @@ __device__ __forceinline__ Acc<NF> shfl_xor_acc(const Acc<NF>& a, int m) {
     return r;
 }
 
-template <typename T, int NF>
+template <typename T, int NF, int K>
 __global__ __launch_bounds__(64) void k_vjp_pair(VjpArgs a, int64_t rows) {
     using A = Acc<NF>;
-    constexpr int K = 32;
     const int h = threadIdx.x & 1;
     const int64_t row = ((int64_t)blockIdx.x * 64 + threadIdx.x) >> 1;
     if (row >= rows) return;  // both lanes of a pair leave together
-    const int N = (int)a.n;   // 33 .. 64
+    const int N = (int)a.n;   // K + 1 .. 2K
     const int cnt = h ? N - K : K;
     const int64_t e0 = row * a.n + h * K;
     const T* g = (const T*)a.g + e0;
@@ -630,17 +630,17 @@ static hipError_t launch_vjp_t(const VjpLaunch& l) {
     a.sb = l.start_bits;
     a.cb = l.clip_bits;
     a.row_nan = l.row_nan;
-    if (l.n <= kLaneRow) {
-        const dim3 grid((unsigned)((l.rows + 255) / 256));
-        if (l.n <= 16)
-            hipLaunchKernelGGL((k_vjp_lane<T, NF, 16>), grid, dim3(256), 0, l.stream, a, l.rows);
-        else
-            hipLaunchKernelGGL((k_vjp_lane<T, NF, 32>), grid, dim3(256), 0, l.stream, a, l.rows);
+    if (l.n <= 16) {
+        hipLaunchKernelGGL((k_vjp_lane<T, NF, 16>), dim3((unsigned)((l.rows + 255) / 256)), dim3(256), 0, l.stream, a,
+                           l.rows);
         return hipGetLastError();
     }
     if (l.n <= 2 * kLaneRow) {
-        hipLaunchKernelGGL((k_vjp_pair<T, NF>), dim3((unsigned)((2 * l.rows + 63) / 64)), dim3(64), 0, l.stream, a,
-                           l.rows);
+        const dim3 grid((unsigned)((2 * l.rows + 63) / 64));
+        if (l.n <= 32)
+            hipLaunchKernelGGL((k_vjp_pair<T, NF, 16>), grid, dim3(64), 0, l.stream, a, l.rows);
+        else
+            hipLaunchKernelGGL((k_vjp_pair<T, NF, 32>), grid, dim3(64), 0, l.stream, a, l.rows);
         return hipGetLastError();
     }
     static size_t seen[kMaxDevices] = {};
