@@ -79,6 +79,49 @@ __device__ __forceinline__ double4 dpp_move(double4 v) {
                         dpp_move<CTRL, ROWS>(v.w));
 }
 
+// The same moves, but a lane whose source falls outside the pattern (or whose
+// row is masked off) keeps its own value.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_keep(double v) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const int lo = (int)(unsigned)b, hi = (int)(unsigned)(b >> 32);
+    const unsigned rlo = (unsigned)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWS, 0xf, false);
+    const unsigned rhi = (unsigned)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWS, 0xf, false);
+    return __longlong_as_double((long long)(((unsigned long long)rhi << 32) | rlo));
+}
+__device__ __forceinline__ double readlane_d(double v, int lane) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)b, lane);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), lane);
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
+// Least value over the wave (no NaN), the same in every lane: the scan's
+// steps with min, whose result gathers in lane 63.
+__device__ __forceinline__ double wave_min(double v) {
+    v = fmin(v, dpp_keep<0x111, 0xf>(v));
+    v = fmin(v, dpp_keep<0x112, 0xf>(v));
+    v = fmin(v, dpp_keep<0x114, 0xf>(v));
+    v = fmin(v, dpp_keep<0x118, 0xf>(v));
+    v = fmin(v, dpp_keep<0x142, 0xa>(v));
+    v = fmin(v, dpp_keep<0x143, 0xc>(v));
+    return readlane_d(v, kWave - 1);
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_keep_f(float v) {
+    const int b = __float_as_int(v);
+    return __int_as_float(__builtin_amdgcn_update_dpp(b, b, CTRL, ROWS, 0xf, false));
+}
+__device__ __forceinline__ float wave_min_f(float v) {
+    v = fminf(v, dpp_keep_f<0x111, 0xf>(v));
+    v = fminf(v, dpp_keep_f<0x112, 0xf>(v));
+    v = fminf(v, dpp_keep_f<0x114, 0xf>(v));
+    v = fminf(v, dpp_keep_f<0x118, 0xf>(v));
+    v = fminf(v, dpp_keep_f<0x142, 0xa>(v));
+    v = fminf(v, dpp_keep_f<0x143, 0xc>(v));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+}
+
 // Inclusive scan over the 64 lanes of the wave with op(earlier, later), whose
 // identity is the all-zero value: Hillis-Steele steps 1, 2, 4, 8 inside each
 // row of 16 lanes, then the rows' totals by two broadcasts.

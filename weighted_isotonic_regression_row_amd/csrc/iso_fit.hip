@@ -71,10 +71,12 @@ __device__ inline void wg_write_nan(int64_t N, T* out, uint64_t* sbits, uint64_t
 // weight); nvert = the number of lane-hull vertices.  The lane's points stay
 // in xs, ys.
 // With stage set, the inputs pass through the still unused vertex list (each
-// wave K * 64 elements of it).
+// wave K * 64 elements of it).  With nxp, the masks are those of the lanes'
+// half hulls (a superset of the lane hulls' vertices, gw_halves).
 template <typename T, int K>
 __device__ inline int tile_build(const Tile& t, const T* y, const T* w, int increasing, uint64_t& mask,
-                                 double (&xs)[K], double (&ys)[K], int& nvert, bool stage = false) {
+                                 double (&xs)[K], double (&ys)[K], int& nvert, bool stage = false,
+                                 uint64_t (*nxp)[3] = nullptr) {
     constexpr bool ABS = sizeof(T) == 4;
     const int l = threadIdx.x;
     const int cnt = min(max(t.N - l * K, 0), K);
@@ -83,9 +85,10 @@ __device__ inline int tile_build(const Tile& t, const T* y, const T* w, int incr
         const int e0 = (l & ~(kWave - 1)) * K;  // the wave's first element
         T* st = (T*)t.VXY + e0;
         mask = lane_hull<T, K>(y + e0, w ? w + e0 : nullptr, cnt, !increasing, xs, ys, f, st,
-                               min(max(t.N - e0, 0), K * kWave));
+                               min(max(t.N - e0, 0), K * kWave), nxp);
     } else {
-        mask = lane_hull<T, K>(y + (int64_t)l * K, w ? w + (int64_t)l * K : nullptr, cnt, !increasing, xs, ys, f);
+        mask = lane_hull<T, K>(y + (int64_t)l * K, w ? w + (int64_t)l * K : nullptr, cnt, !increasing, xs, ys, f,
+                               nullptr, 0, nxp);
     }
     nvert = tile_lane_starts<!ABS>(t, make_double2(xs[K - 1], ys[K - 1]), f, __popcll(mask));
     return t.flag[0];
@@ -111,6 +114,26 @@ __device__ inline void tile_finish(const Tile& t, uint64_t mask, int increasing,
     }
 }
 
+// The row kernel's exact path: the lane hulls built again from the inputs and
+// merged in rounds.  Its own function (not inlined), so that its registers are
+// allocated apart from the wrap's.  Returns the lane's final vertex mask, or
+// ~0 (uniformly) when the lane hulls' vertices overflow the LDS list.
+template <typename T, int K>
+__device__ __attribute__((noinline)) uint64_t row_exact(RowArgs a) {
+    extern __shared__ __align__(32) char smem[];
+    const int64_t row = blockIdx.x;
+    const Tile t = tile_carve(smem, blockDim.x, a.cap, K, (int)a.n, sizeof(T) == 4);
+    const T* y = (const T*)a.y + row * a.n;
+    const T* w = a.w ? (const T*)a.w + row * a.n : nullptr;
+    uint64_t mask;
+    double xs[K], ys[K];
+    int nvert;
+    (void)tile_build<T, K>(t, y, w, a.increasing, mask, xs, ys, nvert, a.stage != 0);  // inputs already checked
+    if (nvert > a.cap + 1) return ~0ull;
+    tile_merges<K, sizeof(T) == 4>(t, mask, xs, ys);
+    return mask;
+}
+
 // ---------------------------------------------------------------------------
 // one workgroup per row.  The row's phases are latency-bound, so the register
 // budget is capped at 128 VGPRs (four waves per SIMD).  The vertex list lives
@@ -123,7 +146,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     extern __shared__ __align__(32) char smem[];
     const int64_t row = blockIdx.x;
     const int N = (int)a.n;
-    const Tile t = tile_carve(smem, blockDim.x, a.cap, K, N);
+    const Tile t = tile_carve(smem, blockDim.x, a.cap, K, N, sizeof(T) == 4);
     const T* y = (const T*)a.y + row * a.n;
     const T* w = a.w ? (const T*)a.w + row * a.n : nullptr;
     T* out = (T*)a.fit + row * a.n;
@@ -132,20 +155,44 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     uint64_t mask;
     double xs[K], ys[K];
     int nvert;
-    const int flag = tile_build<T, K>(t, y, w, a.increasing, mask, xs, ys, nvert, a.stage != 0);
-    const bool over = !flag && nvert > a.cap + 1;  // the list holds point 0 and cap vertices; uniform
-    if (a.ovf_row && threadIdx.x == 0) a.ovf_row[row] = over ? 1 : 0;
+    uint64_t nxp[3];
+    constexpr bool HALVES = K >= 12;  // rows of several waves
+    const int flag = tile_build<T, K>(t, y, w, a.increasing, mask, xs, ys, nvert, a.stage != 0,
+                                      HALVES ? &nxp : nullptr);
     if (flag) {
         wg_write_nan<T>(N, out, sb, cb);
         if (threadIdx.x == 0) {
+            if (a.ovf_row) a.ovf_row[row] = 0;
             if (a.row_nan) a.row_nan[row] = 1u;
             if (flag == 2) report_weight_error(a.status, a.epoch);
         }
         return;
     }
-    if (over) return;
     constexpr bool ABS = sizeof(T) == 4;
-    tile_merges<K, ABS>(t, mask, xs, ys);
+    bool over = false;
+    if constexpr (HALVES) {
+        // Noisy rows: the half hulls' vertices are few, and wrapping them
+        // gives the row's hull directly.  Other rows, and rows whose wrap
+        // gives up, take the exact path.  The list holds point 0 and cap
+        // vertices; every condition here is uniform.
+        bool done = false;
+        if (5 * nvert <= 3 * N + 5 && nvert <= a.cap + 1) {
+            tile_compact<K, ABS>(t, mask, xs, ys);
+            if (tile_wrap<K, ABS>(t)) {
+                tile_masks<K>(t, mask);
+                done = true;
+            }
+        }
+        if (!done) {
+            mask = row_exact<T, K>(a);
+            over = mask == ~0ull;
+        }
+    } else {
+        over = nvert > a.cap + 1;
+        if (!over) tile_merges<K, ABS>(t, mask, xs, ys, true);
+    }
+    if (a.ovf_row && threadIdx.x == 0) a.ovf_row[row] = over ? 1 : 0;
+    if (over) return;
     tile_finish<T, K>(t, mask, a.increasing, a.lo, a.hi, out, sb, cb);
     if (a.row_nan && threadIdx.x == 0) a.row_nan[row] = 0u;
 }
@@ -1249,12 +1296,12 @@ static void row_shape(int N, bool f32, int& K, int& nl) {
 // waves puts ceil(W/4) of them on its busiest SIMD, so 4 / ceil(W/4) share
 // it.  The list takes what their share of the 160 KiB leaves (at least a
 // quarter of the points).  Rows that need more go to k_row_ovf.
-static int row_list_cap(int N, int nl, int K) {
+static int row_list_cap(int N, int nl, int K, bool ls2) {
     const int W = nl / 64;
     const int per_simd = (W + 3) / 4;
     const long wgs = (W <= 4) ? 16 / W : (per_simd >= 4 ? 1 : 4 / per_simd);
     const long target = kLdsBytes / wgs - 512;
-    const long fixed = (long)tile_smem_bytes(nl, 0, K);
+    const long fixed = (long)tile_smem_bytes(nl, 0, K, ls2);
     const long room = (target - fixed) / 18;
     const long cap = room > N / 4 ? room : N / 4;
     return (int)(cap < N ? cap : N);
@@ -1262,8 +1309,9 @@ static int row_list_cap(int N, int nl, int K) {
 
 template <typename T, int K>
 static hipError_t launch_row(const FitLaunch& a, RowArgs r, int nl) {
-    r.cap = row_list_cap((int)a.n, nl, K);
-    const size_t smem = tile_smem_bytes(nl, r.cap, K);
+    constexpr bool ls2 = sizeof(T) == 4;  // float32 tiles: plain lane starts
+    r.cap = row_list_cap((int)a.n, nl, K, ls2);
+    const size_t smem = tile_smem_bytes(nl, r.cap, K, ls2);
     static size_t seen[kMaxDevices] = {};
     (void)ensure_lds((const void*)k_row_fit<T, K>, smem, seen);
     r.ovf = a.ws + a.L.ovf;

@@ -49,16 +49,28 @@ namespace iso {
 struct Tile {
     unsigned short* V;  // the current vertices, sorted (point indices): the tile's list, or one per wave
     double2* VXY;       // their coordinates (local to the point's lane, or absolute)
-    double4* LS;        // [nl + 1] lane starts (double-double pairs), LS[nl] = tile total
+    double4* LS;        // [nl + 1] lane starts (double-double pairs), LS[nl] = tile total; plain
+                        // (x, y) double pairs instead when ls2 (tiles whose starts are not double-double)
     uint64_t* M;        // [nl] final lane vertex masks
     uint64_t* CM;       // [nl] lane clip masks
     int* I;             // [nl] index in V of each lane's first vertex
     int2* MR;           // [nl / 2 + 1] bridge (alpha, beta) points of the merges of a round
+    int* R;             // wrap results: [nw * kWrapWave] per wave, then (nw > 1) the tile's candidates and hull
     int* W;             // [32] per-wave scratch
     int* flag;          // [4]
     int nl;             // lanes (= threads of the workgroup)
     int N;              // elements
+    bool ls2;           // LS holds double2 entries
 };
+
+// Step caps of the output-sensitive finish (tile_wrap): hull vertices a wave
+// may find among its lane hulls' vertices, and the tile among the waves'.
+constexpr int kWrapWave = 32;
+constexpr int kWrapTile = 128;
+__host__ __device__ inline size_t tile_wrap_ints(int nl) {
+    const int nw = nl / 64;
+    return (size_t)nw * kWrapWave + (nw > 1 ? (size_t)(4 + nw * kWrapWave + kWrapTile) : 0);
+}
 
 // List capacity: the tile's vertices plus point 0.
 __host__ __device__ inline size_t tile_list_len(int nl, int cap, int K) {
@@ -67,21 +79,30 @@ __host__ __device__ inline size_t tile_list_len(int nl, int cap, int K) {
     return (size_t)cap + 1;
 }
 
-__host__ __device__ inline size_t tile_smem_bytes(int nl, int cap, int K) {
-    const size_t n = tile_list_len(nl, cap, K);
-    const size_t v = (2 * n + 15) & ~(size_t)15;
-    return v + 16 * n + 32 * (size_t)(nl + 1) + 16 * (size_t)nl + 4 * (size_t)nl + 8 * (size_t)(nl / 2 + 1) + 128 +
-           16 + 128;
+// The wrap's results share the clip-mask array when they fit in it (the two
+// are never in use at once).
+__host__ __device__ inline size_t tile_wrap_own_bytes(int nl) {
+    const size_t b = 4 * tile_wrap_ints(nl);
+    return b <= 8 * (size_t)nl ? 0 : ((b + 15) & ~(size_t)15);
 }
 
-__device__ inline Tile tile_carve(char* base, int nl, int cap, int K, int N) {
+// ls2: lane starts as plain double pairs (16 bytes a lane instead of 32).
+__host__ __device__ inline size_t tile_smem_bytes(int nl, int cap, int K, bool ls2 = false) {
+    const size_t n = tile_list_len(nl, cap, K);
+    const size_t v = (2 * n + 15) & ~(size_t)15;
+    return v + 16 * n + (ls2 ? 16 : 32) * (size_t)(nl + 1) + 16 * (size_t)nl + 4 * (size_t)nl +
+           8 * (size_t)(nl / 2 + 1) + 128 + 16 + 128 + tile_wrap_own_bytes(nl);
+}
+
+__device__ inline Tile tile_carve(char* base, int nl, int cap, int K, int N, bool ls2 = false) {
     Tile t;
     char* p = base;
     const size_t n = tile_list_len(nl, cap, K);
     t.VXY = (double2*)p;
     p += 16 * n;
     t.LS = (double4*)p;
-    p += 32 * (size_t)(nl + 1);
+    t.ls2 = ls2;
+    p += (ls2 ? 16 : 32) * (size_t)(nl + 1);
     t.M = (uint64_t*)p;
     p += 8 * (size_t)nl;
     t.CM = (uint64_t*)p;
@@ -94,6 +115,12 @@ __device__ inline Tile tile_carve(char* base, int nl, int cap, int K, int N) {
     p += 128;
     t.flag = (int*)p;
     p += 16;
+    if (tile_wrap_own_bytes(nl)) {
+        t.R = (int*)p;
+        p += tile_wrap_own_bytes(nl);
+    } else {
+        t.R = (int*)t.CM;
+    }
     t.V = (unsigned short*)p;
     t.nl = nl;
     t.N = N;
@@ -124,33 +151,46 @@ __device__ __forceinline__ double vturn(const Tile& t, int i, int j, int k) {
 // ---------------------------------------------------------------------------
 // 1. lane hull, in registers
 // Gift wrapping over the lane's points (xs, ys)[0..cnt) (point j+1 of the
-// lane at index j; the lane's start is the origin): the bit mask of the hull's
-// vertices, bit j for point j+1.
+// lane at index j; the lane's start is the origin).  From point j the next
+// vertex is the point k of least slope (the farthest one on ties); the
+// pointers are kept as offsets nx - j - 1, PB bits each, PE per word.
 template <int K>
-__device__ __forceinline__ uint64_t lane_gift_wrap(const double (&xs)[K], const double (&ys)[K], int cnt) {
-    // next-vertex pointers, as offsets nx - j - 1 in PB-bit fields, PE per word
-    constexpr int PB = (K <= 16) ? 4 : 5, PE = 64 / PB, PW = (K + PE - 1) / PE;
-    uint64_t nxp[PW];
+struct GiftWrap {
+    static constexpr int PB = (K <= 16) ? 4 : 5, PE = 64 / PB, PW = (K + PE - 1) / PE;
+    static_assert(PW <= 3, "next-vertex offsets are packed in at most three words");
+};
+
+// Pointers of the points j in [J0, J1) over the candidates k <= KMAX.
+template <int K, int J0, int J1, int KMAX>
+__device__ __forceinline__ void gw_ptrs(const double (&xs)[K], const double (&ys)[K], int cnt, uint64_t (&nxp)[3]) {
+    constexpr int PB = GiftWrap<K>::PB, PE = GiftWrap<K>::PE;
 #pragma unroll
-    for (int q = 0; q < PW; ++q) nxp[q] = 0ull;
-#pragma unroll
-    for (int j = 0; j < K; ++j) {
+    for (int j = J0; j < J1; ++j) {
         const double xj = j ? xs[j - 1] : 0.0, yj = j ? ys[j - 1] : 0.0;
         double bdx = xs[j] - xj, bdy = ys[j] - yj;
         int bk = 0;
 #pragma unroll
-        for (int k = j + 2; k <= K; ++k) {
+        for (int k = j + 2; k <= KMAX; ++k) {
             const double dx = xs[k - 1] - xj, dy = ys[k - 1] - yj;
             const bool take = (k <= cnt) && (dy * bdx <= bdy * dx);
             bdx = take ? dx : bdx;
             bdy = take ? dy : bdy;
             bk = take ? (k - j - 1) : bk;
         }
-        nxp[j / PE] |= (uint64_t)bk << (PB * (j % PE));
+        const uint64_t field = ((1ull << PB) - 1ull) << (PB * (j % PE));
+        nxp[j / PE] = (nxp[j / PE] & ~field) | ((uint64_t)bk << (PB * (j % PE)));
     }
+}
+
+// The chain of pointers from point v0 until it reaches min(vend, cnt): the
+// mask of the points it visits (bit j for point j+1).
+template <int K>
+__device__ __forceinline__ uint64_t gw_walk(const uint64_t (&nxp)[3], int v0, int vend, int cnt) {
+    constexpr int PB = GiftWrap<K>::PB, PE = GiftWrap<K>::PE, PW = GiftWrap<K>::PW;
+    const int end = min(vend, cnt);
     uint64_t mask = 0ull;
-    int v = 0;
-    for (int s = 0; s < K && v < cnt; ++s) {
+    int v = v0;
+    for (int s = 0; s < K && v < end; ++s) {
         uint64_t word = nxp[0];
 #pragma unroll
         for (int q = 1; q < PW; ++q) word = v >= q * PE ? nxp[q] : word;
@@ -158,6 +198,40 @@ __device__ __forceinline__ uint64_t lane_gift_wrap(const double (&xs)[K], const 
         mask |= 1ull << (v - 1);
     }
     return mask;
+}
+
+// The lane's hull: the mask of its vertices (bit j for point j+1).  All
+// K(K+1)/2 pairs are compared with compile-time indices: no divergence and no
+// indexed access to the lane's registers.
+template <int K>
+__device__ __forceinline__ uint64_t lane_gift_wrap(const double (&xs)[K], const double (&ys)[K], int cnt) {
+    uint64_t nxp[3] = {0ull, 0ull, 0ull};
+    gw_ptrs<K, 0, K, K>(xs, ys, cnt, nxp);
+    return gw_walk<K>(nxp, 0, K, cnt);
+}
+
+// The hulls of the lane's two halves (points 0..H and H..K, H = K/2), about
+// half the comparisons: their vertices include every vertex of the lane's
+// hull (subset lemma), so they serve as candidates where a superset will do.
+// nxp keeps the pointers for gw_whole.
+template <int K>
+__device__ __forceinline__ uint64_t gw_halves(const double (&xs)[K], const double (&ys)[K], int cnt,
+                                              uint64_t (&nxp)[3]) {
+    constexpr int H = K / 2;
+    nxp[0] = nxp[1] = nxp[2] = 0ull;
+    gw_ptrs<K, 0, H, H>(xs, ys, cnt, nxp);
+    gw_ptrs<K, H, K, K>(xs, ys, cnt, nxp);
+    return gw_walk<K>(nxp, 0, H, cnt) | gw_walk<K>(nxp, H, K, cnt);
+}
+
+// The lane's exact hull after gw_halves: the second half's pointers already
+// see every later point; the first half's are recomputed over all of them.
+template <int K>
+__device__ __forceinline__ uint64_t gw_whole(const double (&xs)[K], const double (&ys)[K], int cnt,
+                                             uint64_t (&nxp)[3]) {
+    constexpr int H = K / 2;
+    gw_ptrs<K, 0, H, K>(xs, ys, cnt, nxp);
+    return gw_walk<K>(nxp, 0, K, cnt);
 }
 
 // ---------------------------------------------------------------------------
@@ -214,10 +288,12 @@ __device__ __forceinline__ void lane_load_staged(const T* __restrict__ base, int
 // the hull is the chain of these pointers from point 0.  All K(K+1)/2 pairs
 // are compared with compile-time indices: no divergence and no indexed access
 // to the lane's registers.
+// With nxp, the hulls of the lane's two halves (gw_halves) instead, to be
+// completed by gw_whole where the exact hull is needed.
 template <typename T, int K>
 __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restrict__ w, int cnt, int negate,
                                      double (&xs)[K], double (&ys)[K], int& f, T* stage = nullptr,
-                                     int avail = 0) {
+                                     int avail = 0, uint64_t (*nxp)[3] = nullptr) {
     static_assert(K <= 32, "next-vertex offsets are packed in at most three words");
     double X = 0.0, Y = 0.0;
     auto take = [&](int j, double yi, double wi) {
@@ -281,6 +357,7 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
             take(j, yi, wi);
         }
     }
+    if (nxp) return gw_halves<K>(xs, ys, cnt, *nxp);
     return lane_gift_wrap<K>(xs, ys, cnt);
 }
 
@@ -342,10 +419,28 @@ __device__ inline int tile_lane_starts(const Tile& t, double2 total, int f, int 
         nvert += t.W[k];
     }
     const double4 ex = wave_shift_up1(v);
-    t.LS[threadIdx.x] = add4(DD, acc, ex);
-    if (threadIdx.x == 0) t.LS[t.nl] = all;
+    const double4 st = add4(DD, acc, ex);
+    if (!DD && t.ls2) {
+        ((double2*)t.LS)[threadIdx.x] = make_double2(st.x, st.z);
+        if (threadIdx.x == 0) ((double2*)t.LS)[t.nl] = make_double2(all.x, all.z);
+    } else {
+        t.LS[threadIdx.x] = st;
+        if (threadIdx.x == 0) t.LS[t.nl] = all;
+    }
     __syncthreads();
     return nvert;
+}
+
+// Vertices of the tile's lane masks, point 0 included (block scope; ends
+// with a barrier).
+__device__ inline int tile_count(const Tile& t, uint64_t mask) {
+    const int lane = lane_id(), wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int incl = wave_incl_scan_int(__popcll(mask));
+    if (lane == kWave - 1) t.W[24 + wid] = incl;
+    __syncthreads();
+    int tot = 1;
+    for (int k = 0; k < nw; ++k) tot += t.W[24 + k];
+    return tot;
 }
 
 // ---------------------------------------------------------------------------
@@ -385,9 +480,15 @@ __device__ inline void tile_compact(const Tile& t, uint64_t mask, const double (
     t.I[l] = r;
     double sx = 0.0, sy = 0.0;
     if (ABS) {
-        const double4 s = t.LS[l];
-        sx = s.x;
-        sy = s.z;
+        if (t.ls2) {
+            const double2 s = ((const double2*)t.LS)[l];
+            sx = s.x;
+            sy = s.y;
+        } else {
+            const double4 s = t.LS[l];
+            sx = s.x;
+            sy = s.z;
+        }
     }
 #pragma unroll
     for (int b = 0; b < K; ++b) {
@@ -556,6 +657,307 @@ __device__ inline int group_merge(const Tile& t, int a0, int a1, int b0, int b1,
     return al + 1 + (b1 - be);
 }
 
+template <int K>
+__device__ inline void tile_masks(const Tile& t, uint64_t& mask);
+
+// ---------------------------------------------------------------------------
+// Output-sensitive finish.  Every vertex of the tile's hull is a vertex of
+// its lane's hull (the subset lemma of the first page, Sec. 3.1), so the hull
+// of the compacted list is the tile's hull, and from a hull vertex v the next
+// one is the entry after v of least slope from v (the farthest of equal
+// slopes, so collinear middle points are dropped): a gift wrap whose steps
+// are the hull's edges.  Noisy tiles end with a few dozen vertices out of
+// thousands of points, so a few steps replace the merge rounds; a wrap that
+// takes more than its cap of steps gives up and the rounds run instead on
+// the untouched list.
+// ---------------------------------------------------------------------------
+
+// One wrap by the calling wave over the candidates c0 .. c1 (list entries
+// cand(c)), from c0 (a hull vertex) to c1 (the last point, always a vertex).
+// Writes the candidates it steps to, c1 last, to out[0..) and returns their
+// number, or -1 after cap steps short of c1.  Each lane keeps the best of its
+// strided candidates by exact cross-multiplied comparison; the wave's least
+// slope then picks the winner, and the few lanes whose slopes lie within
+// rounding of it are compared exactly (ties to the farthest).
+template <int K, bool ABS, class Cand>
+__device__ inline int wave_wrap(const Tile& t, int c0, int c1, Cand cand, int* out, int cap) {
+    const int lane = lane_id();
+    int v = c0, n = 0;
+    while (v < c1) {
+        if (n == cap) return -1;
+        const int ev = cand(v);
+        double bx = 1.0, by = 0.0;
+        int bc = -1;
+        for (int c = v + 1 + lane; c <= c1; c += kWave) {
+            const double2 d = vdiff<K, ABS>(t, ev, cand(c));
+            // candidates come in increasing order: on equal slopes the later one
+            if (bc < 0 || d.y * bx <= by * d.x) {
+                bx = d.x;
+                by = d.y;
+                bc = c;
+            }
+        }
+        const double sl = (bc < 0) ? INFINITY : by / bx;
+        const double m = wave_min(sl);
+        const uint64_t con = __ballot(bc >= 0 && sl <= m + fabs(m) * 2e-15);
+        int wl = lo_bit(con);
+        if (con & (con - 1)) {
+            double wx = readlane_d(bx, wl), wy = readlane_d(by, wl);
+            int wc = __builtin_amdgcn_readlane(bc, wl);
+            for (uint64_t rest = con & (con - 1); rest; rest &= rest - 1) {
+                const int q = lo_bit(rest);
+                const double qx = readlane_d(bx, q), qy = readlane_d(by, q);
+                const int qc = __builtin_amdgcn_readlane(bc, q);
+                const double lhs = qy * wx, rhs = wy * qx;
+                if (lhs < rhs || (lhs == rhs && qc > wc)) {
+                    wx = qx;
+                    wy = qy;
+                    wc = qc;
+                }
+            }
+            v = wc;
+        } else {
+            v = __builtin_amdgcn_readlane(bc, wl);
+        }
+        if (lane == 0) out[n] = v;
+        ++n;
+    }
+    return n;
+}
+
+// The same wrap with the candidates held in registers, Q per lane (lane l
+// holds c0 + 1 + l + 64q), for tiles with absolute coordinates and at most
+// 64 Q candidates: a step then reads no LDS.  Each lane's best is found by
+// exact comparisons; across lanes a float32 image of the slopes picks the
+// winner, and the lanes whose images lie within its rounding are compared
+// exactly.  The next origin is the old one plus the winner's difference
+// (within a few ulp of the vertex: enough to pick the next one, whose
+// coordinates the list keeps exactly).
+template <int K, int Q, class Cand>
+__device__ inline int wave_wrap_regs(const Tile& t, int c0, int c1, Cand cand, int* out, int cap) {
+    const int lane = lane_id();
+    double X[Q], Y[Q];
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+        const int c = c0 + 1 + lane + kWave * q;
+        const double2 p = (c <= c1) ? t.VXY[cand(c)] : make_double2(0.0, 0.0);
+        X[q] = p.x;
+        Y[q] = p.y;
+    }
+    const double2 p0 = t.VXY[cand(c0)];
+    double xv = p0.x, yv = p0.y;
+    int v = c0, n = 0;
+    while (v < c1) {
+        if (n == cap) return -1;
+        double bx = 1.0, by = 0.0;
+        int bq = -1;
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            if (c0 + kWave * (q + 1) > v) {  // uniform: the slot holds candidates after v
+                const int c = c0 + 1 + lane + kWave * q;
+                const double dx = X[q] - xv, dy = Y[q] - yv;
+                // later slots hold later candidates: on equal slopes the later one
+                const bool take = c > v && c <= c1 && (bq < 0 || dy * bx <= by * dx);
+                bx = take ? dx : bx;
+                by = take ? dy : by;
+                bq = take ? q : bq;
+            }
+        }
+        const int bc = (bq < 0) ? -1 : c0 + 1 + lane + kWave * bq;
+        const float sl = (bq < 0) ? INFINITY : (float)(by * __builtin_amdgcn_rcp(bx));
+        const float m = wave_min_f(sl);
+        uint64_t con = __ballot(bq >= 0 && sl <= m + fabsf(m) * 0x1p-16f + 0x1p-100f);
+        if (!con) con = __ballot(bq >= 0);  // slopes beyond float32's range: compare them all exactly
+        int wl = lo_bit(con);
+        if (con & (con - 1)) {
+            double wx = readlane_d(bx, wl), wy = readlane_d(by, wl);
+            int wc = __builtin_amdgcn_readlane(bc, wl);
+            for (uint64_t rest = con & (con - 1); rest; rest &= rest - 1) {
+                const int q = lo_bit(rest);
+                const double qx = readlane_d(bx, q), qy = readlane_d(by, q);
+                const int qc = __builtin_amdgcn_readlane(bc, q);
+                const double lhs = qy * wx, rhs = wy * qx;
+                if (lhs < rhs || (lhs == rhs && qc > wc)) {
+                    wx = qx;
+                    wy = qy;
+                    wc = qc;
+                    wl = q;
+                }
+            }
+        }
+        v = __builtin_amdgcn_readlane(bc, wl);
+        xv += readlane_d(bx, wl);
+        yv += readlane_d(by, wl);
+        if (lane == 0) out[n] = v;
+        ++n;
+    }
+    return n;
+}
+
+template <int K, bool ABS, class Cand>
+__device__ inline int wave_wrap_any(const Tile& t, int c0, int c1, Cand cand, int* out, int cap) {
+    if constexpr (ABS) {
+        if (c1 - c0 <= kWave * 2) return wave_wrap_regs<K, 2>(t, c0, c1, cand, out, cap);
+        if (c1 - c0 <= kWave * 4) return wave_wrap_regs<K, 4>(t, c0, c1, cand, out, cap);
+        if (c1 - c0 <= kWave * 6) return wave_wrap_regs<K, 6>(t, c0, c1, cand, out, cap);
+        if (c1 - c0 <= kWave * 8) return wave_wrap_regs<K, 8>(t, c0, c1, cand, out, cap);
+    }
+    return wave_wrap<K, ABS>(t, c0, c1, cand, out, cap);
+}
+
+// The hull of a few candidates C[0..nc) (list entries in increasing order),
+// all at once: a middle candidate p is a vertex iff the steepest slope into
+// it from an earlier candidate is strictly less than the least slope out of
+// it to a later one (both found by cross-multiplied comparisons over every
+// other candidate); the first and last are always vertices.
+// The same test by the whole workgroup, L consecutive lanes per candidate
+// (each over every L-th other candidate, then combined across the L lanes), for
+// nc <= blockDim.x / L.  Returns the number of vertices after the first (the
+// same in every thread); their entries go to out[0..).  Ends with a barrier.
+template <int K, bool ABS, int L>
+__device__ inline int tile_hull_small(const Tile& t, const int* C, int nc, int* out) {
+    const int tid = threadIdx.x, p = tid / L, part = tid % L, lane = lane_id(), wid = tid >> 6;
+    const int nw = blockDim.x >> 6;
+    const int ep = C[min(p, nc - 1)];
+    const double2 P = t.VXY[ep];
+    double lx = 1.0, ly = -INFINITY, rx = 1.0, ry = INFINITY;
+#pragma unroll 4
+    for (int q = part; q < nc; q += L) {
+        double2 d;  // P_p - P_q
+        if constexpr (ABS) {
+            d = sub2(P, t.VXY[C[q]]);
+        } else {
+            d = vdiff<K, ABS>(t, C[q], ep);
+        }
+        if (q > p) d = make_double2(-d.x, -d.y);
+        if (q < p && d.y * lx >= ly * d.x) {
+            lx = d.x;
+            ly = d.y;
+        }
+        if (q > p && d.y * rx <= ry * d.x) {
+            rx = d.x;
+            ry = d.y;
+        }
+    }
+#pragma unroll
+    for (int o = 1; o < L; o <<= 1) {
+        const double ox = __shfl_xor(lx, o), oy = __shfl_xor(ly, o);
+        const double qx = __shfl_xor(rx, o), qy = __shfl_xor(ry, o);
+        if (oy * lx > ly * ox) {
+            lx = ox;
+            ly = oy;
+        }
+        if (qy * rx < ry * qx) {
+            rx = qx;
+            ry = qy;
+        }
+    }
+    const bool vert = part == 0 && p < nc && (p == 0 || p == nc - 1 || ly * rx < ry * lx);
+    const uint64_t b = __ballot(vert);
+    if (lane == 0) t.W[24 + wid] = __popcll(b);
+    __syncthreads();
+    int before = 0, total = 0;
+    for (int k = 0; k < nw; ++k) {
+        const int c = t.W[24 + k];
+        before += (k < wid) ? c : 0;
+        total += c;
+    }
+    const int rank = before + __popcll(b & bits_upto(lane - 1));
+    if (vert && p > 0) out[rank - 1] = ep;
+    __syncthreads();
+    return total - 1;
+}
+
+// After tile_compact: the tile's hull by wrapping, waves first (each over its
+// lanes' node, no barriers), then one wave over the waves' hull vertices.  On
+// success the list holds exactly the hull, flag[1] = its length, and true is
+// returned (uniformly); otherwise the list is unchanged.  Ends with a barrier.
+template <int K, bool ABS>
+__device__ inline bool tile_wrap(const Tile& t) {
+    const int used = (t.N + K - 1) / K;
+    const int lane = lane_id(), wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    const int nwu = (used + kWave - 1) / kWave;
+    const int nv = t.flag[1];
+    int* Rw = t.R + wid * kWrapWave;
+    if (wid < nwu) {
+        const int w0 = wid * kWave;
+        const int s = t.I[w0] - 1;
+        const int e = (w0 + kWave < used) ? t.I[w0 + kWave] - 1 : nv - 1;
+        const int h = wave_wrap_any<K, ABS>(t, s, e, [](int c) { return c; }, Rw, kWrapWave);
+        if (lane == 0) t.W[wid] = h;
+    }
+    __syncthreads();
+    int* C = t.R + nw * kWrapWave;  // nw > 1 only
+    int* F = C + 4 + nw * kWrapWave;
+    int nf = -1;  // hull entries after point 0, in F (or in wave 0's results)
+    const int* fin = Rw;
+    bool ok = true;
+    for (int q = 0; q < nwu; ++q) ok = ok && t.W[q] >= 0;
+    if (ok && nwu == 1) {
+        nf = t.W[0];
+        fin = t.R;
+    } else if (ok) {
+        // the candidates: point 0, then every wave's vertices in order (a
+        // wave's last vertex is the next wave's first point)
+        int base = 1;
+        for (int q = 0; q < nwu; ++q) base += t.W[q];
+        if (wid == 0) {
+            int b = 1;
+            for (int q = 0; q < nwu; ++q) {
+                const int h = t.W[q];
+                for (int k = lane; k < h; k += kWave) C[b + k] = t.R[q * kWrapWave + k];
+                b += h;
+            }
+            if (lane == 0) C[0] = 0;
+        }
+        __syncthreads();
+        if (base * 4 <= (int)blockDim.x && base <= kWrapTile + 1) {
+            nf = tile_hull_small<K, ABS, 4>(t, C, base, F);
+        } else if (base * 2 <= (int)blockDim.x && base <= kWrapTile + 1) {
+            nf = tile_hull_small<K, ABS, 2>(t, C, base, F);
+        } else {
+            if (wid == 0) {
+                const int h = wave_wrap_any<K, ABS>(t, 0, base - 1, [C](int c) { return C[c]; }, F, kWrapTile);
+                wave_sync();
+                for (int k = lane; k < h; k += kWave) F[k] = C[F[k]];
+                if (lane == 0) t.W[16] = h;
+            }
+            __syncthreads();
+            nf = t.W[16];
+        }
+        fin = F;
+    }
+    if (nf < 0) {  // uniform: the rounds take over
+        __syncthreads();
+        return false;
+    }
+    // the hull's entries to the front of the list (entries only move down)
+    if (wid == 0) {
+        unsigned short pv[(kWrapTile + kWave) / kWave];
+        double2 xy[(kWrapTile + kWave) / kWave];
+#pragma unroll
+        for (int b = 0; b < (kWrapTile + kWave) / kWave; ++b) {
+            const int k = b * kWave + lane;
+            if (k < nf) {
+                pv[b] = t.V[fin[k]];
+                xy[b] = t.VXY[fin[k]];
+            }
+        }
+        wave_sync();
+#pragma unroll
+        for (int b = 0; b < (kWrapTile + kWave) / kWave; ++b) {
+            const int k = b * kWave + lane;
+            if (k < nf) {
+                t.V[k + 1] = pv[b];
+                t.VXY[k + 1] = xy[b];
+            }
+        }
+        if (lane == 0) t.flag[1] = nf + 1;
+    }
+    __syncthreads();
+    return true;
+}
+
 // Steps 3a-3d: merges of the lane hulls into the tile's hull.
 //   3a. one block-wide compaction writes the list of every lane hull's
 //       vertices in order (the lane's points xs, ys are not needed after it);
@@ -567,12 +969,19 @@ __device__ inline int group_merge(const Tile& t, int a0, int a1, int b0, int b1,
 //   3d. the final lane masks are rebuilt from the list, and I[l] = index of
 //       lane l's first vertex.
 // On return the sorted vertex list of the whole tile is V, VXY [0, flag[1]).
+// With wrap, the output-sensitive finish (tile_wrap) is tried first when the
+// lane hulls kept at most 3/5 of the points.
 template <int K, bool ABS>
-__device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (&xs)[K], const double (&ys)[K]) {
+__device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (&xs)[K], const double (&ys)[K],
+                                   bool wrap = false) {
     const int used = (t.N + K - 1) / K;
     const int l = threadIdx.x, lane = lane_id(), wid = l >> 6, nw = blockDim.x >> 6;
     const int nwu = (used + kWave - 1) / kWave;  // waves holding elements
     tile_compact<K, ABS>(t, mask, xs, ys);
+    if (wrap && 5 * t.flag[1] <= 3 * t.N + 5 && tile_wrap<K, ABS>(t)) {
+        tile_masks<K>(t, mask);
+        return;
+    }
     const int w0 = wid * kWave, wend = min(w0 + kWave, used);
     int ns = t.I[l] - 1;
     int ne = (l + 1 < used) ? t.I[l + 1] - 1 : t.flag[1] - 1;
@@ -612,6 +1021,15 @@ __device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (
         __syncthreads();
     }
     if (l == 0) t.flag[1] = t.W[8] + 1;  // wave 0's node starts at entry 0 (point 0)
+    tile_masks<K>(t, mask);
+    (void)nw;
+}
+
+// Step 3d: the final lane masks from the list V[0, flag[1]), and I[l] = index
+// of lane l's first vertex.  flag[1] is read after the first barrier.
+template <int K>
+__device__ inline void tile_masks(const Tile& t, uint64_t& mask) {
+    const int l = threadIdx.x, lane = lane_id(), wid = l >> 6;
     t.M[l] = 0ull;
     __syncthreads();
     const int nv = t.flag[1];
@@ -631,7 +1049,6 @@ __device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (
     int r = 1;
     for (int q = 0; q < wid; ++q) r += t.W[16 + q];
     t.I[l] = r + incl - pc;
-    (void)nw;
 }
 
 // ---------------------------------------------------------------------------
