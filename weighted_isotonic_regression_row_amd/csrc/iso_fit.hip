@@ -100,10 +100,10 @@ template <typename T, int K>
 __device__ inline void tile_finish(const Tile& t, uint64_t mask, int increasing, double lo, double hi, T* out,
                                    uint64_t* sb, uint64_t* cb) {
     constexpr bool ABS = sizeof(T) == 4;
-    tile_edge_slopes<K, ABS>(t);
+    tile_edge_slopes<K, ABS>(t, increasing, lo, hi);
     double vals[K];
     uint64_t clipm;
-    tile_expand<K>(t, mask, increasing, lo, hi, vals, clipm);
+    tile_expand<K>(t, mask, vals, clipm);
     const int l = threadIdx.x;
     const int cnt = min(max(t.N - l * K, 0), K);
     store_lane<T, K>(out + (int64_t)l * K, cnt, vals);

@@ -172,10 +172,10 @@ __global__ __launch_bounds__(64) void k_rank_fused(FusedArgs a) {
         return;
     }
     tile_merges<E, ABS>(tl, mask, xs, ys);
-    tile_edge_slopes<E, ABS>(tl);
+    tile_edge_slopes<E, ABS>(tl, 0, -INFINITY, INFINITY);
     double vals[E];
     uint64_t clipm;
-    tile_expand<E>(tl, mask, 0, -INFINITY, INFINITY, vals, clipm);
+    tile_expand<E>(tl, mask, vals, clipm);
 #pragma unroll
     for (int e = 0; e < E; ++e)
         if (e < cnt && (unsigned)idx[e] < (unsigned)n) r[idx[e]] = (T)(sv[e] - vals[e]);

@@ -296,8 +296,23 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
                                      int avail = 0, uint64_t (*nxp)[3] = nullptr) {
     static_assert(K <= 32, "next-vertex offsets are packed in at most three words");
     double X = 0.0, Y = 0.0;
+    // float32 inputs take no branches: a product of two floats is exact in
+    // float64, so the fused multiply-add rounds as the sum of the product
+    // does; a non-finite input leaves a lane total non-finite (infinities and
+    // NaN absorb finite terms, opposite infinities give NaN) while finite
+    // inputs cannot overflow, so the totals are checked once at the end; the
+    // least weight finds a weight <= 0.
+    constexpr bool F32 = sizeof(T) == 4;
+    const double sg = negate ? -1.0 : 1.0;
+    float wmin = INFINITY;
     auto take = [&](int j, double yi, double wi) {
-        if (j < cnt) {
+        if constexpr (F32) {
+            const bool in = j < cnt;
+            wi = in ? wi : 0.0;
+            X += wi;
+            Y = fma(wi * sg, in ? yi : 0.0, Y);
+            wmin = fminf(wmin, in ? (float)wi : 1.f);
+        } else if (j < cnt) {
             if (!isfinite(yi) || !isfinite(wi))
                 f |= 1;
             else if (!(wi > 0.0))
@@ -309,6 +324,12 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
         }
         xs[j] = X;
         ys[j] = Y;
+    };
+    auto checks = [&]() {
+        if constexpr (F32) {
+            if (!isfinite(X) || !isfinite(Y)) f |= 1;
+            if (!(wmin > 0.f)) f |= 2;
+        }
     };
     constexpr int VW = 16 / (int)sizeof(T);
     bool done = false;
@@ -357,6 +378,7 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
             take(j, yi, wi);
         }
     }
+    checks();
     if (nxp) return gw_halves<K>(xs, ys, cnt, *nxp);
     return lane_gift_wrap<K>(xs, ys, cnt);
 }
@@ -1052,39 +1074,41 @@ __device__ inline void tile_masks(const Tile& t, uint64_t& mask) {
 }
 
 // ---------------------------------------------------------------------------
-// 4. expand (Sec. 3.4).  First the slope of every edge of the tile's hull is
-// written over the list (VXY[i].x = slope of the edge from entry i to i+1);
-// then every element takes the slope of the edge that starts at the last
-// vertex at or before its left point: for element lK + j that is list entry
-// I[l] - 1 + (number of lane l's vertices among its local points 1..j).
+// 4. expand (Sec. 3.4).  First every edge of the tile's hull gets its value,
+// written over the list: VXY[i] = (the slope of the edge from entry i to
+// i+1, oriented and clipped; 1 where clipping changed it, else 0).  Then
+// every element takes the value of the edge that starts at the last vertex at
+// or before its left point: for element lK + j that is list entry I[l] - 1 +
+// (number of lane l's vertices among its local points 1..j).
 // ---------------------------------------------------------------------------
 template <int K, bool ABS>
-__device__ inline void tile_edge_slopes(const Tile& t) {
+__device__ inline void tile_edge_slopes(const Tile& t, int increasing, double clo, double chi) {
     const int nv = t.flag[1];
     double sv[K + 1];
+    bool cv[K + 1];
 #pragma unroll
     for (int k = 0; k <= K; ++k) {
         const int i = threadIdx.x + k * t.nl;
         sv[k] = 0.0;
-        if (i < nv - 1) {
+        cv[k] = false;
+        if (k * t.nl < nv - 1 && i < nv - 1) {  // the first test is uniform
             const double2 d = vdiff<K, ABS>(t, i, i + 1);
-            sv[k] = d.y / d.x;
+            sv[k] = finish(d.y / d.x, increasing, clo, chi, cv[k]);
         }
     }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k <= K; ++k) {
         const int i = threadIdx.x + k * t.nl;
-        if (i < nv - 1) t.VXY[i].x = sv[k];
+        if (k * t.nl < nv - 1 && i < nv - 1) t.VXY[i] = make_double2(sv[k], cv[k] ? 1.0 : 0.0);
     }
     __syncthreads();
 }
 
-// Slopes of the calling lane's elements, oriented and clipped, into
-// vals[0..cnt); clip flags into clipm (bit j <-> element lK + j).
+// Values of the calling lane's elements into vals[0..cnt); clip flags into
+// clipm (bit j <-> element lK + j).
 template <int K>
-__device__ inline void tile_expand(const Tile& t, uint64_t mask, int increasing, double clo, double chi,
-                                   double (&vals)[K], uint64_t& clipm) {
+__device__ inline void tile_expand(const Tile& t, uint64_t mask, double (&vals)[K], uint64_t& clipm) {
     const int l = threadIdx.x;
     const int cnt = min(max(t.N - l * K, 0), K);
     const int i0 = t.I[l] - 1;
@@ -1093,10 +1117,9 @@ __device__ inline void tile_expand(const Tile& t, uint64_t mask, int increasing,
     for (int j = 0; j < K; ++j) {
         vals[j] = 0.0;
         if (j < cnt) {
-            const double sl = t.VXY[i0 + __popcll(mask & bits_upto(j - 1))].x;
-            bool c;
-            vals[j] = finish(sl, increasing, clo, chi, c);
-            if (c) clipm |= 1ull << j;
+            const double2 e = t.VXY[i0 + __popcll(mask & bits_upto(j - 1))];
+            vals[j] = e.x;
+            if (e.y != 0.0) clipm |= 1ull << j;
         }
     }
 }
