@@ -71,8 +71,8 @@ __device__ inline void wg_write_nan(int64_t N, T* out, uint64_t* sbits, uint64_t
 // weight); nvert = the number of lane-hull vertices.  The lane's points stay
 // in xs, ys.
 // With stage set, the inputs pass through the still unused vertex list (each
-// wave K * 64 elements of it).  With nxp, the masks are those of the lanes'
-// half hulls (a superset of the lane hulls' vertices, gw_halves).
+// wave K * 64 elements of it).  With nxp, the masks are those of the hulls of
+// the lanes' parts (a superset of the lane hulls' vertices, gw_parts).
 template <typename T, int K>
 __device__ inline int tile_build(const Tile& t, const T* y, const T* w, int increasing, uint64_t& mask,
                                  double (&xs)[K], double (&ys)[K], int& nvert, bool stage = false,
@@ -171,11 +171,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     constexpr bool ABS = sizeof(T) == 4;
     bool over = false;
     if constexpr (HALVES) {
-        // Noisy rows: the half hulls' vertices are few, and wrapping them
-        // gives the row's hull directly.  Other rows, and rows whose wrap
+        // Noisy rows: the parts' hull vertices below the chord are few, and
+        // wrapping them gives the row's hull directly.  Other rows, and rows whose wrap
         // gives up, take the exact path.  The list holds point 0 and cap
         // vertices; every condition here is uniform.
         bool done = false;
+        if constexpr (ABS) {
+            mask = chord_filter<K>(t, mask, xs, ys);
+            nvert = tile_count(t, mask);
+        }
         if (5 * nvert <= 3 * N + 5 && nvert <= a.cap + 1) {
             tile_compact<K, ABS>(t, mask, xs, ys);
             if (tile_wrap<K, ABS>(t)) {

@@ -210,28 +210,33 @@ __device__ __forceinline__ uint64_t lane_gift_wrap(const double (&xs)[K], const 
     return gw_walk<K>(nxp, 0, K, cnt);
 }
 
-// The hulls of the lane's two halves (points 0..H and H..K, H = K/2), about
-// half the comparisons: their vertices include every vertex of the lane's
-// hull (subset lemma), so they serve as candidates where a superset will do.
-// nxp keeps the pointers for gw_whole.
-template <int K>
-__device__ __forceinline__ uint64_t gw_halves(const double (&xs)[K], const double (&ys)[K], int cnt,
-                                              uint64_t (&nxp)[3]) {
-    constexpr int H = K / 2;
-    nxp[0] = nxp[1] = nxp[2] = 0ull;
-    gw_ptrs<K, 0, H, H>(xs, ys, cnt, nxp);
-    gw_ptrs<K, H, K, K>(xs, ys, cnt, nxp);
-    return gw_walk<K>(nxp, 0, H, cnt) | gw_walk<K>(nxp, H, K, cnt);
-}
-
-// The lane's exact hull after gw_halves: the second half's pointers already
-// see every later point; the first half's are recomputed over all of them.
-template <int K>
-__device__ __forceinline__ uint64_t gw_whole(const double (&xs)[K], const double (&ys)[K], int cnt,
+// The hulls of P consecutive parts of the lane (points 0..K/P, K/P..2K/P, ...),
+// a P-th of the comparisons or less: their vertices include every vertex of
+// the lane's hull (subset lemma), so they serve as candidates where a superset
+// will do.  nxp keeps the pointers.
+template <int K, int P>
+__device__ __forceinline__ uint64_t gw_parts(const double (&xs)[K], const double (&ys)[K], int cnt,
                                              uint64_t (&nxp)[3]) {
-    constexpr int H = K / 2;
-    gw_ptrs<K, 0, H, K>(xs, ys, cnt, nxp);
-    return gw_walk<K>(nxp, 0, K, cnt);
+    static_assert(K % P == 0, "equal parts");
+    constexpr int S = K / P;
+    nxp[0] = nxp[1] = nxp[2] = 0ull;
+    uint64_t m = 0ull;
+    gw_ptrs<K, 0, S, S>(xs, ys, cnt, nxp);
+    m |= gw_walk<K>(nxp, 0, S, cnt);
+    if constexpr (P > 1) {
+        gw_ptrs<K, S, 2 * S, 2 * S>(xs, ys, cnt, nxp);
+        m |= gw_walk<K>(nxp, S, 2 * S, cnt);
+    }
+    if constexpr (P > 2) {
+        gw_ptrs<K, 2 * S, 3 * S, 3 * S>(xs, ys, cnt, nxp);
+        m |= gw_walk<K>(nxp, 2 * S, 3 * S, cnt);
+    }
+    if constexpr (P > 3) {
+        gw_ptrs<K, 3 * S, 4 * S, 4 * S>(xs, ys, cnt, nxp);
+        m |= gw_walk<K>(nxp, 3 * S, 4 * S, cnt);
+    }
+    static_assert(P <= 4, "at most four parts");
+    return m;
 }
 
 // ---------------------------------------------------------------------------
@@ -288,8 +293,8 @@ __device__ __forceinline__ void lane_load_staged(const T* __restrict__ base, int
 // the hull is the chain of these pointers from point 0.  All K(K+1)/2 pairs
 // are compared with compile-time indices: no divergence and no indexed access
 // to the lane's registers.
-// With nxp, the hulls of the lane's two halves (gw_halves) instead, to be
-// completed by gw_whole where the exact hull is needed.
+// With nxp, the hulls of the lane's two halves instead: a superset of the
+// lane hull's vertices (gw_parts).
 template <typename T, int K>
 __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restrict__ w, int cnt, int negate,
                                      double (&xs)[K], double (&ys)[K], int& f, T* stage = nullptr,
@@ -379,7 +384,7 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
         }
     }
     checks();
-    if (nxp) return gw_halves<K>(xs, ys, cnt, *nxp);
+    if (nxp) return gw_parts<K, 2>(xs, ys, cnt, *nxp);
     return lane_gift_wrap<K>(xs, ys, cnt);
 }
 
@@ -451,6 +456,25 @@ __device__ inline int tile_lane_starts(const Tile& t, double2 total, int f, int 
     }
     __syncthreads();
     return nvert;
+}
+
+// Drops from the lane's mask the points that lie above the chord from the
+// tile's first point to its last by more than rounding: the lower hull lies
+// on or below that chord (its ends are hull vertices and the hull is convex),
+// so no such point is a vertex.  Absolute coordinates (float32 tiles, lane
+// starts as plain pairs); needs the lane starts written.
+template <int K>
+__device__ inline uint64_t chord_filter(const Tile& t, uint64_t mask, const double (&xs)[K], const double (&ys)[K]) {
+    const double2 tot = ((const double2*)t.LS)[t.nl], st = ((const double2*)t.LS)[threadIdx.x];
+    uint64_t keep = 0ull;
+#pragma unroll
+    for (int b = 0; b < K; ++b) {
+        const double X = st.x + xs[b], Y = st.y + ys[b];
+        const double a1 = Y * tot.x, a2 = tot.y * X;
+        const bool in = a1 - a2 <= (fabs(a1) + fabs(a2)) * 1e-14;
+        keep |= (in ? 1ull : 0ull) << b;
+    }
+    return mask & keep;
 }
 
 // Vertices of the tile's lane masks, point 0 included (block scope; ends
@@ -833,24 +857,24 @@ __device__ inline int wave_wrap_any(const Tile& t, int c0, int c1, Cand cand, in
 // it to a later one (both found by cross-multiplied comparisons over every
 // other candidate); the first and last are always vertices.
 // The same test by the whole workgroup, L consecutive lanes per candidate
-// (each over every L-th other candidate, then combined across the L lanes), for
-// nc <= blockDim.x / L.  Returns the number of vertices after the first (the
-// same in every thread); their entries go to out[0..).  Ends with a barrier.
+// (each over every L-th other candidate, loaded four at a time, then combined
+// across the L lanes), for nc <= blockDim.x / L.  The vertices after the first
+// are written straight to the front of the list (entries 1..), their number
+// returned (the same in every thread) and stored in flag[1] with point 0.
+// With absolute coordinates CXY[q] holds candidate q's point (a copy made with
+// C).  The list is read before the first barrier and written after it; the
+// caller orders the writes before the next reads of the list.
 template <int K, bool ABS, int L>
-__device__ inline int tile_hull_small(const Tile& t, const int* C, int nc, int* out) {
+__device__ inline int tile_hull_small(const Tile& t, const int* C, const double2* CXY, int nc) {
     const int tid = threadIdx.x, p = tid / L, part = tid % L, lane = lane_id(), wid = tid >> 6;
     const int nw = blockDim.x >> 6;
-    const int ep = C[min(p, nc - 1)];
-    const double2 P = t.VXY[ep];
+    const int pc = min(p, nc - 1);
+    const int ep = C[pc];
+    const unsigned short pv = t.V[ep];
+    const double2 pxy = t.VXY[ep];
+    const double2 P = ABS ? CXY[pc] : pxy;
     double lx = 1.0, ly = -INFINITY, rx = 1.0, ry = INFINITY;
-#pragma unroll 4
-    for (int q = part; q < nc; q += L) {
-        double2 d;  // P_p - P_q
-        if constexpr (ABS) {
-            d = sub2(P, t.VXY[C[q]]);
-        } else {
-            d = vdiff<K, ABS>(t, C[q], ep);
-        }
+    auto cmp = [&](int q, double2 d) {  // d = P_p - P_q
         if (q > p) d = make_double2(-d.x, -d.y);
         if (q < p && d.y * lx >= ly * d.x) {
             lx = d.x;
@@ -860,6 +884,21 @@ __device__ inline int tile_hull_small(const Tile& t, const int* C, int nc, int* 
             rx = d.x;
             ry = d.y;
         }
+    };
+    for (int q0 = part; q0 < nc; q0 += 4 * L) {
+        double2 d[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int q = min(q0 + u * L, nc - 1);
+            if constexpr (ABS) {
+                d[u] = sub2(P, CXY[q]);
+            } else {
+                d[u] = vdiff<K, ABS>(t, C[q], ep);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            if (q0 + u * L < nc) cmp(q0 + u * L, d[u]);
     }
 #pragma unroll
     for (int o = 1; o < L; o <<= 1) {
@@ -885,8 +924,11 @@ __device__ inline int tile_hull_small(const Tile& t, const int* C, int nc, int* 
         total += c;
     }
     const int rank = before + __popcll(b & bits_upto(lane - 1));
-    if (vert && p > 0) out[rank - 1] = ep;
-    __syncthreads();
+    if (vert && p > 0) {
+        t.V[rank] = pv;
+        t.VXY[rank] = pxy;
+    }
+    if (tid == 0) t.flag[1] = total;
     return total - 1;
 }
 
@@ -921,32 +963,44 @@ __device__ inline bool tile_wrap(const Tile& t) {
     } else if (ok) {
         // the candidates: point 0, then every wave's vertices in order (a
         // wave's last vertex is the next wave's first point)
-        int base = 1;
-        for (int q = 0; q < nwu; ++q) base += t.W[q];
-        if (wid == 0) {
-            int b = 1;
-            for (int q = 0; q < nwu; ++q) {
-                const int h = t.W[q];
-                for (int k = lane; k < h; k += kWave) C[b + k] = t.R[q * kWrapWave + k];
-                b += h;
+        int base = 1, off = 1;
+        for (int q = 0; q < nwu; ++q) {
+            off += (q < wid) ? t.W[q] : 0;
+            base += t.W[q];
+        }
+        const bool small = base * 2 <= (int)blockDim.x && base <= kWrapTile + 1;  // uniform
+        double2* CXY = (double2*)t.M;  // free until the final masks; holds nl / 2 points
+        // every wave copies its own vertices to their place among the candidates
+        if (wid < nwu) {
+            const int h = t.W[wid];
+            for (int k = lane; k < h; k += kWave) {
+                const int e = Rw[k];
+                C[off + k] = e;
+                if (ABS && small) CXY[off + k] = t.VXY[e];
             }
-            if (lane == 0) C[0] = 0;
+        }
+        if (threadIdx.x == 0) {
+            C[0] = 0;
+            if (ABS && small) CXY[0] = t.VXY[0];
         }
         __syncthreads();
-        if (base * 4 <= (int)blockDim.x && base <= kWrapTile + 1) {
-            nf = tile_hull_small<K, ABS, 4>(t, C, base, F);
-        } else if (base * 2 <= (int)blockDim.x && base <= kWrapTile + 1) {
-            nf = tile_hull_small<K, ABS, 2>(t, C, base, F);
-        } else {
-            if (wid == 0) {
-                const int h = wave_wrap_any<K, ABS>(t, 0, base - 1, [C](int c) { return C[c]; }, F, kWrapTile);
-                wave_sync();
-                for (int k = lane; k < h; k += kWave) F[k] = C[F[k]];
-                if (lane == 0) t.W[16] = h;
-            }
+        if (small) {
+            // the hull goes straight to the front of the list
+            if (base * 4 <= (int)blockDim.x)
+                (void)tile_hull_small<K, ABS, 4>(t, C, CXY, base);
+            else
+                (void)tile_hull_small<K, ABS, 2>(t, C, CXY, base);
             __syncthreads();
-            nf = t.W[16];
+            return true;
         }
+        if (wid == 0) {
+            const int h = wave_wrap_any<K, ABS>(t, 0, base - 1, [C](int c) { return C[c]; }, F, kWrapTile);
+            wave_sync();
+            for (int k = lane; k < h; k += kWave) F[k] = C[F[k]];
+            if (lane == 0) t.W[16] = h;
+        }
+        __syncthreads();
+        nf = t.W[16];
         fin = F;
     }
     if (nf < 0) {  // uniform: the rounds take over
