@@ -114,24 +114,33 @@ __device__ inline void tile_finish(const Tile& t, uint64_t mask, int increasing,
     }
 }
 
-// The row kernel's exact path: the lane hulls built again from the inputs and
-// merged in rounds.  Its own function (not inlined), so that its registers are
-// allocated apart from the wrap's.  Returns the lane's final vertex mask, or
-// ~0 (uniformly) when the lane hulls' vertices overflow the LDS list.
+// The row kernel's exact path, to the end of the row: the lane hulls built
+// again from the inputs, merged in rounds, the fit and bits stored.  Its own
+// function (not inlined), so that its registers are allocated apart from the
+// wrap's.  A row whose lane hulls' vertices overflow the LDS list keeps its
+// list in the row's area of the workspace.
 template <typename T, int K>
-__device__ __attribute__((noinline)) uint64_t row_exact(RowArgs a) {
+__device__ __attribute__((noinline)) void row_exact(RowArgs a) {
     extern __shared__ __align__(32) char smem[];
     const int64_t row = blockIdx.x;
-    const Tile t = tile_carve(smem, blockDim.x, a.cap, K, (int)a.n, sizeof(T) == 4);
+    Tile t = tile_carve(smem, blockDim.x, a.cap, K, (int)a.n, sizeof(T) == 4);
     const T* y = (const T*)a.y + row * a.n;
     const T* w = a.w ? (const T*)a.w + row * a.n : nullptr;
+    T* out = (T*)a.fit + row * a.n;
+    uint64_t* sb = a.start_bits ? a.start_bits + row * a.words : nullptr;
+    uint64_t* cb = a.clip_bits ? a.clip_bits + row * a.words : nullptr;
     uint64_t mask;
     double xs[K], ys[K];
     int nvert;
     (void)tile_build<T, K>(t, y, w, a.increasing, mask, xs, ys, nvert, a.stage != 0);  // inputs already checked
-    if (nvert > a.cap + 1) return ~0ull;
+    if (nvert > a.cap + 1) {  // uniform
+        char* o = a.ovf + row * a.ovf_stride;
+        t.VXY = (double2*)o;
+        t.V = (unsigned short*)(o + 16 * (a.n + 1));
+    }
     tile_merges<K, sizeof(T) == 4>(t, mask, xs, ys);
-    return mask;
+    tile_finish<T, K>(t, mask, a.increasing, a.lo, a.hi, out, sb, cb);
+    if (a.row_nan && threadIdx.x == 0) a.row_nan[row] = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -172,8 +181,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     bool over = false;
     if constexpr (HALVES) {
         // Noisy rows: the parts' hull vertices below the chord are few, and
-        // wrapping them gives the row's hull directly.  Other rows, and rows whose wrap
-        // gives up, take the exact path.  The list holds point 0 and cap
+        // wrapping them gives the row's hull directly.  Other rows, and rows
+        // whose wrap gives up, take the exact path (row_exact, which also
+        // handles lists beyond the LDS).  The list holds point 0 and cap
         // vertices; every condition here is uniform.
         bool done = false;
         if constexpr (ABS) {
@@ -188,8 +198,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
             }
         }
         if (!done) {
-            mask = row_exact<T, K>(a);
-            over = mask == ~0ull;
+            row_exact<T, K>(a);
+            return;
         }
     } else {
         over = nvert > a.cap + 1;
@@ -1324,7 +1334,9 @@ static hipError_t launch_row(const FitLaunch& a, RowArgs r, int nl) {
     // 64-byte segments and the list has room for every wave's span
     r.stage = ((K * (int)sizeof(T)) % 64 != 0) && ((K * (int)sizeof(T)) % 16 == 0) &&
               ((size_t)nl * K * sizeof(T) <= tile_list_len(nl, r.cap, K) * 16);
-    const bool may_overflow = r.cap < a.n;
+    // rows of several waves keep an overflowing list in the workspace within
+    // k_row_fit (row_exact); one-wave rows leave it to k_row_ovf
+    const bool may_overflow = r.cap < a.n && K < 12;
     r.ovf_row = may_overflow ? (int*)(a.ws + a.L.ovfrow) : nullptr;
     hipLaunchKernelGGL((k_row_fit<T, K>), dim3((unsigned)a.rows), dim3(nl), smem, a.stream, r);
     hipError_t e = hipGetLastError();
