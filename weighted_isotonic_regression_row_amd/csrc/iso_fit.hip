@@ -193,7 +193,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
         if (5 * nvert <= 3 * N + 5 && nvert <= a.cap + 1) {
             tile_compact<K, ABS>(t, mask, xs, ys);
             if (tile_wrap<K, ABS>(t)) {
-                tile_masks<K>(t, mask);
+                tile_masks_short<K>(t, mask);
                 done = true;
             }
         }

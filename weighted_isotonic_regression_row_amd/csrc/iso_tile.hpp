@@ -705,6 +705,8 @@ __device__ inline int group_merge(const Tile& t, int a0, int a1, int b0, int b1,
 
 template <int K>
 __device__ inline void tile_masks(const Tile& t, uint64_t& mask);
+template <int K>
+__device__ inline void tile_masks_short(const Tile& t, uint64_t& mask);
 
 // ---------------------------------------------------------------------------
 // Output-sensitive finish.  Every vertex of the tile's hull is a vertex of
@@ -1055,7 +1057,7 @@ __device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (
     const int nwu = (used + kWave - 1) / kWave;  // waves holding elements
     tile_compact<K, ABS>(t, mask, xs, ys);
     if (wrap && 5 * t.flag[1] <= 3 * t.N + 5 && tile_wrap<K, ABS>(t)) {
-        tile_masks<K>(t, mask);
+        tile_masks_short<K>(t, mask);
         return;
     }
     const int w0 = wid * kWave, wend = min(w0 + kWave, used);
@@ -1099,6 +1101,27 @@ __device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (
     if (l == 0) t.flag[1] = t.W[8] + 1;  // wave 0's node starts at entry 0 (point 0)
     tile_masks<K>(t, mask);
     (void)nw;
+}
+
+// Step 3d for a short final list (the wrap's): every lane scans the whole
+// list for its own vertices (points lK+1 .. lK+K) and counts the vertices
+// before them, so no atomics, scans or barriers are needed.  The list must be
+// final (a barrier after its last write); M and I are read by others only
+// after the next barrier.
+template <int K>
+__device__ inline void tile_masks_short(const Tile& t, uint64_t& mask) {
+    const int l = threadIdx.x, nv = t.flag[1], lo = l * K;
+    uint64_t m = 0ull;
+    int before = 0;
+#pragma unroll 4
+    for (int i = 1; i < nv; ++i) {
+        const int p = t.V[i];
+        before += (p <= lo) ? 1 : 0;
+        m |= (p > lo && p <= lo + K) ? (1ull << ((p - 1 - lo) & 63)) : 0ull;
+    }
+    mask = m;
+    t.M[l] = m;
+    t.I[l] = 1 + before;
 }
 
 // Step 3d: the final lane masks from the list V[0, flag[1]), and I[l] = index
