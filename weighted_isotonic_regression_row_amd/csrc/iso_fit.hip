@@ -120,27 +120,24 @@ __device__ inline void tile_finish(const Tile& t, uint64_t mask, int increasing,
 // wrap's.  A row whose lane hulls' vertices overflow the LDS list keeps its
 // list in the row's area of the workspace.
 template <typename T, int K>
-__device__ __attribute__((noinline)) void row_exact(RowArgs a) {
+__device__ __attribute__((noinline)) void row_exact(const T* y, const T* w, T* out, uint64_t* sb, uint64_t* cb,
+                                                    uint32_t* row_nan, char* ovf, int n, int increasing, double lo,
+                                                    double hi, int cap, int stage) {
+    // the arguments are plain values, passed in registers (a structure passed
+    // by value would be staged through scratch memory by every thread)
     extern __shared__ __align__(32) char smem[];
-    const int64_t row = blockIdx.x;
-    Tile t = tile_carve(smem, blockDim.x, a.cap, K, (int)a.n, sizeof(T) == 4);
-    const T* y = (const T*)a.y + row * a.n;
-    const T* w = a.w ? (const T*)a.w + row * a.n : nullptr;
-    T* out = (T*)a.fit + row * a.n;
-    uint64_t* sb = a.start_bits ? a.start_bits + row * a.words : nullptr;
-    uint64_t* cb = a.clip_bits ? a.clip_bits + row * a.words : nullptr;
+    Tile t = tile_carve(smem, blockDim.x, cap, K, n, sizeof(T) == 4);
     uint64_t mask;
     double xs[K], ys[K];
     int nvert;
-    (void)tile_build<T, K>(t, y, w, a.increasing, mask, xs, ys, nvert, a.stage != 0);  // inputs already checked
-    if (nvert > a.cap + 1) {  // uniform
-        char* o = a.ovf + row * a.ovf_stride;
-        t.VXY = (double2*)o;
-        t.V = (unsigned short*)(o + 16 * (a.n + 1));
+    (void)tile_build<T, K>(t, y, w, increasing, mask, xs, ys, nvert, stage != 0);  // inputs already checked
+    if (nvert > cap + 1) {  // uniform
+        t.VXY = (double2*)ovf;
+        t.V = (unsigned short*)(ovf + 16 * ((int64_t)n + 1));
     }
     tile_merges<K, sizeof(T) == 4>(t, mask, xs, ys);
-    tile_finish<T, K>(t, mask, a.increasing, a.lo, a.hi, out, sb, cb);
-    if (a.row_nan && threadIdx.x == 0) a.row_nan[row] = 0u;
+    tile_finish<T, K>(t, mask, increasing, lo, hi, out, sb, cb);
+    if (row_nan && threadIdx.x == 0) *row_nan = 0u;
 }
 
 // ---------------------------------------------------------------------------
@@ -198,7 +195,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
             }
         }
         if (!done) {
-            row_exact<T, K>(a);
+            row_exact<T, K>(y, w, out, sb, cb, a.row_nan ? a.row_nan + row : nullptr, a.ovf + row * a.ovf_stride, N,
+                            a.increasing, a.lo, a.hi, a.cap, a.stage);
             return;
         }
     } else {

@@ -1009,26 +1009,23 @@ __device__ inline bool tile_wrap(const Tile& t) {
         __syncthreads();
         return false;
     }
-    // the hull's entries to the front of the list (entries only move down)
+    // the hull's entries to the front of the list, 64 at a time: entries only
+    // move down, so a batch's writes land below every entry a later batch reads
     if (wid == 0) {
-        unsigned short pv[(kWrapTile + kWave) / kWave];
-        double2 xy[(kWrapTile + kWave) / kWave];
-#pragma unroll
-        for (int b = 0; b < (kWrapTile + kWave) / kWave; ++b) {
-            const int k = b * kWave + lane;
+        for (int k0 = 0; k0 < nf; k0 += kWave) {
+            const int k = k0 + lane;
+            unsigned short pv = 0;
+            double2 xy = make_double2(0.0, 0.0);
             if (k < nf) {
-                pv[b] = t.V[fin[k]];
-                xy[b] = t.VXY[fin[k]];
+                pv = t.V[fin[k]];
+                xy = t.VXY[fin[k]];
             }
-        }
-        wave_sync();
-#pragma unroll
-        for (int b = 0; b < (kWrapTile + kWave) / kWave; ++b) {
-            const int k = b * kWave + lane;
+            wave_sync();
             if (k < nf) {
-                t.V[k + 1] = pv[b];
-                t.VXY[k + 1] = xy[b];
+                t.V[k + 1] = pv;
+                t.VXY[k + 1] = xy;
             }
+            wave_sync();
         }
         if (lane == 0) t.flag[1] = nf + 1;
     }
