@@ -310,12 +310,17 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
     constexpr bool F32 = sizeof(T) == 4;
     const double sg = negate ? -1.0 : 1.0;
     float wmin = INFINITY;
-    auto take = [&](int j, double yi, double wi) {
+    // The staged path gives zeros past cnt (zero = true), which leave the sums
+    // as they are; only the least weight skips them.
+    auto take = [&](int j, double yi, double wi, bool zero = false) {
         if constexpr (F32) {
             const bool in = j < cnt;
-            wi = in ? wi : 0.0;
+            if (!zero) {
+                wi = in ? wi : 0.0;
+                yi = in ? yi : 0.0;
+            }
             X += wi;
-            Y = fma(wi * sg, in ? yi : 0.0, Y);
+            Y = fma(wi * sg, yi, Y);
             wmin = fminf(wmin, in ? (float)wi : 1.f);
         } else if (j < cnt) {
             if (!isfinite(yi) || !isfinite(wi))
@@ -346,10 +351,10 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
                 lane_load_staged<T, K>(w, avail, stage, wv);
             } else {
 #pragma unroll
-                for (int j = 0; j < K; ++j) wv[j] = (T)1;
+                for (int j = 0; j < K; ++j) wv[j] = (j < cnt) ? (T)1 : (T)0;
             }
 #pragma unroll
-            for (int j = 0; j < K; ++j) take(j, (double)yv[j], (double)wv[j]);
+            for (int j = 0; j < K; ++j) take(j, (double)yv[j], (double)wv[j], true);
             done = true;
         }
     }
