@@ -106,6 +106,30 @@ def test_rows_past_the_lds_list_mixed_with_others(n, dtype):
     check_fit(fit.cpu().numpy(), z, wl.y, dtype, True, wl.name)
 
 
+@pytest.mark.parametrize("n", [2500, 5000, 6144])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_rows_whose_wrap_gives_up(n, dtype):
+    """A staircase rising by one every tenth element under small noise: the
+    lanes' half hulls keep about 30% of the points (5000: about 1500, within
+    the LDS list), all below the row's chord, so the output-sensitive finish
+    is tried, but every wave's hull has hundreds of vertices and the wrap
+    gives up at its step cap; the row is then fitted by the exact path in the
+    same launch.  Mixed with noise rows (which the wrap finishes) and fitted
+    in both orientations, with unit and uniform weights."""
+    r = workloads.rng(4400 + n)
+    i = np.arange(n)
+    stairs = np.floor(i / 10.0)[None, :] + 0.1 * r.standard_normal((3, n))
+    noise = r.standard_normal((3, n))
+    y = np.concatenate([stairs, noise]).astype(dtype)
+    for inc in (True, False):
+        yy = y if inc else y[:, ::-1].copy()
+        for w in (None, r.uniform(0.1, 1.1, y.shape).astype(dtype)):
+            wl = workloads.Workload(f"stairs_6x{n}_{np.dtype(dtype).name}", yy, w, inc)
+            fit, *_ = gpu_fit(wl)
+            z, *_ = oracle_fit(wl)
+            check_fit(fit.cpu().numpy(), z, wl.y, dtype, inc, f"{wl.name} inc={inc} w={w is not None}")
+
+
 @pytest.mark.parametrize("n", [1, 2, 5, 15, 16, 17, 24, 31, 32, 33, 40, 48, 64, 65])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 def test_short_rows_one_per_lane(n, dtype):
