@@ -602,14 +602,20 @@ __global__ __launch_bounds__(1024) void k_vjp_row(VjpArgs a) {
     __syncthreads();
     // 4. totals per element, backward; elements after the lane's last block end
     //    belong to the block open at its end
+    //    The quotients change only where a block ends, so they are formed
+    //    there (a branch that a wave skips unless one of its lanes takes it).
     A tot = acc_zero<NF>();
     if (cnt > 0 && last_end < cnt - 1) tot = slot[end_open];
+    double gw = tot.v[0] / tot.v[1], mean = (NF == 3) ? tot.v[NF - 1] / tot.v[1] : 0.0;
 #pragma unroll
     for (int j = K - 1; j >= 0; --j) {
-        tot = acc_pick(j == last_end || (j < last_end && ((sbit >> (j + 1)) & 1u)), P[j], tot);
-        const double gw = tot.v[0] / tot.v[1];
+        if (j == last_end || (j < last_end && ((sbit >> (j + 1)) & 1u))) {
+            tot = P[j];
+            gw = tot.v[0] / tot.v[1];
+            if (NF == 3) mean = tot.v[NF - 1] / tot.v[1];
+        }
         gv[j] = wv[j] * gw;
-        if (NF == 3) yv[j] = gw * (yv[j] - tot.v[NF - 1] / tot.v[1]);
+        if (NF == 3) yv[j] = gw * (yv[j] - mean);
     }
     if (cnt > 0) {
         if (out) store_lane<T, K>(out + e0, cnt, gv);
