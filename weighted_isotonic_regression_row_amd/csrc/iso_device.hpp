@@ -107,19 +107,22 @@ __device__ __forceinline__ double wave_min(double v) {
     return readlane_d(v, kWave - 1);
 }
 
-template <int CTRL, int ROWS>
-__device__ __forceinline__ float dpp_keep_f(float v) {
-    const int b = __float_as_int(v);
-    return __int_as_float(__builtin_amdgcn_update_dpp(b, b, CTRL, ROWS, 0xf, false));
-}
+// Least value over the wave (no NaN), the same in every lane.  The floats are
+// mapped to unsigned keys that decrease as the value increases (the sort key
+// of the float's bits, complemented), so the least value is the greatest key
+// and a lane whose source falls outside a move reads 0, which never wins: the
+// moves fold into the maximum instructions.
 __device__ __forceinline__ float wave_min_f(float v) {
-    v = fminf(v, dpp_keep_f<0x111, 0xf>(v));
-    v = fminf(v, dpp_keep_f<0x112, 0xf>(v));
-    v = fminf(v, dpp_keep_f<0x114, 0xf>(v));
-    v = fminf(v, dpp_keep_f<0x118, 0xf>(v));
-    v = fminf(v, dpp_keep_f<0x142, 0xa>(v));
-    v = fminf(v, dpp_keep_f<0x143, 0xc>(v));
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+    const unsigned b = __float_as_uint(v);
+    unsigned r = ~(b ^ ((b >> 31) ? 0xffffffffu : 0x80000000u));
+    r = max(r, (unsigned)dpp_move<0x111, 0xf>((int)r));
+    r = max(r, (unsigned)dpp_move<0x112, 0xf>((int)r));
+    r = max(r, (unsigned)dpp_move<0x114, 0xf>((int)r));
+    r = max(r, (unsigned)dpp_move<0x118, 0xf>((int)r));
+    r = max(r, (unsigned)dpp_move<0x142, 0xa>((int)r));
+    r = max(r, (unsigned)dpp_move<0x143, 0xc>((int)r));
+    const unsigned u = ~(unsigned)__builtin_amdgcn_readlane((int)r, kWave - 1);
+    return __uint_as_float(u ^ ((u >> 31) ? 0x80000000u : 0xffffffffu));
 }
 
 // Inclusive scan over the 64 lanes of the wave with op(earlier, later), whose
