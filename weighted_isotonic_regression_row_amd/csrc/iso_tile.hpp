@@ -471,13 +471,18 @@ __device__ inline int tile_lane_starts(const Tile& t, double2 total, int f, int 
 template <int K>
 __device__ inline uint64_t chord_filter(const Tile& t, uint64_t mask, const double (&xs)[K], const double (&ys)[K]) {
     const double2 tot = ((const double2*)t.LS)[t.nl], st = ((const double2*)t.LS)[threadIdx.x];
+    // the cross product of point (st + (xs, ys)[b]) with the chord splits into
+    // a part of the lane's start and one of the local point; its rounding is
+    // bounded by the magnitudes of the four products (scaled once per lane)
+    constexpr double e = 1e-13;
+    const double c0 = st.y * tot.x - tot.y * st.x;
+    const double a0 = (fabs(st.y * tot.x) + fabs(tot.y * st.x)) * e, ax = fabs(tot.x) * e, ay = fabs(tot.y) * e;
     uint64_t keep = 0ull;
 #pragma unroll
     for (int b = 0; b < K; ++b) {
-        const double X = st.x + xs[b], Y = st.y + ys[b];
-        const double a1 = Y * tot.x, a2 = tot.y * X;
-        const bool in = a1 - a2 <= (fabs(a1) + fabs(a2)) * 1e-14;
-        keep |= (in ? 1ull : 0ull) << b;
+        const double d = c0 + fma(ys[b], tot.x, -(tot.y * xs[b]));
+        const double tol = fma(fabs(ys[b]), ax, fma(ay, xs[b], a0));
+        keep |= (d <= tol ? 1ull : 0ull) << b;
     }
     return mask & keep;
 }
