@@ -171,7 +171,7 @@ __global__ __launch_bounds__(64) void k_rank_fused(FusedArgs a) {
         if (t == 0) a.row_nan[row] = 1u;
         return;
     }
-    tile_merges<E, ABS>(tl, mask, xs, ys);
+    tile_merges<E, ABS>(tl, mask, xs, ys, true);
     tile_edge_slopes<E, ABS>(tl, 0, -INFINITY, INFINITY);
     double vals[E];
     uint64_t clipm;
