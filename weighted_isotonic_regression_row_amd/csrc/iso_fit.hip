@@ -470,7 +470,7 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
         }
         return;
     }
-    tile_merges<K, sizeof(T) == 4>(t, mask, xs, ys);  // the LDS list holds every point of a chunk
+    tile_merges<K, sizeof(T) == 4>(t, mask, xs, ys, true);  // the LDS list holds every point of a chunk
     __syncthreads();  // every lane's final mask in M
     const int l = threadIdx.x;
     const int nv = t.flag[1];  // vertices of the chunk hull; rank r is list entry r
