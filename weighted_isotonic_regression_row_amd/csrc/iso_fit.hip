@@ -2,8 +2,10 @@
 //
 // Page "Merge Hulls Without Copying Vertices: GPU Isotonic Regression":
 //   k_row_fit      rows of at most 6144 elements: one workgroup per row builds
-//                  the row's hull in LDS and writes the fit (Sec. 3: "a row that
-//                  fits in one chunk is finished at the second level").
+//                  the row's hull in LDS and writes the fit (Sec. 3: a row that
+//                  fits in one chunk is finished by the chunk level).  Noisy
+//                  float32 rows are finished by gift wrapping a few candidate
+//                  vertices; the others merge their lane hulls in rounds.
 //   k_chunk_hull   longer rows: one workgroup per chunk of 3584 elements builds
 //                  the chunk's hull once and stores it compactly (vertex bit
 //                  set, group starts, the coordinates of its end vertices),

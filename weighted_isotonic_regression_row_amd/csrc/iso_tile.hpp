@@ -19,7 +19,14 @@
 //                merge finding the bridge (Sec. 4, Lemma 4.2 and the walk
 //                after it) and moving the right node's surviving suffix
 //                behind the left node's surviving prefix; then a tree over
-//                the waves' nodes;
+//                the waves' nodes.  Tiles whose candidates are few first try
+//                an output-sensitive finish instead (tile_wrap): every wave
+//                gift-wraps its candidates, one step per hull edge, and the
+//                waves' vertices are reduced to the tile's hull by a parallel
+//                vertex test; the rounds run only if a wrap exceeds its cap.
+//                Candidates may be any superset of the hull's vertices: the
+//                lane hulls' vertices, or for float32 rows of several waves
+//                those of the lanes' half hulls below the tile's chord;
 //   4. expand    every lane computes the slope of the hull edge above each of
 //                its elements (Sec. 3.4: the edge from the last vertex at or
 //                before the element's left point to the first vertex at or
