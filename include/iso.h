@@ -86,7 +86,15 @@ typedef struct iso_blocks {
  */
 size_t iso_workspace_bytes(int64_t rows, int64_t n, int dtype);
 
-/* Bytes of device memory backing an iso_blocks handle for rows x n. */
+/*
+ * Bytes of device memory backing an iso_blocks handle for rows x n: the
+ * block-start and clip bit words and the row-NaN flags described above, which
+ * record the partition of each row into the pooled blocks of its fit (first
+ * page, Sec. 2.1: the hull's vertices split the row into blocks sharing one
+ * value) and the elements that clipping changed (PyPI page, "Semantics").
+ * The backward pass averages over exactly these blocks (first page,
+ * Appendix C).  Returns 0 for negative sizes.
+ */
 size_t iso_blocks_bytes(int64_t rows, int64_t n);
 
 /*
@@ -264,13 +272,23 @@ int iso_calibrate(const void* xs_dev, const void* fit_dev, const int32_t* m_dev,
                   const void* q_dev, int64_t k, int dtype, void* out_dev, void* stream);
 
 /*
- * Synchronises `stream` and returns the data error of the most recent iso_fit
- * that used this workspace: ISO_OK or ISO_EWEIGHT (ISO_EHIP if the read fails,
- * ISO_EINVAL for a NULL workspace).
+ * Data errors of a fit (PyPI page, "Semantics": the weights must be strictly
+ * positive).  The kernels cannot return an error to the host without a
+ * synchronisation, so a row holding a finite weight <= 0 comes back NaN and
+ * the error is recorded in the workspace.  iso_status synchronises `stream`
+ * and returns the data error of the most recent iso_fit that used this
+ * workspace: ISO_OK or ISO_EWEIGHT (ISO_EHIP if the read fails, ISO_EINVAL
+ * for a NULL workspace).  The answer is defined only for a workspace that an
+ * iso_fit has used; the library keeps no host state per workspace (the call's
+ * epoch and error live in the workspace's first 16 bytes).
  */
 int iso_status(const void* workspace_dev, void* stream);
 
-/* Static, human-readable text for a return code. */
+/*
+ * Static, human-readable text for a return code of this library (ISO_OK,
+ * ISO_EINVAL, ISO_EHIP, ISO_EWEIGHT: the last is the PyPI page's "Semantics"
+ * rule that weights be strictly positive); "unknown error" for any other.
+ */
 const char* iso_strerror(int code);
 
 #ifdef __cplusplus

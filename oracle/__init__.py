@@ -12,6 +12,7 @@ and Sec. 2.1 Eq. (1); semantics from the "torchisotonic" PyPI page, section
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 import subprocess
 
@@ -177,11 +178,14 @@ def soft_rank_vjp(g, eps, perm, block_start, row_nan=None):
 
 def calibration_fit(scores, labels):
     """Calibration curve of each row (first page, Sec. 7.7; "torchisotonic" PyPI page, "What it is for":
-    scikit-learn's IsotonicRegression curve): the scores are sorted, equal scores are pooled (their labels
-    summed and counted), and the non-decreasing fit of the pooled means is computed with the counts as
-    weights.  Returns (xs, fit, m): xs and fit [rows, n] float64 hold the m[r] distinct scores of row r in
-    increasing order and the curve's values there (the rest NaN).  A row holding a NaN (score or label) has
-    no curve: m = 0."""
+    scikit-learn's IsotonicRegression curve), written from its definition.  The curve's points are the
+    row's distinct scores in increasing order; the value at a point comes from the labels of all the
+    elements holding that score, which share one fitted value: by Eq. (1) their squared errors around a
+    common value v add up to c (v - mean)^2 plus a constant, so the group acts as one observation, its mean
+    label, with its count c as the weight.  The curve is the non-decreasing weighted fit of those
+    observations.  Returns (xs, fit, m): xs and fit [rows, n] float64 hold the m[r] points of row r and the
+    curve's values there (the rest NaN).  A row holding a NaN (score or label) has no curve: m = 0.  -0 and
+    +0 are one score, reported as +0."""
     s2 = _as2d(scores)
     l2 = _as2d(labels)
     if s2.shape != l2.shape:
@@ -195,12 +199,16 @@ def calibration_fit(scores, labels):
         if n == 0 or np.isnan(s).any() or np.isnan(lab).any():
             continue
         order = np.argsort(s, kind="stable")
-        u, inv, cnt = np.unique(s[order], return_inverse=True, return_counts=True)
-        sums = np.zeros(len(u))
-        np.add.at(sums, inv, lab[order])
-        z, *_ = fit(sums / cnt, cnt.astype(np.float64), increasing=True)
-        k = len(u)
-        xs[r, :k] = u
+        ss = s[order] + 0.0          # -0 becomes +0
+        ll = lab[order]
+        # a group of equal scores begins where the sorted score differs from the one before it
+        first = np.flatnonzero(np.concatenate(([True], ss[1:] != ss[:-1])))
+        last = np.append(first[1:], n)
+        counts = (last - first).astype(np.float64)
+        sums = np.array([math.fsum(ll[a:b]) for a, b in zip(first, last)]) if first.size < n else ll.copy()
+        z, *_ = fit(sums / counts, counts, increasing=True)
+        k = first.size
+        xs[r, :k] = ss[first]
         fv[r, :k] = z[0]
         m[r] = k
     return xs, fv, m
@@ -208,7 +216,8 @@ def calibration_fit(scores, labels):
 
 def calibrate(q, xs, fv, m):
     """Calibrated values of the queries q [rows, k] on each row's curve ("torchisotonic" PyPI page, "What it
-    is for"): linear between the curve's points, constant beyond them; a NaN query, or a row without a curve,
+    is for"): the piecewise-linear function through the curve's points, held constant before the first point
+    and after the last (numpy's interp is exactly that function); a NaN query, or a row without a curve,
     gives NaN."""
     q2 = _as2d(q)
     out = np.full(q2.shape, np.nan)
@@ -216,12 +225,6 @@ def calibrate(q, xs, fv, m):
         k = int(m[r])
         if k == 0:
             continue
-        x, f = xs[r, :k], fv[r, :k]
-        if k == 1:
-            out[r] = f[0]
-        else:
-            i = np.clip(np.searchsorted(x, q2[r], side="left"), 1, k - 1)
-            t = np.clip((q2[r] - x[i - 1]) / (x[i] - x[i - 1]), 0.0, 1.0)
-            out[r] = f[i - 1] + t * (f[i] - f[i - 1])
+        out[r] = np.interp(q2[r], xs[r, :k], fv[r, :k])
         out[r, np.isnan(q2[r])] = np.nan
     return out

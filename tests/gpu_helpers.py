@@ -1,10 +1,25 @@
 """Shared helpers for the GPU parity tests: run the HIP path and the oracle on
 the same seeded inputs and compare them to the stated tolerances.
 
-Tolerances (written out here, used by every GPU test):
-  float64: max |z_gpu - z_oracle| <= 1e-10 * max|y|
-  float32: max |z_gpu - z_oracle| <= 2e-5 * max|y|, and the largest step the
-           wrong way between neighbours <= 4 ulp_f32(max|y|).
+Tolerances (written out here, used by every GPU test), each taken row by row
+with s_r = max |y_r| over the row's finite entries:
+  float64: max |z_gpu - z_oracle| <= 1e-10 * s_r
+  float32: max |z_gpu - z_oracle| <= 2e-5 * s_r, and the largest step the
+           wrong way between neighbours <= 4 ulp_f32(s_r).
+Partitions (block starts) and clip flags are decided in float64 on both
+sides whatever the data type (float32 inputs and their products with float32
+weights are exact in float64), so they are checked at the float64 bound:
+  - every GPU block is a block of the oracle's unclipped fit: the weighted mean
+    of y over the block equals that fit at each of its elements within
+    1e-10 * s_r (so a block may keep a split at an exactly collinear point, or
+    pool two blocks whose means tie, but nothing else);
+  - away from ties the start bits equal the oracle's bit for bit.  A position
+    is a tie where an oracle block starts whose mean lies within 1e-8 * s_r
+    of the previous block's, or where a point inside an oracle block lies that
+    close to collinear with the block's edge (the mean of the block's elements
+    before it is within 1e-8 * s_r of the block's mean);
+  - clip bits equal the oracle's wherever the unclipped fit lies more than
+    1e-9 * s_r away from both bounds.
 """
 from __future__ import annotations
 
@@ -15,6 +30,9 @@ import oracle
 TOL_F64 = 1e-10
 TOL_F32 = 2e-5
 MONO_ULPS_F32 = 4
+PART_TOL = 1e-10      # block means against the oracle's unclipped fit, relative to s_r
+TIE_GAP = 1e-8        # neighbouring block means closer than this (relative to s_r) count as a tie
+CLIP_MARGIN = 1e-9    # unclipped values this close to a bound may be flagged either way
 
 
 def to_dev(a, device="cuda:0"):
@@ -42,30 +60,46 @@ def oracle_fit(wl, rows=None, threads=8):
 
 
 def scale_of(y):
+    """max |y| over the finite entries of the whole array (1.0 if there are none)."""
     finite = np.abs(y[np.isfinite(y)]).astype(np.float64)
     return float(finite.max()) if finite.size else 1.0
 
 
+def row_scales(y):
+    """s_r = max |y_r| over each row's finite entries (0 for a row without any)."""
+    y2 = np.atleast_2d(np.asarray(y))
+    a = np.abs(np.where(np.isfinite(y2), y2, 0).astype(np.float64))
+    return a.max(axis=-1) if a.shape[-1] else np.zeros(a.shape[0])
+
+
 def check_fit(z_gpu, z_ref, y, dtype, increasing, what=""):
-    """Compare one batch of rows; NaN rows must match exactly in NaN-ness."""
-    z_gpu = np.asarray(z_gpu, dtype=np.float64)
+    """Compare one batch of rows, each at its own scale; NaN rows must match
+    exactly in NaN-ness.  Returns the largest error relative to its row's scale."""
+    z_gpu = np.atleast_2d(np.asarray(z_gpu, dtype=np.float64))
+    z_ref = np.atleast_2d(np.asarray(z_ref, dtype=np.float64))
     nan_g, nan_r = np.isnan(z_gpu), np.isnan(z_ref)
     assert np.array_equal(nan_g, nan_r), f"{what}: NaN pattern differs"
     ok = ~nan_r
     if not ok.any():
         return 0.0
-    s = scale_of(y)
-    err = float(np.max(np.abs(z_gpu[ok] - z_ref[ok])))
-    tol = (TOL_F64 if dtype == np.float64 else TOL_F32) * s
-    assert err <= tol, f"{what}: max abs error {err:.3e} > {tol:.3e} (scale {s:.3e})"
-    if dtype == np.float32:
-        ulp = float(np.spacing(np.float32(s)))
+    s = row_scales(y)
+    rel = TOL_F64 if np.dtype(dtype) == np.float64 else TOL_F32
+    err = np.where(ok, np.abs(z_gpu - z_ref), 0.0).max(axis=1)
+    tol = rel * s
+    bad = err > tol
+    if bad.any():
+        r = int(np.argmax(np.where(bad, err / np.maximum(s, 1e-300), 0.0)))
+        raise AssertionError(f"{what}: row {r}: max abs error {err[r]:.3e} > {tol[r]:.3e} (row scale {s[r]:.3e})")
+    if np.dtype(dtype) == np.float32 and z_gpu.shape[1] > 1:
+        ulp = np.spacing(s.astype(np.float32)).astype(np.float64)
         d = np.diff(z_gpu, axis=-1)
-        wrong = -d if increasing else d
-        rows_ok = ~np.isnan(z_gpu).any(axis=-1)
-        viol = float(np.max(wrong[rows_ok], initial=0.0))
-        assert viol <= MONO_ULPS_F32 * ulp, f"{what}: monotonicity violation {viol:.3e} > 4 ulp ({ulp:.3e})"
-    return err
+        wrong = np.where(np.isnan(d), 0.0, -d if increasing else d)
+        viol = wrong.max(axis=1)
+        badm = viol > MONO_ULPS_F32 * ulp
+        if badm.any():
+            r = int(np.argmax(np.where(badm, viol / ulp, 0.0)))
+            raise AssertionError(f"{what}: row {r}: monotonicity violation {viol[r]:.3e} > 4 ulp ({ulp[r]:.3e})")
+    return float(np.max(err / np.maximum(s, 1e-300)))
 
 
 def unpack_bits(words, n):
@@ -80,3 +114,79 @@ def gpu_blocks(b):
     sb, cb, rn = b.bits()
     n = b.c.n
     return unpack_bits(sb.cpu().numpy(), n), unpack_bits(cb.cpu().numpy(), n), rn.cpu().numpy()
+
+
+def check_partition(gs, gc, grn, y, w, increasing, y_min, y_max, what="", threads=8):
+    """The GPU's block-start and clip bits against the oracle (rules in the module
+    docstring).  Returns (rows without any tie position, rows checked)."""
+    y64 = np.atleast_2d(np.asarray(y, dtype=np.float64))
+    rows, n = y64.shape
+    w64 = np.ones_like(y64) if w is None else np.atleast_2d(np.asarray(w, dtype=np.float64))
+    zu, bs, _, rn, _ = oracle.fit(y64, None if w is None else w64, increasing, None, None, threads=threads)
+    np.testing.assert_array_equal(np.asarray(grn).astype(bool), rn.astype(bool), err_msg=f"{what}: NaN rows")
+    live = ~rn.astype(bool)
+    if n == 0 or not live.any():
+        return 0, 0
+    s = row_scales(y64)
+    gs = np.asarray(gs, dtype=np.uint8)
+    assert (gs[live, 0] == 1).all(), f"{what}: element 0 must start a block"
+    # every GPU block's weighted mean against the oracle's unclipped fit, in extended precision
+    sub = np.flatnonzero(live)
+    ysub, wsub, zsub, gsub = y64[sub], w64[sub], zu[sub], gs[sub]
+    flat = np.flatnonzero(gsub.ravel())
+    num = np.add.reduceat((wsub.astype(np.longdouble) * ysub).ravel(), flat)
+    den = np.add.reduceat(wsub.astype(np.longdouble).ravel(), flat)
+    mean = (num / den).astype(np.float64)  # either orientation: a block's value is its weighted mean
+    bid = np.cumsum(gsub.ravel()) - 1
+    dev = np.abs(mean[bid] - zsub.ravel()).reshape(gsub.shape).max(axis=1)
+    tol = PART_TOL * s[sub]
+    bad = dev > tol
+    if bad.any():
+        k = int(np.argmax(np.where(bad, dev / np.maximum(s[sub], 1e-300), 0.0)))
+        r = int(sub[k])
+        st = np.flatnonzero(gs[r])
+        raise AssertionError(f"{what}: row {r}: a GPU block's mean is {dev[k]:.3e} off the oracle's fit "
+                             f"(tol {tol[k]:.3e}); GPU blocks {st.size}, oracle blocks {int(bs[r].sum())}")
+    # away from ties the start bits equal the oracle's.  A position is a tie
+    # when it starts an oracle block whose mean (nearly) equals the previous
+    # block's, or when it lies inside an oracle block at a point (nearly)
+    # collinear with the block's edge: the mean of the block's elements before
+    # it (nearly) equals the block's mean.  Either way a GPU may split there
+    # or not.  Every other position must agree bit for bit.
+    ws_l = wsub.astype(np.longdouble)
+    P = np.concatenate([np.zeros((sub.size, 1), np.longdouble), np.cumsum(ws_l * ysub, axis=1)], axis=1)
+    Q = np.concatenate([np.zeros((sub.size, 1), np.longdouble), np.cumsum(ws_l, axis=1)], axis=1)
+    idx = np.arange(n)[None, :]
+    bsub = bs[sub]
+    a = np.maximum.accumulate(np.where(bsub == 1, idx, 0), axis=1)
+    inner = idx > a
+    rows_i = np.arange(sub.size)[:, None]
+    dq = np.where(inner, Q[:, :n] - Q[rows_i, a], 1)
+    left = ((P[:, :n] - P[rows_i, a]) / dq).astype(np.float64)
+    gap = TIE_GAP * s[sub][:, None]
+    amb = inner & (np.abs(left - zsub) <= gap)
+    jump = np.abs(np.diff(zsub, axis=1, prepend=zsub[:, :1]))
+    amb |= (bsub == 1) & (idx > 0) & (jump <= gap)
+    diff = (gsub != bsub) & ~amb
+    if diff.any():
+        k = int(np.flatnonzero(diff.any(axis=1))[0])
+        d = np.flatnonzero(diff[k])
+        r = int(sub[k])
+        raise AssertionError(f"{what}: row {r}: start bits differ from the oracle's away from ties at "
+                             f"{d[:8].tolist()} (GPU {int(gs[r].sum())} blocks, oracle {int(bs[r].sum())})")
+    exact = int((~amb.any(axis=1)).sum())
+    # clip bits where the decision is clear
+    lo = -np.inf if y_min is None or np.isnan(y_min) else float(y_min)
+    hi = np.inf if y_max is None or np.isnan(y_max) else float(y_max)
+    zl = zu[sub]
+    want = (zl < lo) | (zl > hi)
+    margin = CLIP_MARGIN * s[sub][:, None]
+    clear = (np.abs(zl - lo) > margin) & (np.abs(zl - hi) > margin)
+    gcs = np.asarray(gc, dtype=np.uint8)[sub].astype(bool)
+    badc = clear & (gcs != want)
+    if badc.any():
+        k, i = np.argwhere(badc)[0]
+        raise AssertionError(f"{what}: row {int(sub[k])}: clip bit of element {int(i)} is {int(gcs[k, i])}, "
+                             f"unclipped fit {zl[k, i]!r} against [{lo}, {hi}]")
+    return exact, int(sub.size)
+

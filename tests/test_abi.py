@@ -237,7 +237,8 @@ def test_calibration_rejects_bad_arguments_on_host(lib):
 def test_status_without_calls(lib):
     import weighted_isotonic_regression_row_amd as iso
     assert lib.iso_status(None, None) == iso.ISO_EINVAL
-    assert lib.iso_status(123456, None) == iso.ISO_OK  # no fit used this workspace
+    # a workspace's status lives in its own first 16 bytes (no host map per
+    # workspace), so any other call reads device memory and is for the GPU tests
 
 
 def test_binding_refuses_host_tensors():

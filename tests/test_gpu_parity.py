@@ -13,7 +13,8 @@ import pytest
 
 import oracle
 import workloads
-from gpu_helpers import (TOL_F32, TOL_F64, check_fit, gpu_blocks, gpu_fit, oracle_fit, scale_of, to_dev)
+from gpu_helpers import (TOL_F32, TOL_F64, check_fit, check_partition, gpu_blocks, gpu_fit, oracle_fit, scale_of,
+                         to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -22,16 +23,45 @@ def _print(*a):
     print(*a, flush=True)
 
 
+def _check_vjp(wl, fit_blocks, gs, gc, grn, seed, what):
+    """Both backward products on the GPU's partition (checked against the
+    oracle's by check_partition first) against the oracle's products."""
+    import weighted_isotonic_regression_row_amd as iso
+    dtype = wl.y.dtype
+    g = workloads.rng(seed).standard_normal(wl.y.shape).astype(dtype)
+    gy, gw = iso.iso_vjp_yw(to_dev(g), fit_blocks, to_dev(wl.y))
+    w64 = None if wl.w is None else wl.w.astype(np.float64)
+    ref_y = oracle.vjp(g.astype(np.float64), gs, gc, grn, w64)
+    ref_w = oracle.vjp_w(g.astype(np.float64), wl.y.astype(np.float64), gs, gc, grn, w64)
+    tol = 1e-12 if dtype == np.float64 else 2e-6
+    for got, ref, name in ((gy, ref_y, "grad_y"), (gw, ref_w, "grad_w")):
+        got = got.cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isnan(got), np.isnan(ref)), f"{what}: {name} NaN pattern"
+        ok = ~np.isnan(ref)
+        err = float(np.max(np.abs(got[ok] - ref[ok]), initial=0.0))
+        assert err <= tol * max(1.0, float(np.abs(ref[ok]).max(initial=0.0))), f"{what}: {name} off by {err:.3e}"
+
+
 @pytest.mark.parametrize("k", [1, 2, 3])
 def test_config_full_size(k):
+    """The workload at its full size: the fit, then its block starts and clip
+    flags against the oracle's (config 2: 1000 x 5000 float32, non-increasing,
+    clipped to [0, 1], on the 20-point row kernel), then both backward products."""
     wl = workloads.CONFIGS[k]()
     _print(f"config {k}: {wl.name} {wl.y.shape}")
     fit, b, *_ = gpu_fit(wl)
     z, bs, cl, rn, st = oracle_fit(wl)
     check_fit(fit.cpu().numpy(), z, wl.y, wl.y.dtype, wl.increasing, wl.name)
+    gs, gc, grn = gpu_blocks(b)
+    exact, rows = check_partition(gs, gc, grn, wl.y, wl.w, wl.increasing, wl.y_min, wl.y_max, wl.name)
+    _print(f"config {k}: {exact} of {rows} rows without a tie position")
+    _check_vjp(wl, b, gs, gc, grn, 100 + k, wl.name)
 
 
 def test_config4_calibration_full():
+    """1 x 6.5e6 float64 with integer counts as weights and rational labels
+    (many exact ties): the fit, the partition's validity and clip flags
+    against the oracle's, and both backward products at full size."""
     wl = workloads.cfg4_calibration()
     _print(f"config 4: {wl.name} {wl.y.shape}")
     fit, b, *_ = gpu_fit(wl)
@@ -39,7 +69,8 @@ def test_config4_calibration_full():
     check_fit(fit.cpu().numpy(), z, wl.y, wl.y.dtype, wl.increasing, wl.name)
     gs, gc, grn = gpu_blocks(b)
     assert grn[0] == 0
-    np.testing.assert_array_equal(gc, cl)  # clip flags follow the (equal) fit
+    check_partition(gs, gc, grn, wl.y, wl.w, True, 0.0, 1.0, wl.name)
+    _check_vjp(wl, b, gs, gc, grn, 104, wl.name)
 
 
 def test_config5_dense_full_sampled_rows():
@@ -50,12 +81,89 @@ def test_config5_dense_full_sampled_rows():
     rows = [0, 13, 31]
     z, *_ = oracle_fit(wl, rows=rows)
     check_fit(f[rows], z, wl.y[rows], wl.y.dtype, True, wl.name)
+    gs, gc, grn = gpu_blocks(b)
+    check_partition(gs[rows], gc[rows], grn[rows], wl.y[rows], wl.w[rows], True, None, None, wl.name)
     # every row: monotone up to rounding and the weighted sum preserved
     s = scale_of(wl.y)
     assert np.all(np.diff(f, axis=1) >= -1e-12 * s)
     lhs = np.einsum("ij,ij->i", wl.w, f)
     rhs = np.einsum("ij,ij->i", wl.w, wl.y)
     assert np.all(np.abs(lhs - rhs) <= 1e-9 * np.abs(wl.w * wl.y).sum(axis=1))
+
+
+@pytest.mark.parametrize("kind", ["increasing", "trend_noise"])
+def test_rows_past_4096_chunks(kind):
+    """Rows of 1.6e7 float64 elements (4465 chunks, more than the top merge keeps
+    in LDS, so its descriptors stay in global memory): every point a vertex
+    (increasing data, the first page's Sec. 7.5 regime) and trend plus noise.
+    The fit, the partition and the clip flags against the oracle's."""
+    n = 16_000_000
+    wl = workloads.family(kind, 1, n, seed=17, dtype=np.float64, weights="uniform")
+    wl.y_min, wl.y_max = 0.05, 0.95
+    _print(f"long row: {wl.name}")
+    fit, b, *_ = gpu_fit(wl)
+    z, bs, cl, rn, _ = oracle_fit(wl)
+    check_fit(fit.cpu().numpy(), z, wl.y, np.float64, True, wl.name)
+    del z, bs, cl
+    gs, gc, grn = gpu_blocks(b)
+    check_partition(gs, gc, grn, wl.y, wl.w, True, wl.y_min, wl.y_max, wl.name)
+
+
+# Row lengths that reach each path of the fit: one row per lane (24), two lanes
+# (50), one wave with K = 2, 4, 8 points per lane (100, 200, 400), several waves
+# with K = 16 (3000), K = 20 for float32 and 12 for float64 (5000), K = 12
+# (6000), and the chunked path (20000).
+SHAPE_SIZES = [24, 50, 100, 200, 400, 3000, 5000, 6000, 20000]
+
+
+@pytest.mark.parametrize("n", SHAPE_SIZES)
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+@pytest.mark.parametrize("inc", [True, False])
+def test_partition_and_clip_bits_every_row_shape(n, dtype, inc):
+    """Block-start and clip bits against the oracle's on tie-free data for every
+    row kernel, both dtypes, both orientations, clipped (the first page's
+    Appendix B, "Tests": gradients against the CPU on data without near-ties),
+    then both backward products."""
+    rows = 12
+    a = workloads.family("trend_noise", rows - 4, n, seed=n % 61, dtype=dtype, weights="uniform")
+    b_ = workloads.family("noise", 4, n, seed=n % 67, dtype=dtype, weights="extreme")
+    y = np.concatenate([a.y, b_.y])
+    w = np.concatenate([a.w, b_.w])
+    if not inc:
+        y = y[:, ::-1].copy()
+        w = w[:, ::-1].copy()
+    wl = workloads.Workload(f"shapes_{rows}x{n}_{np.dtype(dtype).name}_inc{int(inc)}", y, w, inc, 0.2, 0.7)
+    fit, b, *_ = gpu_fit(wl)
+    z, *_ = oracle_fit(wl)
+    check_fit(fit.cpu().numpy(), z, wl.y, dtype, inc, wl.name)
+    gs, gc, grn = gpu_blocks(b)
+    check_partition(gs, gc, grn, wl.y, wl.w, inc, 0.2, 0.7, wl.name)
+    _check_vjp(wl, b, gs, gc, grn, n, wl.name)
+
+
+@pytest.mark.parametrize("n", [330, 400, 450, 512])
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+@pytest.mark.parametrize("inc", [True, False])
+def test_one_wave_rows_past_the_lds_list(n, dtype, inc):
+    """One-wave rows (8 points per lane) whose lane hulls hold more vertices than
+    the kernel's LDS list (dense data: increasing, or a sawtooth under a trend),
+    so the second kernel refits them with the whole list in LDS, mixed in one
+    launch with noise rows that the first kernel finishes."""
+    parts = [workloads.family("increasing", 3, n, seed=n, dtype=dtype, weights="uniform"),
+             workloads.family("sawtooth", 3, n, seed=n + 1, dtype=dtype, weights="extreme"),
+             workloads.family("noise", 3, n, seed=n + 2, dtype=dtype, weights="uniform")]
+    y = np.concatenate([p.y for p in parts])
+    w = np.concatenate([p.w for p in parts])
+    if not inc:
+        y = y[:, ::-1].copy()
+        w = w[:, ::-1].copy()
+    wl = workloads.Workload(f"ovf_9x{n}_{np.dtype(dtype).name}_inc{int(inc)}", y, w, inc, -0.5, 0.9)
+    fit, b, *_ = gpu_fit(wl)
+    z, *_ = oracle_fit(wl)
+    check_fit(fit.cpu().numpy(), z, wl.y, dtype, inc, wl.name)
+    gs, gc, grn = gpu_blocks(b)
+    check_partition(gs, gc, grn, wl.y, wl.w, inc, -0.5, 0.9, wl.name)
+    _check_vjp(wl, b, gs, gc, grn, n + 7, wl.name)
 
 
 SIZES = [1, 2, 3, 63, 64, 65, 127, 129, 257, 513, 1000, 3583, 3584, 3585, 4096, 4097, 4500, 5120, 5121, 6143, 6144, 6145, 7168, 7169,
@@ -69,9 +177,10 @@ def test_ragged_sizes(n, dtype):
         wl = workloads.family(kind, 3, n, seed=n % 97, dtype=dtype, weights=weights, increasing=inc)
         if clip:
             wl.y_min, wl.y_max = clip
-        fit, *_ = gpu_fit(wl)
+        fit, b, *_ = gpu_fit(wl)
         z, *_ = oracle_fit(wl)
         check_fit(fit.cpu().numpy(), z, wl.y, dtype, inc, f"{wl.name} n={n}")
+        check_partition(*gpu_blocks(b), wl.y, wl.w, inc, wl.y_min, wl.y_max, f"{wl.name} n={n}")
 
 
 @pytest.mark.parametrize("kind", workloads.FAMILIES)
@@ -82,9 +191,10 @@ def test_families(kind, n, dtype):
         n = 20000
     for weights in ("unit", "uniform", "extreme"):
         wl = workloads.family(kind, 2, n, seed=3, dtype=dtype, weights=weights)
-        fit, *_ = gpu_fit(wl)
+        fit, b, *_ = gpu_fit(wl)
         z, *_ = oracle_fit(wl)
         check_fit(fit.cpu().numpy(), z, wl.y, dtype, True, f"{wl.name}")
+        check_partition(*gpu_blocks(b), wl.y, wl.w, True, None, None, wl.name)
 
 
 @pytest.mark.parametrize("n", [2500, 5000, 6144])
@@ -167,22 +277,6 @@ def test_short_rows_one_per_lane(n, dtype):
         # block starts agree with the oracle's on the tie-free noise rows
         k = rows // 6
         np.testing.assert_array_equal(gs[:k], bs[:k])
-
-
-@pytest.mark.parametrize("n", [700, 5000, 30000])
-def test_block_starts_match_oracle_on_tie_free_data(n):
-    wl = workloads.family("trend_noise", 4, n, seed=11, dtype=np.float64, weights="uniform")
-    fit, b, *_ = gpu_fit(wl)
-    gs, gc, grn = gpu_blocks(b)
-    z, bs, cl, rn, _ = oracle_fit(wl)
-    for r in range(wl.rows):
-        starts = np.nonzero(bs[r])[0]
-        means = z[r][starts]
-        gaps = np.diff(means)
-        if gaps.size and gaps.min() < 1e-9 * scale_of(wl.y):
-            continue  # near-tie: the partition is not unique to this precision
-        np.testing.assert_array_equal(gs[r], bs[r])
-    assert not grn.any()
 
 
 def test_partition_is_valid_on_tie_data():
@@ -554,3 +648,23 @@ def test_fit_replayed_from_a_hip_graph(n):
                             check=False)[0]
         torch.cuda.synchronize()
         del other
+
+
+@pytest.mark.parametrize("n", [24, 50, 300, 5000, 20000])
+def test_status_belongs_to_the_latest_call(n):
+    """A weight error is reported by iso_status for the call that made it and
+    not for a later clean call on the same workspace (the status words live in
+    the workspace: the call's epoch and its last error), on every first kernel
+    of the fit (one row per lane, two lanes, one workgroup, chunks)."""
+    import torch
+    import weighted_isotonic_regression_row_amd as iso
+    r = workloads.rng(n)
+    y = to_dev(r.standard_normal((4, n)))
+    w_ok = r.random((4, n)) + 0.1
+    w_bad = w_ok.copy()
+    w_bad[2, n // 2] = 0.0
+    ws = iso.workspace(4, n, torch.float64, y.device)
+    for w, want in ((w_bad, iso.ISO_EWEIGHT), (w_ok, iso.ISO_OK), (w_ok, iso.ISO_OK), (w_bad, iso.ISO_EWEIGHT),
+                    (w_ok, iso.ISO_OK)):
+        iso.iso_fit(y, to_dev(w), ws=ws, blocks=False, check=False)
+        assert iso.iso_status(ws) == want

@@ -183,6 +183,36 @@ class Blocks:
         return sb, cb, rn
 
 
+def _check_like(t: torch.Tensor | None, like: torch.Tensor, name: str) -> None:
+    """t must be a contiguous tensor of like's shape (as rows), dtype and device."""
+    if t is None:
+        return
+    t2 = t.unsqueeze(0) if t.dim() == 1 else t
+    if tuple(t2.shape) != tuple(like.shape) or t.dtype != like.dtype or t.device != like.device:
+        raise ValueError(f"{name} must be a tensor of shape {tuple(like.shape)}, dtype {like.dtype} on {like.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _check_ws(ws: torch.Tensor | None, device, name: str = "ws") -> None:
+    """A caller's workspace: a contiguous uint8 tensor on the device of the data (its size is checked by the
+    library, which returns ISO_EINVAL when it is too small)."""
+    if ws is None:
+        return
+    if ws.dtype != torch.uint8 or ws.device != device or not ws.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous uint8 tensor on {device}")
+
+
+def _check_device(t: torch.Tensor, device, name: str) -> None:
+    if t.device != device:
+        raise ValueError(f"{name} must be on {device} (it is on {t.device})")
+
+
+def _require_cuda(t: torch.Tensor, what: str) -> None:
+    if not t.is_cuda:
+        raise ValueError(f"{what} runs on the GPU: its tensors must be device tensors")
+
+
 def _as_rows(t: torch.Tensor) -> torch.Tensor:
     if t.dim() == 1:
         return t.unsqueeze(0)
@@ -200,9 +230,6 @@ def iso_fit(y: torch.Tensor, w: torch.Tensor | None = None, increasing: bool = T
     dtype; w None means unit weights.  check=True synchronises once to raise
     ValueError if a weight was not strictly positive (those rows are NaN).
     """
-    if not y.is_cuda:
-        raise ValueError("iso_fit runs on the GPU: y must be a device tensor")
-    lib = load_library()
     shape = y.shape
     y2 = _as_rows(y)
     if not y2.is_contiguous():
@@ -212,8 +239,11 @@ def iso_fit(y: torch.Tensor, w: torch.Tensor | None = None, increasing: bool = T
     w2 = None
     if w is not None:
         w2 = _as_rows(w)
-        if w2.shape != y2.shape or w2.dtype != y2.dtype or w2.device != y2.device or not w2.is_contiguous():
-            raise ValueError("w must be a contiguous tensor of y's shape, dtype and device")
+        _check_like(w2, y2, "w")
+    _check_like(out, y2, "out")
+    _check_ws(ws, y2.device)
+    _require_cuda(y2, "iso_fit")
+    lib = load_library()
     if out is None:
         out = torch.empty_like(y2)
     if ws is None:
@@ -242,13 +272,17 @@ def iso_fit(y: torch.Tensor, w: torch.Tensor | None = None, increasing: bool = T
 def iso_vjp(grad: torch.Tensor, blocks: Blocks, *, out: torch.Tensor | None = None,
             ws: torch.Tensor | None = None) -> torch.Tensor:
     """grad_y = w_j * sum_{i in B(j), clip inactive} grad_i / sum_{i in B(j)} w_i."""
-    lib = load_library()
     g2 = _as_rows(grad)
     rows, n = blocks.c.rows, blocks.c.n
     if tuple(g2.shape) != (rows, n) or not g2.is_contiguous():
         raise ValueError("grad must be a contiguous tensor of the fit's shape")
     if _dtype_code(g2) != blocks.c.dtype:
         raise ValueError("grad must have the fit's dtype")
+    _check_device(g2, blocks.mem.device, "grad")
+    _check_like(out, g2, "out")
+    _check_ws(ws, g2.device)
+    _require_cuda(g2, "iso_vjp")
+    lib = load_library()
     if out is None:
         out = torch.empty_like(g2)
     if ws is None:
@@ -264,7 +298,6 @@ def iso_vjp_yw(grad: torch.Tensor, blocks: Blocks, y: torch.Tensor, *, want_y: b
                ws: torch.Tensor | None = None):
     """(grad_y or None, grad_w): grad_w = G_B (y_j - mean_B) / W_B over the fit's blocks, where y is the
     tensor the fit was computed from (page "torchisotonic", "Semantics": differentiable in y and in w)."""
-    lib = load_library()
     g2 = _as_rows(grad)
     y2 = _as_rows(y)
     rows, n = blocks.c.rows, blocks.c.n
@@ -273,6 +306,10 @@ def iso_vjp_yw(grad: torch.Tensor, blocks: Blocks, y: torch.Tensor, *, want_y: b
             raise ValueError(f"{name} must be a contiguous tensor of the fit's shape")
         if _dtype_code(t) != blocks.c.dtype:
             raise ValueError(f"{name} must have the fit's dtype")
+        _check_device(t, blocks.mem.device, name)
+    _check_ws(ws, g2.device)
+    _require_cuda(g2, "iso_vjp_yw")
+    lib = load_library()
     gy = torch.empty_like(g2) if want_y else None
     gw = torch.empty_like(g2)
     if ws is None:
@@ -319,15 +356,16 @@ def soft_rank(x: torch.Tensor, eps: float = 1.0, *, out: torch.Tensor | None = N
               ws: torch.Tensor | None = None):
     """Soft ranks of every row of x (first page, Sec. 7.9): the projection of x / eps onto the
     permutahedron of (1..n).  Returns (ranks, state); rows of at most SOFT_RANK_MAX_N elements."""
-    if not x.is_cuda:
-        raise ValueError("soft_rank runs on the GPU: x must be a device tensor")
-    lib = load_library()
     shape = x.shape
     x2 = _as_rows(x)
     if not x2.is_contiguous():
         raise ValueError("x must be contiguous")
     rows, n = x2.shape
     dt = _dtype_code(x2)
+    _check_like(out, x2, "out")
+    _check_ws(ws, x2.device)
+    _require_cuda(x2, "soft_rank")
+    lib = load_library()
     if out is None:
         out = torch.empty_like(x2)
     if ws is None:
@@ -344,13 +382,17 @@ def soft_rank(x: torch.Tensor, eps: float = 1.0, *, out: torch.Tensor | None = N
 def soft_rank_vjp(grad: torch.Tensor, state: SoftRankState, *, out: torch.Tensor | None = None,
                   ws: torch.Tensor | None = None) -> torch.Tensor:
     """Gradient in x of <grad, soft_rank(x, eps)>: P^T (g_s - A g_s) / eps over the fit's blocks."""
-    lib = load_library()
     g2 = _as_rows(grad)
     rows, n = state.c.blocks.rows, state.c.blocks.n
     if tuple(g2.shape) != (rows, n) or not g2.is_contiguous():
         raise ValueError("grad must be a contiguous tensor of the ranks' shape")
     if _dtype_code(g2) != state.c.blocks.dtype:
         raise ValueError("grad must have the ranks' dtype")
+    _check_device(g2, state.mem.device, "grad")
+    _check_like(out, g2, "out")
+    _check_ws(ws, g2.device)
+    _require_cuda(g2, "soft_rank_vjp")
+    lib = load_library()
     if out is None:
         out = torch.empty_like(g2)
     if ws is None:
@@ -371,9 +413,6 @@ def calibration_workspace(rows: int, n: int, dtype: torch.dtype, device) -> torc
 def calibration_fit(scores: torch.Tensor, labels: torch.Tensor, *, ws: torch.Tensor | None = None):
     """Calibration curve of every row (first page, Sec. 7.7; PyPI page, "What it is for"): returns (xs, fit, m),
     the m[r] distinct scores of row r in increasing order and the curve there (entries past m[r] unspecified)."""
-    if not scores.is_cuda:
-        raise ValueError("calibration_fit runs on the GPU: scores must be a device tensor")
-    lib = load_library()
     s2 = _as_rows(scores)
     l2 = _as_rows(labels)
     if s2.shape != l2.shape or s2.dtype != l2.dtype or s2.device != l2.device:
@@ -382,6 +421,9 @@ def calibration_fit(scores: torch.Tensor, labels: torch.Tensor, *, ws: torch.Ten
         raise ValueError("scores and labels must be contiguous")
     rows, n = s2.shape
     dt = _dtype_code(s2)
+    _check_ws(ws, s2.device)
+    _require_cuda(s2, "calibration_fit")
+    lib = load_library()
     xs = torch.empty_like(s2)
     fit = torch.empty_like(s2)
     m = torch.empty(rows, dtype=torch.int32, device=s2.device)
@@ -397,13 +439,20 @@ def calibration_fit(scores: torch.Tensor, labels: torch.Tensor, *, ws: torch.Ten
 def calibrate(q: torch.Tensor, xs: torch.Tensor, fit: torch.Tensor, m: torch.Tensor, *,
               out: torch.Tensor | None = None) -> torch.Tensor:
     """Calibrated values of the queries q [rows, k] on the curves (linear between points, constant beyond)."""
-    lib = load_library()
     shape = q.shape
     q2 = _as_rows(q)
-    if not q2.is_contiguous() or q2.dtype != xs.dtype or xs.shape != fit.shape or q2.shape[0] != xs.shape[0]:
+    if xs.dim() != 2 or not xs.is_contiguous():
+        raise ValueError("xs must be the contiguous [rows, n] points of calibration_fit")
+    _check_like(fit, xs, "fit")
+    if not q2.is_contiguous() or q2.dtype != xs.dtype or q2.shape[0] != xs.shape[0]:
         raise ValueError("q must be contiguous, of the curve's dtype, one row per curve")
-    if m.dtype != torch.int32 or m.numel() != xs.shape[0]:
+    if m.dtype != torch.int32 or m.numel() != xs.shape[0] or not m.is_contiguous():
         raise ValueError("m must be the int32 counts of calibration_fit")
+    for t, name in ((q2, "q"), (m, "m")):
+        _check_device(t, xs.device, name)
+    _check_like(out, q2, "out")
+    _require_cuda(q2, "calibrate")
+    lib = load_library()
     rows, k = q2.shape
     if out is None:
         out = torch.empty_like(q2)

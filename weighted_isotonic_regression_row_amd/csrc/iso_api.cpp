@@ -5,8 +5,6 @@
 #include <string.h>
 
 #include <atomic>
-#include <mutex>
-#include <unordered_map>
 
 #include "../../include/iso.h"
 #include "iso_compose.hpp"
@@ -14,13 +12,12 @@
 
 namespace {
 
-// Every iso_fit call gets a fresh epoch; a data error is recorded on the
-// device as max(status, epoch << 8 | code), so the status word never needs
-// clearing and iso_status only reports errors of the latest call that used
-// the workspace.
+// Every iso_fit call gets a fresh epoch (never 0).  Its first kernel stores
+// the epoch in the workspace's second status word, and a data error is
+// recorded in the first as epoch << 8 | code, so the status words never need
+// clearing and iso_status reports an error only when it belongs to the
+// latest call that used the workspace.  No host state is kept per workspace.
 std::atomic<unsigned long long> g_epoch{0};
-std::mutex g_mu;
-std::unordered_map<const void*, unsigned long long> g_last_epoch;
 
 bool valid_dtype(int d) { return d == ISO_F32 || d == ISO_F64; }
 
@@ -86,10 +83,6 @@ int iso_fit(const void* y, const void* w, int64_t rows, int64_t n, int increasin
     if (overlaps(y) || overlaps(w)) return ISO_EINVAL;
 
     const unsigned long long epoch = ++g_epoch;
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        g_last_epoch[workspace] = epoch;
-    }
     iso::FitLaunch a{};
     a.y = y;
     a.w = w;
@@ -316,17 +309,10 @@ int iso_calibrate(const void* xs, const void* fit, const int32_t* m, int64_t row
 
 int iso_status(const void* workspace, void* stream) {
     if (!workspace) return ISO_EINVAL;
-    unsigned long long last = 0;
-    {
-        std::lock_guard<std::mutex> lk(g_mu);
-        auto it = g_last_epoch.find(workspace);
-        if (it == g_last_epoch.end()) return ISO_OK;
-        last = it->second;
-    }
     if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return ISO_EHIP;
-    unsigned long long word = 0;
-    if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return ISO_EHIP;
-    if ((word >> 8) == last) return -(int)(word & 0xff);
+    unsigned long long word[2] = {0, 0};
+    if (hipMemcpy(word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return ISO_EHIP;
+    if (word[1] != 0 && (word[0] >> 8) == word[1]) return -(int)(word[0] & 0xff);
     return ISO_OK;
 }
 

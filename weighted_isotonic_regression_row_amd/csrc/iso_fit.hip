@@ -50,10 +50,16 @@ struct RowArgs {
 };
 
 // Every writer of one call stores the same value, so a plain exchange is
-// enough; the epoch tells iso_status whether the word belongs to the latest
-// call (the word is never cleared, and may hold garbage before a first error).
+// enough.  status[0] is never cleared (it may hold garbage before a first
+// error); status[1] holds the epoch of the latest call, written by thread 0 of
+// workgroup 0 of the call's first kernel, so after the call iso_status reports
+// status[0]'s code only when its epoch is status[1].
 __device__ inline void report_weight_error(unsigned long long* status, unsigned long long epoch) {
     atomicExch(status, (epoch << 8) | 3ull);
+}
+
+__device__ inline void mark_epoch(unsigned long long* status, unsigned long long epoch) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) status[1] = epoch;
 }
 
 template <typename T>
@@ -152,6 +158,7 @@ __device__ __attribute__((noinline)) void row_exact(const T* y, const T* w, T* o
 template <typename T, int K>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k_row_fit(RowArgs a) {
     extern __shared__ __align__(32) char smem[];
+    mark_epoch(a.status, a.epoch);
     const int64_t row = blockIdx.x;
     const int N = (int)a.n;
     const Tile t = tile_carve(smem, blockDim.x, a.cap, K, N, sizeof(T) == 4);
@@ -252,6 +259,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
 // ---------------------------------------------------------------------------
 template <typename T, int K>
 __global__ __launch_bounds__(256) void k_rows_lane(RowArgs a, int64_t rows) {
+    mark_epoch(a.status, a.epoch);
     const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= rows) return;
     const int N = (int)a.n;
@@ -321,6 +329,7 @@ __global__ __launch_bounds__(64) void k_rows_pair(RowArgs a, int64_t rows) {
     __shared__ double2 Pt[32][2 * K + 1];  // per row: its points 0 .. n, absolute
     const int rl = threadIdx.x >> 1, h = threadIdx.x & 1;
     const int64_t row = (int64_t)blockIdx.x * 32 + rl;
+    mark_epoch(a.status, a.epoch);
     if (row >= rows) return;  // both lanes of a pair leave together
     const int N = (int)a.n;   // K + 1 .. 2K
     const int cnt = h ? N - K : K;
@@ -450,6 +459,7 @@ template <typename T>
 __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
     constexpr int K = kLaneK;
     extern __shared__ __align__(32) char smem[];
+    mark_epoch(a.r.status, a.r.epoch);
     const int64_t bid = blockIdx.x;
     const int64_t row = bid / a.m, c = bid % a.m;
     const int64_t e0 = c * kChunk;
