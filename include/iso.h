@@ -48,6 +48,8 @@ extern "C" {
 #define ISO_EINVAL (-1)  /* bad argument, detected on the host; nothing queued   */
 #define ISO_EHIP (-2)    /* a HIP launch or runtime call failed                   */
 #define ISO_EWEIGHT (-3) /* a finite weight <= 0 in some row (that row is NaN)    */
+#define ISO_ETOOBIG (-4) /* iso_fit_noalloc: the problem needs more workspace than
+                            the library's static scratch holds; nothing queued   */
 
 /*
  * Partition handle for the backward pass: which elements start a pooled block
@@ -121,6 +123,34 @@ size_t iso_blocks_bytes(int64_t rows, int64_t n);
 int iso_fit(const void* y_dev, const void* w_dev, int64_t rows, int64_t n, int increasing,
             double y_min, double y_max, int dtype, void* fit_dev, iso_blocks* blocks_out,
             void* blocks_mem_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * iso_fit without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  It runs exactly iso_fit's checks and kernels, with
+ * the workspace in a static array of ISO_NOALLOC_SCRATCH_BYTES bytes that the
+ * library holds on each GPU it runs on until the process ends.  It calls no
+ * allocating routine.
+ *
+ *   Arguments as for iso_fit; the caller still passes y, w, fit and, when it
+ *   wants the partition, blocks_out and blocks_mem_dev.
+ *   Returns ISO_ETOOBIG, queuing nothing, when iso_workspace_bytes(rows, n,
+ *   dtype) exceeds ISO_NOALLOC_SCRATCH_BYTES (128 MiB: every single-workgroup
+ *   batch up to 1000 x 6144 elements, and rows of up to about 1.2e7 elements).
+ *
+ * Every call on one GPU shares that GPU's array, and the array keeps the last
+ * call's contents: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller.  Nothing needs to start
+ * at zero (each call writes what it reads).  iso_status cannot read this
+ * entry point's data errors (the caller has no workspace pointer); a row with
+ * a weight <= 0 still comes back NaN, with its row-NaN flag set in the
+ * partition handle.
+ */
+#define ISO_NOALLOC_SCRATCH_BYTES (128ull << 20)
+
+int iso_fit_noalloc(const void* y_dev, const void* w_dev, int64_t rows, int64_t n, int increasing,
+                    double y_min, double y_max, int dtype, void* fit_dev, iso_blocks* blocks_out,
+                    void* blocks_mem_dev, void* stream);
 
 /*
  * Vector-Jacobian product of the fit with respect to y (first page,
@@ -286,8 +316,8 @@ int iso_status(const void* workspace_dev, void* stream);
 
 /*
  * Static, human-readable text for a return code of this library (ISO_OK,
- * ISO_EINVAL, ISO_EHIP, ISO_EWEIGHT: the last is the PyPI page's "Semantics"
- * rule that weights be strictly positive); "unknown error" for any other.
+ * ISO_EINVAL, ISO_EHIP, ISO_EWEIGHT: the PyPI page's "Semantics" rule that
+ * weights be strictly positive, ISO_ETOOBIG); "unknown error" for any other.
  */
 const char* iso_strerror(int code);
 

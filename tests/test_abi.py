@@ -36,7 +36,7 @@ def lib():
 
 def test_header_declares_the_boundary():
     fns = declared_functions()
-    assert fns == sorted(["iso_blocks_bytes", "iso_fit", "iso_status", "iso_strerror", "iso_vjp", "iso_vjp_yw",
+    assert fns == sorted(["iso_blocks_bytes", "iso_fit", "iso_fit_noalloc", "iso_status", "iso_strerror", "iso_vjp", "iso_vjp_yw",
                           "iso_workspace_bytes", "iso_soft_rank", "iso_soft_rank_vjp", "iso_soft_rank_state_bytes",
                           "iso_soft_rank_workspace_bytes", "iso_calibration_workspace_bytes", "iso_calibration_fit",
                           "iso_calibrate"])
@@ -74,6 +74,7 @@ def test_sizes(lib):
 def test_strerror(lib):
     assert lib.iso_strerror(0) == b"success"
     assert b"positive" in lib.iso_strerror(-3)
+    assert b"scratch" in lib.iso_strerror(-4)
     assert lib.iso_strerror(-99) == b"unknown error"
 
 
@@ -246,3 +247,20 @@ def test_binding_refuses_host_tensors():
     import weighted_isotonic_regression_row_amd as iso
     with pytest.raises(ValueError):
         iso.iso_fit(torch.zeros(3, 4))
+
+
+def test_noalloc_refuses_problems_past_its_scratch_on_host(lib):
+    """iso_fit_noalloc checks the problem's workspace against its static scratch
+    before any HIP call: too large gives ISO_ETOOBIG, bad sizes ISO_EINVAL, an
+    empty problem fills the handle and returns ISO_OK."""
+    import weighted_isotonic_regression_row_amd as iso
+    f = lib.iso_fit_noalloc
+    assert f(256, None, 32, 1 << 22, 1, -math.inf, math.inf, 1, 512, None, None, None) == iso.ISO_ETOOBIG
+    assert f(256, None, 2000, 5000, 1, -math.inf, math.inf, 0, 512, None, None, None) == iso.ISO_ETOOBIG
+    assert f(256, None, -1, 5, 1, -math.inf, math.inf, 0, 512, None, None, None) == iso.ISO_EINVAL
+    assert f(256, None, 2, 5, 1, -math.inf, math.inf, 9, 512, None, None, None) == iso.ISO_EINVAL
+    bc = iso.IsoBlocksC()
+    assert f(None, None, 0, 5, 1, -math.inf, math.inf, 0, None, ctypes.byref(bc), 8192, None) == iso.ISO_OK
+    assert bc.valid == 1 and bc.rows == 0
+    assert lib.iso_workspace_bytes(1000, 6144, 0) <= iso.NOALLOC_SCRATCH_BYTES
+    assert lib.iso_workspace_bytes(1, 12_000_000, 1) <= iso.NOALLOC_SCRATCH_BYTES

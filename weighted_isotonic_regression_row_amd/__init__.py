@@ -40,8 +40,10 @@ ISO_OK = 0
 ISO_EINVAL = -1
 ISO_EHIP = -2
 ISO_EWEIGHT = -3
+ISO_ETOOBIG = -4
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
-SYMBOLS = ("iso_workspace_bytes", "iso_blocks_bytes", "iso_fit", "iso_vjp", "iso_vjp_yw", "iso_soft_rank_state_bytes",
+SYMBOLS = ("iso_workspace_bytes", "iso_blocks_bytes", "iso_fit", "iso_fit_noalloc", "iso_vjp", "iso_vjp_yw", "iso_soft_rank_state_bytes",
            "iso_soft_rank_workspace_bytes", "iso_soft_rank", "iso_soft_rank_vjp", "iso_calibration_workspace_bytes",
            "iso_calibration_fit", "iso_calibrate", "iso_status", "iso_strerror")
 SOFT_RANK_MAX_N = 8192
@@ -101,6 +103,9 @@ def load_library(path: str | None = None):
     lib.iso_fit.restype = c_int
     lib.iso_fit.argtypes = [vp, vp, i64, i64, c_int, c_double, c_double, c_int, vp,
                             ctypes.POINTER(IsoBlocksC), vp, vp, c_size, vp]
+    lib.iso_fit_noalloc.restype = c_int
+    lib.iso_fit_noalloc.argtypes = [vp, vp, i64, i64, c_int, c_double, c_double, c_int, vp,
+                                    ctypes.POINTER(IsoBlocksC), vp, vp]
     lib.iso_vjp.restype = c_int
     lib.iso_vjp.argtypes = [vp, ctypes.POINTER(IsoBlocksC), vp, vp, c_size, vp]
     lib.iso_vjp_yw.restype = c_int
@@ -267,6 +272,42 @@ def iso_fit(y: torch.Tensor, w: torch.Tensor | None = None, increasing: bool = T
         if st != ISO_OK:
             raise IsoError(st, "iso_status")
     return out.view(shape), (Blocks(bc, mem, w2, shape) if blocks else None)
+
+
+def iso_fit_noalloc(y: torch.Tensor, w: torch.Tensor | None = None, increasing: bool = True,
+                    y_min: float | None = None, y_max: float | None = None, *, out: torch.Tensor,
+                    blocks_mem: torch.Tensor | None = None):
+    """iso_fit with the library's static scratch as its workspace (include/iso.h, iso_fit_noalloc): the caller
+    passes the output (and, for the partition, blocks_mem of iso_blocks_bytes(rows, n) bytes) and nothing is
+    allocated.  Returns (out, Blocks or None).  Raises IsoError(ISO_ETOOBIG) for problems whose workspace
+    exceeds NOALLOC_SCRATCH_BYTES.  Calls on one GPU share the scratch: overlapping calls race."""
+    shape = y.shape
+    y2 = _as_rows(y)
+    if not y2.is_contiguous():
+        raise ValueError("y must be contiguous")
+    rows, n = y2.shape
+    dt = _dtype_code(y2)
+    w2 = None
+    if w is not None:
+        w2 = _as_rows(w)
+        _check_like(w2, y2, "w")
+    _check_like(out, y2, "out")
+    if blocks_mem is not None:
+        _check_ws(blocks_mem, y2.device, "blocks_mem")
+    _require_cuda(y2, "iso_fit_noalloc")
+    lib = load_library()
+    bc = IsoBlocksC()
+    if blocks_mem is not None and blocks_mem.numel() < iso_blocks_bytes(rows, n):
+        raise ValueError("blocks_mem holds fewer than iso_blocks_bytes(rows, n) bytes")
+    lo = -math.inf if y_min is None else float(y_min)
+    hi = math.inf if y_max is None else float(y_max)
+    code = lib.iso_fit_noalloc(y2.data_ptr(), None if w2 is None else w2.data_ptr(), rows, n,
+                               1 if increasing else 0, lo, hi, dt, out.data_ptr(),
+                               ctypes.byref(bc) if blocks_mem is not None else None,
+                               None if blocks_mem is None else blocks_mem.data_ptr(), _stream_ptr(y2.device))
+    if code != ISO_OK:
+        raise IsoError(code, "iso_fit_noalloc")
+    return out.view(shape), (Blocks(bc, blocks_mem, w2, shape) if blocks_mem is not None else None)
 
 
 def iso_vjp(grad: torch.Tensor, blocks: Blocks, *, out: torch.Tensor | None = None,
@@ -467,7 +508,7 @@ def iso_status(ws: torch.Tensor) -> int:
     return int(load_library().iso_status(ws.data_ptr(), _stream_ptr(ws.device)))
 
 
-__all__ = ["iso_fit", "iso_vjp", "iso_vjp_yw", "soft_rank", "soft_rank_vjp", "SoftRankState", "soft_rank_workspace",
+__all__ = ["iso_fit", "iso_fit_noalloc", "iso_vjp", "iso_vjp_yw", "soft_rank", "soft_rank_vjp", "SoftRankState", "soft_rank_workspace",
            "calibration_fit", "calibrate", "calibration_workspace",
            "SOFT_RANK_MAX_N", "iso_status", "iso_workspace_bytes", "iso_blocks_bytes", "workspace",
            "Blocks", "IsoError", "load_library", "SYMBOLS"]

@@ -326,6 +326,8 @@ const char* iso_strerror(int code) {
             return "HIP runtime error";
         case ISO_EWEIGHT:
             return "a weight is not strictly positive";
+        case ISO_ETOOBIG:
+            return "the problem needs more workspace than iso_fit_noalloc's static scratch holds";
         default:
             return "unknown error";
     }
