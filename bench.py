@@ -1,34 +1,44 @@
 """Benchmark of the batched weighted isotonic fit on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload batch|dense|soft_rank|calibration|all]
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+                    [--workload batch|cfg1|cfg3|cfg4|dense|all_vertices|soft_rank|calibration|fits|all]
                     [--no-cpu] [--copy-probe] [--cpu-seconds S]
 
 A step is one whole fit (every kernel of the path) over one batch of
-synthetic input already resident in HBM (the backward products of the batch
-are timed separately and reported in "backward"):
+synthetic input already resident in HBM.  Every leg reports elements/s, the
+fraction of HBM peak its algorithmic bytes reach, and the CPU oracle on the
+host's cores on a bounded sample of the same input:
 
   batch (the headline line; `value` is its elements/s):
          1000 rows x 5000 float32, y ~ N(0,1), w ~ U(0.1, 1.1), non-increasing,
-         clipped to [0, 1]; one launch of k_row_fit;
+         clipped to [0, 1]; one launch of k_row_fit; both backward products
+         are timed as well ("backward");
+  cfg1:  1 row x 4096 float64, y ~ N(0,1), unit weights, increasing;
+  cfg3:  4096 x 512 float32, y_i = s_i - i/512 (s sorted descending N(0,1)),
+         unit weights, increasing: the fit with its blocks and the product in y
+         of an N(0,1) upstream gradient, one step = both;
+  cfg4:  1 row x 6.5e6 float64, calibration-shaped (sorted scores, counts as
+         weights, rational labels), increasing, clipped to [0, 1];
   dense: 32 rows x 2^22 float64, y_i = i/n with 1% of positions pushed down by
-         |N(0, 0.01)|, w ~ U(0.5, 1.5), increasing; k_chunk_hull, k_merge_sub,
-         k_merge_top, k_fixup (reported in "dense");
+         |N(0, 0.01)|, w ~ U(0.5, 1.5), increasing (k_chunk_hull, k_merge_sub,
+         k_merge_top, k_fixup);
+  all_vertices: 32 rows x 2^22 float64 increasing data (every point a hull
+         vertex, the first page's Sec. 7.5 regime), w ~ U(0.1, 1.1);
   soft rank: 4096 x 512 float32 standard normal scores, forward and backward
-         of the first page's Sec. 7.9 composition at eps = 1 and 1/n
-         (reported in "soft_rank");
+         of the first page's Sec. 7.9 composition at eps = 1 and 1/n;
   calibration: one curve over 6.5e6 float64 scores (the first page's Sec. 7.7
-         day), sort, pooling and fit, then 100001 queries (reported in
-         "calibration").
+         day), sort, pooling and fit, then 100001 queries.
 
 Prints ONE JSON line.  Algorithmic bytes are y and w read once and the fit
-written once (12 B/element for the batch, 24 B/element for the dense rows);
-"% of HBM peak" divides them by the measured time and 8 TB/s.  The roofline
-object times the batch's kernel with HIP events on the stream it is launched
-on.  Its `traffic` is the HBM bytes per launch that rocprofv3 counted
-(FETCH_SIZE and WRITE_SIZE, scaled against a plain copy of known size), read
-from the committed summary under profiles/ and reported only while the kernel
-sources are the ones that summary was taken from.  The CPU baseline is the
-float64 oracle on the host cores, on a bounded sample.
+written once (12 B/element for the batch, 16 for cfg1, 16 for cfg3's fit and
+product, 24 for the float64 weighted rows); "% of HBM peak" divides them by
+the measured time and 8 TB/s.  The roofline object times the batch's kernel
+with HIP events on the stream it is launched on.  Its `traffic` is the HBM
+bytes per launch that rocprofv3 counted (FETCH_SIZE and WRITE_SIZE, scaled
+against a plain copy of known size), read from the committed summary under
+profiles/ and reported only while the kernel sources are the ones that summary
+was taken from.  The CPU baseline is the float64 oracle on the host cores, on
+a bounded sample.
 """
 from __future__ import annotations
 
@@ -49,6 +59,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 METRIC = "fit elements/s and % of HBM peak, 1000×5000 f32 and 32×2^22 f64 dense"
 TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "k_row_fit_1000x5000_f32.md")
+DENSE_SUMMARY = os.path.join(ROOT, "profiles", "dense_32x4194304_f64.md")
 CSRC = os.path.join(ROOT, "weighted_isotonic_regression_row_amd", "csrc")
 
 
@@ -78,11 +89,12 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def committed_traffic():
-    """HBM bytes per launch of k_row_fit from the committed counter summary, if
-    it was taken from the current sources; else None."""
+def committed_traffic(path=TRAFFIC_SUMMARY):
+    """HBM bytes per fit call from a committed counter summary (the batch's one
+    launch of k_row_fit, or the dense fit's four kernels summed), if it was
+    taken from the current sources; else None."""
     try:
-        text = open(TRAFFIC_SUMMARY).read()
+        text = open(path).read()
     except OSError:
         return None
     m_hash = re.search(r"source hash:\s*([0-9a-f]+)", text)
@@ -96,7 +108,37 @@ def make_inputs(which):
     import workloads
     if which == "batch":
         return workloads.cfg2_batch_noise()
+    if which == "cfg1":
+        return workloads.cfg1_single_row()
+    if which == "cfg3":
+        return workloads.cfg3_soft_rank()
+    if which == "cfg4":
+        return workloads.cfg4_calibration()
+    if which == "all_vertices":
+        wl = workloads.family("increasing", 32, 1 << 22, seed=55, dtype=np.float64, weights="uniform")
+        wl.name = "all_vertices_32x2^22_f64"
+        return wl
     return workloads.cfg5_dense()
+
+
+def host_cores() -> int:
+    """Threads the oracle may use: the CPUs this process may run on (at most 16,
+    a GPU's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def time_gpu(wl, steps, warmup):
@@ -169,6 +211,80 @@ def time_backward(wl, steps):
     return {"vjp_ms": ms_y, "vjp_algorithmic_bytes": by, "vjp_hbm_frac": by / (ms_y * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "vjp_yw_ms": ms_yw, "vjp_yw_algorithmic_bytes": byw,
             "vjp_yw_hbm_frac": byw / (ms_yw * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+
+def time_fit_and_vjp(wl, steps, warmup):
+    """One step = the fit with its blocks and the product in y of the upstream
+    gradient wl.g over them.  Returns (ms per step from the wall clock, mean
+    event-timed ms of the fit call, of the product call)."""
+    import torch
+    import weighted_isotonic_regression_row_amd as iso
+    dev = torch.device("cuda:0")
+    y = torch.from_numpy(wl.y).to(dev)
+    w = None if wl.w is None else torch.from_numpy(wl.w).to(dev)
+    g = torch.from_numpy(wl.g).to(dev)
+    out = torch.empty_like(y)
+    gy = torch.empty_like(y)
+    ws = iso.workspace(wl.rows, wl.n, y.dtype, dev)
+    _, blocks = iso.iso_fit(y, w, wl.increasing, wl.y_min, wl.y_max, out=out, ws=ws, check=True)
+
+    def step():
+        _, b = iso.iso_fit(y, w, wl.increasing, wl.y_min, wl.y_max, out=out, ws=ws, check=False)
+        iso.iso_vjp(g, b, out=gy, ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stream = torch.cuda.current_stream(dev)
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(3 * steps)]
+    for k in range(steps):
+        e[3 * k].record(stream)
+        _, b = iso.iso_fit(y, w, wl.increasing, wl.y_min, wl.y_max, out=out, ws=ws, check=False)
+        e[3 * k + 1].record(stream)
+        iso.iso_vjp(g, b, out=gy, ws=ws)
+        e[3 * k + 2].record(stream)
+    torch.cuda.synchronize()
+    fit_ms = float(np.mean([e[3 * k].elapsed_time(e[3 * k + 1]) for k in range(steps)]))
+    vjp_ms = float(np.mean([e[3 * k + 1].elapsed_time(e[3 * k + 2]) for k in range(steps)]))
+    return (t1 - t0) * 1e3 / steps, fit_ms, vjp_ms
+
+
+FIT_LEGS = {
+    # name: (description, bytes per element, steps cap, cpu rows cap)
+    "cfg1": ("1 row x 4096 float64, y~N(0,1), unit weights, increasing, no clipping", 16, None, None),
+    "cfg4": ("1 row x 6.5e6 float64, sorted N(0,1) scores, counts 1+Poisson(2) as weights, "
+             "y = Binomial(count, sigmoid(1.5 s - 3))/count, increasing, clipped to [0,1]", 24, 20, None),
+    "dense": ("32 rows x 2^22 float64, y_i = i/n with 1% pushed down by |N(0,0.01)|, w~U(0.5,1.5), increasing",
+              24, 10, None),
+    "all_vertices": ("32 rows x 2^22 float64, y_i = i/n (every point a hull vertex), w~U(0.1,1.1), increasing",
+                     24, 10, None),
+}
+
+
+def fit_leg(name, steps, warmup, cpu_seconds, no_cpu):
+    """A fit-only leg: wall-clock ms per step, event-timed fit calls, elements/s,
+    the fraction of HBM peak, and the oracle on the host on the same input."""
+    desc, bpe, cap, cpu_rows = FIT_LEGS[name]
+    wl = make_inputs(name)
+    log(f"{name}: {wl.name} {wl.y.shape}")
+    k = steps if cap is None else max(1, min(steps, cap))
+    ms, kmean, kmed = time_gpu(wl, k, min(warmup, 3) if cap else warmup)
+    elems = wl.rows * wl.n
+    algo = elems * bpe
+    leg = {"workload": desc, "rows": wl.rows, "n": wl.n, "steps": k, "ms_per_step": ms,
+           "fit_ms_events_mean": kmean, "fit_ms_events_median": kmed,
+           "elements_per_s": elems / (ms * 1e-3), "algorithmic_bytes": algo, "bytes_per_element": bpe,
+           "hbm_frac_end_to_end": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           "hbm_frac_events": algo / (kmean * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if not no_cpu:
+        log(f"cpu baseline ({name}) ...")
+        leg["cpu_baseline"] = cpu_baseline(wl, seconds=cpu_seconds, max_rows=cpu_rows)
+    return leg
 
 
 def time_soft_rank(steps, rows=4096, n=512):
@@ -270,11 +386,12 @@ def copy_probe(nbytes=256 << 20, reps=20):
 
 
 def cpu_baseline(wl, seconds=10.0, max_rows=None):
-    """The oracle as it stands, timed on the host cores on a bounded sample."""
+    """The oracle as it stands, timed on the host cores on a bounded sample (rows
+    split over the threads; one row is sequential in pool adjacent violators)."""
     import oracle
-    threads = min(os.cpu_count() or 1, 16)
+    threads = host_cores()
     rows = wl.rows if max_rows is None else min(wl.rows, max_rows)
-    threads = min(threads, rows)  # rows are split over threads; one row is sequential
+    threads = min(threads, rows)
     y = wl.y[:rows].astype(np.float64)
     w = None if wl.w is None else wl.w[:rows].astype(np.float64)
     elems = 0
@@ -288,6 +405,7 @@ def cpu_baseline(wl, seconds=10.0, max_rows=None):
             break
     dt = time.perf_counter() - t0
     return {"value": elems / dt, "unit": "elements/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{rows} of {wl.rows} rows x {wl.n}, float64 pool adjacent violators, "
                       f"{threads} threads, {reps} repetitions in {dt:.1f} s"}
 
@@ -297,10 +415,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["batch", "dense", "soft_rank", "calibration", "all", "both"], default="all")
+    ap.add_argument("--workload", choices=["batch", "cfg1", "cfg3", "cfg4", "dense", "all_vertices", "soft_rank",
+                                           "calibration", "fits", "all", "both"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true", help="time a plain device copy (also done by default runs)")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle time for the batch; the other legs take half of it")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only (--gpus 1); rows are independent and would "
@@ -318,7 +438,7 @@ def main():
            "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f64", "data": "synthetic"}
 
-    if args.workload in ("batch", "all", "both"):
+    if args.workload in ("batch", "all", "both", "fits"):
         wl = make_inputs("batch")
         log(f"batch: {wl.name} {wl.y.shape}")
         ms, kmean, kmed = time_gpu(wl, args.steps, args.warmup)
@@ -345,27 +465,49 @@ def main():
             rec["cpu_baseline"] = cpu_baseline(wl, seconds=args.cpu_seconds)
         del wl
 
-    if args.workload in ("dense", "all", "both"):
-        wl = make_inputs("dense")
-        log(f"dense: {wl.name} {wl.y.shape}")
-        steps = max(1, min(args.steps, 10))
-        ms, kmean, kmed = time_gpu(wl, steps, min(args.warmup, 2))
+    fits = ("fits", "all")
+    if args.workload in ("cfg1",) + fits:
+        rec["cfg1"] = fit_leg("cfg1", args.steps, args.warmup, args.cpu_seconds / 2, args.no_cpu)
+
+    if args.workload in ("cfg3",) + fits:
+        wl = make_inputs("cfg3")
+        log(f"cfg3: {wl.name} {wl.y.shape}")
+        ms, fit_ms, vjp_ms = time_fit_and_vjp(wl, args.steps, args.warmup)
         elems = wl.rows * wl.n
-        algo = elems * 24
-        dense = {"workload": "32 rows x 2^22 float64, y_i = i/n with 1% pushed down by |N(0,0.01)|, "
-                             "w~U(0.5,1.5), increasing",
-                 "steps": steps, "ms_per_step": ms, "fit_ms_events_mean": kmean,
-                 "elements_per_s": elems / (ms * 1e-3), "algorithmic_bytes": algo,
-                 "hbm_frac_end_to_end": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        algo = elems * 16  # y read, fit written; g read, grad_y written
+        leg = {"workload": "4096 rows x 512 float32, y_i = s_i - i/512 (s sorted descending N(0,1)), unit weights, "
+                           "increasing; the fit with its blocks and the product in y of an N(0,1) gradient",
+               "rows": wl.rows, "n": wl.n, "steps": args.steps, "ms_per_step": ms,
+               "fit_ms_events_mean": fit_ms, "vjp_ms_events_mean": vjp_ms,
+               "elements_per_s": elems / (ms * 1e-3), "algorithmic_bytes": algo, "bytes_per_element": 16,
+               "hbm_frac_end_to_end": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+               "hbm_frac_events": algo / ((fit_ms + vjp_ms) * 1e-3) / 1e9 / HBM_PEAK_GBS}
         if not args.no_cpu:
-            log("cpu baseline (dense, 2 rows) ...")
-            dense["cpu_baseline"] = cpu_baseline(wl, seconds=min(args.cpu_seconds, 10.0), max_rows=2)
+            log("cpu baseline (cfg3, fit only) ...")
+            leg["cpu_baseline"] = cpu_baseline(wl, seconds=args.cpu_seconds / 2)
+            leg["cpu_baseline"]["sample"] += " (the fit; the oracle's product is not timed)"
+        rec["cfg3"] = leg
+        del wl
+
+    if args.workload in ("cfg4",) + fits:
+        rec["cfg4"] = fit_leg("cfg4", args.steps, args.warmup, args.cpu_seconds / 2, args.no_cpu)
+
+    if args.workload in ("dense", "both") + fits:
+        dense = fit_leg("dense", args.steps, args.warmup, args.cpu_seconds / 2, args.no_cpu)
+        ach = dense["algorithmic_bytes"] / (dense["fit_ms_events_mean"] * 1e-3) / 1e9
+        dense["roofline"] = {"bound": "hbm", "timed": "the whole fit call (k_chunk_hull, k_merge_sub, k_merge_top, "
+                                                      "k_fixup), events on the launch stream",
+                             "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+                             "traffic": committed_traffic(DENSE_SUMMARY), "bytes_per_element": 24,
+                             "elements_per_launch": dense["rows"] * dense["n"]}
         rec["dense"] = dense
         if rec["value"] is None:
             rec["value"] = dense["elements_per_s"]
-            rec["ms_per_step"] = ms
+            rec["ms_per_step"] = dense["ms_per_step"]
             rec["config"] = {"workload": dense["workload"]}
-        del wl
+
+    if args.workload in ("all_vertices",) + fits:
+        rec["all_vertices"] = fit_leg("all_vertices", args.steps, args.warmup, args.cpu_seconds / 2, args.no_cpu)
 
     if args.workload in ("soft_rank", "all"):
         log("soft rank 4096 x 512 ...")
