@@ -95,6 +95,13 @@ __device__ __forceinline__ double readlane_d(double v, int lane) {
     const unsigned hi = (unsigned)__builtin_amdgcn_readlane((int)(unsigned)(b >> 32), lane);
     return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
 }
+// A value every lane of the wave holds alike, moved to scalar registers.
+__device__ __forceinline__ double uniform_d(double v) {
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);
+    const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)b);
+    const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(b >> 32));
+    return __longlong_as_double((long long)(((unsigned long long)hi << 32) | lo));
+}
 // Least value over the wave (no NaN), the same in every lane: the scan's
 // steps with min, whose result gathers in lane 63.
 __device__ __forceinline__ double wave_min(double v) {

@@ -80,8 +80,9 @@ __device__ inline void wg_write_nan(int64_t N, T* out, uint64_t* sbits, uint64_t
 // in xs, ys.
 // With stage set, the inputs pass through the still unused vertex list (each
 // wave K * 64 elements of it).  With nxp, the masks are those of the hulls of
-// the lanes' parts (a superset of the lane hulls' vertices, gw_parts).
-template <typename T, int K>
+// the lanes' parts (a superset of the lane hulls' vertices, gw_parts); without
+// HULL the masks are 0 (the caller chooses candidates, lane_chords).
+template <typename T, int K, bool HULL = true>
 __device__ inline int tile_build(const Tile& t, const T* y, const T* w, int increasing, uint64_t& mask,
                                  double (&xs)[K], double (&ys)[K], int& nvert, bool stage = false,
                                  uint64_t (*nxp)[3] = nullptr) {
@@ -92,10 +93,10 @@ __device__ inline int tile_build(const Tile& t, const T* y, const T* w, int incr
     if (stage) {
         const int e0 = (l & ~(kWave - 1)) * K;  // the wave's first element
         T* st = (T*)t.VXY + e0;
-        mask = lane_hull<T, K>(y + e0, w ? w + e0 : nullptr, cnt, !increasing, xs, ys, f, st,
+        mask = lane_hull<T, K, HULL>(y + e0, w ? w + e0 : nullptr, cnt, !increasing, xs, ys, f, st,
                                min(max(t.N - e0, 0), K * kWave), nxp);
     } else {
-        mask = lane_hull<T, K>(y + (int64_t)l * K, w ? w + (int64_t)l * K : nullptr, cnt, !increasing, xs, ys, f,
+        mask = lane_hull<T, K, HULL>(y + (int64_t)l * K, w ? w + (int64_t)l * K : nullptr, cnt, !increasing, xs, ys, f,
                                nullptr, 0, nxp);
     }
     nvert = tile_lane_starts<!ABS>(t, make_double2(xs[K - 1], ys[K - 1]), f, __popcll(mask));
@@ -171,9 +172,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     double xs[K], ys[K];
     int nvert;
     uint64_t nxp[3];
-    constexpr bool HALVES = K >= 12;  // rows of several waves
-    const int flag = tile_build<T, K>(t, y, w, a.increasing, mask, xs, ys, nvert, a.stage != 0,
-                                      HALVES ? &nxp : nullptr);
+    constexpr bool HALVES = K >= 12;                  // rows of several waves
+    constexpr bool CHORDS = HALVES && sizeof(T) == 4;  // float32 ones take chord candidates (lane_chords)
+    const int flag = tile_build<T, K, !CHORDS>(t, y, w, a.increasing, mask, xs, ys, nvert, a.stage != 0,
+                                               (HALVES && !CHORDS) ? &nxp : nullptr);
     if (flag) {
         wg_write_nan<T>(N, out, sb, cb);
         if (threadIdx.x == 0) {
@@ -193,10 +195,32 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
         // vertices; every condition here is uniform.
         bool done = false;
         if constexpr (ABS) {
-            mask = chord_filter<K>(t, mask, xs, ys);
+            // candidates: the points not above the hull of the lane ends
+            // (found by QuickHull, one lane end per thread), then the exact
+            // hull of the candidates by QuickHull again, one per thread; each
+            // step falls back (to chords inside the lanes, to the wrap) when
+            // its LDS room or its thread count is short.  Conditions are uniform.
+            const int cnt = min(max(N - (int)threadIdx.x * K, 0), K);
+            const int used = (N + K - 1) / K;
+            if (24 * (used + 1) <= 16 * (a.cap + 1)) {
+                int ca, cb;
+                (void)tile_quickhull((const double2*)t.LS, used, (unsigned long long*)t.VXY, 0.0, ca, cb);
+                mask = lane_coarse_filter<K>(t, xs, ys, cnt, ca, cb);
+            } else {
+                mask = lane_chords<K>(t, xs, ys, cnt);
+            }
             nvert = tile_count(t, mask);
+            const int m = nvert - 1;
+            if (m <= (int)blockDim.x && 40 * (m + 1) <= 16 * (a.cap + 1)) {
+                tile_compact<K, ABS>(t, mask, xs, ys);
+                int qa, qb;
+                const bool vert = tile_quickhull(t.VXY, m, (unsigned long long*)(t.VXY + m + 1), 0x1p-48, qa, qb);
+                tile_hull_to_front(t, m, vert);
+                tile_masks_short<K>(t, mask);
+                done = true;
+            }
         }
-        if (5 * nvert <= 3 * N + 5 && nvert <= a.cap + 1) {
+        if (!done && 5 * nvert <= 3 * N + 5 && nvert <= a.cap + 1) {
             tile_compact<K, ABS>(t, mask, xs, ys);
             if (tile_wrap<K, ABS>(t)) {
                 tile_masks_short<K>(t, mask);

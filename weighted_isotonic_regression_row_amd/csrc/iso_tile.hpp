@@ -301,8 +301,9 @@ __device__ __forceinline__ void lane_load_staged(const T* __restrict__ base, int
 // are compared with compile-time indices: no divergence and no indexed access
 // to the lane's registers.
 // With nxp, the hulls of the lane's two halves instead: a superset of the
-// lane hull's vertices (gw_parts).
-template <typename T, int K>
+// lane hull's vertices (gw_parts).  Without HULL only the points are formed
+// (mask 0): the caller picks its candidates itself (lane_chords).
+template <typename T, int K, bool HULL = true>
 __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restrict__ w, int cnt, int negate,
                                      double (&xs)[K], double (&ys)[K], int& f, T* stage = nullptr,
                                      int avail = 0, uint64_t (*nxp)[3] = nullptr) {
@@ -396,6 +397,7 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
         }
     }
     checks();
+    if constexpr (!HULL) return 0ull;
     if (nxp) return gw_parts<K, 2>(xs, ys, cnt, *nxp);
     return lane_gift_wrap<K>(xs, ys, cnt);
 }
@@ -492,6 +494,242 @@ __device__ inline uint64_t chord_filter(const Tile& t, uint64_t mask, const doub
         keep |= (d <= tol ? 1ull : 0ull) << b;
     }
     return mask & keep;
+}
+
+// Candidates of a noisy float32 tile without lane hulls: the lane's points
+// that no chord between two points of the tile lies clearly below.  The lower
+// hull lies on or below every chord between two of its points, so a point
+// strictly above the chord of two points on either side of it is not a
+// vertex; the chords used, all between points of the tile, are
+//   - the lane's: from its start (local origin) to its last point E, and,
+//     split at the interior point v lowest under it, from the start to v and
+//     from v to E (any point v would do; the lowest removes the most: one
+//     level of QuickHull inside the lane);
+//   - the wave's: from the start of its first lane to the end of its last;
+//   - the tile's: from point 0 to point N.
+// A point is dropped only when its cross product with a chord exceeds a
+// bound on the rounding of that product and of the float64 coordinates the
+// later steps use (absolute, the lane start plus the local point), so every
+// vertex of the tile's hull in those coordinates is kept.  About 10% of the
+// points of N(0,1) noise remain (half hulls below the tile's chord keep 14%),
+// at about a twentieth of the comparisons.  Needs the lane starts written
+// (plain pairs, ls2).  Returns the lane's mask (bit b <-> local point b+1).
+template <int K>
+__device__ inline uint64_t lane_chords(const Tile& t, const double (&xs)[K], const double (&ys)[K], int cnt) {
+    if (cnt <= 0) return 0ull;
+    const int l = threadIdx.x, wid = l >> 6;
+    const double2* LS = (const double2*)t.LS;
+    const double2 st = LS[l];
+    // the tile's and the wave's chords are the same in every lane of a wave
+    const int wend = min((wid + 1) * kWave, t.nl);
+    const double2 wa = LS[wid * kWave], wb = LS[wend], tt = LS[t.nl];
+    const double2 tot = make_double2(uniform_d(tt.x), uniform_d(tt.y));
+    // local points past cnt repeat the lane's last one (their weights are 0)
+    const double ex = xs[K - 1], ey = ys[K - 1];
+    double ymax = 0.0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) ymax = fmax(ymax, fabs(ys[j]));
+    // rounding bound of every cross product below, in local units: the
+    // coordinates the wrap compares carry errors of an ulp of their absolute
+    // size (st + local), times the lane's extents; the local products' own
+    // rounding is smaller than the slack factor covers
+    const double xa = st.x + ex, ya = fabs(st.y) + ymax;
+    const double tol = 0x1p-44 * (xa * ymax + ya * ex + ex * ymax);
+    // the wave's and the tile's chords on absolute points st + (xs, ys): the
+    // cross product splits into a part of the lane's start and a local one
+    uint32_t keep = 0u;
+    {
+        const double wax = uniform_d(wa.x), way = uniform_d(wa.y);
+        const double wdx = uniform_d(wb.x - wa.x), wdy = uniform_d(wb.y - wa.y);
+        const double wc = fma(st.y - way, wdx, -(wdy * (st.x - wax)));
+        const double wtol = 0x1p-44 * ((fabs(st.y) + fabs(way) + ymax) * wdx + fabs(wdy) * xa);
+        const double tc = fma(st.y, tot.x, -(tot.y * st.x));
+        const double ttol = 0x1p-44 * ((fabs(st.y) + ymax) * tot.x + fabs(tot.y) * xa);
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const double dw = wc + fma(ys[j], wdx, -(wdy * xs[j]));
+            const double dt = tc + fma(ys[j], tot.x, -(tot.y * xs[j]));
+            keep |= (dw <= wtol && dt <= ttol && j < cnt) ? (1u << j) : 0u;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // the lane's chord and its lowest interior point
+    double dmin = INFINITY;
+    int v = -1;
+#pragma unroll
+    for (int j = 0; j + 1 < K; ++j) {
+        const double d = fma(ys[j], ex, -(ey * xs[j]));
+        const bool take = j + 1 < cnt && d < dmin;
+        dmin = take ? d : dmin;
+        v = take ? j : v;
+    }
+    double xv = 0.0, yv = 0.0;
+#pragma unroll
+    for (int j = 0; j + 1 < K; ++j) {
+        xv = (j == v) ? xs[j] : xv;
+        yv = (j == v) ? ys[j] : yv;
+    }
+    const bool split = v >= 0 && dmin <= tol;  // some interior point lies under (or on) the lane's chord
+    static_assert(K <= 32, "a lane's candidates fit one 32-bit word");
+    __builtin_amdgcn_sched_barrier(0);
+    {
+        const double rdx = ex - xv, rdy = ey - yv;
+        const double rc = fma(-yv, rdx, rdy * xv);
+        uint32_t lq = 1u << (K - 1);  // the lane's last point (E): no lane chord spans it
+#pragma unroll
+        for (int j = 0; j + 1 < K; ++j) {
+            // left of v: chord start-v; right of v: chord v-E; v itself is kept
+            const double cl = fma(ys[j], xv, -(yv * xs[j]));
+            const double cr = fma(ys[j], rdx, rc) - rdy * xs[j];
+            const double c = (j < v) ? cl : cr;
+            bool k = split && (j == v || c <= tol);
+            k = (j + 1 == cnt) ? true : k;  // a partial lane's last point is its E
+            lq |= k ? (1u << j) : 0u;
+        }
+        keep &= lq;
+    }
+    return (uint64_t)keep;
+}
+
+// ---------------------------------------------------------------------------
+// QuickHull by the workgroup (the lower hull of a few hundred points, one per
+// thread).  Entries 0..m of E hold points in increasing x; thread t holds
+// entry e = t + 1, entries 0 and m are the ends and always vertices.  Each
+// level, every interior point still strictly below the chord of its segment
+// (a, b) offers its cross product with the chord (its depth below the chord,
+// scaled by the chord's length) to the segment's slot; the deepest point of
+// each segment is a vertex and splits it, and every thread follows the part
+// that holds it.  A point on or above its segment's chord is not a vertex and
+// stays above the chords of the parts, so it drops out.  Strictly below
+// means a cross product under -tolrel times the magnitude of its two terms
+// (collinear points are not vertices).
+// A slot's key orders by the cross product (its sign, exponent and first 42
+// bits of mantissa) and then by the entry (10 bits), one 64-bit LDS atomic
+// minimum per point and level; the slots of a level are keyed by the
+// segment's first entry, in three arrays used in turn (an array is cleared
+// one level after its last read and one level before its next use).
+// Returns whether the calling thread's entry is a vertex, with (a, b) the
+// entries of the hull edge over the interval [e - 1, e] (for a vertex: the
+// previous vertex and e).  slots: 3 (m + 1) words of LDS.  Block scope; every
+// thread calls it; m <= min(1023, blockDim.x).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ unsigned long long qh_key(double d, int e) {
+    // d < 0: the complement of its bits orders by depth (deeper = smaller)
+    const unsigned long long b = ~(unsigned long long)__double_as_longlong(d);
+    return (b & ~1023ull) | (unsigned long long)e;
+}
+
+__device__ inline bool tile_quickhull(const double2* E, int m, unsigned long long* slots, double tolrel, int& a,
+                                      int& b) {
+    const int tid = threadIdx.x, e = tid + 1, ns = m + 1;
+    for (int i = tid; i < 3 * ns; i += blockDim.x) slots[i] = ~0ull;
+    a = 0;
+    b = m;
+    const bool held = e <= m;
+    double2 A = E[0], B = E[m];
+    const double2 P = held ? E[e] : make_double2(0.0, 0.0);
+    bool vert = e == m, cand = e < m;
+    __syncthreads();
+    for (int k = 0;; ++k) {
+        unsigned long long* cur = slots + (k % 3) * ns;
+        if (cand) {
+            const double dx = B.x - A.x, dy = B.y - A.y, px = P.x - A.x, py = P.y - A.y;
+            const double t1 = py * dx, t2 = dy * px;
+            const double d = t1 - t2;
+            if (d < -tolrel * (fabs(t1) + fabs(t2)) && d < 0.0)
+                atomicMin(cur + a, qh_key(d, e));
+            else
+                cand = false;
+        }
+        if (!__syncthreads_or(cand ? 1 : 0)) break;
+        if (held) {
+            const unsigned long long w = cur[a];
+            if (w != ~0ull) {
+                const int v = (int)(w & 1023ull);
+                if (v == e) {
+                    vert = true;
+                    cand = false;
+                    b = e;
+                    B = P;
+                } else if (e < v) {
+                    b = v;
+                    B = E[v];
+                } else {
+                    a = v;
+                    A = E[v];
+                }
+            }
+        }
+        unsigned long long* old = slots + ((k + 2) % 3) * ns;
+        for (int i = tid; i < ns; i += blockDim.x) old[i] = ~0ull;
+    }
+    return vert;
+}
+
+// Candidates of a noisy float32 tile: the lane's points that do not lie
+// clearly above the hull of the lanes' end points.  Every edge of that coarse
+// hull joins two points of the tile, and the tile's lower hull lies on or
+// below every such chord over its span, so a point strictly above the coarse
+// edge that spans its lane is not a vertex.  (a, b): the coarse edge over the
+// lane, as lane-end indices into the lane starts (tile_quickhull on LS).  A
+// point is dropped only when its cross product with the edge exceeds a bound
+// on the rounding of that product and of the coordinates the later steps use
+// (absolute: the lane start plus the local point).  On N(0,1) noise rows of
+// 5000 elements about 80 points remain (1.6%).  Needs the lane starts (plain
+// pairs, ls2).  Returns the lane's mask (bit b <-> local point b+1).
+template <int K>
+__device__ inline uint64_t lane_coarse_filter(const Tile& t, const double (&xs)[K], const double (&ys)[K], int cnt,
+                                              int a, int b) {
+    if (cnt <= 0) return 0ull;
+    const double2* LS = (const double2*)t.LS;
+    const double2 st = LS[threadIdx.x], A = LS[a], B = LS[b];
+    const double ex = xs[K - 1];
+    double ymax = 0.0;
+#pragma unroll
+    for (int j = 0; j < K; ++j) ymax = fmax(ymax, fabs(ys[j]));
+    const double xa = st.x + ex;
+    const double dx = B.x - A.x, dy = B.y - A.y;
+    const double c0 = fma(st.y - A.y, dx, -(dy * (st.x - A.x)));
+    const double tol = 0x1p-44 * ((fabs(st.y) + fabs(A.y) + ymax) * dx + fabs(dy) * xa);
+    static_assert(K <= 32, "a lane's candidates fit one 32-bit word");
+    uint32_t keep = 0u;
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        const double d = c0 + fma(ys[j], dx, -(dy * xs[j]));
+        keep |= (d <= tol && j < cnt) ? (1u << j) : 0u;
+    }
+    return (uint64_t)keep;
+}
+
+// After tile_compact and tile_quickhull over the list: the vertices (vert in
+// the thread holding entry tid + 1; entry 0 always) moved to the front of the
+// list in order, flag[1] = their number.  Entries only move down; each thread
+// reads its entry before the first barrier.  Ends with a barrier.
+__device__ inline void tile_hull_to_front(const Tile& t, int m, bool vert) {
+    const int tid = threadIdx.x, e = tid + 1, lane = lane_id(), wid = tid >> 6, nw = blockDim.x >> 6;
+    const bool mine = vert && e <= m;
+    unsigned short pv = 0;
+    double2 xy = make_double2(0.0, 0.0);
+    if (mine) {
+        pv = t.V[e];
+        xy = t.VXY[e];
+    }
+    const uint64_t bal = __ballot(mine);
+    if (lane == 0) t.W[wid] = __popcll(bal);
+    __syncthreads();
+    int before = 1, total = 1;
+    for (int q = 0; q < nw; ++q) {
+        const int c = t.W[q];
+        before += (q < wid) ? c : 0;
+        total += c;
+    }
+    if (mine) {
+        const int r = before + __popcll(bal & bits_upto(lane - 1));
+        t.V[r] = pv;
+        t.VXY[r] = xy;
+    }
+    if (tid == 0) t.flag[1] = total;
+    __syncthreads();
 }
 
 // Vertices of the tile's lane masks, point 0 included (block scope; ends
