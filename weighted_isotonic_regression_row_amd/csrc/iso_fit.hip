@@ -82,6 +82,13 @@ __device__ inline void wg_write_nan(int64_t N, T* out, uint64_t* sbits, uint64_t
 // wave K * 64 elements of it).  With nxp, the masks are those of the hulls of
 // the lanes' parts (a superset of the lane hulls' vertices, gw_parts); without
 // HULL the masks are 0 (the caller chooses candidates, lane_chords).
+// Float32 rows of K = 12 or 20 (lanes of 48 or 80 bytes) are always staged:
+// the launcher reserves the room in the list.
+template <typename T, int K>
+constexpr bool always_staged() {
+    return sizeof(T) == 4 && (K * 4) % 64 != 0 && (K * 4) % 16 == 0;
+}
+
 template <typename T, int K, bool HULL = true>
 __device__ inline int tile_build(const Tile& t, const T* y, const T* w, int increasing, uint64_t& mask,
                                  double (&xs)[K], double (&ys)[K], int& nvert, bool stage = false,
@@ -90,17 +97,35 @@ __device__ inline int tile_build(const Tile& t, const T* y, const T* w, int incr
     const int l = threadIdx.x;
     const int cnt = min(max(t.N - l * K, 0), K);
     int f = 0;
-    if (stage) {
+    constexpr bool SO = always_staged<T, K>();
+    if (SO || stage) {
         const int e0 = (l & ~(kWave - 1)) * K;  // the wave's first element
         T* st = (T*)t.VXY + e0;
-        mask = lane_hull<T, K, HULL>(y + e0, w ? w + e0 : nullptr, cnt, !increasing, xs, ys, f, st,
-                               min(max(t.N - e0, 0), K * kWave), nxp);
+        mask = lane_hull<T, K, HULL, SO>(y + e0, w ? w + e0 : nullptr, cnt, !increasing, xs, ys, f, st,
+                                         min(max(t.N - e0, 0), K * kWave), nxp);
     } else {
         mask = lane_hull<T, K, HULL>(y + (int64_t)l * K, w ? w + (int64_t)l * K : nullptr, cnt, !increasing, xs, ys, f,
                                nullptr, 0, nxp);
     }
     nvert = tile_lane_starts<!ABS>(t, make_double2(xs[K - 1], ys[K - 1]), f, __popcll(mask));
     return t.flag[0];
+}
+
+// The stores of step 4, the list holding the edges' values (tile_edge_slopes
+// or tile_hull_to_front): fit (and bits) of the tile's elements.
+template <typename T, int K>
+__device__ inline void tile_store(const Tile& t, uint64_t mask, T* out, uint64_t* sb, uint64_t* cb) {
+    double vals[K];
+    uint64_t clipm;
+    tile_expand<K>(t, mask, vals, clipm);
+    const int l = threadIdx.x;
+    const int cnt = min(max(t.N - l * K, 0), K);
+    store_lane<T, K>(out + (int64_t)l * K, cnt, vals);
+    if (sb) {
+        t.CM[l] = clipm;
+        __syncthreads();
+        tile_bits<K>(t, sb, cb);
+    }
 }
 
 // Step 4 and the stores: fit (and bits) of the tile's elements.  Overwrites
@@ -188,49 +213,56 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
     constexpr bool ABS = sizeof(T) == 4;
     bool over = false;
     if constexpr (HALVES) {
-        // Noisy rows: the parts' hull vertices below the chord are few, and
-        // wrapping them gives the row's hull directly.  Other rows, and rows
-        // whose wrap gives up, take the exact path (row_exact, which also
-        // handles lists beyond the LDS).  The list holds point 0 and cap
+        // Noisy rows have few hull vertices among few candidates, found
+        // output-sensitively: float32 rows by QuickHull over the points under
+        // the hull of the lane ends, float64 rows by wrapping the vertices of
+        // the lanes' half hulls.  The rest take the exact path (row_exact, its
+        // own function, which also handles lists beyond the LDS), so this
+        // kernel holds one path's registers.  The list holds point 0 and cap
         // vertices; every condition here is uniform.
-        bool done = false;
         if constexpr (ABS) {
             // candidates: the points not above the hull of the lane ends
             // (found by QuickHull, one lane end per thread), then the exact
-            // hull of the candidates by QuickHull again, one per thread; each
-            // step falls back (to chords inside the lanes, to the wrap) when
-            // its LDS room or its thread count is short.  Conditions are uniform.
+            // hull of the candidates by QuickHull again, one per thread.  A
+            // row with more candidates than threads, or without the LDS room,
+            // takes the exact path.
             const int cnt = min(max(N - (int)threadIdx.x * K, 0), K);
             const int used = (N + K - 1) / K;
-            if (24 * (used + 1) <= 16 * (a.cap + 1)) {
-                int ca, cb;
-                (void)tile_quickhull((const double2*)t.LS, used, (unsigned long long*)t.VXY, 0.0, ca, cb);
-                mask = lane_coarse_filter<K>(t, xs, ys, cnt, ca, cb);
-            } else {
-                mask = lane_chords<K>(t, xs, ys, cnt);
+            if (8 * qh_slot_words(used) <= 16 * (a.cap + 1)) {
+                int ea, eb;  // the hull edge of the lane ends over this lane
+                (void)tile_quickhull((const double2*)t.LS, used, (unsigned long long*)t.VXY, 0.0, ea, eb);
+                mask = lane_coarse_filter<K>(t, xs, ys, cnt, ea, eb);
+                nvert = tile_count(t, mask);
+                const int m = nvert - 1;
+                if (m <= (int)blockDim.x && 16 * (m + 1) + 8 * qh_slot_words(m) <= 16 * (a.cap + 1)) {
+                    tile_compact<K, ABS>(t, mask, xs, ys);
+                    int qa, qb;
+                    const bool vert =
+                        tile_quickhull(t.VXY, m, (unsigned long long*)(t.VXY + m + 1), 0x1p-48, qa, qb);
+                    tile_hull_to_front(t, m, vert, qa, a.increasing, a.lo, a.hi);
+                    tile_masks_short<K>(t, mask);
+                    tile_store<T, K>(t, mask, out, sb, cb);
+                    if (a.row_nan && threadIdx.x == 0) a.row_nan[row] = 0u;
+                    return;
+                }
             }
-            nvert = tile_count(t, mask);
-            const int m = nvert - 1;
-            if (m <= (int)blockDim.x && 40 * (m + 1) <= 16 * (a.cap + 1)) {
-                tile_compact<K, ABS>(t, mask, xs, ys);
-                int qa, qb;
-                const bool vert = tile_quickhull(t.VXY, m, (unsigned long long*)(t.VXY + m + 1), 0x1p-48, qa, qb);
-                tile_hull_to_front(t, m, vert);
-                tile_masks_short<K>(t, mask);
-                done = true;
-            }
-        }
-        if (!done && 5 * nvert <= 3 * N + 5 && nvert <= a.cap + 1) {
-            tile_compact<K, ABS>(t, mask, xs, ys);
-            if (tile_wrap<K, ABS>(t)) {
-                tile_masks_short<K>(t, mask);
-                done = true;
-            }
-        }
-        if (!done) {
             row_exact<T, K>(y, w, out, sb, cb, a.row_nan ? a.row_nan + row : nullptr, a.ovf + row * a.ovf_stride, N,
                             a.increasing, a.lo, a.hi, a.cap, a.stage);
             return;
+        } else {
+            bool done = false;
+            if (5 * nvert <= 3 * N + 5 && nvert <= a.cap + 1) {
+                tile_compact<K, ABS>(t, mask, xs, ys);
+                if (tile_wrap<K, ABS>(t)) {
+                    tile_masks_short<K>(t, mask);
+                    done = true;
+                }
+            }
+            if (!done) {
+                row_exact<T, K>(y, w, out, sb, cb, a.row_nan ? a.row_nan + row : nullptr, a.ovf + row * a.ovf_stride,
+                                N, a.increasing, a.lo, a.hi, a.cap, a.stage);
+                return;
+            }
         }
     } else {
         over = nvert > a.cap + 1;
@@ -1344,21 +1376,25 @@ static void row_shape(int N, bool f32, int& K, int& nl) {
 // waves puts ceil(W/4) of them on its busiest SIMD, so 4 / ceil(W/4) share
 // it.  The list takes what their share of the 160 KiB leaves (at least a
 // quarter of the points).  Rows that need more go to k_row_ovf.
-static int row_list_cap(int N, int nl, int K, bool ls2) {
+static int row_list_cap(int N, int nl, int K, bool ls2, int stage_bytes = 0) {
     const int W = nl / 64;
     const int per_simd = (W + 3) / 4;
     const long wgs = (W <= 4) ? 16 / W : (per_simd >= 4 ? 1 : 4 / per_simd);
     const long target = kLdsBytes / wgs - 512;
     const long fixed = (long)tile_smem_bytes(nl, 0, K, ls2);
     const long room = (target - fixed) / 18;
-    const long cap = room > N / 4 ? room : N / 4;
-    return (int)(cap < N ? cap : N);
+    long cap = room > N / 4 ? room : N / 4;
+    cap = cap < N ? cap : N;
+    // a list of 16-byte entries that holds the staged inputs of every wave
+    const long stage = (stage_bytes + 15) / 16 - 1;
+    return (int)(cap > stage ? cap : stage);
 }
 
 template <typename T, int K>
 static hipError_t launch_row(const FitLaunch& a, RowArgs r, int nl) {
     constexpr bool ls2 = sizeof(T) == 4;  // float32 tiles: plain lane starts
-    r.cap = row_list_cap((int)a.n, nl, K, ls2);
+    constexpr bool SO = always_staged<T, K>();
+    r.cap = row_list_cap((int)a.n, nl, K, ls2, SO ? nl * K * (int)sizeof(T) : 0);
     const size_t smem = tile_smem_bytes(nl, r.cap, K, ls2);
     static size_t seen[kMaxDevices] = {};
     (void)ensure_lds((const void*)k_row_fit<T, K>, smem, seen);
@@ -1366,8 +1402,8 @@ static hipError_t launch_row(const FitLaunch& a, RowArgs r, int nl) {
     r.ovf_stride = (int64_t)a.L.ovf_stride;
     // stage the inputs through LDS when a lane's K elements are not whole
     // 64-byte segments and the list has room for every wave's span
-    r.stage = ((K * (int)sizeof(T)) % 64 != 0) && ((K * (int)sizeof(T)) % 16 == 0) &&
-              ((size_t)nl * K * sizeof(T) <= tile_list_len(nl, r.cap, K) * 16);
+    r.stage = SO || (((K * (int)sizeof(T)) % 64 != 0) && ((K * (int)sizeof(T)) % 16 == 0) &&
+                     ((size_t)nl * K * sizeof(T) <= tile_list_len(nl, r.cap, K) * 16));
     // rows of several waves keep an overflowing list in the workspace within
     // k_row_fit (row_exact); one-wave rows leave it to k_row_ovf
     const bool may_overflow = r.cap < a.n && K < 12;

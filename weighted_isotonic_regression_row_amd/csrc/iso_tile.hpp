@@ -256,6 +256,28 @@ __device__ __forceinline__ uint64_t gw_parts(const double (&xs)[K], const double
 // each lane then reads its own K values.  avail = elements of the span that
 // exist; the rest read as 0.
 template <typename T, int K>
+__device__ __forceinline__ void stage_wave(const T* __restrict__ base, int avail, T* stage) {
+    constexpr int VW = 16 / (int)sizeof(T);
+    constexpr int NV = K * kWave / VW;
+    const int lane = lane_id();
+    if ((((uintptr_t)base) & 15) == 0) {
+#pragma unroll
+        for (int q = 0; q < NV / kWave; ++q) {
+            const int e = (q * kWave + lane) * VW;
+            if (e + VW <= avail) {
+                *(uint4*)(stage + e) = *(const uint4*)(base + e);
+            } else {
+#pragma unroll
+                for (int r = 0; r < VW; ++r) stage[e + r] = (e + r < avail) ? base[e + r] : (T)0;
+            }
+        }
+    } else {
+        for (int e = lane; e < K * kWave; e += kWave) stage[e] = (e < avail) ? base[e] : (T)0;
+    }
+    wave_sync();
+}
+
+template <typename T, int K>
 __device__ __forceinline__ void lane_load_staged(const T* __restrict__ base, int avail, T* stage, T (&v)[K]) {
     constexpr int VW = 16 / (int)sizeof(T);
     constexpr int NV = K * kWave / VW;
@@ -303,7 +325,9 @@ __device__ __forceinline__ void lane_load_staged(const T* __restrict__ base, int
 // With nxp, the hulls of the lane's two halves instead: a superset of the
 // lane hull's vertices (gw_parts).  Without HULL only the points are formed
 // (mask 0): the caller picks its candidates itself (lane_chords).
-template <typename T, int K, bool HULL = true>
+// STAGED: the caller always passes a stage (the other load paths are left
+// out of the code, which keeps the kernel's registers for the points).
+template <typename T, int K, bool HULL = true, bool STAGED = false>
 __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restrict__ w, int cnt, int negate,
                                      double (&xs)[K], double (&ys)[K], int& f, T* stage = nullptr,
                                      int avail = 0, uint64_t (*nxp)[3] = nullptr) {
@@ -353,20 +377,30 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
     bool done = false;
     if constexpr ((K * (int)sizeof(T)) % 16 == 0) {
         if (stage) {
-            T yv[K], wv[K];
-            lane_load_staged<T, K>(y, avail, stage, yv);
+            // the weights first, into registers; then y through the stage,
+            // read back 16 bytes at a time as the sums consume it (the values
+            // of y never all sit in registers beside the points)
+            T wv[K];
             if (w) {
                 lane_load_staged<T, K>(w, avail, stage, wv);
             } else {
 #pragma unroll
                 for (int j = 0; j < K; ++j) wv[j] = (j < cnt) ? (T)1 : (T)0;
             }
+            stage_wave<T, K>(y, avail, stage);
+            const int lane = lane_id();
 #pragma unroll
-            for (int j = 0; j < K; ++j) take(j, (double)yv[j], (double)wv[j], true);
+            for (int q = 0; q < K / VW; ++q) {
+                const uint4 u = *(const uint4*)(stage + lane * K + q * VW);
+                const T* pu = (const T*)&u;
+#pragma unroll
+                for (int r = 0; r < VW; ++r) take(q * VW + r, (double)pu[r], (double)wv[q * VW + r], true);
+            }
+            wave_sync();  // every lane has its values before the stage is reused
             done = true;
         }
     }
-    if constexpr (K % VW == 0) {
+    if constexpr (K % VW == 0 && !STAGED) {
         // whole, aligned lanes: 16-byte loads, each consumed at once
         if (!done && cnt == K && (((uintptr_t)y) & 15) == 0 && (w == nullptr || (((uintptr_t)w) & 15) == 0)) {
 #pragma unroll
@@ -388,7 +422,7 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
             done = true;
         }
     }
-    if (!done) {
+    if (!STAGED && !done) {
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             const double yi = (j < cnt) ? (double)y[j] : 0.0;
@@ -607,10 +641,11 @@ __device__ inline uint64_t lane_chords(const Tile& t, const double (&xs)[K], con
 // bits of mantissa) and then by the entry (10 bits), one 64-bit LDS atomic
 // minimum per point and level; the slots of a level are keyed by the
 // segment's first entry, in three arrays used in turn (an array is cleared
-// one level after its last read and one level before its next use).
+// one level after its last read and one level before its next use), each
+// with a word that says whether any point made an offer (plain stores of 1).
 // Returns whether the calling thread's entry is a vertex, with (a, b) the
 // entries of the hull edge over the interval [e - 1, e] (for a vertex: the
-// previous vertex and e).  slots: 3 (m + 1) words of LDS.  Block scope; every
+// previous vertex and e).  slots: 3 (m + 2) words of LDS.  Block scope; every
 // thread calls it; m <= min(1023, blockDim.x).
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ unsigned long long qh_key(double d, int e) {
@@ -619,10 +654,13 @@ __device__ __forceinline__ unsigned long long qh_key(double d, int e) {
     return (b & ~1023ull) | (unsigned long long)e;
 }
 
+__host__ __device__ inline int qh_slot_words(int m) { return 3 * (m + 2); }
+
 __device__ inline bool tile_quickhull(const double2* E, int m, unsigned long long* slots, double tolrel, int& a,
                                       int& b) {
     const int tid = threadIdx.x, e = tid + 1, ns = m + 1;
-    for (int i = tid; i < 3 * ns; i += blockDim.x) slots[i] = ~0ull;
+    unsigned long long* F = slots + 3 * ns;  // the offer words of the three arrays
+    for (int i = tid; i < 3 * ns + 3; i += blockDim.x) slots[i] = (i < 3 * ns) ? ~0ull : 0ull;
     a = 0;
     b = m;
     const bool held = e <= m;
@@ -631,17 +669,21 @@ __device__ inline bool tile_quickhull(const double2* E, int m, unsigned long lon
     bool vert = e == m, cand = e < m;
     __syncthreads();
     for (int k = 0;; ++k) {
-        unsigned long long* cur = slots + (k % 3) * ns;
+        const int r = k % 3;
+        unsigned long long* cur = slots + r * ns;
         if (cand) {
             const double dx = B.x - A.x, dy = B.y - A.y, px = P.x - A.x, py = P.y - A.y;
             const double t1 = py * dx, t2 = dy * px;
             const double d = t1 - t2;
-            if (d < -tolrel * (fabs(t1) + fabs(t2)) && d < 0.0)
+            if (d < -tolrel * (fabs(t1) + fabs(t2)) && d < 0.0) {
                 atomicMin(cur + a, qh_key(d, e));
-            else
+                F[r] = 1ull;
+            } else {
                 cand = false;
+            }
         }
-        if (!__syncthreads_or(cand ? 1 : 0)) break;
+        __syncthreads();
+        if (F[r] == 0ull) break;  // uniform: no segment split
         if (held) {
             const unsigned long long w = cur[a];
             if (w != ~0ull) {
@@ -660,8 +702,10 @@ __device__ inline bool tile_quickhull(const double2* E, int m, unsigned long lon
                 }
             }
         }
-        unsigned long long* old = slots + ((k + 2) % 3) * ns;
+        const int o = (k + 2) % 3;
+        unsigned long long* old = slots + o * ns;
         for (int i = tid; i < ns; i += blockDim.x) old[i] = ~0ull;
+        if (tid == 0) F[o] = 0ull;
     }
     return vert;
 }
@@ -701,18 +745,26 @@ __device__ inline uint64_t lane_coarse_filter(const Tile& t, const double (&xs)[
     return (uint64_t)keep;
 }
 
-// After tile_compact and tile_quickhull over the list: the vertices (vert in
-// the thread holding entry tid + 1; entry 0 always) moved to the front of the
-// list in order, flag[1] = their number.  Entries only move down; each thread
-// reads its entry before the first barrier.  Ends with a barrier.
-__device__ inline void tile_hull_to_front(const Tile& t, int m, bool vert) {
+// After tile_compact and tile_quickhull over the list (absolute coordinates):
+// the hull's vertices (vert in the thread holding entry tid + 1, whose
+// previous vertex is entry a; entry 0 always) move to the front of the list
+// in order, flag[1] = their number, and each vertex's thread writes the value
+// of the edge that ends at it over the coordinates of the entry before it:
+// VXY[i] = (the slope of the edge from vertex i to vertex i + 1, oriented and
+// clipped; 1 where clipping changed it, else 0), as tile_edge_slopes does.
+// Entries only move down, and every read precedes the first barrier.  Ends
+// with a barrier.
+__device__ inline void tile_hull_to_front(const Tile& t, int m, bool vert, int a, int increasing, double lo,
+                                          double hi) {
     const int tid = threadIdx.x, e = tid + 1, lane = lane_id(), wid = tid >> 6, nw = blockDim.x >> 6;
     const bool mine = vert && e <= m;
     unsigned short pv = 0;
-    double2 xy = make_double2(0.0, 0.0);
+    double sl = 0.0;
+    bool cl = false;
     if (mine) {
         pv = t.V[e];
-        xy = t.VXY[e];
+        const double2 d = sub2(t.VXY[e], t.VXY[a]);
+        sl = finish(d.y / d.x, increasing, lo, hi, cl);
     }
     const uint64_t bal = __ballot(mine);
     if (lane == 0) t.W[wid] = __popcll(bal);
@@ -726,7 +778,7 @@ __device__ inline void tile_hull_to_front(const Tile& t, int m, bool vert) {
     if (mine) {
         const int r = before + __popcll(bal & bits_upto(lane - 1));
         t.V[r] = pv;
-        t.VXY[r] = xy;
+        t.VXY[r - 1] = make_double2(sl, cl ? 1.0 : 0.0);
     }
     if (tid == 0) t.flag[1] = total;
     __syncthreads();
