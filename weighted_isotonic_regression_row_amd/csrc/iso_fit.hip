@@ -232,10 +232,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
                 int ea, eb;  // the hull edge of the lane ends over this lane
                 (void)tile_quickhull((const double2*)t.LS, used, (unsigned long long*)t.VXY, 0.0, ea, eb);
                 mask = lane_coarse_filter<K>(t, xs, ys, cnt, ea, eb);
-                nvert = tile_count(t, mask);
+                // at most one candidate per thread, with room for the slots after them
+                const int mmax = min((int)blockDim.x, (16 * (a.cap + 1) - 8 * qh_slot_words(0) - 16) / 40);
+                nvert = tile_compact_upto<K, ABS>(t, mask, xs, ys, mmax + 1);
                 const int m = nvert - 1;
-                if (m <= (int)blockDim.x && 16 * (m + 1) + 8 * qh_slot_words(m) <= 16 * (a.cap + 1)) {
-                    tile_compact<K, ABS>(t, mask, xs, ys);
+                if (m <= mmax) {
                     int qa, qb;
                     const bool vert =
                         tile_quickhull(t.VXY, m, (unsigned long long*)(t.VXY + m + 1), 0x1p-48, qa, qb);

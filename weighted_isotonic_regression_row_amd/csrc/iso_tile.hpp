@@ -683,9 +683,10 @@ __device__ inline bool tile_quickhull(const double2* E, int m, unsigned long lon
             }
         }
         __syncthreads();
-        if (F[r] == 0ull) break;  // uniform: no segment split
+        const unsigned long long f = F[r];                // both reads in flight at once
+        const unsigned long long w = held ? cur[a] : ~0ull;
+        if (f == 0ull) break;  // uniform: no segment split
         if (held) {
-            const unsigned long long w = cur[a];
             if (w != ~0ull) {
                 const int v = (int)(w & 1023ull);
                 if (v == e) {
@@ -852,6 +853,53 @@ __device__ inline void tile_compact(const Tile& t, uint64_t mask, const double (
         }
     }
     __syncthreads();
+}
+
+// tile_count and tile_compact in one: the number of candidates (point 0
+// included) is returned, and the list is written (as tile_compact does) only
+// when that number is at most maxv.  One scan and two barriers; ends with a
+// barrier.
+template <int K, bool ABS>
+__device__ inline int tile_compact_upto(const Tile& t, uint64_t mask, const double (&xs)[K], const double (&ys)[K],
+                                        int maxv) {
+    const int l = threadIdx.x, lane = lane_id(), wid = l >> 6, nw = blockDim.x >> 6;
+    const int pc = __popcll(mask);
+    const int incl = wave_incl_scan_int(pc);
+    if (lane == kWave - 1) t.W[wid] = incl;
+    __syncthreads();
+    int r = 1, tot = 1;
+    for (int k = 0; k < nw; ++k) {
+        const int c = t.W[k];
+        r += (k < wid) ? c : 0;
+        tot += c;
+    }
+    if (tot <= maxv) {  // uniform
+        r += incl - pc;
+        if (l == 0) {
+            t.flag[1] = tot;
+            t.V[0] = 0;
+            t.VXY[0] = make_double2(0.0, 0.0);
+        }
+        t.I[l] = r;
+        double sx = 0.0, sy = 0.0;
+        if (ABS) {
+            const double2 s = ((const double2*)t.LS)[l];
+            sx = s.x;
+            sy = s.y;
+        }
+        if (mask) {
+#pragma unroll
+            for (int b = 0; b < K; ++b) {
+                if ((mask >> b) & 1ull) {
+                    t.V[r] = (unsigned short)(l * K + b + 1);
+                    t.VXY[r] = ABS ? make_double2(sx + xs[b], sy + ys[b]) : make_double2(xs[b], ys[b]);
+                    ++r;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    return tot;
 }
 
 // One test of the pairs nearest the shared point (points with absolute
