@@ -539,7 +539,39 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
         }
         return;
     }
-    tile_merges<K, sizeof(T) == 4>(t, mask, xs, ys, true);  // the LDS list holds every point of a chunk
+    // Only points under the hull of the lane ends can be vertices of the
+    // chunk's hull (its edges are chords between points of the chunk): the
+    // lane hulls keep just those of their vertices, and always their last
+    // point, so that each lane's node is still a convex chain from its start
+    // to its end (the merges need both ends: a node starts at the previous
+    // lane's end and shares it), and the merges see every vertex of the chunk
+    // hull on a fraction of the points (dense data: about 420 of 3584 plus
+    // the lane ends, where the lane hulls hold about 3300).  The hull of the
+    // lane ends is found by QuickHull (one per thread) on a plain copy of the
+    // lane starts.
+    {
+        const int used = (N + K - 1) / K;
+        double2* E = (double2*)t.VXY;  // free until the merges compact the list
+        unsigned long long* slots = (unsigned long long*)(E + kChunkLanes + 1);
+        for (int l = threadIdx.x; l <= used; l += blockDim.x) E[l] = lane_start2(t, l);
+        if (threadIdx.x == 0) t.flag[2] = 0;  // vertices of the hull of the lane ends
+        __syncthreads();
+        int ea, eb;
+        const bool cv = tile_quickhull(E, used, slots, 0.0, ea, eb);
+        const uint64_t cvb = __ballot(cv);
+        if (lane_id() == 0 && cvb) atomicAdd(&t.flag[2], __popcll(cvb));
+        const int cnt = min(max(N - (int)threadIdx.x * K, 0), K);
+        const uint64_t end = (cnt > 0) ? (1ull << (cnt - 1)) : 0ull;
+        mask &= lane_coarse_filter<K>(t, xs, ys, cnt, ea, eb, E) | end;
+        __syncthreads();  // E and the slots are read before the merges reuse the list
+    }
+    // The wrap is tried only where the hull is likely short: a wave's wrap
+    // stops after kWrapWave vertices.  The hull of the lane ends tells:
+    // noisy chunks (the 6.5e6 calibration row) have 3 to 14 of its vertices
+    // and about as many in their hull; dense chunks (the 32 x 2^22 rows)
+    // mostly 18 to 70, with hundreds in their hull (their wrap would give up).
+    // The LDS list holds every point of a chunk.
+    tile_merges<K, sizeof(T) == 4>(t, mask, xs, ys, t.flag[2] <= 12);
     __syncthreads();  // every lane's final mask in M
     const int l = threadIdx.x;
     const int nv = t.flag[1];  // vertices of the chunk hull; rank r is list entry r

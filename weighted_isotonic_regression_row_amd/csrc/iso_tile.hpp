@@ -722,11 +722,20 @@ __device__ inline bool tile_quickhull(const double2* E, int m, unsigned long lon
 // (absolute: the lane start plus the local point).  On N(0,1) noise rows of
 // 5000 elements about 80 points remain (1.6%).  Needs the lane starts (plain
 // pairs, ls2).  Returns the lane's mask (bit b <-> local point b+1).
+// A lane start as one float64 pair, from either layout of LS.
+__device__ __forceinline__ double2 lane_start2(const Tile& t, int l) {
+    if (t.ls2) return ((const double2*)t.LS)[l];
+    const double4 s = t.LS[l];
+    return make_double2(s.x + s.y, s.z + s.w);
+}
+
+// E: the lane ends as pairs (entry l = the start of lane l); nullptr reads
+// them from LS (plain pairs, ls2).
 template <int K>
 __device__ inline uint64_t lane_coarse_filter(const Tile& t, const double (&xs)[K], const double (&ys)[K], int cnt,
-                                              int a, int b) {
+                                              int a, int b, const double2* E = nullptr) {
     if (cnt <= 0) return 0ull;
-    const double2* LS = (const double2*)t.LS;
+    const double2* LS = E ? E : (const double2*)t.LS;
     const double2 st = LS[threadIdx.x], A = LS[a], B = LS[b];
     const double ex = xs[K - 1];
     double ymax = 0.0;
@@ -1400,15 +1409,16 @@ __device__ inline bool tile_wrap(const Tile& t) {
 //       lane l's first vertex.
 // On return the sorted vertex list of the whole tile is V, VXY [0, flag[1]).
 // With wrap, the output-sensitive finish (tile_wrap) is tried first when the
-// lane hulls kept at most 3/5 of the points.
+// lane hulls kept at most 3/5 of the points, and (wrap_max) at most
+// wrap_max candidates.
 template <int K, bool ABS>
 __device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (&xs)[K], const double (&ys)[K],
-                                   bool wrap = false) {
+                                   bool wrap = false, int wrap_max = 1 << 30) {
     const int used = (t.N + K - 1) / K;
     const int l = threadIdx.x, lane = lane_id(), wid = l >> 6, nw = blockDim.x >> 6;
     const int nwu = (used + kWave - 1) / kWave;  // waves holding elements
     tile_compact<K, ABS>(t, mask, xs, ys);
-    if (wrap && 5 * t.flag[1] <= 3 * t.N + 5 && tile_wrap<K, ABS>(t)) {
+    if (wrap && 5 * t.flag[1] <= 3 * t.N + 5 && t.flag[1] <= wrap_max && tile_wrap<K, ABS>(t)) {
         tile_masks_short<K>(t, mask);
         return;
     }
