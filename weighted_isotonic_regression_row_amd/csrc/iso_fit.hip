@@ -510,18 +510,31 @@ struct ChunkArgs {
     double4* cgs;      // [rows*m*kGroups]
     double4* cvx;      // [rows*m*kVMax]
     int* cvi;          // [rows*m*kVMax]
+    int* cover;        // [rows*m] chunks left to the second pass
+    int cap;           // list entries of this pass (kChunk in the second)
+    int pass;          // 0: every chunk, a list of cap entries; 1: the chunks the first left
 };
+
+// The first pass gives each chunk a list of kChunkCap entries, small enough
+// for four chunks to share a CU's LDS; a chunk with more candidates than that
+// (rare: dense chunks keep about 620 of 3585 points) is flagged and fitted by
+// the second pass, whose list holds every point (two chunks per CU).
+constexpr int kChunkCap = (kLdsBytes / 4 - 512 - (int)tile_smem_bytes(kChunkLanes, 0, kLaneK)) / 18;
 
 template <typename T>
 __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
     constexpr int K = kLaneK;
     extern __shared__ __align__(32) char smem[];
-    mark_epoch(a.r.status, a.r.epoch);
     const int64_t bid = blockIdx.x;
+    if (a.pass == 0) {
+        mark_epoch(a.r.status, a.r.epoch);
+    } else if (a.cover[bid] == 0) {
+        return;  // the first pass fitted this chunk
+    }
     const int64_t row = bid / a.m, c = bid % a.m;
     const int64_t e0 = c * kChunk;
     const int N = (int)((a.r.n - e0) < kChunk ? (a.r.n - e0) : kChunk);
-    const Tile t = tile_carve(smem, blockDim.x, kChunk, K, N);
+    const Tile t = tile_carve(smem, blockDim.x, a.cap, K, N);
     const T* y = (const T*)a.r.y + row * a.r.n + e0;
     const T* w = a.r.w ? (const T*)a.r.w + row * a.r.n + e0 : nullptr;
     T* out = (T*)a.r.fit + row * a.r.n + e0;
@@ -536,6 +549,7 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
         if (threadIdx.x == 0) {
             a.cflag[bid] = flag;
             a.nv[bid] = 0;
+            if (a.pass == 0) a.cover[bid] = 0;
         }
         return;
     }
@@ -564,6 +578,11 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
         const uint64_t end = (cnt > 0) ? (1ull << (cnt - 1)) : 0ull;
         mask &= lane_coarse_filter<K>(t, xs, ys, cnt, ea, eb, E) | end;
         __syncthreads();  // E and the slots are read before the merges reuse the list
+    }
+    if (a.pass == 0) {
+        const bool fits = tile_count(t, mask) <= a.cap + 1;  // uniform
+        if (threadIdx.x == 0) a.cover[bid] = fits ? 0 : 1;
+        if (!fits) return;  // nothing written: the second pass fits the chunk
     }
     // The wrap is tried only where the hull is likely short: a wave's wrap
     // stops after kWrapWave vertices.  The hull of the lane ends tells:
@@ -1504,13 +1523,20 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
     ca.cgs = (double4*)(a.ws + a.L.cgs);
     ca.cvx = (double4*)(a.ws + a.L.cvx);
     ca.cvi = (int*)(a.ws + a.L.cvi);
+    ca.cover = (int*)(a.ws + a.L.cover);
     {
-        const size_t smem = tile_smem_bytes(kChunkLanes, kChunk, kLaneK);
+        const size_t smem1 = tile_smem_bytes(kChunkLanes, kChunk, kLaneK);
+        const size_t smem0 = tile_smem_bytes(kChunkLanes, kChunkCap, kLaneK);
         static size_t seen[kMaxDevices] = {};
-        (void)ensure_lds((const void*)k_chunk_hull<T>, smem, seen);
-        hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)(a.rows * m)), dim3(kChunkLanes), smem, a.stream, ca);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+        (void)ensure_lds((const void*)k_chunk_hull<T>, smem1, seen);
+        for (int pass = 0; pass < 2; ++pass) {
+            ca.pass = pass;
+            ca.cap = pass ? kChunk : kChunkCap;
+            hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)(a.rows * m)), dim3(kChunkLanes), pass ? smem1 : smem0,
+                               a.stream, ca);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
     }
     MergeArgs ma;
     ma.y = a.y;

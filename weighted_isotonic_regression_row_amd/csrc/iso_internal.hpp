@@ -79,6 +79,7 @@ struct Layout {
     size_t gsd;          // Desc [rows*m] the subtrees' lists
     size_t gsn;          // int [rows*ceil(m/kSub)]
     size_t nc;           // int [rows*m]
+    size_t cover;        // int [rows*m] 1 where the chunk kernel's first pass left the chunk to its second
     size_t mrec;         // MRec [rows*m]
     size_t so;           // double [rows*m]
     size_t cmask;        // u64 [rows*m*kMaskWords]
@@ -119,6 +120,7 @@ inline Layout make_layout(int64_t rows, int64_t n) {
     L.gsd = take(sizeof(Desc) * rm);
     L.gsn = take(4 * (size_t)rows * (size_t)((L.m + kSub - 1) / kSub));
     L.nc = take(4 * rm);
+    L.cover = take(4 * rm);
     L.mrec = take(sizeof(MRec) * rm);
     L.so = take(8 * rm);
     L.cmask = take(8 * rm * kMaskWords);

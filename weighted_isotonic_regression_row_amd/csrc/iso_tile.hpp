@@ -74,13 +74,13 @@ struct Tile {
 // may find among its lane hulls' vertices, and the tile among the waves'.
 constexpr int kWrapWave = 32;
 constexpr int kWrapTile = 128;
-__host__ __device__ inline size_t tile_wrap_ints(int nl) {
+__host__ __device__ constexpr size_t tile_wrap_ints(int nl) {
     const int nw = nl / 64;
     return (size_t)nw * kWrapWave + (nw > 1 ? (size_t)(4 + nw * kWrapWave + kWrapTile) : 0);
 }
 
 // List capacity: the tile's vertices plus point 0.
-__host__ __device__ inline size_t tile_list_len(int nl, int cap, int K) {
+__host__ __device__ constexpr size_t tile_list_len(int nl, int cap, int K) {
     (void)nl;
     (void)K;
     return (size_t)cap + 1;
@@ -88,13 +88,13 @@ __host__ __device__ inline size_t tile_list_len(int nl, int cap, int K) {
 
 // The wrap's results share the clip-mask array when they fit in it (the two
 // are never in use at once).
-__host__ __device__ inline size_t tile_wrap_own_bytes(int nl) {
+__host__ __device__ constexpr size_t tile_wrap_own_bytes(int nl) {
     const size_t b = 4 * tile_wrap_ints(nl);
     return b <= 8 * (size_t)nl ? 0 : ((b + 15) & ~(size_t)15);
 }
 
 // ls2: lane starts as plain double pairs (16 bytes a lane instead of 32).
-__host__ __device__ inline size_t tile_smem_bytes(int nl, int cap, int K, bool ls2 = false) {
+__host__ __device__ constexpr size_t tile_smem_bytes(int nl, int cap, int K, bool ls2 = false) {
     const size_t n = tile_list_len(nl, cap, K);
     const size_t v = (2 * n + 15) & ~(size_t)15;
     return v + 16 * n + (ls2 ? 16 : 32) * (size_t)(nl + 1) + 16 * (size_t)nl + 4 * (size_t)nl +
