@@ -510,27 +510,25 @@ struct ChunkArgs {
     double4* cgs;      // [rows*m*kGroups]
     double4* cvx;      // [rows*m*kVMax]
     int* cvi;          // [rows*m*kVMax]
-    int* cover;        // [rows*m] chunks left to the second pass
+    int* cover;        // [rows*m] the chunks left to the second pass, ncover of them
+    int* ncover;
     int cap;           // list entries of this pass (kChunk in the second)
     int pass;          // 0: every chunk, a list of cap entries; 1: the chunks the first left
 };
 
 // The first pass gives each chunk a list of kChunkCap entries, small enough
 // for four chunks to share a CU's LDS; a chunk with more candidates than that
-// (rare: dense chunks keep about 620 of 3585 points) is flagged and fitted by
-// the second pass, whose list holds every point (two chunks per CU).
+// (rare: dense chunks keep about 620 of 3585 points) is appended to the
+// cover list and fitted by the second pass, whose list holds every point.
 constexpr int kChunkCap = (kLdsBytes / 4 - 512 - (int)tile_smem_bytes(kChunkLanes, 0, kLaneK)) / 18;
 
+__global__ void k_zero_int(int* p) { *p = 0; }
+
+// One chunk by the workgroup: its hull stored, its tentative fit written.
 template <typename T>
-__global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
+__device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
     constexpr int K = kLaneK;
     extern __shared__ __align__(32) char smem[];
-    const int64_t bid = blockIdx.x;
-    if (a.pass == 0) {
-        mark_epoch(a.r.status, a.r.epoch);
-    } else if (a.cover[bid] == 0) {
-        return;  // the first pass fitted this chunk
-    }
     const int64_t row = bid / a.m, c = bid % a.m;
     const int64_t e0 = c * kChunk;
     const int N = (int)((a.r.n - e0) < kChunk ? (a.r.n - e0) : kChunk);
@@ -549,7 +547,6 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
         if (threadIdx.x == 0) {
             a.cflag[bid] = flag;
             a.nv[bid] = 0;
-            if (a.pass == 0) a.cover[bid] = 0;
         }
         return;
     }
@@ -579,10 +576,9 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
         mask &= lane_coarse_filter<K>(t, xs, ys, cnt, ea, eb, E) | end;
         __syncthreads();  // E and the slots are read before the merges reuse the list
     }
-    if (a.pass == 0) {
-        const bool fits = tile_count(t, mask) <= a.cap + 1;  // uniform
-        if (threadIdx.x == 0) a.cover[bid] = fits ? 0 : 1;
-        if (!fits) return;  // nothing written: the second pass fits the chunk
+    if (a.pass == 0 && tile_count(t, mask) > a.cap + 1) {  // uniform
+        if (threadIdx.x == 0) a.cover[atomicAdd(a.ncover, 1)] = (int)bid;
+        return;  // nothing written: the second pass fits the chunk
     }
     // The wrap is tried only where the hull is likely short: a wave's wrap
     // stops after kWrapWave vertices.  The hull of the lane ends tells:
@@ -626,6 +622,24 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
     // tentative fit from the chunk's own hull; k_fixup corrects the elements
     // outside the chunk's surviving segment
     tile_finish<T, K>(t, mask, a.r.increasing, a.r.lo, a.r.hi, out, sb, cb);
+}
+
+// The first pass: one workgroup per chunk.
+template <typename T>
+__global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
+    mark_epoch(a.r.status, a.r.epoch);
+    chunk_fit<T>(a, blockIdx.x);
+}
+
+// The second pass: a grid of workgroups over the cover list (read after the
+// first pass has completed, in stream order).
+template <typename T>
+__global__ __launch_bounds__(kChunkLanes) void k_chunk_cover(ChunkArgs a) {
+    const int count = *a.ncover;
+    for (int i = blockIdx.x; i < count; i += gridDim.x) {
+        chunk_fit<T>(a, a.cover[i]);
+        __syncthreads();  // the next chunk reuses the LDS
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -1524,19 +1538,27 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
     ca.cvx = (double4*)(a.ws + a.L.cvx);
     ca.cvi = (int*)(a.ws + a.L.cvi);
     ca.cover = (int*)(a.ws + a.L.cover);
+    ca.ncover = (int*)(a.ws + a.L.status + 16);
     {
         const size_t smem1 = tile_smem_bytes(kChunkLanes, kChunk, kLaneK);
         const size_t smem0 = tile_smem_bytes(kChunkLanes, kChunkCap, kLaneK);
-        static size_t seen[kMaxDevices] = {};
-        (void)ensure_lds((const void*)k_chunk_hull<T>, smem1, seen);
-        for (int pass = 0; pass < 2; ++pass) {
-            ca.pass = pass;
-            ca.cap = pass ? kChunk : kChunkCap;
-            hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)(a.rows * m)), dim3(kChunkLanes), pass ? smem1 : smem0,
-                               a.stream, ca);
-            hipError_t e = hipGetLastError();
-            if (e != hipSuccess) return e;
-        }
+        static size_t seen0[kMaxDevices] = {}, seen1[kMaxDevices] = {};
+        (void)ensure_lds((const void*)k_chunk_hull<T>, smem0, seen0);
+        (void)ensure_lds((const void*)k_chunk_cover<T>, smem1, seen1);
+        hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(1), 0, a.stream, ca.ncover);
+        const int64_t chunks = a.rows * m;
+        ca.pass = 0;
+        ca.cap = kChunkCap;
+        hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)chunks), dim3(kChunkLanes), smem0, a.stream, ca);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        // two workgroups per CU (the full list) loop over the cover list
+        ca.pass = 1;
+        ca.cap = kChunk;
+        hipLaunchKernelGGL(k_chunk_cover<T>, dim3((unsigned)(chunks < 512 ? chunks : 512)), dim3(kChunkLanes), smem1,
+                           a.stream, ca);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     MergeArgs ma;
     ma.y = a.y;
