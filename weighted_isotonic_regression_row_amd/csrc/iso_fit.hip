@@ -950,6 +950,115 @@ __device__ inline void bisect_bridge(const MCtx& X, int j0, int la, int jB, int 
 // Window steps a merge may take before it switches to bisection.
 constexpr int kWindowSteps = 64;
 
+// LDS of one wave's window search (window_bridge): kBW vertices of each list
+// nearest the shared point.
+constexpr int kBW = 128;
+struct BWin {
+    double2 A[kBW], B[kBW];    // coordinates relative to the shared point
+    int2 IA[kBW], IB[kBW];     // (slot, rank) of each entry
+    int cA[kWave], cB[kWave];  // vertices in the first 1..64 descriptors read from the shared point
+};
+
+// The bridge of a merge from windows of the two lists, with the calling wave
+// (first page, Sec. 4, Lemma 4.2 and the walk after it, at LDS latency).  The
+// kBW vertices of A before the shared point s (A[0] = s, A[i] = the i-th
+// predecessor) and of B after it are read once, as double-double differences
+// from s rounded to float64 (a difference loses nothing to the size of the
+// coordinates, first page, App. B), together with their (slot, rank); then the
+// walk of find_merge runs on them, 64 candidates per step.  Returns false when
+// the walk reaches the end of a window that does not hold its whole list (the
+// bridge may lie beyond it); the caller then walks the lists themselves.
+template <typename T>
+__device__ __forceinline__ bool window_bridge(const MCtx& X, int j0, int la, int jB, int sB1, int g, BWin* W, VR& al,
+                                     VR& be) {
+    const Desc* D = X.D;
+    int lenA = 0, lenB = 0;
+    if (la - g >= j0) {
+        const Desc d = D[la - g];
+        lenA = (int)d.h - (int)d.l + 1;
+    }
+    if (jB + g <= sB1) {
+        const Desc d = D[jB + g];
+        lenB = (int)d.h - (int)d.l + 1;
+    }
+    const int cumA = wave_incl_scan_int(lenA), cumB = wave_incl_scan_int(lenB);
+    W->cA[g] = cumA;
+    W->cB[g] = cumB;
+    const int totA = __builtin_amdgcn_readlane(cumA, kWave - 1), totB = __builtin_amdgcn_readlane(cumB, kWave - 1);
+    const bool allA = la - (kWave - 1) <= j0 && totA <= kBW;  // the window holds all of A
+    const bool allB = jB + (kWave - 1) >= sB1 && totB <= kBW;
+    const int nA = min(totA, kBW), nB = min(totB, kBW);
+    const PtD Ps = ptv<T>(X, VR{la, (int)D[la].h});
+    wave_sync();
+    // entries g, g + 64 of each window: one vertex read per pass (a loop, not
+    // unrolled, keeps one vertex access inlined)
+#pragma unroll 1
+    for (int q = 0; q < 2 * (kBW / kWave); ++q) {
+        const bool onA = q < kBW / kWave;
+        const int i = g + kWave * (onA ? q : q - kBW / kWave);
+        const int* cnt = onA ? W->cA : W->cB;
+        if (i < (onA ? nA : nB)) {
+            int lo = 0, hi = kWave - 1;  // the first descriptor whose count passes i
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (cnt[mid] > i)
+                    hi = mid;
+                else
+                    lo = mid + 1;
+            }
+            const int off = i - (lo ? cnt[lo - 1] : 0);
+            const int sl = onA ? la - lo : jB + lo;
+            const int k = onA ? (int)D[sl].h - off : (int)D[sl].l + off;
+            const PtD P = ptd<T>(X, D[sl].c, k);
+            const double2 rel = make_double2(pdx(Ps, P), pdy(Ps, P));
+            if (onA) {
+                W->A[i] = rel;
+                W->IA[i] = make_int2(sl, k);
+            } else {
+                W->B[i] = rel;
+                W->IB[i] = make_int2(sl, k);
+            }
+        }
+    }
+    wave_sync();
+    auto turn = [](double2 a, double2 b, double2 d) { return (b.x - a.x) * (d.y - a.y) - (b.y - a.y) * (d.x - a.x); };
+    int ia = 1, ib = 1;  // the neighbours of s
+    for (int it = 0; it < kWindowSteps; ++it) {
+        // left side against B[ib]: pass over a while it is not a strict
+        // vertex of {pred(a), a, B[ib]}
+        const double2 pb = W->B[ib];
+        for (;;) {
+            const int i = ia + g;
+            bool cont = false;
+            if (i + 1 < nA) cont = !(turn(W->A[i + 1], W->A[i], pb) > 0.0);
+            const int run = trailing_ones(__ballot(cont));
+            ia += run;
+            if (run < kWave) break;
+        }
+        if (ia == nA - 1 && !allA) return false;
+        // right side against the new A[ia]
+        const double2 pa = W->A[ia];
+        bool moved = false;
+        for (;;) {
+            const int j = ib + g;
+            bool cont = false;
+            if (j + 1 < nB) cont = !(turn(pa, W->B[j], W->B[j + 1]) > 0.0);
+            const int run = trailing_ones(__ballot(cont));
+            ib += run;
+            moved = moved || run > 0;
+            if (run < kWave) break;
+        }
+        if (ib == nB - 1 && !allB) return false;
+        if (!moved) {
+            const int2 a2 = W->IA[ia], b2 = W->IB[ib];
+            al = VR{a2.x, a2.y};
+            be = VR{b2.x, b2.y};
+            return true;
+        }
+    }
+    return false;
+}
+
 // Merge of the node at slots j0.. (cntA descriptors) with its right neighbour
 // at jB.. (cntB) by a group of G lanes (g = 0..G-1, G a power of two <= 64)
 // (Sec. 3.3, Lemma 4.2, Theorem 4.4).  From the neighbours of the shared
@@ -958,7 +1067,8 @@ constexpr int kWindowSteps = 64;
 // kWindowSteps steps is finished by nested bisection.  Returns the rewrite of
 // the merged list; reads the descriptors only.
 template <typename T>
-__device__ inline MRec find_merge(const MCtx& X, int j0, int jB, int cntA, int cntB, int g, int G) {
+__device__ __forceinline__ MRec find_merge(const MCtx& X, int j0, int jB, int cntA, int cntB, int g, int G,
+                                  BWin* win = nullptr) {
     const Desc* D = X.D;
     const int la = j0 + cntA - 1;
     const int sB1 = jB + cntB - 1;
@@ -989,56 +1099,71 @@ __device__ inline MRec find_merge(const MCtx& X, int j0, int jB, int cntA, int c
     const int gb = lane_id() & ~(G - 1);
     VR al = pA, be = nB;
     int steps = 0;
-    bool ok = true;
-    for (;;) {
-        // left side against be: pass over a while it is not a strict vertex
-        // of {pred(a), a, be}
+    // the walk, until it converges (true), or has taken cap steps of G
+    // candidates in all, or (iters) that many steps of any length (false)
+    auto walk = [&](int cap, int iters) -> bool {
+        Pbe = ptv<T>(X, be);  // a walk that stopped inside the right side left it behind be
         for (;;) {
-            VR c0 = al, c1 = al;
-            const bool v0 = step_back(X, al, j0, g, c0);
-            const bool v1 = v0 && step_back(X, c0, j0, 1, c1);
-            bool cont = false;
-            if (v1) cont = !(turnD(ptv<T>(X, c1), ptv<T>(X, c0), Pbe) > 0.0);
-            const int run = trailing_ones(group_bits(__ballot(cont), G));
-            const int step = run < G ? run : G;
-            const int src = gb + (step < G ? step : G - 1);
-            const int ts = __shfl(step < G ? c0.s : c1.s, src, kWave);
-            const int tk = __shfl(step < G ? c0.k : c1.k, src, kWave);
-            if (step > 0) al = VR{ts, tk};
-            if (step < G) break;
-            if (++steps > kWindowSteps) {
-                ok = false;
-                break;
+            // left side against be: pass over a while it is not a strict vertex
+            // of {pred(a), a, be}
+            for (;;) {
+                VR c0 = al, c1 = al;
+                const bool v0 = step_back(X, al, j0, g, c0);
+                const bool v1 = v0 && step_back(X, c0, j0, 1, c1);
+                bool cont = false;
+                if (v1) cont = !(turnD(ptv<T>(X, c1), ptv<T>(X, c0), Pbe) > 0.0);
+                const int run = trailing_ones(group_bits(__ballot(cont), G));
+                const int step = run < G ? run : G;
+                const int src = gb + (step < G ? step : G - 1);
+                const int ts = __shfl(step < G ? c0.s : c1.s, src, kWave);
+                const int tk = __shfl(step < G ? c0.k : c1.k, src, kWave);
+                if (step > 0) al = VR{ts, tk};
+                if (--iters < 0) return false;
+                if (step < G) break;
+                if (++steps > cap) return false;
             }
+            // right side against the new al
+            const PtD Pal = ptv<T>(X, al);
+            bool movedB = false;
+            for (;;) {
+                VR c0 = be, c1 = be;
+                const bool v0 = step_fwd(X, be, sB1, g, c0);
+                const bool v1 = v0 && step_fwd(X, c0, sB1, 1, c1);
+                bool cont = false;
+                if (v1) cont = !(turnD(Pal, ptv<T>(X, c0), ptv<T>(X, c1)) > 0.0);
+                const int run = trailing_ones(group_bits(__ballot(cont), G));
+                const int step = run < G ? run : G;
+                const int src = gb + (step < G ? step : G - 1);
+                const int ts = __shfl(step < G ? c0.s : c1.s, src, kWave);
+                const int tk = __shfl(step < G ? c0.k : c1.k, src, kWave);
+                if (step > 0) {
+                    be = VR{ts, tk};
+                    movedB = true;
+                }
+                if (--iters < 0) return false;
+                if (step < G) break;
+                if (++steps > cap) return false;
+            }
+            if (!movedB) return true;
+            Pbe = ptv<T>(X, be);
         }
-        if (!ok) break;
-        // right side against the new al
-        const PtD Pal = ptv<T>(X, al);
-        bool movedB = false;
-        for (;;) {
-            VR c0 = be, c1 = be;
-            const bool v0 = step_fwd(X, be, sB1, g, c0);
-            const bool v1 = v0 && step_fwd(X, c0, sB1, 1, c1);
-            bool cont = false;
-            if (v1) cont = !(turnD(Pal, ptv<T>(X, c0), ptv<T>(X, c1)) > 0.0);
-            const int run = trailing_ones(group_bits(__ballot(cont), G));
-            const int step = run < G ? run : G;
-            const int src = gb + (step < G ? step : G - 1);
-            const int ts = __shfl(step < G ? c0.s : c1.s, src, kWave);
-            const int tk = __shfl(step < G ? c0.k : c1.k, src, kWave);
-            if (step > 0) {
-                be = VR{ts, tk};
-                movedB = true;
-            }
-            if (step < G) break;
-            if (++steps > kWindowSteps) {
-                ok = false;
-                break;
-            }
-        }
-        if (!ok || !movedB) break;
-        Pbe = ptv<T>(X, be);
+    };
+    // with windows, the walk first runs on them at LDS latency; else (or when
+    // the bridge lies beyond them) on the lists, to its cap; then bisection.
+    // Windows pay where the segments at the shared point are short (noisy
+    // rows: chunk hulls of a few vertices, bridges many segments away); long
+    // ones (dense rows: hundreds of vertices a chunk) have their bridge close
+    // to the shared point, which the walk reaches in a step or two.
+    const bool shortseg = ((int)dA.h - (int)dA.l) + ((int)dB.h - (int)dB.l) + 2 <= kBW;
+    if (win && G == kWave && shortseg && window_bridge<T>(X, j0, la, jB, sB1, g, win, al, be)) {
+        r.newA = al.s - j0 + 1;
+        r.alk = al.k;
+        r.bs = be.s;
+        r.nBk = sB1 - be.s + 1;
+        r.bek = be.k;
+        return r;
     }
+    const bool ok = walk(kWindowSteps, 1 << 30);
     if (!ok) {
         int as = 0, ak = 0, bs = 0, bk = 0;
         if (g == 0) {
@@ -1105,6 +1230,8 @@ constexpr int kMergeThreads = 512;
 // subtree's hull as a list of at most kSub segments.
 template <typename T>
 __global__ __launch_bounds__(kMergeThreads) void k_merge_sub(MergeArgs a) {
+    extern __shared__ __align__(32) char smem[];
+    BWin* wins = (BWin*)smem;  // one window per wave
     __shared__ Desc D0[kSub], D1[kSub];
     __shared__ int NC[kSub], nvl[kSub];
     __shared__ MRec MR[kSub / 2];
@@ -1155,7 +1282,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_sub(MergeArgs a) {
         X.D = Dc;
         for (int k = wid; k < nm; k += nwv) {
             const int j0 = k * 2 * h;
-            const MRec r = find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h], g, kWave);
+            const MRec r = find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h], g, kWave, wins + wid);
             if (g == 0) MR[k] = r;
         }
         __syncthreads();
@@ -1170,12 +1297,15 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_sub(MergeArgs a) {
     if (tid == 0) a.gsn[row * a.nsub + sub] = cnt;
 }
 
+// LDS of the merge windows (one per wave).
+constexpr size_t kMergeWinBytes = sizeof(BWin) * (kMergeThreads / kWave);
+
 __host__ __device__ inline size_t merge_top_smem_bytes(int64_t m, int use_lds) {
     const size_t scan = sizeof(double4) * kMergeThreads;
     const size_t mr = sizeof(MRec) * (size_t)(m / (2 * kSub) + 1);
     size_t b = (scan > mr ? scan : mr) + 16;
     if (use_lds) b += (2 * sizeof(Desc) + 2 * sizeof(int)) * (size_t)m;
-    return b;
+    return ((b + 15) & ~(size_t)15) + kMergeWinBytes;
 }
 
 // Upper levels of the merge tree of one long row: double-double chunk starts
@@ -1220,6 +1350,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_top(MergeArgs a) {
         nvl = nullptr;
     }
     Rec* rec = a.rec + base;
+    BWin* wins = (BWin*)(smem + merge_top_smem_bytes(m, a.use_lds) - kMergeWinBytes);
 
     // 1. row flag: any chunk with a NaN / infinite input or a bad weight
     if (tid == 0) sflag[0] = 0;
@@ -1289,7 +1420,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_top(MergeArgs a) {
         X.D = Dc;
         for (int k = wid; k < nm; k += nw) {
             const int j0 = k * 2 * h;
-            const MRec r = find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h], g, kWave);
+            const MRec r = find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h], g, kWave, wins + wid);
             if (g == 0) MR[k] = r;
         }
         __threadfence_block();
@@ -1583,7 +1714,12 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
     ma.status = status;
     ma.epoch = a.epoch;
     ma.use_lds = (m <= kMergeLdsChunks) ? 1 : 0;
-    hipLaunchKernelGGL(k_merge_sub<T>, dim3((unsigned)(a.rows * ma.nsub)), dim3(kMergeThreads), 0, a.stream, ma);
+    {
+        static size_t seen[kMaxDevices] = {};
+        (void)ensure_lds((const void*)k_merge_sub<T>, kMergeWinBytes, seen);
+    }
+    hipLaunchKernelGGL(k_merge_sub<T>, dim3((unsigned)(a.rows * ma.nsub)), dim3(kMergeThreads), kMergeWinBytes,
+                       a.stream, ma);
     {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;

@@ -38,8 +38,9 @@ constexpr int kGroups = kChunk / kGroup;
 constexpr int kVMax = 1024;
 // The lower levels of the merge tree run on subtrees of this many chunks.
 constexpr int kSub = 64;
-// Segment descriptors of a row are kept in LDS up to this many chunks.
-constexpr int64_t kMergeLdsChunks = 4096;
+// Segment descriptors of a row are kept in LDS up to this many chunks (the
+// top merge's LDS also holds the waves' merge windows).
+constexpr int64_t kMergeLdsChunks = 3584;
 // Elements per tile of the backward pass on long rows.
 constexpr int kVjpTile = 4096;
 
