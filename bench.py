@@ -495,8 +495,9 @@ def main():
     if args.workload in ("dense", "both") + fits:
         dense = fit_leg("dense", args.steps, args.warmup, args.cpu_seconds / 2, args.no_cpu)
         ach = dense["algorithmic_bytes"] / (dense["fit_ms_events_mean"] * 1e-3) / 1e9
-        dense["roofline"] = {"bound": "hbm", "timed": "the whole fit call (k_chunk_hull, k_merge_sub, k_merge_top, "
-                                                      "k_fixup), events on the launch stream",
+        dense["roofline"] = {"bound": "hbm", "timed": "the whole fit call (k_zero_int, k_chunk_hull, k_chunk_cover, "
+                                                      "k_merge_sub, k_merge_top, k_fixup), events on the launch "
+                                                      "stream",
                              "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
                              "traffic": committed_traffic(DENSE_SUMMARY), "bytes_per_element": 24,
                              "elements_per_launch": dense["rows"] * dense["n"]}
