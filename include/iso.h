@@ -42,6 +42,10 @@ extern "C" {
 /* element types */
 #define ISO_F32 0
 #define ISO_F64 1
+#define ISO_F16 2  /* IEEE binary16; views only (iso_fit_view, iso_vjp_view)      */
+#define ISO_BF16 3 /* bfloat16 (the high half of a binary32); views only          */
+#define ISO_I32 4  /* int32 inputs of views (converted to float32)                */
+#define ISO_I64 5  /* int64 inputs of views (converted to float32)                */
 
 /* return codes */
 #define ISO_OK 0
@@ -193,6 +197,94 @@ int iso_vjp(const void* grad_dev, const iso_blocks* blocks, void* grad_y_dev, vo
  */
 int iso_vjp_yw(const void* grad_dev, const iso_blocks* blocks, const void* y_dev, void* grad_y_dev,
                void* grad_w_dev, void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * Strided, typed views: the operator's full input semantics (page
+ * "torchisotonic", "Semantics": weights of y's shape or broadcast to it, `dim`
+ * picks the axis, float input keeps its dtype with float16 and bfloat16
+ * computed in float32, integer input becomes the default float dtype).
+ *
+ * A view describes a logical [outer, inner, n] array: row r = o * inner + j
+ * (o < outer, j < inner) and its element i live at element offset
+ *     o * stride_outer + j * stride_inner + i * stride_elem
+ * from data, counted in elements of the view's dtype.  Strides are >= 0; a
+ * stride of 0 repeats the data along that axis (broadcasting).  Every tensor
+ * layout whose non-fit axes fold into at most two strides is one view: a
+ * fit along any axis of a 2-D or 3-D tensor, a weight vector shared by every
+ * row (stride_outer = stride_inner = 0), one weight per row (stride_elem = 0),
+ * an expanded y.
+ *
+ * Computation.  The compute type is float64 when y or the fit's output view
+ * is float64, else float32 (float16, bfloat16, float32 and integer y with an
+ * output of float32, float16 or bfloat16); accumulation is float64 as in
+ * iso_fit.  Weights are converted to the compute type.  Inputs that are not already contiguous rows of the compute
+ * type are converted into the workspace by a gather kernel (a tiled transpose
+ * through LDS when stride_elem != 1); the fit then runs exactly as iso_fit on
+ * those rows, and a scatter kernel converts the result to the output view
+ * (float16: round to nearest even by the hardware conversion; bfloat16: round
+ * to nearest even of the float32 bits, NaN kept NaN).
+ */
+typedef struct iso_view {
+    void* data;           /* device memory (read only for inputs)                  */
+    int dtype;            /* ISO_F16, ISO_BF16, ISO_F32, ISO_F64; inputs also ISO_I32, ISO_I64 */
+    int64_t stride_outer; /* elements from row (o, j) to row (o + 1, j)            */
+    int64_t stride_inner; /* elements from row (o, j) to row (o, j + 1)            */
+    int64_t stride_elem;  /* elements from element i to element i + 1 of a row     */
+} iso_view;
+
+/* Bytes of device workspace iso_fit_view and iso_vjp_view need for
+ * outer * inner = rows rows of n elements in the compute type compute_dtype
+ * (ISO_F32 or ISO_F64; 0 for invalid sizes or dtype): the solver's workspace
+ * and four [rows, n] arrays for converted inputs and outputs. */
+size_t iso_view_workspace_bytes(int64_t rows, int64_t n, int compute_dtype);
+
+/* Bytes of device memory backing the partition handle of iso_fit_view:
+ * iso_blocks_bytes(rows, n) plus, when weighted, room for the weights
+ * converted to the compute type (the backward pass reads them from there
+ * when the caller's weights are not already contiguous rows of that type). */
+size_t iso_view_blocks_bytes(int64_t rows, int64_t n, int compute_dtype, int weighted);
+
+/*
+ * iso_fit on views (first page, Sec. 2-4; PyPI page, "Semantics").
+ *   y            view of the data (required).
+ *   w            view of the weights, or NULL for unit weights.
+ *   outer, inner the logical row shape: rows = outer * inner.
+ *   fit          view written with the result: ISO_F32, ISO_F64, or, when y
+ *                is not float64, ISO_F16 / ISO_BF16.  Its strides must not map
+ *                two elements to one place (stride_elem 0 is ISO_EINVAL for
+ *                n > 1; other repeats are not checked), and it may not
+ *                overlap y or w.
+ *   blocks_out, blocks_mem_dev  as for iso_fit, with
+ *                iso_view_blocks_bytes(rows, n, compute type, w != NULL) bytes;
+ *                the handle's rows are the logical rows r = o * inner + j, its
+ *                dtype the compute type, and its w_dev the caller's weights
+ *                or their converted copy inside blocks_mem_dev.
+ *   workspace_dev  iso_view_workspace_bytes(rows, n, compute type) bytes,
+ *                256-aligned; iso_status reads it as for iso_fit.
+ * ISO_EINVAL for a bad dtype or stride, NULL pointers, misaligned or short
+ * buffers.  rows == 0 or n == 0 queues nothing.
+ */
+int iso_fit_view(const iso_view* y, const iso_view* w, int64_t outer, int64_t inner, int64_t n, int increasing,
+                 double y_min, double y_max, const iso_view* fit, iso_blocks* blocks_out, void* blocks_mem_dev,
+                 void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * iso_vjp_yw on views: the products in y and in the weights of a fit made by
+ * iso_fit_view (the same formulas), computed in the fit's compute type
+ * (blocks->dtype).  grad and y are input views (any input dtype), grad_y and
+ * grad_w output views (ISO_F32 or ISO_F64, or ISO_F16 / ISO_BF16 when the
+ * compute type is float32), each NULL when not wanted; y is required with
+ * grad_w and is the y the fit was given.  grad_w is written at every element of the logical [rows, n] array:
+ * for weights that were broadcast, the product in the caller's weights is
+ * its sum over the broadcast axes, which the library leaves to the caller.
+ *   workspace_dev  iso_view_workspace_bytes(rows, n, blocks->dtype) bytes
+ *                  (may be the fit's workspace: the calls are stream-ordered).
+ * ISO_EINVAL for a bad handle, dtype or stride, NULL pointers, both outputs
+ * NULL, outer * inner != blocks->rows, a short or misaligned workspace.
+ */
+int iso_vjp_view(const iso_view* grad, const iso_blocks* blocks, const iso_view* y, const iso_view* grad_y,
+                 const iso_view* grad_w, int64_t outer, int64_t inner, void* workspace_dev, size_t workspace_bytes,
+                 void* stream);
 
 /*
  * Soft rank with quadratic regularization of strength eps (first page,

@@ -39,7 +39,8 @@ def test_header_declares_the_boundary():
     assert fns == sorted(["iso_blocks_bytes", "iso_fit", "iso_fit_noalloc", "iso_status", "iso_strerror", "iso_vjp", "iso_vjp_yw",
                           "iso_workspace_bytes", "iso_soft_rank", "iso_soft_rank_vjp", "iso_soft_rank_state_bytes",
                           "iso_soft_rank_workspace_bytes", "iso_calibration_workspace_bytes", "iso_calibration_fit",
-                          "iso_calibrate"])
+                          "iso_calibrate", "iso_view_workspace_bytes", "iso_view_blocks_bytes", "iso_fit_view",
+                          "iso_vjp_view"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -264,3 +265,85 @@ def test_noalloc_refuses_problems_past_its_scratch_on_host(lib):
     assert bc.valid == 1 and bc.rows == 0
     assert lib.iso_workspace_bytes(1000, 6144, 0) <= iso.NOALLOC_SCRATCH_BYTES
     assert lib.iso_workspace_bytes(1, 12_000_000, 1) <= iso.NOALLOC_SCRATCH_BYTES
+
+
+def test_view_sizes(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    base = lib.iso_workspace_bytes(100, 5000, 0)
+    # the solver's workspace and four converted [rows, n] arrays of the compute type
+    assert lib.iso_view_workspace_bytes(100, 5000, iso.ISO_F32) >= base + 4 * 100 * 5000 * 4
+    assert lib.iso_view_workspace_bytes(100, 5000, iso.ISO_F64) >= lib.iso_workspace_bytes(100, 5000, 1) + 4 * 100 * 5000 * 8
+    assert lib.iso_view_workspace_bytes(100, 5000, iso.ISO_F16) == 0   # not a compute type
+    assert lib.iso_view_workspace_bytes(-1, 5, iso.ISO_F32) == 0
+    b = lib.iso_view_blocks_bytes(100, 5000, iso.ISO_F32, 0)
+    assert b >= lib.iso_blocks_bytes(100, 5000)
+    assert lib.iso_view_blocks_bytes(100, 5000, iso.ISO_F32, 1) >= b + 100 * 5000 * 4
+    assert lib.iso_view_blocks_bytes(100, 5000, iso.ISO_I32, 1) == 0
+
+
+def _v(data=256, dt=0, so=3, si=0, se=1):
+    import weighted_isotonic_regression_row_amd as iso
+    return ctypes.byref(iso.IsoViewC(data, dt, so, si, se))
+
+
+def _fitv(lib, y=None, w=None, outer=2, inner=1, n=3, inc=1, lo=-math.inf, hi=math.inf, fit=None, bo=None,
+          bm=None, ws=1 << 16, wsb=1 << 26):
+    y = _v() if y is None else y
+    fit = _v(data=1 << 20) if fit is None else fit
+    return lib.iso_fit_view(y, w, outer, inner, n, inc, lo, hi, fit, bo, bm, ws, wsb, None)
+
+
+def test_fit_view_rejects_bad_arguments_on_host(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    E = iso.ISO_EINVAL
+    assert lib.iso_fit_view(None, None, 2, 1, 3, 1, -math.inf, math.inf, _v(), None, None, 1 << 16, 1 << 26,
+                            None) == E
+    assert _fitv(lib, outer=-1) == E
+    assert _fitv(lib, n=-1) == E
+    assert _fitv(lib, y=_v(dt=9)) == E                    # unknown dtype
+    assert _fitv(lib, fit=_v(data=1 << 20, dt=iso.ISO_I32)) == E   # integer output
+    assert _fitv(lib, y=_v(dt=iso.ISO_F64), fit=_v(data=1 << 20, dt=iso.ISO_F16)) == E  # float16 from float64
+    assert _fitv(lib, y=_v(data=None)) == E
+    assert _fitv(lib, y=_v(data=258)) == E               # not aligned to its element
+    assert _fitv(lib, y=_v(se=-1)) == E                  # negative stride
+    assert _fitv(lib, w=_v(dt=iso.ISO_F16, so=-3)) == E
+    assert _fitv(lib, fit=_v(data=1 << 20, se=0)) == E    # an output that repeats itself
+    assert _fitv(lib, ws=None) == E
+    assert _fitv(lib, wsb=8) == E                        # workspace too small
+    assert _fitv(lib, ws=(1 << 16) + 8) == E             # misaligned workspace
+    assert _fitv(lib, inc=2) == E
+    assert _fitv(lib, lo=1.0, hi=0.0) == E
+    assert _fitv(lib, outer=1 << 62, inner=1 << 10) == E  # the row count overflows
+    bc = iso.IsoBlocksC()
+    assert _fitv(lib, bo=ctypes.byref(bc)) == E           # handle without memory
+
+
+def test_fit_view_empty_is_a_noop(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    bc = iso.IsoBlocksC()
+    assert _fitv(lib, outer=0, ws=None, bo=ctypes.byref(bc), bm=8192) == iso.ISO_OK
+    assert bc.valid == 1 and bc.rows == 0
+    assert _fitv(lib, n=0, ws=None, y=_v(dt=iso.ISO_BF16), fit=_v(data=1 << 20, dt=iso.ISO_BF16)) == iso.ISO_OK
+
+
+def test_vjp_view_rejects_bad_arguments_on_host(lib):
+    import weighted_isotonic_regression_row_amd as iso
+    E = iso.ISO_EINVAL
+    bc = iso.IsoBlocksC()
+    g, out = _v(), _v(data=1 << 20)
+    assert lib.iso_vjp_view(g, ctypes.byref(bc), None, out, None, 2, 1, 1 << 16, 1 << 26, None) == E  # invalid
+    bc.valid = 1
+    bc.rows, bc.n, bc.words, bc.dtype = 2, 3, 1, 0
+    bc.start_bits_dev, bc.clip_bits_dev, bc.row_nan_dev = 8192, 8192 + 256, 8192 + 512
+    call = lambda g=g, y=None, gy=out, gw=None, outer=2, inner=1, ws=1 << 16, wsb=1 << 26: lib.iso_vjp_view(  # noqa
+        g, ctypes.byref(bc), y, gy, gw, outer, inner, ws, wsb, None)
+    assert call(g=None) == E
+    assert call(gy=None) == E                              # no output
+    assert call(gw=_v(data=1 << 21)) == E                  # grad_w without y
+    assert call(outer=3) == E                              # rows differ from the handle's
+    assert call(gy=_v(data=1 << 20, dt=iso.ISO_F64)) == E  # float64 output of a float32 fit
+    assert call(gy=_v(data=1 << 20, se=0)) == E
+    assert call(ws=None) == E
+    assert call(wsb=8) == E
+    bc.rows = 0
+    assert call(outer=0) == iso.ISO_OK

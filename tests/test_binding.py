@@ -113,3 +113,39 @@ def test_calibration_arguments_are_checked():
         iso.calibrate(_y(shape=(3, 7)), xs, fit, m, out=_y(shape=(3, 8)))
     with pytest.raises(ValueError, match="GPU"):
         iso.calibrate(_y(shape=(3, 7)), xs, fit, m)
+
+
+def test_view_entry_points_need_device_tensors():
+    with pytest.raises(ValueError, match="GPU"):
+        iso.iso_fit_view(_y())
+    with pytest.raises(ValueError, match="GPU"):
+        iso.isotonic(_y(), dim=0)
+
+
+def test_fold_gives_the_logical_rows():
+    """_fold reads only shapes and strides: the [outer, inner, n] geometry of a fit along an axis."""
+    y = torch.zeros(6, 50)
+    assert iso._fold(y.shape, 1, [y]) == (1, 6, 50, [(0, 50, 1)])
+    assert iso._fold(y.shape, 0, [y]) == (1, 50, 6, [(0, 1, 50)])          # down the columns
+    z = torch.zeros(3, 70, 5)
+    assert iso._fold(z.shape, 1, [z]) == (3, 5, 70, [(350, 1, 5)])         # two batch strides
+    q = torch.zeros(2, 3, 4, 9)
+    assert iso._fold(q.shape, 3, [q]) == (1, 24, 9, [(0, 9, 1)])           # batch axes folded into one
+    w = torch.zeros(9).expand(2, 3, 4, 9)
+    assert iso._fold(q.shape, 3, [q, w]) == (1, 24, 9, [(0, 9, 1), (0, 0, 1)])  # a shared weight vector
+    c = torch.zeros(6, 1).expand(6, 50)
+    assert iso._fold(y.shape, 1, [y, c]) == (1, 6, 50, [(0, 50, 1), (0, 1, 0)])  # one weight per row
+    one = torch.zeros(1, 7)
+    assert iso._fold(one.shape, 1, [one]) == (1, 1, 7, [(0, 0, 1)])
+    assert iso._fold((5, 1), 1, [torch.zeros(5, 1)])[2:] == (1, [(0, 1, 1)])  # n = 1: elements adjacent
+    p = torch.zeros(3, 4, 5, 60).permute(1, 0, 2, 3)
+    with pytest.raises(ValueError, match="two batch strides"):
+        iso._fold(p.shape, 3, [p])
+
+
+def test_result_dtype_follows_the_semantics():
+    assert iso._result_dtype(torch.zeros(2, dtype=torch.float16)) == torch.float16
+    assert iso._result_dtype(torch.zeros(2, dtype=torch.bfloat16)) == torch.bfloat16
+    assert iso._result_dtype(torch.zeros(2, dtype=torch.int64)) == torch.get_default_dtype()
+    with pytest.raises(TypeError):
+        iso._result_dtype(torch.zeros(2, dtype=torch.complex64))

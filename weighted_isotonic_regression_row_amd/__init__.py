@@ -36,6 +36,10 @@ LIB_PATH = os.path.join(_HERE, "libiso.so")
 
 ISO_F32 = 0
 ISO_F64 = 1
+ISO_F16 = 2
+ISO_BF16 = 3
+ISO_I32 = 4
+ISO_I64 = 5
 ISO_OK = 0
 ISO_EINVAL = -1
 ISO_EHIP = -2
@@ -45,7 +49,8 @@ NOALLOC_SCRATCH_BYTES = 128 << 20
 
 SYMBOLS = ("iso_workspace_bytes", "iso_blocks_bytes", "iso_fit", "iso_fit_noalloc", "iso_vjp", "iso_vjp_yw", "iso_soft_rank_state_bytes",
            "iso_soft_rank_workspace_bytes", "iso_soft_rank", "iso_soft_rank_vjp", "iso_calibration_workspace_bytes",
-           "iso_calibration_fit", "iso_calibrate", "iso_status", "iso_strerror")
+           "iso_calibration_fit", "iso_calibrate", "iso_status", "iso_strerror", "iso_view_workspace_bytes",
+           "iso_view_blocks_bytes", "iso_fit_view", "iso_vjp_view")
 SOFT_RANK_MAX_N = 8192
 
 
@@ -74,6 +79,18 @@ class IsoSoftRankStateC(ctypes.Structure):
         ("rank_dev", ctypes.c_void_p),
         ("eps", ctypes.c_double),
         ("valid", ctypes.c_int),
+    ]
+
+
+class IsoViewC(ctypes.Structure):
+    """Mirror of struct iso_view (include/iso.h)."""
+
+    _fields_ = [
+        ("data", ctypes.c_void_p),
+        ("dtype", ctypes.c_int),
+        ("stride_outer", ctypes.c_int64),
+        ("stride_inner", ctypes.c_int64),
+        ("stride_elem", ctypes.c_int64),
     ]
 
 
@@ -125,6 +142,16 @@ def load_library(path: str | None = None):
     lib.iso_calibration_fit.argtypes = [vp, vp, i64, i64, c_int, vp, vp, vp, vp, c_size, vp]
     lib.iso_calibrate.restype = c_int
     lib.iso_calibrate.argtypes = [vp, vp, vp, i64, i64, vp, i64, c_int, vp, vp]
+    lib.iso_view_workspace_bytes.restype = c_size
+    lib.iso_view_workspace_bytes.argtypes = [i64, i64, c_int]
+    lib.iso_view_blocks_bytes.restype = c_size
+    lib.iso_view_blocks_bytes.argtypes = [i64, i64, c_int, c_int]
+    pv = ctypes.POINTER(IsoViewC)
+    lib.iso_fit_view.restype = c_int
+    lib.iso_fit_view.argtypes = [pv, pv, i64, i64, i64, c_int, c_double, c_double, pv, ctypes.POINTER(IsoBlocksC),
+                                 vp, vp, c_size, vp]
+    lib.iso_vjp_view.restype = c_int
+    lib.iso_vjp_view.argtypes = [pv, ctypes.POINTER(IsoBlocksC), pv, pv, pv, i64, i64, vp, c_size, vp]
     lib.iso_status.restype = c_int
     lib.iso_status.argtypes = [vp, vp]
     lib.iso_strerror.restype = ctypes.c_char_p
@@ -363,6 +390,200 @@ def iso_vjp_yw(grad: torch.Tensor, blocks: Blocks, y: torch.Tensor, *, want_y: b
     return (None if gy is None else gy.view(blocks.shape)), gw.view(blocks.shape)
 
 
+# ---------------------------------------------------------------------------
+# views: any axis, broadcast weights, float16 / bfloat16 / integer inputs
+# (page "torchisotonic", "Semantics")
+# ---------------------------------------------------------------------------
+
+_VIEW_CODES = {torch.float32: ISO_F32, torch.float64: ISO_F64, torch.float16: ISO_F16, torch.bfloat16: ISO_BF16,
+               torch.int32: ISO_I32, torch.int64: ISO_I64}
+
+
+def _view_code(t: torch.Tensor, output: bool = False) -> int:
+    c = _VIEW_CODES.get(t.dtype)
+    if c is None or (output and c > ISO_BF16):
+        raise TypeError(f"unsupported dtype {t.dtype}")
+    return c
+
+
+def _result_dtype(y: torch.Tensor) -> torch.dtype:
+    """Float input keeps its dtype; integer input becomes the default float dtype (PyPI page, "Semantics")."""
+    if y.dtype in (torch.float16, torch.bfloat16, torch.float32, torch.float64):
+        return y.dtype
+    if y.dtype in (torch.int32, torch.int64, torch.int16, torch.int8, torch.uint8, torch.bool):
+        return torch.get_default_dtype()
+    raise TypeError(f"unsupported dtype {y.dtype}")
+
+
+def _fold(shape, axis: int, tensors):
+    """The logical [outer, inner, n] geometry of a fit along `axis`: the other axes, in order, with size-1 axes
+    dropped and neighbours merged where every tensor's strides allow it.  Returns (outer, inner, n, strides),
+    strides[k] = (outer, inner, elem) element strides of tensors[k]; ValueError if more than two batch strides
+    remain."""
+    n = shape[axis]
+    groups = []  # [size, [stride of each tensor at the group's innermost axis]]
+    for k, size in enumerate(shape):
+        if k == axis or size == 1:
+            continue
+        st = [t.stride(k) for t in tensors]
+        if groups and all(g == s_ * size for g, s_ in zip(groups[-1][1], st)):
+            groups[-1][0] *= size
+            groups[-1][1] = st
+        else:
+            groups.append([size, st])
+    if len(groups) > 2:
+        raise ValueError("this layout needs more than two batch strides; pass a contiguous tensor")
+    while len(groups) < 2:
+        groups.insert(0, [1, [0] * len(tensors)])
+    (outer, so), (inner, si) = groups
+    strides = [(so[k], si[k], t.stride(axis) if n > 1 else 1) for k, t in enumerate(tensors)]
+    return outer, inner, n, strides
+
+
+def _view(t: torch.Tensor | None, strides, output: bool = False):
+    if t is None:
+        return None
+    return IsoViewC(t.data_ptr(), _view_code(t, output), *strides)
+
+
+def _view_ws(rows: int, n: int, cdt: int, device) -> torch.Tensor:
+    return torch.empty(max(int(load_library().iso_view_workspace_bytes(rows, n, cdt)), 256), dtype=torch.uint8,
+                       device=device)
+
+
+class ViewBlocks(Blocks):
+    """Partition handle of iso_fit_view: the logical rows r = o * inner + j of the fit, plus the geometry."""
+
+    def __init__(self, c, mem, w, shape, axis, outer, inner, out_dtype):
+        super().__init__(c, mem, w, shape)
+        self.axis, self.outer, self.inner, self.out_dtype = axis, outer, inner, out_dtype
+
+
+def iso_fit_view(y: torch.Tensor, w: torch.Tensor | None = None, increasing: bool = True,
+                 y_min: float | None = None, y_max: float | None = None, *, dim: int = -1, blocks: bool = True,
+                 ws: torch.Tensor | None = None, check: bool = True):
+    """Fit y along axis `dim` (include/iso.h, iso_fit_view).  y: any strided device tensor of float16, bfloat16,
+    float32, float64, int32 or int64; w: None or a tensor that broadcasts to y's shape.  The result has y's shape
+    and y's dtype (integer y: the default float dtype).  Returns (fit, ViewBlocks or None)."""
+    _require_cuda(y, "iso_fit_view")
+    if y.dim() == 0:
+        raise ValueError("y needs at least one axis")
+    axis = dim % y.dim()
+    shape = tuple(y.shape)
+    if w is not None:
+        _check_device(w, y.device, "w")
+        try:
+            w = w.expand(shape)
+        except RuntimeError as e:
+            raise ValueError(f"w of shape {tuple(w.shape)} does not broadcast to {shape}") from e
+    _check_ws(ws, y.device)
+    # the output keeps y's layout when y is dense (so it folds as y does), else it is contiguous
+    out = torch.empty_like(y, dtype=_result_dtype(y), memory_format=torch.preserve_format)
+    tensors = [y, out] + ([w] if w is not None else [])
+    outer, inner, n, strides = _fold(shape, axis, tensors)
+    rows = outer * inner
+    cdt = ISO_F64 if (y.dtype == torch.float64 or out.dtype == torch.float64) else ISO_F32
+    lib = load_library()
+    if ws is None:
+        ws = _view_ws(rows, n, cdt, y.device)
+    bc = IsoBlocksC()
+    mem = None
+    if blocks:
+        nb = int(lib.iso_view_blocks_bytes(rows, n, cdt, 1 if w is not None else 0))
+        mem = torch.empty(max(nb, 256), dtype=torch.uint8, device=y.device)
+    lo = -math.inf if y_min is None else float(y_min)
+    hi = math.inf if y_max is None else float(y_max)
+    yv, ov = _view(y, strides[0]), _view(out, strides[1], output=True)
+    wv = _view(w, strides[2]) if w is not None else None
+    code = lib.iso_fit_view(ctypes.byref(yv), None if wv is None else ctypes.byref(wv), outer, inner, n,
+                            1 if increasing else 0, lo, hi, ctypes.byref(ov), ctypes.byref(bc) if blocks else None,
+                            None if mem is None else mem.data_ptr(), ws.data_ptr(), ws.numel(),
+                            _stream_ptr(y.device))
+    if code != ISO_OK:
+        raise IsoError(code, "iso_fit_view")
+    if check and rows * n > 0:
+        st = lib.iso_status(ws.data_ptr(), _stream_ptr(y.device))
+        if st == ISO_EWEIGHT:
+            raise ValueError("weights must be strictly positive")
+        if st != ISO_OK:
+            raise IsoError(st, "iso_status")
+    vb = ViewBlocks(bc, mem, w, shape, axis, outer, inner, out.dtype) if blocks else None
+    return out, vb
+
+
+def iso_vjp_view(grad: torch.Tensor, blocks: ViewBlocks, y: torch.Tensor | None = None, *, want_y: bool = True,
+                 ws: torch.Tensor | None = None):
+    """(grad_y or None, grad_w or None) of a fit made by iso_fit_view (include/iso.h, iso_vjp_view).  grad has
+    the fit's shape; grad_w (when y, the tensor the fit was given, is passed) is per element of y's shape: for
+    broadcast weights its sum over the broadcast axes is the product in the caller's weights."""
+    _require_cuda(grad, "iso_vjp_view")
+    shape = blocks.shape
+    if tuple(grad.shape) != shape:
+        raise ValueError(f"grad must have the fit's shape {shape}")
+    _check_device(grad, blocks.mem.device, "grad")
+    if y is not None:
+        if tuple(y.shape) != shape:
+            raise ValueError(f"y must have the fit's shape {shape}")
+        _check_device(y, grad.device, "y")
+    if not want_y and y is None:
+        raise ValueError("nothing to compute: want_y=False and no y for the product in w")
+    _check_ws(ws, grad.device)
+    like = y if y is not None else grad
+    gy = torch.empty_like(like, dtype=blocks.out_dtype, memory_format=torch.preserve_format) if want_y else None
+    gw = torch.empty_like(like, dtype=blocks.out_dtype, memory_format=torch.preserve_format) if y is not None else None
+    tensors = [grad] + [t for t in (y, gy, gw) if t is not None]
+    outer, inner, n, strides = _fold(shape, blocks.axis, tensors)
+    if outer * inner != blocks.c.rows:
+        raise ValueError("grad's layout does not match the fit's rows")
+    k = iter(strides[1:])
+    yv = _view(y, next(k)) if y is not None else None
+    gyv = _view(gy, next(k), output=True) if gy is not None else None
+    gwv = _view(gw, next(k), output=True) if gw is not None else None
+    gv = _view(grad, strides[0])
+    lib = load_library()
+    if ws is None:
+        ws = _view_ws(outer * inner, n, blocks.c.dtype, grad.device)
+    ref = lambda v: None if v is None else ctypes.byref(v)  # noqa: E731
+    code = lib.iso_vjp_view(ctypes.byref(gv), ctypes.byref(blocks.c), ref(yv), ref(gyv), ref(gwv), outer, inner,
+                            ws.data_ptr(), ws.numel(), _stream_ptr(grad.device))
+    if code != ISO_OK:
+        raise IsoError(code, "iso_vjp_view")
+    return gy, gw
+
+
+class _Isotonic(torch.autograd.Function):
+    """The fit as a differentiable function of y and of (broadcast-expanded) w."""
+
+    @staticmethod
+    def forward(ctx, y, w, increasing, y_min, y_max, dim):
+        fit, blocks = iso_fit_view(y, w, increasing, y_min, y_max, dim=dim)
+        ctx.blocks = blocks
+        ctx.save_for_backward(y)
+        return fit
+
+    @staticmethod
+    def backward(ctx, grad):
+        (y,) = ctx.saved_tensors
+        need_y, need_w = ctx.needs_input_grad[0], ctx.needs_input_grad[1]
+        gy, gw = iso_vjp_view(grad, ctx.blocks, y if need_w else None, want_y=True)
+        return (gy if need_y else None), gw, None, None, None, None
+
+
+def isotonic(y: torch.Tensor, w: torch.Tensor | None = None, *, increasing: bool = True,
+             y_min: float | None = None, y_max: float | None = None, dim: int = -1) -> torch.Tensor:
+    """The isotonic fit with the PyPI page's semantics ("Semantics"): strictly positive weights of y's shape or
+    broadcast to it, clipping to [y_min, y_max] after the fit, `dim` picks the axis, a row holding a NaN comes
+    back NaN, float input keeps its dtype (float16 and bfloat16 computed in float32), integer input becomes the
+    default float dtype; differentiable in y and in w (for a broadcast w, autograd sums the per-element product
+    over the broadcast axes)."""
+    if w is not None and w.requires_grad:
+        w = w.expand(y.shape)  # the expand's backward reduces grad_w to w's shape
+    if torch.is_grad_enabled() and (y.requires_grad or (w is not None and w.requires_grad)):
+        return _Isotonic.apply(y, w, increasing, y_min, y_max, dim)
+    fit, _ = iso_fit_view(y, w, increasing, y_min, y_max, dim=dim, blocks=False)
+    return fit
+
+
 class SoftRankState:
     """Backward state of soft_rank (struct iso_soft_rank_state plus the memory behind it)."""
 
@@ -508,7 +729,7 @@ def iso_status(ws: torch.Tensor) -> int:
     return int(load_library().iso_status(ws.data_ptr(), _stream_ptr(ws.device)))
 
 
-__all__ = ["iso_fit", "iso_fit_noalloc", "iso_vjp", "iso_vjp_yw", "soft_rank", "soft_rank_vjp", "SoftRankState", "soft_rank_workspace",
+__all__ = ["isotonic", "iso_fit_view", "iso_vjp_view", "ViewBlocks", "iso_fit", "iso_fit_noalloc", "iso_vjp", "iso_vjp_yw", "soft_rank", "soft_rank_vjp", "SoftRankState", "soft_rank_workspace",
            "calibration_fit", "calibrate", "calibration_workspace",
            "SOFT_RANK_MAX_N", "iso_status", "iso_workspace_bytes", "iso_blocks_bytes", "workspace",
            "Blocks", "IsoError", "load_library", "SYMBOLS"]

@@ -9,6 +9,7 @@
 #include "../../include/iso.h"
 #include "iso_compose.hpp"
 #include "iso_internal.hpp"
+#include "iso_prepare.hpp"
 
 namespace {
 
@@ -23,23 +24,14 @@ bool valid_dtype(int d) { return d == ISO_F32 || d == ISO_F64; }
 
 }  // namespace
 
-extern "C" {
+namespace iso {
 
-size_t iso_workspace_bytes(int64_t rows, int64_t n, int dtype) {
-    if (rows < 0 || n < 0 || !valid_dtype(dtype)) return 0;
-    return iso::make_layout(rows, n).total;
-}
-
-size_t iso_blocks_bytes(int64_t rows, int64_t n) {
-    if (rows < 0 || n < 0) return 0;
-    const size_t words = (size_t)((n + 63) / 64);
-    const size_t bits = iso::align256(8 * words * (size_t)rows);
-    return 2 * bits + iso::align256(4 * (size_t)rows) + 256;
-}
-
-int iso_fit(const void* y, const void* w, int64_t rows, int64_t n, int increasing, double y_min, double y_max,
-            int dtype, void* fit, iso_blocks* blocks_out, void* blocks_mem, void* workspace,
-            size_t workspace_bytes, void* stream) {
+// iso_fit's argument checks, the partition handle and the launch record:
+// returns 1 when kernels are to be launched (a is filled), else the code the
+// call returns (ISO_OK for an empty problem, ISO_EINVAL).  Nothing is queued.
+int fit_prepare(const void* y, const void* w, int64_t rows, int64_t n, int increasing, double y_min, double y_max,
+                int dtype, void* fit, iso_blocks* blocks_out, void* blocks_mem, void* workspace,
+                size_t workspace_bytes, void* stream, FitLaunch& a) {
     if (rows < 0 || n < 0 || !valid_dtype(dtype)) return ISO_EINVAL;
     if (increasing != 0 && increasing != 1) return ISO_EINVAL;
     if ((blocks_out == nullptr) != (blocks_mem == nullptr)) return ISO_EINVAL;
@@ -83,7 +75,7 @@ int iso_fit(const void* y, const void* w, int64_t rows, int64_t n, int increasin
     if (overlaps(y) || overlaps(w)) return ISO_EINVAL;
 
     const unsigned long long epoch = ++g_epoch;
-    iso::FitLaunch a{};
+    a = iso::FitLaunch{};
     a.y = y;
     a.w = w;
     a.fit = fit;
@@ -101,13 +93,12 @@ int iso_fit(const void* y, const void* w, int64_t rows, int64_t n, int increasin
     a.L = L;
     a.epoch = epoch;
     a.stream = (hipStream_t)stream;
-    if (iso::launch_fit(a) != hipSuccess) return ISO_EHIP;
-    if (blocks_out) blocks_out->valid = 1;
-    return ISO_OK;
+    return 1;
 }
 
-int iso_vjp_yw(const void* grad, const iso_blocks* blocks, const void* y, void* grad_y, void* grad_w,
-               void* workspace, size_t workspace_bytes, void* stream) {
+// iso_vjp_yw's argument checks and launch record (returns as fit_prepare).
+int vjp_prepare(const void* grad, const iso_blocks* blocks, const void* y, void* grad_y, void* grad_w,
+                void* workspace, size_t workspace_bytes, void* stream, VjpLaunch& v) {
     if (!blocks || !blocks->valid) return ISO_EINVAL;
     if (blocks->rows < 0 || blocks->n < 0 || !valid_dtype(blocks->dtype)) return ISO_EINVAL;
     if (blocks->rows == 0 || blocks->n == 0) return ISO_OK;
@@ -118,7 +109,7 @@ int iso_vjp_yw(const void* grad, const iso_blocks* blocks, const void* y, void* 
     if (((uintptr_t)workspace & 255u) != 0) return ISO_EINVAL;
     const iso::Layout L = iso::make_layout(blocks->rows, blocks->n);
     if (workspace_bytes < L.total) return ISO_EINVAL;
-    iso::VjpLaunch v{};
+    v = iso::VjpLaunch{};
     v.g = grad;
     v.w = blocks->w_dev;
     v.y = y;
@@ -134,6 +125,42 @@ int iso_vjp_yw(const void* grad, const iso_blocks* blocks, const void* y, void* 
     v.ws = (char*)workspace;
     v.L = L;
     v.stream = (hipStream_t)stream;
+    return 1;
+}
+
+}  // namespace iso
+
+extern "C" {
+
+size_t iso_workspace_bytes(int64_t rows, int64_t n, int dtype) {
+    if (rows < 0 || n < 0 || !valid_dtype(dtype)) return 0;
+    return iso::make_layout(rows, n).total;
+}
+
+size_t iso_blocks_bytes(int64_t rows, int64_t n) {
+    if (rows < 0 || n < 0) return 0;
+    const size_t words = (size_t)((n + 63) / 64);
+    const size_t bits = iso::align256(8 * words * (size_t)rows);
+    return 2 * bits + iso::align256(4 * (size_t)rows) + 256;
+}
+
+int iso_fit(const void* y, const void* w, int64_t rows, int64_t n, int increasing, double y_min, double y_max,
+            int dtype, void* fit, iso_blocks* blocks_out, void* blocks_mem, void* workspace,
+            size_t workspace_bytes, void* stream) {
+    iso::FitLaunch a{};
+    const int rc = iso::fit_prepare(y, w, rows, n, increasing, y_min, y_max, dtype, fit, blocks_out, blocks_mem,
+                                    workspace, workspace_bytes, stream, a);
+    if (rc != 1) return rc;
+    if (iso::launch_fit(a) != hipSuccess) return ISO_EHIP;
+    if (blocks_out) blocks_out->valid = 1;
+    return ISO_OK;
+}
+
+int iso_vjp_yw(const void* grad, const iso_blocks* blocks, const void* y, void* grad_y, void* grad_w,
+               void* workspace, size_t workspace_bytes, void* stream) {
+    iso::VjpLaunch v{};
+    const int rc = iso::vjp_prepare(grad, blocks, y, grad_y, grad_w, workspace, workspace_bytes, stream, v);
+    if (rc != 1) return rc;
     if (iso::launch_vjp(v) != hipSuccess) return ISO_EHIP;
     return ISO_OK;
 }
