@@ -513,6 +513,10 @@ def main():
     if args.workload in ("soft_rank", "all"):
         log("soft rank 4096 x 512 ...")
         rec["soft_rank"] = time_soft_rank(args.steps)
+        # the long shapes of the first page's Table 6, sorted by tiles and merge passes
+        log("soft rank 64 x 10^4 and 1 x 10^6 ...")
+        rec["soft_rank_64x10000"] = time_soft_rank(max(2, args.steps // 5), 64, 10_000)
+        rec["soft_rank_1x1000000"] = time_soft_rank(max(2, args.steps // 5), 1, 1_000_000)
 
     if args.workload in ("calibration", "all"):
         log("calibration 6.5e6 ...")

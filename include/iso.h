@@ -297,8 +297,10 @@ int iso_vjp_view(const iso_view* grad, const iso_blocks* blocks, const iso_view*
  * when eps is small enough, and tied values share one rank.  Equal values are
  * sorted in index order.  A row holding a NaN comes back NaN.
  *
- * Rows of at most ISO_SOFT_RANK_MAX_N elements (one workgroup sorts a row).
- * The state keeps what the backward pass needs: the sorting permutation, its
+ * Rows of any length up to INT32_MAX elements: rows of at most 8192 are
+ * sorted by one workgroup each, longer rows (the first page's Table 6 runs
+ * rows of 10^4 to 10^6) by tiles of 2048 and merge passes, as the
+ * calibration scores are.  The state keeps what the backward pass needs: the sorting permutation, its
  * inverse, and the fit's partition over the sorted positions.
  *   blocks     partition of the fit of z in sorted order (w_dev is NULL, no
  *              clipping);
@@ -307,8 +309,6 @@ int iso_vjp_view(const iso_view* grad, const iso_blocks* blocks, const iso_view*
  *   rank_dev   [rows, n] int32: the inverse of perm within each row;
  *   eps        the strength the ranks were computed with.
  */
-#define ISO_SOFT_RANK_MAX_N 8192
-
 typedef struct iso_soft_rank_state {
     iso_blocks blocks;
     int32_t* perm_dev;
@@ -321,7 +321,9 @@ typedef struct iso_soft_rank_state {
 size_t iso_soft_rank_state_bytes(int64_t rows, int64_t n);
 
 /* Bytes of device workspace iso_soft_rank and iso_soft_rank_vjp need
- * (256-byte aligned; 0 for invalid sizes or n > ISO_SOFT_RANK_MAX_N). */
+ * (256-byte aligned; 0 for invalid sizes, n > INT32_MAX or a bad dtype):
+ * the solver's workspace, z and its fit, and for rows longer than 8192 the
+ * sort's keys and indices (24 bytes per element). */
 size_t iso_soft_rank_workspace_bytes(int64_t rows, int64_t n, int dtype);
 
 /*
@@ -333,7 +335,7 @@ size_t iso_soft_rank_workspace_bytes(int64_t rows, int64_t n, int dtype);
  *   state_mem_dev  iso_soft_rank_state_bytes(rows, n) bytes, 256-aligned.
  *   workspace_dev  iso_soft_rank_workspace_bytes(rows, n, dtype) bytes,
  *                  256-aligned; one call in flight per workspace.
- * ISO_EINVAL for n > ISO_SOFT_RANK_MAX_N, a bad eps or dtype, NULL pointers,
+ * ISO_EINVAL for n or rows > INT32_MAX, a bad eps or dtype, NULL pointers,
  * misaligned or short buffers.  rows == 0 or n == 0 queues nothing.
  */
 int iso_soft_rank(const void* x_dev, int64_t rows, int64_t n, double eps, int dtype, void* r_dev,

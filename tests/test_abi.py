@@ -150,7 +150,9 @@ def test_vjp_yw_rejects_bad_arguments_on_host(lib):
 
 def test_soft_rank_sizes(lib):
     assert lib.iso_soft_rank_workspace_bytes(4096, 512, 0) >= 2 * 4096 * 512 * 4
-    assert lib.iso_soft_rank_workspace_bytes(4, 8193, 0) == 0      # longer than one workgroup sorts
+    # longer than one workgroup sorts: the tiled sort's keys and indices too
+    assert lib.iso_soft_rank_workspace_bytes(4, 8193, 0) >= lib.iso_soft_rank_workspace_bytes(4, 8192, 0) + 4 * 8193 * 24
+    assert lib.iso_soft_rank_workspace_bytes(1, 1 << 31, 0) == 0
     assert lib.iso_soft_rank_workspace_bytes(4, 8192, 1) >= 2 * 4 * 8192 * 8
     assert lib.iso_soft_rank_workspace_bytes(-1, 5, 0) == 0
     assert lib.iso_soft_rank_workspace_bytes(2, 5, 3) == 0
@@ -169,7 +171,7 @@ def _sr(lib, x=256, rows=2, n=3, eps=1.0, dt=0, r=512, st=True, mem=8192, ws=1 <
 def test_soft_rank_rejects_bad_arguments_on_host(lib):
     import weighted_isotonic_regression_row_amd as iso
     E = iso.ISO_EINVAL
-    for kw in ({"rows": -1}, {"n": -1}, {"n": 8193}, {"dt": 2}, {"eps": 0.0}, {"eps": -1.0}, {"eps": math.inf},
+    for kw in ({"rows": -1}, {"n": -1}, {"n": 1 << 31}, {"rows": 1 << 31}, {"dt": 2}, {"eps": 0.0}, {"eps": -1.0}, {"eps": math.inf},
                {"eps": math.nan}, {"st": False}, {"mem": None}, {"mem": 8192 + 8}, {"x": None}, {"r": None},
                {"ws": None}, {"ws": (1 << 16) + 8}, {"wsb": 8}, {"r": 256 + 4}):
         assert _sr(lib, **kw)[0] == E, kw

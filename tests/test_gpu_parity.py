@@ -432,7 +432,7 @@ def test_empty_inputs():
 
 # ---------------------------------------------------------------- soft rank (first page, Sec. 7.9)
 
-SR_SIZES = [1, 2, 63, 65, 100, 512, 1000, 4096, 5000, 6144, 6145, 8192]
+SR_SIZES = [1, 2, 63, 65, 100, 512, 1000, 4096, 5000, 6144, 6145, 8192, 8193, 10000, 30001]
 
 
 def _soft_rank_case(x, eps, dtype, what, check_partition=None):
@@ -504,6 +504,27 @@ def test_soft_rank_config3_shape():
         d = iso.soft_rank_vjp(to_dev(g), st).cpu().numpy().astype(np.float64)
         ref = oracle.soft_rank_vjp(g.astype(np.float64), eps, perm, gsb, grn)
         assert float(np.max(np.abs(d - ref))) <= 2e-6 * max(1.0, float(np.abs(ref).max()))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("rows,n,dtype", [(64, 10_000, np.float32), (1, 1_000_000, np.float32),
+                                          (1, 1_000_000, np.float64)])
+def test_soft_rank_long_rows(rows, n, dtype):
+    """The long soft-rank shapes of the first page's Table 6 (64 x 10^4 and 1 x 10^6), sorted by tiles and
+    merge passes: permutation bit for bit, ranks and the product against the oracle, at eps = 1 and 1/n."""
+    import weighted_isotonic_regression_row_amd as iso
+    x, g = workloads.soft_rank_input(rows, n, seed=29, dtype=dtype)
+    if rows > 1:
+        x[rows // 2, n // 3] = np.nan  # that row alone comes back NaN
+    for eps in (1.0, 1.0 / n):
+        _print(f"soft rank {rows}x{n} {np.dtype(dtype).name} eps={eps}")
+        st, perm, (gsb, grn), _ = _soft_rank_case(x, eps, dtype, f"{rows}x{n} eps={eps}")
+        d = iso.soft_rank_vjp(to_dev(g), st).cpu().numpy().astype(np.float64)
+        ref = oracle.soft_rank_vjp(g.astype(np.float64), eps, perm, gsb, grn)
+        assert np.array_equal(np.isnan(d), np.isnan(ref)), f"{rows}x{n} eps={eps}: NaN rows of the product"
+        ok = ~np.isnan(ref)
+        tol = (1e-12 if dtype == np.float64 else 2e-6) * max(1.0, float(np.abs(ref[ok]).max()))
+        assert float(np.max(np.abs(d[ok] - ref[ok]))) <= tol, f"{rows}x{n} eps={eps}: product"
 
 
 @pytest.mark.gpu

@@ -51,7 +51,6 @@ SYMBOLS = ("iso_workspace_bytes", "iso_blocks_bytes", "iso_fit", "iso_fit_noallo
            "iso_soft_rank_workspace_bytes", "iso_soft_rank", "iso_soft_rank_vjp", "iso_calibration_workspace_bytes",
            "iso_calibration_fit", "iso_calibrate", "iso_status", "iso_strerror", "iso_view_workspace_bytes",
            "iso_view_blocks_bytes", "iso_fit_view", "iso_vjp_view")
-SOFT_RANK_MAX_N = 8192
 
 
 class IsoBlocksC(ctypes.Structure):
@@ -610,14 +609,15 @@ def soft_rank_workspace(rows: int, n: int, dtype: torch.dtype, device) -> torch.
     code = ISO_F32 if dtype == torch.float32 else ISO_F64
     nb = int(load_library().iso_soft_rank_workspace_bytes(rows, n, code))
     if nb == 0:
-        raise ValueError(f"soft rank needs rows of at most {SOFT_RANK_MAX_N} elements")
+        raise ValueError(f"bad soft-rank sizes {rows} x {n} or dtype {dtype}")
     return torch.empty(nb, dtype=torch.uint8, device=device)
 
 
 def soft_rank(x: torch.Tensor, eps: float = 1.0, *, out: torch.Tensor | None = None,
               ws: torch.Tensor | None = None):
     """Soft ranks of every row of x (first page, Sec. 7.9): the projection of x / eps onto the
-    permutahedron of (1..n).  Returns (ranks, state); rows of at most SOFT_RANK_MAX_N elements."""
+    permutahedron of (1..n).  Returns (ranks, state); rows of any length (longer than 8192: sorted by tiles
+    and merge passes)."""
     shape = x.shape
     x2 = _as_rows(x)
     if not x2.is_contiguous():
@@ -731,5 +731,5 @@ def iso_status(ws: torch.Tensor) -> int:
 
 __all__ = ["isotonic", "iso_fit_view", "iso_vjp_view", "ViewBlocks", "iso_fit", "iso_fit_noalloc", "iso_vjp", "iso_vjp_yw", "soft_rank", "soft_rank_vjp", "SoftRankState", "soft_rank_workspace",
            "calibration_fit", "calibrate", "calibration_workspace",
-           "SOFT_RANK_MAX_N", "iso_status", "iso_workspace_bytes", "iso_blocks_bytes", "workspace",
+           "iso_status", "iso_workspace_bytes", "iso_blocks_bytes", "workspace",
            "Blocks", "IsoError", "load_library", "SYMBOLS"]

@@ -177,9 +177,13 @@ size_t iso_soft_rank_state_bytes(int64_t rows, int64_t n) {
 }
 
 size_t iso_soft_rank_workspace_bytes(int64_t rows, int64_t n, int dtype) {
-    if (rows < 0 || n < 0 || n > iso::kRankMaxN || !valid_dtype(dtype)) return 0;
+    if (rows < 0 || n < 0 || n > (int64_t)INT32_MAX || !valid_dtype(dtype)) return 0;
     const size_t esz = dtype == ISO_F32 ? 4 : 8;
-    return iso::align256(iso::make_layout(rows, n).total) + 2 * iso::align256(esz * (size_t)rows * (size_t)n);
+    const size_t zoff = iso::align256(iso::make_layout(rows, n).total);
+    const size_t voff = zoff + iso::align256(esz * (size_t)rows * (size_t)n);
+    const size_t end = voff + iso::align256(esz * (size_t)rows * (size_t)n);
+    // rows sorted by tiles and merge passes also hold the sort's keys and indices
+    return n > iso::kRankMaxN ? iso::rank_sort_areas(rows, n, voff, esz).end : end;
 }
 
 namespace {
@@ -211,7 +215,9 @@ int iso_soft_rank(const void* x, int64_t rows, int64_t n, double eps, int dtype,
                   iso_soft_rank_state* state_out, void* state_mem, void* workspace, size_t workspace_bytes,
                   void* stream) {
     if (rows < 0 || n < 0 || !valid_dtype(dtype)) return ISO_EINVAL;
-    if (n > iso::kRankMaxN || rows > (int64_t)INT32_MAX) return ISO_EINVAL;
+    if (n > (int64_t)INT32_MAX || rows > (int64_t)INT32_MAX) return ISO_EINVAL;
+    // the merge passes' grids: one workgroup per 2048 outputs of every row
+    if (n > iso::kRankMaxN && rows * ((n + 2047) / 2048) > (int64_t)UINT32_MAX) return ISO_EINVAL;
     if (!(eps > 0.0) || !isfinite(eps)) return ISO_EINVAL;
     if (!state_out || !state_mem) return ISO_EINVAL;
     if (((uintptr_t)state_mem & 255u) != 0) return ISO_EINVAL;
@@ -241,6 +247,8 @@ int iso_soft_rank(const void* x, int64_t rows, int64_t n, double eps, int dtype,
     if (!x || !r || !workspace) return ISO_EINVAL;
     if (((uintptr_t)workspace & 255u) != 0) return ISO_EINVAL;
     if (workspace_bytes < iso_soft_rank_workspace_bytes(rows, n, dtype)) return ISO_EINVAL;
+    const iso::Layout L = iso::make_layout(rows, n);
+    if (L.m > 0 && rows * L.m > (int64_t)UINT32_MAX) return ISO_EINVAL;  // the chunk grids of the fit
     const size_t bytes = (size_t)rows * (size_t)n * (dtype == ISO_F32 ? 4 : 8);
     const char* rb = (const char*)r;
     const char* xb = (const char*)x;
@@ -258,7 +266,7 @@ int iso_soft_rank_vjp(const void* grad, const iso_soft_rank_state* state, void* 
                       size_t workspace_bytes, void* stream) {
     if (!state || !state->valid || !state->blocks.valid) return ISO_EINVAL;
     const int64_t rows = state->blocks.rows, n = state->blocks.n;
-    if (rows < 0 || n < 0 || n > iso::kRankMaxN || !valid_dtype(state->blocks.dtype)) return ISO_EINVAL;
+    if (rows < 0 || n < 0 || n > (int64_t)INT32_MAX || !valid_dtype(state->blocks.dtype)) return ISO_EINVAL;
     if (rows == 0 || n == 0) return ISO_OK;
     if (!grad || !grad_x || !workspace || !state->perm_dev || !state->rank_dev) return ISO_EINVAL;
     if (!state->blocks.start_bits_dev || !state->blocks.clip_bits_dev || !state->blocks.row_nan_dev)

@@ -39,16 +39,18 @@ constexpr int kCalSortTile = 2048;
 constexpr int kPoolTile = 2048;  // 256 threads x 8
 constexpr int kMergeOut = 8;     // outputs per thread of a merge pass
 
-// Scores are sorted in increasing order by sorting -score in the network's
-// decreasing order (equal scores, -0 and +0 included, keep index order).
+// The network sorts in decreasing order of the key.  Scores are sorted in
+// increasing order by sorting -score (neg = 1); the soft rank sorts x itself
+// (neg = 0).  Equal values, -0 and +0 included, keep index order.
 template <typename T>
-__device__ __forceinline__ Ent cal_entry(T x, uint32_t idx) {
+__device__ __forceinline__ Ent cal_entry(T x, uint32_t idx, int neg) {
     Ent e;
+    const T v = neg ? -x : x;
     if constexpr (sizeof(T) == 4) {
-        e.k = ((uint64_t)sort_key((float)-x) << 32) | (uint32_t)~idx;
+        e.k = ((uint64_t)sort_key((float)v) << 32) | (uint32_t)~idx;
         e.i = 0u;
     } else {
-        e.k = sort_key((double)-x);
+        e.k = sort_key((double)v);
         e.i = idx;
     }
     return e;
@@ -61,6 +63,7 @@ struct CalSortArgs {
     int64_t n;
     int tiles;  // per row
     int P;      // network width of a tile
+    int neg;    // sort -x (increasing order of x) instead of x
 };
 
 template <typename T, int E>
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(1024) void k_cal_sort(CalSortArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
         if (e < cnt) {
-            v[e] = cal_entry<T>((T)xv[e], (uint32_t)(t0 + p0 + e));
+            v[e] = cal_entry<T>((T)xv[e], (uint32_t)(t0 + p0 + e), a.neg);
         } else {
             v[e].k = 0ull;
             v[e].i = 0xffffffffu;
@@ -488,39 +491,39 @@ hipError_t launch_cal_sort(const CalSortArgs& s, int64_t rows, hipStream_t strea
     return hipGetLastError();
 }
 
+// Every row sorted by tiles and merge passes into K[cur], I[cur] (indices
+// within the row; float32 keeps them in the key's low word).
 template <typename T>
-hipError_t cal_fit_t(const CalLaunch& l) {
-    const int64_t rows = l.rows, n = l.n;
-    char* ws = l.ws;
-    uint64_t* K[2] = {(uint64_t*)(ws + l.C.k0), (uint64_t*)(ws + l.C.k1)};
-    uint32_t* I[2] = {(uint32_t*)(ws + l.C.i0), (uint32_t*)(ws + l.C.i1)};
+hipError_t sort_rows_t(const void* x, int64_t rows, int64_t n, int neg, uint64_t* const K[2], uint32_t* const I[2],
+                       hipStream_t stream, int& cur) {
     // 1. sorted tiles
     CalSortArgs s{};
-    s.s = l.scores;
+    s.s = x;
     s.K = K[0];
     s.I = I[0];
     s.n = n;
     s.tiles = (int)((n + kCalSortTile - 1) / kCalSortTile);
+    s.neg = neg;
     int P = 64;
     while (P < n && P < kCalSortTile) P <<= 1;
     s.P = P;
     hipError_t e;
     switch (P) {
         case 64:
-            e = launch_cal_sort<T, 1>(s, rows, l.stream);
+            e = launch_cal_sort<T, 1>(s, rows, stream);
             break;
         case 128:
-            e = launch_cal_sort<T, 2>(s, rows, l.stream);
+            e = launch_cal_sort<T, 2>(s, rows, stream);
             break;
         case 256:
-            e = launch_cal_sort<T, 4>(s, rows, l.stream);
+            e = launch_cal_sort<T, 4>(s, rows, stream);
             break;
         default:
-            e = launch_cal_sort<T, 8>(s, rows, l.stream);
+            e = launch_cal_sort<T, 8>(s, rows, stream);
     }
     if (e != hipSuccess) return e;
     // 2. merges
-    int cur = 0;
+    cur = 0;
     for (int64_t L = kCalSortTile; L < n; L *= 2) {
         CalMergeArgs m{};
         m.Ki = K[cur];
@@ -530,10 +533,22 @@ hipError_t cal_fit_t(const CalLaunch& l) {
         m.n = n;
         m.L = L;
         const int64_t tiles = (n + kMergeTile - 1) / kMergeTile;
-        k_cal_merge<T><<<dim3((unsigned)(rows * tiles)), dim3(256), 0, l.stream>>>(m);
+        k_cal_merge<T><<<dim3((unsigned)(rows * tiles)), dim3(256), 0, stream>>>(m);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         cur ^= 1;
     }
+    return hipSuccess;
+}
+
+template <typename T>
+hipError_t cal_fit_t(const CalLaunch& l) {
+    const int64_t rows = l.rows, n = l.n;
+    char* ws = l.ws;
+    uint64_t* const K[2] = {(uint64_t*)(ws + l.C.k0), (uint64_t*)(ws + l.C.k1)};
+    uint32_t* const I[2] = {(uint32_t*)(ws + l.C.i0), (uint32_t*)(ws + l.C.i1)};
+    int cur = 0;
+    hipError_t e = sort_rows_t<T>(l.scores, rows, n, 1, K, I, l.stream, cur);
+    if (e != hipSuccess) return e;
     // 3. pooling of equal scores
     PoolArgs p{};
     p.K = K[cur];
@@ -600,6 +615,12 @@ hipError_t cal_predict_t(const CalPredictLaunch& l) {
 
 hipError_t launch_calibration_fit(const CalLaunch& l) {
     return l.dtype == 0 ? cal_fit_t<float>(l) : cal_fit_t<double>(l);
+}
+
+hipError_t launch_sort_rows(int dtype, const void* x, int64_t rows, int64_t n, int neg, uint64_t* const K[2],
+                           uint32_t* const I[2], hipStream_t stream, int& cur) {
+    return dtype == 0 ? sort_rows_t<float>(x, rows, n, neg, K, I, stream, cur)
+                      : sort_rows_t<double>(x, rows, n, neg, K, I, stream, cur);
 }
 
 hipError_t launch_calibrate(const CalPredictLaunch& l) {

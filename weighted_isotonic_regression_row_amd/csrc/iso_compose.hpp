@@ -74,7 +74,31 @@ struct CalPredictLaunch {
     hipStream_t stream;
 };
 
+// Soft-rank rows longer than one workgroup sorts: the sort's key and index
+// buffers follow the z and v arrays of the soft-rank workspace (v at voff).
+struct RankSortAreas {
+    size_t k0, k1, i0, i1, end;
+};
+
+inline RankSortAreas rank_sort_areas(int64_t rows, int64_t n, size_t voff, size_t esz) {
+    const size_t rn = (size_t)rows * (size_t)n;
+    RankSortAreas A{};
+    A.k0 = voff + align256(esz * rn);
+    A.k1 = A.k0 + align256(8 * rn);
+    A.i0 = A.k1 + align256(8 * rn);
+    A.i1 = A.i0 + align256(4 * rn);
+    A.end = A.i1 + align256(4 * rn);
+    return A;
+}
+
 hipError_t launch_calibration_fit(const CalLaunch& l);
+// Every row of x ([rows, n] of dtype) sorted by tiles of 2048 and merge passes
+// (iso_calib.hip) in decreasing order of x, or of -x when neg: K[cur] holds
+// the sorted keys and I[cur] the elements' indices within the row (float64;
+// float32 keeps the complemented index in the key's low word).  K[0..1] are
+// [rows * n] u64 and I[0..1] [rows * n] u32 buffers (I unused for float32).
+hipError_t launch_sort_rows(int dtype, const void* x, int64_t rows, int64_t n, int neg, uint64_t* const K[2],
+                           uint32_t* const I[2], hipStream_t stream, int& cur);
 hipError_t launch_calibrate(const CalPredictLaunch& l);
 
 }  // namespace iso

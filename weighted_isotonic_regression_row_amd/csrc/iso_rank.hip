@@ -14,6 +14,9 @@
 //   launch_fit     the fit of z and its block bits (the partition the backward
 //                  pass uses), over the sorted order;
 //   k_rank_finish  r[k] = x[k] / eps - v[rank[k]], element-wise.
+// Rows longer than one workgroup sorts (8192) are sorted like the calibration
+// scores (tiles of 2048 and merge passes, launch_sort_rows), and k_rank_long_z
+// then forms perm, rank and z from the sorted entries.
 // Backward, with g_s the upstream gradient in sorted order and A the block
 // averaging of the fit: d/dx = P^T (g_s - A g_s) / eps.
 //   k_rank_gather      g_s[i] = g[perm[i]];
@@ -21,6 +24,7 @@
 //   k_rank_vjp_finish  grad[k] = (g[k] - (A g_s)[rank[k]]) / eps.
 #include <math.h>
 
+#include "iso_compose.hpp"
 #include "iso_device.hpp"
 #include "iso_internal.hpp"
 #include "iso_sort.hpp"
@@ -237,6 +241,40 @@ __global__ __launch_bounds__(256) void k_rank_vjp_finish(EwArgs a) {
     }
 }
 
+// Rows sorted by launch_sort_rows: the entry at sorted position p of a row is
+// the element of index idx and value x; z[p] = x / eps - (n - p).
+struct LongZArgs {
+    const uint64_t* K;
+    const uint32_t* I;
+    int32_t* perm;
+    int32_t* rank;
+    void* z;
+    int64_t total;
+    int n;
+    int narrow;
+    double eps;
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rank_long_z(LongZArgs a) {
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < a.total; e += (int64_t)gridDim.x * 256) {
+        const int64_t base = row_base(e, a.n, a.narrow);
+        const int p = (int)(e - base);
+        uint32_t idx;
+        double x;
+        if constexpr (sizeof(T) == 4) {
+            idx = ~(uint32_t)a.K[e];
+            x = (double)key_value((uint32_t)(a.K[e] >> 32));
+        } else {
+            idx = a.I[e];
+            x = key_value(a.K[e]);
+        }
+        ((T*)a.z)[e] = (T)(x / a.eps - (double)(a.n - p));
+        a.perm[e] = (int32_t)idx;
+        if (idx < (uint32_t)a.n) a.rank[base + idx] = p;
+    }
+}
+
 int sort_width(int64_t n) {
     int P = 64;
     while (P < n) P <<= 1;
@@ -296,29 +334,50 @@ hipError_t soft_rank_t(const RankLaunch& l) {
         if (l.n <= 256) return launch_fused<T, 4>(l);
         return launch_fused<T, 8>(l);
     }
-    SortArgs s{};
-    s.x = l.in;
-    s.perm = l.perm;
-    s.rank = l.rank;
-    s.z = l.ws + l.zoff;
-    s.n = (int)l.n;
-    s.P = sort_width(l.n);
-    s.eps = l.eps;
     hipError_t e;
-    switch (s.P) {
-        case 64:
-            e = launch_sort<T, 1>(s, l.rows, l.stream);
-            break;
-        case 128:
-            e = launch_sort<T, 2>(s, l.rows, l.stream);
-            break;
-        case 256:
-            e = launch_sort<T, 4>(s, l.rows, l.stream);
-            break;
-        default:
-            e = launch_sort<T, 8>(s, l.rows, l.stream);
+    if (l.n > kRankMaxN) {
+        const RankSortAreas A = rank_sort_areas(l.rows, l.n, l.voff, sizeof(T));
+        uint64_t* const K[2] = {(uint64_t*)(l.ws + A.k0), (uint64_t*)(l.ws + A.k1)};
+        uint32_t* const I[2] = {(uint32_t*)(l.ws + A.i0), (uint32_t*)(l.ws + A.i1)};
+        int cur = 0;
+        if ((e = launch_sort_rows(sizeof(T) == 4 ? 0 : 1, l.in, l.rows, l.n, 0, K, I, l.stream, cur)) != hipSuccess)
+            return e;
+        LongZArgs z{};
+        z.K = K[cur];
+        z.I = I[cur];
+        z.perm = l.perm;
+        z.rank = l.rank;
+        z.z = l.ws + l.zoff;
+        z.total = l.rows * l.n;
+        z.n = (int)l.n;
+        z.narrow = z.total <= (int64_t)UINT32_MAX ? 1 : 0;
+        z.eps = l.eps;
+        k_rank_long_z<T><<<dim3(ew_grid(z.total)), dim3(256), 0, l.stream>>>(z);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        SortArgs s{};
+        s.x = l.in;
+        s.perm = l.perm;
+        s.rank = l.rank;
+        s.z = l.ws + l.zoff;
+        s.n = (int)l.n;
+        s.P = sort_width(l.n);
+        s.eps = l.eps;
+        switch (s.P) {
+            case 64:
+                e = launch_sort<T, 1>(s, l.rows, l.stream);
+                break;
+            case 128:
+                e = launch_sort<T, 2>(s, l.rows, l.stream);
+                break;
+            case 256:
+                e = launch_sort<T, 4>(s, l.rows, l.stream);
+                break;
+            default:
+                e = launch_sort<T, 8>(s, l.rows, l.stream);
+        }
+        if (e != hipSuccess) return e;
     }
-    if (e != hipSuccess) return e;
 
     FitLaunch f{};
     f.y = l.ws + l.zoff;
