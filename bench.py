@@ -114,6 +114,11 @@ def make_inputs(which):
         return workloads.cfg3_soft_rank()
     if which == "cfg4":
         return workloads.cfg4_calibration()
+    if which in ("packed65", "packed512"):
+        rows, n = (1_000_000, 65) if which == "packed65" else (10_000, 512)
+        wl = workloads.family("noise", rows, n, seed=65, dtype=np.float32, weights="uniform")
+        wl.name = f"packed_{rows}x{n}_f32"
+        return wl
     if which == "all_vertices":
         wl = workloads.family("increasing", 32, 1 << 22, seed=55, dtype=np.float64, weights="uniform")
         wl.name = "all_vertices_32x2^22_f64"
@@ -263,6 +268,9 @@ FIT_LEGS = {
               24, 10, None),
     "all_vertices": ("32 rows x 2^22 float64, y_i = i/n (every point a hull vertex), w~U(0.1,1.1), increasing",
                      24, 10, None),
+    # rows of 65 to 512 packed several to a wave (first page, Sec. 3.5)
+    "packed65": ("10^6 rows x 65 float32, y~N(0,1), w~U(0.1,1.1), increasing", 12, 20, 200_000),
+    "packed512": ("10^4 rows x 512 float32, y~N(0,1), w~U(0.1,1.1), increasing", 12, None, None),
 }
 
 
@@ -415,7 +423,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", choices=["batch", "cfg1", "cfg3", "cfg4", "dense", "all_vertices", "soft_rank",
+    ap.add_argument("--workload", choices=["batch", "cfg1", "cfg3", "cfg4", "dense", "all_vertices", "packed", "soft_rank",
                                            "calibration", "fits", "all", "both"], default="all")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU-baseline leg (profiling runs)")
     ap.add_argument("--copy-probe", action="store_true", help="time a plain device copy (also done by default runs)")
@@ -509,6 +517,10 @@ def main():
 
     if args.workload in ("all_vertices",) + fits:
         rec["all_vertices"] = fit_leg("all_vertices", args.steps, args.warmup, args.cpu_seconds / 2, args.no_cpu)
+
+    if args.workload in ("packed",) + fits:
+        for name in ("packed65", "packed512"):
+            rec[name] = fit_leg(name, args.steps, args.warmup, args.cpu_seconds / 2, args.no_cpu)
 
     if args.workload in ("soft_rank", "all"):
         log("soft rank 4096 x 512 ...")

@@ -166,6 +166,44 @@ def test_one_wave_rows_past_the_lds_list(n, dtype, inc):
     _check_vjp(wl, b, gs, gc, grn, n + 7, wl.name)
 
 
+PACK_SIZES = [65, 80, 81, 100, 127, 128, 129, 200, 256, 257, 300, 400, 511, 512]
+
+
+@pytest.mark.parametrize("n", PACK_SIZES)
+@pytest.mark.parametrize("dtype", [np.float32, np.float64])
+def test_packed_rows(n, dtype):
+    """Rows of 65 to 512 elements: up to 128 packed several to a wave (the first page, Sec. 3.5; dense waves
+    refitted by the second pass with 8 points per lane), longer ones a wave each.  1001 rows (the last wave
+    ragged) of noise, trend noise, increasing data (every point a vertex), a sawtooth and integer ties,
+    interleaved so that every wave mixes them, with a NaN row and a row with a weight <= 0 among them; both
+    orientations, clipped.  The fit, the partition and clip bits against the oracle, and both products."""
+    rows = 1001
+    kinds = [("noise", "uniform"), ("trend_noise", "extreme"), ("increasing", "uniform"), ("sawtooth", "unit"),
+             ("ties", "uniform")]
+    parts = [workloads.family(k, rows // len(kinds) + 1, n, seed=n + 13 * j, dtype=dtype, weights=wt)
+             for j, (k, wt) in enumerate(kinds)]
+    ws = [p.w if p.w is not None else np.ones_like(p.y) for p in parts]
+    y = np.stack([parts[q % len(kinds)].y[q // len(kinds)] for q in range(rows)])
+    w = np.stack([ws[q % len(kinds)][q // len(kinds)] for q in range(rows)])
+    y[7, n // 2] = np.nan
+    w[500, 3] = -1.0
+    for inc, clip in ((True, None), (False, (-0.4, 0.6))):
+        yy = y if inc else y[:, ::-1].copy()
+        ww = w if inc else w[:, ::-1].copy()
+        wl = workloads.Workload(f"packed_{rows}x{n}_{np.dtype(dtype).name}_inc{int(inc)}", yy, ww, inc)
+        if clip:
+            wl.y_min, wl.y_max = clip
+        _print(wl.name)
+        fit, b, *_ = gpu_fit(wl)
+        z, bs, cl, rn, st = oracle_fit(wl)
+        f = fit.cpu().numpy()
+        check_fit(f, z, wl.y, dtype, inc, wl.name)
+        gs, gc, grn = gpu_blocks(b)
+        assert grn[7] == 1 and grn[500] == 1 and grn.sum() == 2
+        check_partition(gs, gc, grn, wl.y, wl.w, inc, wl.y_min, wl.y_max, wl.name)
+        _check_vjp(wl, b, gs, gc, grn, n + 3, wl.name)
+
+
 SIZES = [1, 2, 3, 63, 64, 65, 127, 129, 257, 513, 1000, 3583, 3584, 3585, 4096, 4097, 4500, 5120, 5121, 6143, 6144, 6145, 7168, 7169,
          8193, 12289, 20001, 65537]
 

@@ -7,9 +7,9 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libiso.so")
-SOURCES = ["iso_fit.hip", "iso_vjp.hip", "iso_rank.hip", "iso_calib.hip", "iso_noalloc.hip", "iso_view.hip",
+SOURCES = ["iso_fit.hip", "iso_vjp.hip", "iso_rank.hip", "iso_calib.hip", "iso_noalloc.hip", "iso_pack.hip", "iso_view.hip",
            "iso_api.cpp"]
-HEADERS = ["iso_compose.hpp", "iso_device.hpp", "iso_internal.hpp", "iso_prepare.hpp", "iso_sort.hpp", "iso_tile.hpp"]
+HEADERS = ["iso_compose.hpp", "iso_device.hpp", "iso_internal.hpp", "iso_pack.hpp", "iso_prepare.hpp", "iso_sort.hpp", "iso_tile.hpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

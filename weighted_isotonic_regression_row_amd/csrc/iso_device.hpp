@@ -249,4 +249,18 @@ __device__ __forceinline__ double2 dd4_diff(double4 A, double4 B) {
     return make_double2((B.x - A.x) + (B.y - A.y), (B.z - A.z) + (B.w - A.w));
 }
 
+// Status words of a fit call (the workspace's first 16 bytes).
+// Every writer of one call stores the same value, so a plain exchange is
+// enough.  status[0] is never cleared (it may hold garbage before a first
+// error); status[1] holds the epoch of the latest call, written by thread 0 of
+// workgroup 0 of the call's first kernel, so after the call iso_status reports
+// status[0]'s code only when its epoch is status[1].
+__device__ inline void report_weight_error(unsigned long long* status, unsigned long long epoch) {
+    atomicExch(status, (epoch << 8) | 3ull);
+}
+
+__device__ inline void mark_epoch(unsigned long long* status, unsigned long long epoch) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) status[1] = epoch;
+}
+
 }  // namespace iso

@@ -25,6 +25,7 @@
 #include <math.h>
 
 #include "iso_internal.hpp"
+#include "iso_pack.hpp"
 #include "iso_tile.hpp"
 
 namespace iso {
@@ -48,19 +49,6 @@ struct RowArgs {
     int* ovf_row;        // [rows] 1 where the row kernel left the row to k_row_ovf
     int stage;           // row kernel: read the inputs through LDS (lane_load_staged)
 };
-
-// Every writer of one call stores the same value, so a plain exchange is
-// enough.  status[0] is never cleared (it may hold garbage before a first
-// error); status[1] holds the epoch of the latest call, written by thread 0 of
-// workgroup 0 of the call's first kernel, so after the call iso_status reports
-// status[0]'s code only when its epoch is status[1].
-__device__ inline void report_weight_error(unsigned long long* status, unsigned long long epoch) {
-    atomicExch(status, (epoch << 8) | 3ull);
-}
-
-__device__ inline void mark_epoch(unsigned long long* status, unsigned long long epoch) {
-    if (blockIdx.x == 0 && threadIdx.x == 0) status[1] = epoch;
-}
 
 template <typename T>
 __device__ inline void wg_write_nan(int64_t N, T* out, uint64_t* sbits, uint64_t* cbits) {
@@ -1636,6 +1624,13 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
         const unsigned grid = (unsigned)((a.rows + 31) / 32);
         hipLaunchKernelGGL((k_rows_pair<T, 32>), dim3(grid), dim3(64), 0, a.stream, r, (int64_t)a.rows);
         return hipGetLastError();
+    }
+    if (a.n <= kPackedMax) {
+        const PackedLaunch p{a.y,         a.w,       a.fit,   a.rows,  a.n,
+                             a.increasing, sizeof(T) == 4 ? 0 : 1, a.lo, a.hi,
+                             a.start_bits, a.clip_bits, a.row_nan, a.words, status,
+                             a.epoch,     (int*)(a.ws + a.L.ovf), a.stream};
+        return launch_rows_packed(p);
     }
     if (a.n <= kSingleMax) {
         int K, nl;

@@ -132,7 +132,11 @@ inline Layout make_layout(int64_t rows, int64_t n) {
     L.cvi = take(4 * rm * kVMax);
     if (L.m == 0) {
         L.ovf_stride = align256(16 * ((size_t)n + 1) + 2 * ((size_t)n + 1));
-        L.ovf = take(L.ovf_stride * (size_t)rows);
+        // also the packed rows' overflow lists (iso_pack.hip): 16 counters
+        // 256 bytes apart, then at most one entry per row and 16 more
+        const size_t lists = 16 * 256 + 4 * ((size_t)rows + 16);
+        const size_t lists_of_rows = L.ovf_stride * (size_t)rows;
+        L.ovf = take(lists_of_rows > lists ? lists_of_rows : lists);
         L.ovfrow = take(4 * (size_t)rows);
     }
     // backward: per tile head, tail, carry, total (up to three doubles each) + flag
