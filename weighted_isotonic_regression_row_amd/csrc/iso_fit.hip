@@ -498,19 +498,18 @@ struct ChunkArgs {
     double4* cgs;      // [rows*m*kGroups]
     double4* cvx;      // [rows*m*kVMax]
     int* cvi;          // [rows*m*kVMax]
-    int* cover;        // [rows*m] the chunks left to the second pass, ncover of them
-    int* ncover;
+    int* cover;        // [rows*m] 1 where the first pass left the chunk to the second, else 0
+    int64_t nchunks;   // rows * m
     int cap;           // list entries of this pass (kChunk in the second)
     int pass;          // 0: every chunk, a list of cap entries; 1: the chunks the first left
 };
 
 // The first pass gives each chunk a list of kChunkCap entries, small enough
 // for four chunks to share a CU's LDS; a chunk with more candidates than that
-// (rare: dense chunks keep about 620 of 3585 points) is appended to the
-// cover list and fitted by the second pass, whose list holds every point.
+// (rare: dense chunks keep about 620 of 3585 points) is flagged and fitted by
+// the second pass, whose list holds every point.  Every chunk writes its flag,
+// so nothing needs clearing before the call.
 constexpr int kChunkCap = (kLdsBytes / 4 - 512 - (int)tile_smem_bytes(kChunkLanes, 0, kLaneK)) / 18;
-
-__global__ void k_zero_int(int* p) { *p = 0; }
 
 // One chunk by the workgroup: its hull stored, its tentative fit written.
 template <typename T>
@@ -535,6 +534,7 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
         if (threadIdx.x == 0) {
             a.cflag[bid] = flag;
             a.nv[bid] = 0;
+            if (a.pass == 0) a.cover[bid] = 0;
         }
         return;
     }
@@ -564,9 +564,10 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
         mask &= lane_coarse_filter<K>(t, xs, ys, cnt, ea, eb, E) | end;
         __syncthreads();  // E and the slots are read before the merges reuse the list
     }
-    if (a.pass == 0 && tile_count(t, mask) > a.cap + 1) {  // uniform
-        if (threadIdx.x == 0) a.cover[atomicAdd(a.ncover, 1)] = (int)bid;
-        return;  // nothing written: the second pass fits the chunk
+    if (a.pass == 0) {
+        const bool over = tile_count(t, mask) > a.cap + 1;  // uniform
+        if (threadIdx.x == 0) a.cover[bid] = over ? 1 : 0;
+        if (over) return;  // nothing else written: the second pass fits the chunk
     }
     // The wrap is tried only where the hull is likely short: a wave's wrap
     // stops after kWrapWave vertices.  The hull of the lane ends tells:
@@ -619,14 +620,29 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
     chunk_fit<T>(a, blockIdx.x);
 }
 
-// The second pass: a grid of workgroups over the cover list (read after the
-// first pass has completed, in stream order).
+// The second pass: each workgroup of the grid takes a contiguous range of
+// chunks, reads their flags (written by the first pass, which has completed
+// in stream order) 256 at a time, and fits the flagged ones.
 template <typename T>
 __global__ __launch_bounds__(kChunkLanes) void k_chunk_cover(ChunkArgs a) {
-    const int count = *a.ncover;
-    for (int i = blockIdx.x; i < count; i += gridDim.x) {
-        chunk_fit<T>(a, a.cover[i]);
-        __syncthreads();  // the next chunk reuses the LDS
+    __shared__ uint64_t sel[kChunkLanes / kWave];
+    const int64_t per = (a.nchunks + gridDim.x - 1) / gridDim.x;
+    const int64_t c0 = (int64_t)blockIdx.x * per, c1 = min(c0 + per, a.nchunks);
+    for (int64_t base = c0; base < c1; base += kChunkLanes) {
+        const int64_t c = base + threadIdx.x;
+        const uint64_t b = __ballot(c < c1 && a.cover[c] != 0);
+        if (lane_id() == 0) sel[threadIdx.x / kWave] = b;
+        __syncthreads();
+        for (int q = 0; q < kChunkLanes / kWave; ++q) {
+            uint64_t pend = sel[q];  // the same in every thread
+            while (pend) {
+                const int bit = lo_bit(pend);
+                pend &= pend - 1ull;
+                chunk_fit<T>(a, base + q * kWave + bit);
+                __syncthreads();  // the next chunk reuses the LDS
+            }
+        }
+        __syncthreads();  // every thread has read sel before it is rewritten
     }
 }
 
@@ -1664,21 +1680,20 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
     ca.cvx = (double4*)(a.ws + a.L.cvx);
     ca.cvi = (int*)(a.ws + a.L.cvi);
     ca.cover = (int*)(a.ws + a.L.cover);
-    ca.ncover = (int*)(a.ws + a.L.status + 16);
+    ca.nchunks = a.rows * m;
     {
         const size_t smem1 = tile_smem_bytes(kChunkLanes, kChunk, kLaneK);
         const size_t smem0 = tile_smem_bytes(kChunkLanes, kChunkCap, kLaneK);
         static size_t seen0[kMaxDevices] = {}, seen1[kMaxDevices] = {};
         (void)ensure_lds((const void*)k_chunk_hull<T>, smem0, seen0);
         (void)ensure_lds((const void*)k_chunk_cover<T>, smem1, seen1);
-        hipLaunchKernelGGL(k_zero_int, dim3(1), dim3(1), 0, a.stream, ca.ncover);
         const int64_t chunks = a.rows * m;
         ca.pass = 0;
         ca.cap = kChunkCap;
         hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)chunks), dim3(kChunkLanes), smem0, a.stream, ca);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        // two workgroups per CU (the full list) loop over the cover list
+        // two workgroups per CU (the full list) over the flagged chunks
         ca.pass = 1;
         ca.cap = kChunk;
         hipLaunchKernelGGL(k_chunk_cover<T>, dim3((unsigned)(chunks < 512 ? chunks : 512)), dim3(kChunkLanes), smem1,

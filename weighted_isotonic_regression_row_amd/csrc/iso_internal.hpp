@@ -109,8 +109,7 @@ inline Layout make_layout(int64_t rows, int64_t n) {
         off = align256(off + bytes);
         return at;
     };
-    L.status = take(24);  // [0] last data error (epoch << 8 | code), [1] epoch of the last call,
-                          // [2] chunks left to the chunk kernel's second pass (int)
+    L.status = take(16);  // [0] last data error (epoch << 8 | code), [1] epoch of the last call
     L.vjp = off;  // the backward reuses everything after the status word
     L.tot = take(32 * rm);
     L.nv = take(4 * rm);
