@@ -24,6 +24,8 @@
 //                  a chunk without a segment lies under one edge).
 #include <math.h>
 
+#include <algorithm>
+
 #include "iso_internal.hpp"
 #include "iso_pack.hpp"
 #include "iso_tile.hpp"
@@ -620,17 +622,17 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
     chunk_fit<T>(a, blockIdx.x);
 }
 
-// The second pass: each workgroup of the grid takes a contiguous range of
-// chunks, reads their flags (written by the first pass, which has completed
-// in stream order) 256 at a time, and fits the flagged ones.
+// The second pass: workgroup b of the grid takes the chunks b, b + G, b + 2G,
+// ... (G workgroups; flagged chunks come in runs, which this spreads over the
+// grid), reads their flags (written by the first pass, which has completed in
+// stream order) 256 at a time, and fits the flagged ones.
 template <typename T>
 __global__ __launch_bounds__(kChunkLanes) void k_chunk_cover(ChunkArgs a) {
     __shared__ uint64_t sel[kChunkLanes / kWave];
-    const int64_t per = (a.nchunks + gridDim.x - 1) / gridDim.x;
-    const int64_t c0 = (int64_t)blockIdx.x * per, c1 = min(c0 + per, a.nchunks);
-    for (int64_t base = c0; base < c1; base += kChunkLanes) {
-        const int64_t c = base + threadIdx.x;
-        const uint64_t b = __ballot(c < c1 && a.cover[c] != 0);
+    const int64_t G = gridDim.x;
+    for (int64_t i0 = 0; (int64_t)blockIdx.x + i0 * G < a.nchunks; i0 += kChunkLanes) {
+        const int64_t c = (int64_t)blockIdx.x + (i0 + threadIdx.x) * G;
+        const uint64_t b = __ballot(c < a.nchunks && a.cover[c] != 0);
         if (lane_id() == 0) sel[threadIdx.x / kWave] = b;
         __syncthreads();
         for (int q = 0; q < kChunkLanes / kWave; ++q) {
@@ -638,7 +640,7 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_cover(ChunkArgs a) {
             while (pend) {
                 const int bit = lo_bit(pend);
                 pend &= pend - 1ull;
-                chunk_fit<T>(a, base + q * kWave + bit);
+                chunk_fit<T>(a, (int64_t)blockIdx.x + (i0 + q * kWave + bit) * G);
                 __syncthreads();  // the next chunk reuses the LDS
             }
         }
@@ -1693,11 +1695,13 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
         hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)chunks), dim3(kChunkLanes), smem0, a.stream, ca);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        // two workgroups per CU (the full list) over the flagged chunks
+        // two workgroups per CU (the full list) run at a time; a grid of up
+        // to eight times that many (one workgroup per eight chunks) keeps two
+        // flagged chunks from sharing a workgroup unless there are many
         ca.pass = 1;
         ca.cap = kChunk;
-        hipLaunchKernelGGL(k_chunk_cover<T>, dim3((unsigned)(chunks < 512 ? chunks : 512)), dim3(kChunkLanes), smem1,
-                           a.stream, ca);
+        const int64_t cover_grid = std::min<int64_t>(chunks, std::max<int64_t>(512, std::min<int64_t>(chunks / 8, 4096)));
+        hipLaunchKernelGGL(k_chunk_cover<T>, dim3((unsigned)cover_grid), dim3(kChunkLanes), smem1, a.stream, ca);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1728,8 +1732,13 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
         static size_t seen[kMaxDevices] = {};
         (void)ensure_lds((const void*)k_merge_sub<T>, kMergeWinBytes, seen);
     }
-    hipLaunchKernelGGL(k_merge_sub<T>, dim3((unsigned)(a.rows * ma.nsub)), dim3(kMergeThreads), kMergeWinBytes,
-                       a.stream, ma);
+    // Eight waves per subtree finish its levels in fewer steps, but only one
+    // such workgroup fits on a CU (registers); with more subtrees than CUs,
+    // workgroups of four waves (three to a CU) run them in one generation.
+    const int64_t subtrees = a.rows * ma.nsub;
+    const int sub_threads = subtrees > 256 ? kMergeThreads / 2 : kMergeThreads;
+    hipLaunchKernelGGL(k_merge_sub<T>, dim3((unsigned)subtrees), dim3(sub_threads),
+                       sizeof(BWin) * (sub_threads / kWave), a.stream, ma);
     {
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
