@@ -139,8 +139,10 @@ int iso_fit(const void* y_dev, const void* w_dev, int64_t rows, int64_t n, int i
  *   Arguments as for iso_fit; the caller still passes y, w, fit and, when it
  *   wants the partition, blocks_out and blocks_mem_dev.
  *   Returns ISO_ETOOBIG, queuing nothing, when iso_workspace_bytes(rows, n,
- *   dtype) exceeds ISO_NOALLOC_SCRATCH_BYTES (128 MiB: every single-workgroup
- *   batch up to 1000 x 6144 elements, and rows of up to about 1.2e7 elements).
+ *   dtype) exceeds ISO_NOALLOC_SCRATCH_BYTES (128 MiB: any batch of rows of
+ *   at most 64 elements, up to about 3e7 rows of 65 to 512, every batch of
+ *   rows of several waves up to 1000 x 6144 elements, and single rows of up
+ *   to about 1.2e7 elements).
  *
  * Every call on one GPU shares that GPU's array, and the array keeps the last
  * call's contents: calls that overlap on one GPU (other streams, other host

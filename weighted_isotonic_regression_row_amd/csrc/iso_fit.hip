@@ -1558,7 +1558,7 @@ static void row_shape(int N, bool f32, int& K, int& nl) {
     } else if (N <= 256) {
         K = 4;
         nl = 64;
-    } else if (N <= 512) {
+    } else if (N <= kOneWaveMax) {
         K = 8;
         nl = 64;
     } else if (N <= 4096) {

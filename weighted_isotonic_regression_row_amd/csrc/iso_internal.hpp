@@ -17,6 +17,17 @@ constexpr int kLdsBytes = 163840;
 // lane hulls' vertices listed in LDS (18 bytes per vertex plus about 60 per
 // lane; 512 lanes of 12 elements at most).
 constexpr int64_t kSingleMax = 6144;
+// Rows of kPackedMin to kPackedMax elements are packed several to a wave
+// (shorter rows take the lane kernels).  Longer rows take a wave each
+// (k_row_fit with 4 or 8 points per lane), whose output-sensitive finish
+// measured as fast as the packed kernels on noise rows of 160 to 256 and
+// faster on rows whose every point is a vertex (1e5 rows, float32:
+// increasing rows of 160, 0.29 against 0.41 ms packed).
+constexpr int kPackedMin = 65;
+constexpr int kPackedMax = 128;
+// Rows of up to this many elements take one wave (k_row_fit with 2, 4 or 8
+// points per lane); longer ones several.
+constexpr int64_t kOneWaveMax = 512;
 // Longer rows are cut into chunks of this many elements (first page, Sec. 3:
 // chunks of 1024 to 4096 points), one workgroup of 256 threads, 224 of them
 // holding 16 elements each (76 KiB of LDS, so that two chunks share a CU),
@@ -129,14 +140,20 @@ inline Layout make_layout(int64_t rows, int64_t n) {
     L.cgs = take(32 * rm * kGroups);
     L.cvx = take(32 * rm * kVMax);
     L.cvi = take(4 * rm * kVMax);
-    if (L.m == 0) {
+    if (L.m == 0 && n > kOneWaveMax) {
+        // rows of several waves (k_row_fit): a vertex list per row for lane
+        // hulls that overflow the LDS list, and a flag per row
         L.ovf_stride = align256(16 * ((size_t)n + 1) + 2 * ((size_t)n + 1));
-        // also the packed rows' overflow lists (iso_pack.hip): 16 counters
-        // 256 bytes apart, then at most one entry per row and 16 more
-        const size_t lists = 16 * 256 + 4 * ((size_t)rows + 16);
-        const size_t lists_of_rows = L.ovf_stride * (size_t)rows;
-        L.ovf = take(lists_of_rows > lists ? lists_of_rows : lists);
+        L.ovf = take(L.ovf_stride * (size_t)rows);
         L.ovfrow = take(4 * (size_t)rows);
+    } else if (L.m == 0 && n > kPackedMax) {
+        // rows of one wave: a flag per row for k_row_ovf, which refits a
+        // flagged row with its whole list in LDS
+        L.ovfrow = take(4 * (size_t)rows);
+    } else if (L.m == 0 && n >= kPackedMin) {
+        // packed rows (iso_pack.hip): 16 counters 256 bytes apart, then lists
+        // of at most one entry per wave (fewer than rows + 16 in all)
+        L.ovf = take(16 * 256 + 4 * ((size_t)rows + 16));
     }
     // backward: per tile head, tail, carry, total (up to three doubles each) + flag
     const size_t tiles = (n > kSingleMax) ? (size_t)rows * (size_t)((n + kVjpTile - 1) / kVjpTile) : 0;

@@ -4,16 +4,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "iso_internal.hpp"
+
 namespace iso {
 
-// Rows of kPackedMin to kPackedMax elements are packed several to a wave
-// (shorter rows take the lane kernels).  Longer rows take a wave each
-// (k_row_fit with 4 or 8 points per lane), whose output-sensitive finish
-// measured as fast as the packed kernels on noise rows of 160 to 256 and
-// faster on rows whose every point is a vertex (1e5 rows, float32:
-// increasing rows of 160, 0.29 against 0.41 ms packed).
-constexpr int kPackedMin = 65;
-constexpr int kPackedMax = 128;
+// (kPackedMin, kPackedMax: iso_internal.hpp)
 
 struct PackedLaunch {
     const void* y;
