@@ -503,7 +503,6 @@ struct ChunkArgs {
     int* cover;        // [rows*m] 1 where the first pass left the chunk to the second, else 0
     int64_t nchunks;   // rows * m
     int cap;           // list entries of this pass (kChunk in the second)
-    int pass;          // 0: every chunk, a list of cap entries; 1: the chunks the first left
 };
 
 // The first pass gives each chunk a list of kChunkCap entries, small enough
@@ -512,11 +511,18 @@ struct ChunkArgs {
 // the second pass, whose list holds every point.  Every chunk writes its flag,
 // so nothing needs clearing before the call.
 constexpr int kChunkCap = (kLdsBytes / 4 - 512 - (int)tile_smem_bytes(kChunkLanes, 0, kLaneK)) / 18;
+// Candidates the first pass finishes by QuickHull: the list's entries and the
+// QuickHull's three slot arrays share the list's room (40 bytes an entry).
+constexpr int kChunkQh = (16 * (kChunkCap + 1) - 64) / 40;
+static_assert(kChunkQh <= 3 * kChunkLanes && kChunkQh <= 1023, "three QuickHull entries per thread, 10-bit keys");
 
 // One chunk by the workgroup: its hull stored, its tentative fit written.
-template <typename T>
+// PASS 0: the first pass (every chunk, a list of kChunkCap entries); 1: the
+// second (the chunks the first left, a list of every point).
+template <typename T, int PASS>
 __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
     constexpr int K = kLaneK;
+    constexpr bool ABS = sizeof(T) == 4;
     extern __shared__ __align__(32) char smem[];
     const int64_t row = bid / a.m, c = bid % a.m;
     const int64_t e0 = c * kChunk;
@@ -530,54 +536,68 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
     uint64_t mask;
     double xs[K], ys[K];
     int nvert;
-    const int flag = tile_build<T, K>(t, y, w, a.r.increasing, mask, xs, ys, nvert);
+    // the points and lane starts only: the lane hulls are built below, by the
+    // chunks that merge them
+    const int flag = tile_build<T, K, false>(t, y, w, a.r.increasing, mask, xs, ys, nvert);
     if (flag) {
         // the whole row comes back NaN; k_fixup writes it
         if (threadIdx.x == 0) {
             a.cflag[bid] = flag;
             a.nv[bid] = 0;
-            if (a.pass == 0) a.cover[bid] = 0;
+            if (PASS == 0) a.cover[bid] = 0;
         }
         return;
     }
     // Only points under the hull of the lane ends can be vertices of the
-    // chunk's hull (its edges are chords between points of the chunk): the
-    // lane hulls keep just those of their vertices, and always their last
-    // point, so that each lane's node is still a convex chain from its start
-    // to its end (the merges need both ends: a node starts at the previous
-    // lane's end and shares it), and the merges see every vertex of the chunk
-    // hull on a fraction of the points (dense data: about 420 of 3584 plus
-    // the lane ends, where the lane hulls hold about 3300).  The hull of the
-    // lane ends is found by QuickHull (one per thread) on a plain copy of the
-    // lane starts.
+    // chunk's hull (its edges are chords between points of the chunk), so
+    // the candidates are the points not above the edge of that coarse hull
+    // over their lane (dense data: about 400 of 3584, noise: about 80), and
+    // the chunk's last point.  The coarse hull is found by QuickHull (one
+    // lane end per thread) on a plain copy of the lane starts.
+    const int cnt = min(max(N - (int)threadIdx.x * K, 0), K);
+    uint64_t cand;
     {
         const int used = (N + K - 1) / K;
-        double2* E = (double2*)t.VXY;  // free until the merges compact the list
+        double2* E = (double2*)t.VXY;  // free until the candidates are listed
         unsigned long long* slots = (unsigned long long*)(E + kChunkLanes + 1);
         for (int l = threadIdx.x; l <= used; l += blockDim.x) E[l] = lane_start2(t, l);
-        if (threadIdx.x == 0) t.flag[2] = 0;  // vertices of the hull of the lane ends
         __syncthreads();
         int ea, eb;
-        const bool cv = tile_quickhull(E, used, slots, 0.0, ea, eb);
-        const uint64_t cvb = __ballot(cv);
-        if (lane_id() == 0 && cvb) atomicAdd(&t.flag[2], __popcll(cvb));
-        const int cnt = min(max(N - (int)threadIdx.x * K, 0), K);
+        (void)tile_quickhull(E, used, slots, 0.0, ea, eb);
+        cand = lane_coarse_filter<K>(t, xs, ys, cnt, ea, eb, E);
+        if ((int)threadIdx.x == used - 1) cand |= 1ull << (cnt - 1);
+        __syncthreads();  // E and the slots are read before the list reuses them
+    }
+    bool merged = true;
+    if constexpr (PASS == 0) {
+        // few candidates: their hull by QuickHull on the list, with the
+        // merges' vertex test; no lane hulls are needed
+        const int m = tile_compact_upto<K, ABS>(t, cand, xs, ys, kChunkQh + 1) - 1;
+        if (m <= kChunkQh) {  // uniform
+            bool vert[3];
+            list_quickhull<K, ABS, 3>(t, m, (unsigned long long*)(t.VXY + m + 1), vert);
+            list_to_front<3>(t, m, vert);
+            tile_masks<K>(t, mask);
+            merged = false;
+        }
+    }
+    if (merged) {
+        // the lane hulls' vertices among the candidates, and every lane's
+        // last point, so that each lane's node is still a convex chain from
+        // its start to its end (the merges need both ends: a node starts at
+        // the previous lane's end and shares it)
         const uint64_t end = (cnt > 0) ? (1ull << (cnt - 1)) : 0ull;
-        mask &= lane_coarse_filter<K>(t, xs, ys, cnt, ea, eb, E) | end;
-        __syncthreads();  // E and the slots are read before the merges reuse the list
+        mask = lane_gift_wrap<K>(xs, ys, cnt) & (cand | end);
+        if constexpr (PASS == 0) {
+            const bool over = tile_count(t, mask) > a.cap + 1;  // uniform
+            if (over) {
+                if (threadIdx.x == 0) a.cover[bid] = 1;
+                return;  // nothing else written: the second pass fits the chunk
+            }
+        }
+        tile_merges<K, ABS>(t, mask, xs, ys);
     }
-    if (a.pass == 0) {
-        const bool over = tile_count(t, mask) > a.cap + 1;  // uniform
-        if (threadIdx.x == 0) a.cover[bid] = over ? 1 : 0;
-        if (over) return;  // nothing else written: the second pass fits the chunk
-    }
-    // The wrap is tried only where the hull is likely short: a wave's wrap
-    // stops after kWrapWave vertices.  The hull of the lane ends tells:
-    // noisy chunks (the 6.5e6 calibration row) have 3 to 14 of its vertices
-    // and about as many in their hull; dense chunks (the 32 x 2^22 rows)
-    // mostly 18 to 70, with hundreds in their hull (their wrap would give up).
-    // The LDS list holds every point of a chunk.
-    tile_merges<K, sizeof(T) == 4>(t, mask, xs, ys, t.flag[2] <= 12);
+    if (PASS == 0 && threadIdx.x == 0) a.cover[bid] = 0;
     __syncthreads();  // every lane's final mask in M
     const int l = threadIdx.x;
     const int nv = t.flag[1];  // vertices of the chunk hull; rank r is list entry r
@@ -619,7 +639,7 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
 template <typename T>
 __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
     mark_epoch(a.r.status, a.r.epoch);
-    chunk_fit<T>(a, blockIdx.x);
+    chunk_fit<T, 0>(a, blockIdx.x);
 }
 
 // The second pass: workgroup b of the grid takes the chunks b, b + G, b + 2G,
@@ -640,7 +660,7 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_cover(ChunkArgs a) {
             while (pend) {
                 const int bit = lo_bit(pend);
                 pend &= pend - 1ull;
-                chunk_fit<T>(a, (int64_t)blockIdx.x + (i0 + q * kWave + bit) * G);
+                chunk_fit<T, 1>(a, (int64_t)blockIdx.x + (i0 + q * kWave + bit) * G);
                 __syncthreads();  // the next chunk reuses the LDS
             }
         }
@@ -1690,7 +1710,6 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
         (void)ensure_lds((const void*)k_chunk_hull<T>, smem0, seen0);
         (void)ensure_lds((const void*)k_chunk_cover<T>, smem1, seen1);
         const int64_t chunks = a.rows * m;
-        ca.pass = 0;
         ca.cap = kChunkCap;
         hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)chunks), dim3(kChunkLanes), smem0, a.stream, ca);
         hipError_t e = hipGetLastError();
@@ -1698,7 +1717,6 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
         // two workgroups per CU (the full list) run at a time; a grid of up
         // to eight times that many (one workgroup per eight chunks) keeps two
         // flagged chunks from sharing a workgroup unless there are many
-        ca.pass = 1;
         ca.cap = kChunk;
         const int64_t cover_grid = std::min<int64_t>(chunks, std::max<int64_t>(512, std::min<int64_t>(chunks / 8, 4096)));
         hipLaunchKernelGGL(k_chunk_cover<T>, dim3((unsigned)cover_grid), dim3(kChunkLanes), smem1, a.stream, ca);

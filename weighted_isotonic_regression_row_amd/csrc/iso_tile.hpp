@@ -755,6 +755,136 @@ __device__ inline uint64_t lane_coarse_filter(const Tile& t, const double (&xs)[
     return (uint64_t)keep;
 }
 
+// QuickHull over the tile's list: the lower hull of entries 0..m (points in
+// increasing order; entries 0 and m are its ends and always vertices), with
+// the differences formed as the merges form them (vdiff: part by part over
+// double-double lane starts for float64 data), so the vertex test is the
+// merges' own.  R entries per thread, e = 1 + tid + r * blockDim.x.  Each
+// level, every entry still strictly below the chord of its segment (a, b)
+// (the turn (a, e, b) positive) offers minus that turn to the segment's slot
+// as tile_quickhull does; the deepest entry of each segment is a vertex and
+// splits it, and the other entries follow the part that holds them.  An entry
+// on or above its chord drops out.  Each entry keeps its differences to a and
+// b and forms again only those whose end moved.  vert[r]: entry e is an
+// interior vertex.  slots: 3 (m + 2) words of LDS after the list.  Block
+// scope; the list is complete (a barrier after its last write);
+// m <= min(1023, R * blockDim.x).  Ends with a barrier.
+template <int K, bool ABS, int R>
+__device__ inline void list_quickhull(const Tile& t, int m, unsigned long long* slots, bool (&vert)[R]) {
+    const int tid = threadIdx.x, nt = blockDim.x, ns = m + 1;
+    unsigned long long* F = slots + 3 * ns;  // the offer words of the three arrays
+    for (int i = tid; i < 3 * ns + 3; i += nt) slots[i] = (i < 3 * ns) ? ~0ull : 0ull;
+    int a[R], b[R];
+    double2 dP[R], dB[R];  // P_e - P_a and P_b - P_a
+    bool cand[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int e = 1 + tid + r * nt;
+        vert[r] = false;
+        cand[r] = e < m;
+        a[r] = 0;
+        b[r] = m;
+        dP[r] = make_double2(0.0, 0.0);
+        dB[r] = make_double2(1.0, 0.0);
+        if (cand[r]) {
+            dP[r] = vdiff<K, ABS>(t, 0, e);
+            dB[r] = vdiff<K, ABS>(t, 0, m);
+        }
+    }
+    __syncthreads();  // the slots are clear
+    for (int k = 0;; ++k) {
+        const int q = k % 3;
+        unsigned long long* cur = slots + q * ns;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (cand[r]) {
+                const double turn = cross2(dP[r], dB[r]);  // vturn(a, e, b)
+                if (turn > 0.0) {
+                    atomicMin(cur + a[r], qh_key(-turn, 1 + tid + r * nt));
+                    F[q] = 1ull;
+                } else {
+                    cand[r] = false;
+                }
+            }
+        }
+        __syncthreads();
+        const unsigned long long f = F[q];
+        unsigned long long wv[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) wv[r] = cand[r] ? cur[a[r]] : ~0ull;
+        if (f == 0ull) break;  // uniform: no segment split
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if (cand[r]) {
+                const int e = 1 + tid + r * nt, v = (int)(wv[r] & 1023ull);
+                if (v == e) {
+                    vert[r] = true;
+                    cand[r] = false;
+                } else if (e < v) {
+                    b[r] = v;
+                    dB[r] = vdiff<K, ABS>(t, a[r], v);
+                } else {
+                    a[r] = v;
+                    dP[r] = vdiff<K, ABS>(t, v, e);
+                    dB[r] = vdiff<K, ABS>(t, v, b[r]);
+                }
+            }
+        }
+        const int o = (k + 2) % 3;
+        unsigned long long* old = slots + o * ns;
+        for (int i = tid; i < ns; i += nt) old[i] = ~0ull;
+        if (tid == 0) F[o] = 0ull;
+    }
+}
+
+// After list_quickhull: its vertices (entry 0, the entries with vert, entry
+// m) move to the front of the list in order (V and VXY), flag[1] = their
+// number.  Every read precedes the first barrier.  Ends with a barrier.
+template <int R>
+__device__ inline void list_to_front(const Tile& t, int m, const bool (&vert)[R]) {
+    const int tid = threadIdx.x, nt = blockDim.x, lane = lane_id(), wid = tid >> 6, nw = nt >> 6;
+    static_assert(R * 8 <= 32, "per-wave counts in W");
+    unsigned short pv[R];
+    double2 xy[R];
+    uint64_t bal[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int e = 1 + tid + r * nt;
+        bal[r] = __ballot(vert[r]);
+        if (lane == 0) t.W[r * nw + wid] = __popcll(bal[r]);
+        pv[r] = 0;
+        xy[r] = make_double2(0.0, 0.0);
+        if (vert[r]) {
+            pv[r] = t.V[e];
+            xy[r] = t.VXY[e];
+        }
+    }
+    const unsigned short pm = t.V[m];
+    const double2 xym = t.VXY[m];
+    __syncthreads();
+    int base = 1;  // entry 0 stays
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        int before = base;
+        for (int q = 0; q < nw; ++q) {
+            const int c = t.W[r * nw + q];
+            before += (q < wid) ? c : 0;
+            base += c;
+        }
+        if (vert[r]) {
+            const int i = before + __popcll(bal[r] & bits_upto(lane - 1));
+            t.V[i] = pv[r];
+            t.VXY[i] = xy[r];
+        }
+    }
+    if (tid == 0) {
+        t.V[base] = pm;
+        t.VXY[base] = xym;
+        t.flag[1] = base + 1;
+    }
+    __syncthreads();
+}
+
 // After tile_compact and tile_quickhull over the list (absolute coordinates):
 // the hull's vertices (vert in the thread holding entry tid + 1, whose
 // previous vertex is entry a; entry 0 always) move to the front of the list
@@ -892,7 +1022,7 @@ __device__ inline int tile_compact_upto(const Tile& t, uint64_t mask, const doub
         t.I[l] = r;
         double sx = 0.0, sy = 0.0;
         if (ABS) {
-            const double2 s = ((const double2*)t.LS)[l];
+            const double2 s = lane_start2(t, l);
             sx = s.x;
             sy = s.y;
         }
