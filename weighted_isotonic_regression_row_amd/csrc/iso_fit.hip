@@ -119,12 +119,16 @@ __device__ inline void tile_store(const Tile& t, uint64_t mask, T* out, uint64_t
 }
 
 // Step 4 and the stores: fit (and bits) of the tile's elements.  Overwrites
-// the list's coordinates with edge slopes.
-template <typename T, int K>
+// the list's coordinates with edge slopes.  QR > 0: the list is the QuickHull
+// list (list_compact) of at most QR entries per thread.
+template <typename T, int K, int QR = 0>
 __device__ inline void tile_finish(const Tile& t, uint64_t mask, int increasing, double lo, double hi, T* out,
                                    uint64_t* sb, uint64_t* cb) {
     constexpr bool ABS = sizeof(T) == 4;
-    tile_edge_slopes<K, ABS>(t, increasing, lo, hi);
+    if constexpr (QR > 0)
+        list_edge_slopes<QR>(t, increasing, lo, hi);
+    else
+        tile_edge_slopes<K, ABS>(t, increasing, lo, hi);
     double vals[K];
     uint64_t clipm;
     tile_expand<K>(t, mask, vals, clipm);
@@ -511,9 +515,13 @@ struct ChunkArgs {
 // the second pass, whose list holds every point.  Every chunk writes its flag,
 // so nothing needs clearing before the call.
 constexpr int kChunkCap = (kLdsBytes / 4 - 512 - (int)tile_smem_bytes(kChunkLanes, 0, kLaneK)) / 18;
-// Candidates the first pass finishes by QuickHull: the list's entries and the
-// QuickHull's three slot arrays share the list's room (40 bytes an entry).
-constexpr int kChunkQh = (16 * (kChunkCap + 1) - 64) / 40;
+// Candidates the first pass finishes by QuickHull: its list (32 bytes an
+// entry) takes the list's room, its three slot arrays (24 bytes an entry) the
+// lane starts, masks, bridges and lane indices, which are contiguous in the
+// tile's LDS and free while it runs.
+constexpr int kChunkQh = std::min((16 * (kChunkCap + 1)) / 32 - 1,
+                                  (int)((32 * (kChunkLanes + 1) + 16 * kChunkLanes + 8 * (kChunkLanes / 2 + 1) +
+                                         4 * kChunkLanes - 48) / 24));
 static_assert(kChunkQh <= 3 * kChunkLanes && kChunkQh <= 1023, "three QuickHull entries per thread, 10-bit keys");
 
 // One chunk by the workgroup: its hull stored, its tentative fit written.
@@ -548,6 +556,12 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
         }
         return;
     }
+    const int l = threadIdx.x;
+    // starts of the 256-element groups and the chunk's total (QuickHull
+    // overwrites the lane starts)
+    constexpr int LPG = kGroup / K;
+    if ((l % LPG) == 0 && l * K < N) a.cgs[bid * kGroups + l / LPG] = t.LS[l];
+    if (l == 0) a.tot[bid] = t.LS[t.nl];
     // Only points under the hull of the lane ends can be vertices of the
     // chunk's hull (its edges are chords between points of the chunk), so
     // the candidates are the points not above the edge of that coarse hull
@@ -568,26 +582,33 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
         if ((int)threadIdx.x == used - 1) cand |= 1ull << (cnt - 1);
         __syncthreads();  // E and the slots are read before the list reuses them
     }
-    bool merged = true;
-    if constexpr (PASS == 0) {
-        // few candidates: their hull by QuickHull on the list, with the
-        // merges' vertex test; no lane hulls are needed
-        const int m = tile_compact_upto<K, ABS>(t, cand, xs, ys, kChunkQh + 1) - 1;
-        if (m <= kChunkQh) {  // uniform
-            bool vert[3];
-            list_quickhull<K, ABS, 3>(t, m, (unsigned long long*)(t.VXY + m + 1), vert);
-            list_to_front<3>(t, m, vert);
-            tile_masks<K>(t, mask);
-            merged = false;
-        }
-    }
-    if (merged) {
+    // few candidates: their hull by QuickHull on the list, with the merges'
+    // vertex test; no lane hulls are needed (m is uniform: read as a scalar,
+    // so that the branches below hold registers apart)
+    int m = kChunk;
+    if constexpr (PASS == 0) m = __builtin_amdgcn_readfirstlane(list_compact<K>(t, cand, xs, ys, kChunkQh + 1) - 1);
+    const bool merged = m > kChunkQh;
+    if (!merged) {
+        bool vert[3];
+        list_quickhull<3>(t, m, (unsigned long long*)t.LS, vert);
+        list_to_front<3>(t, m, vert);
+        tile_masks<K>(t, mask);
+    } else {
         // the lane hulls' vertices among the candidates, and every lane's
         // last point, so that each lane's node is still a convex chain from
         // its start to its end (the merges need both ends: a node starts at
-        // the previous lane's end and shares it)
+        // the previous lane's end and shares it).  The first pass forms the
+        // lane's points again from the inputs (the same loads and sums), so
+        // that they are not held in registers through QuickHull.
         const uint64_t end = (cnt > 0) ? (1ull << (cnt - 1)) : 0ull;
-        mask = lane_gift_wrap<K>(xs, ys, cnt) & (cand | end);
+        if constexpr (PASS == 0) {
+            int f2 = 0;
+            mask = lane_hull<T, K>(y + (int64_t)l * K, w ? w + (int64_t)l * K : nullptr, cnt, !a.r.increasing, xs,
+                                   ys, f2);
+        } else {
+            mask = lane_gift_wrap<K>(xs, ys, cnt);
+        }
+        mask &= cand | end;
         if constexpr (PASS == 0) {
             const bool over = tile_count(t, mask) > a.cap + 1;  // uniform
             if (over) {
@@ -599,7 +620,6 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
     }
     if (PASS == 0 && threadIdx.x == 0) a.cover[bid] = 0;
     __syncthreads();  // every lane's final mask in M
-    const int l = threadIdx.x;
     const int nv = t.flag[1];  // vertices of the chunk hull; rank r is list entry r
     // explicit coordinates (relative to the chunk start) of the end windows,
     // or of every vertex of a hull of at most kVMax vertices
@@ -607,10 +627,16 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
         const int r = (nv <= kVMax || q < kVMax / 2) ? q : nv - kVMax + q;
         if (r < nv) {
             const int p = t.V[r];
-            const double2 c = t.VXY[r];
+            double4 c4;
+            if (merged) {
+                const double2 c = t.VXY[r];
+                c4 = ABS ? make_double4(c.x, 0.0, c.y, 0.0) : dd4_add_d(t.LS[lane_of<K>(p)], c);
+            } else {
+                c4 = list_dd(t)[r];
+                if (ABS) c4 = make_double4(c4.x, 0.0, c4.z, 0.0);
+            }
             a.cvi[bid * kVMax + q] = p;
-            a.cvx[bid * kVMax + q] = (sizeof(T) == 4) ? make_double4(c.x, 0.0, c.y, 0.0)
-                                                      : dd4_add_d(t.LS[lane_of<K>(p)], c);
+            a.cvx[bid * kVMax + q] = c4;
         }
     }
     // vertex bit set and the rank of each word's first vertex
@@ -622,17 +648,16 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
         a.cmask[bid * kMaskWords + l / LPW] = word;
         a.cpre[bid * kMaskWords + l / LPW] = t.I[l];
     }
-    // starts of the 256-element groups
-    constexpr int LPG = kGroup / K;
-    if ((l % LPG) == 0 && l * K < N) a.cgs[bid * kGroups + l / LPG] = t.LS[l];
     if (l == 0) {
-        a.tot[bid] = t.LS[t.nl];
         a.nv[bid] = nv;
         a.cflag[bid] = 0;
     }
     // tentative fit from the chunk's own hull; k_fixup corrects the elements
     // outside the chunk's surviving segment
-    tile_finish<T, K>(t, mask, a.r.increasing, a.r.lo, a.r.hi, out, sb, cb);
+    if (merged)
+        tile_finish<T, K>(t, mask, a.r.increasing, a.r.lo, a.r.hi, out, sb, cb);
+    else
+        tile_finish<T, K, 3>(t, mask, a.r.increasing, a.r.lo, a.r.hi, out, sb, cb);
 }
 
 // The first pass: one workgroup per chunk.

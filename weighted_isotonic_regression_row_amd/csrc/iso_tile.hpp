@@ -354,15 +354,13 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
             X += wi;
             Y = fma(wi * sg, yi, Y);
             wmin = fminf(wmin, in ? (float)wi : 1.f);
-        } else if (j < cnt) {
-            if (!isfinite(yi) || !isfinite(wi))
-                f |= 1;
-            else if (!(wi > 0.0))
-                f |= 2;
-            double ti = wi * yi;
-            if (negate) ti = -ti;
-            X += wi;
-            Y += ti;
+        } else {
+            // no branches either: the flags and sums take selects
+            const bool in = j < cnt, fin = isfinite(yi) && isfinite(wi);
+            f |= (in && !fin) ? 1 : 0;
+            f |= (in && fin && !(wi > 0.0)) ? 2 : 0;
+            X += in ? wi : 0.0;
+            Y += in ? (wi * sg) * yi : 0.0;
         }
         xs[j] = X;
         ys[j] = Y;
@@ -401,22 +399,42 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
         }
     }
     if constexpr (K % VW == 0 && !STAGED) {
-        // whole, aligned lanes: 16-byte loads, each consumed at once
+        // whole, aligned lanes: 16-byte loads, all issued before the sums
+        // consume them (one memory latency for the lane, not one per load)
         if (!done && cnt == K && (((uintptr_t)y) & 15) == 0 && (w == nullptr || (((uintptr_t)w) & 15) == 0)) {
+            if constexpr (sizeof(T) == 4) {
+                float4 a[K / 4], b[K / 4];
 #pragma unroll
-            for (int q = 0; q < K / VW; ++q) {
-                if constexpr (sizeof(T) == 4) {
-                    const float4 a = ((const float4*)y)[q];
-                    const float4 b = w ? ((const float4*)w)[q] : make_float4(1.f, 1.f, 1.f, 1.f);
-                    take(4 * q, a.x, b.x);
-                    take(4 * q + 1, a.y, b.y);
-                    take(4 * q + 2, a.z, b.z);
-                    take(4 * q + 3, a.w, b.w);
+                for (int q = 0; q < K / 4; ++q) a[q] = ((const float4*)y)[q];
+                if (w) {
+#pragma unroll
+                    for (int q = 0; q < K / 4; ++q) b[q] = ((const float4*)w)[q];
                 } else {
-                    const double2 a = ((const double2*)y)[q];
-                    const double2 b = w ? ((const double2*)w)[q] : make_double2(1.0, 1.0);
-                    take(2 * q, a.x, b.x);
-                    take(2 * q + 1, a.y, b.y);
+#pragma unroll
+                    for (int q = 0; q < K / 4; ++q) b[q] = make_float4(1.f, 1.f, 1.f, 1.f);
+                }
+#pragma unroll
+                for (int q = 0; q < K / 4; ++q) {
+                    take(4 * q, a[q].x, b[q].x);
+                    take(4 * q + 1, a[q].y, b[q].y);
+                    take(4 * q + 2, a[q].z, b[q].z);
+                    take(4 * q + 3, a[q].w, b[q].w);
+                }
+            } else {
+                double2 a[K / 2], b[K / 2];
+#pragma unroll
+                for (int q = 0; q < K / 2; ++q) a[q] = ((const double2*)y)[q];
+                if (w) {
+#pragma unroll
+                    for (int q = 0; q < K / 2; ++q) b[q] = ((const double2*)w)[q];
+                } else {
+#pragma unroll
+                    for (int q = 0; q < K / 2; ++q) b[q] = make_double2(1.0, 1.0);
+                }
+#pragma unroll
+                for (int q = 0; q < K / 2; ++q) {
+                    take(2 * q, a[q].x, b[q].x);
+                    take(2 * q + 1, a[q].y, b[q].y);
                 }
             }
             done = true;
@@ -755,28 +773,81 @@ __device__ inline uint64_t lane_coarse_filter(const Tile& t, const double (&xs)[
     return (uint64_t)keep;
 }
 
-// QuickHull over the tile's list: the lower hull of entries 0..m (points in
-// increasing order; entries 0 and m are its ends and always vertices), with
-// the differences formed as the merges form them (vdiff: part by part over
-// double-double lane starts for float64 data), so the vertex test is the
-// merges' own.  R entries per thread, e = 1 + tid + r * blockDim.x.  Each
-// level, every entry still strictly below the chord of its segment (a, b)
-// (the turn (a, e, b) positive) offers minus that turn to the segment's slot
-// as tile_quickhull does; the deepest entry of each segment is a vertex and
-// splits it, and the other entries follow the part that holds them.  An entry
-// on or above its chord drops out.  Each entry keeps its differences to a and
-// b and forms again only those whose end moved.  vert[r]: entry e is an
-// interior vertex.  slots: 3 (m + 2) words of LDS after the list.  Block
-// scope; the list is complete (a barrier after its last write);
+// The QuickHull list: entry r is point V[r] with its coordinates relative to
+// the tile's first point as a double-double pair, L[r] = (x, x_lo, y, y_lo)
+// (the lane's start plus the local point, exact), 32 bytes an entry in the
+// list's room at VXY.  Differences of two entries are formed part by part, as
+// the merges form them across lanes.
+__device__ __forceinline__ double4* list_dd(const Tile& t) { return (double4*)t.VXY; }
+
+// tile_compact_upto for the QuickHull list: the candidates of mask (point 0
+// first) are listed only when their number, point 0 included, is at most
+// maxv; returns that number.  Ends with a barrier.
+template <int K>
+__device__ inline int list_compact(const Tile& t, uint64_t mask, const double (&xs)[K], const double (&ys)[K],
+                                   int maxv) {
+    const int l = threadIdx.x, lane = lane_id(), wid = l >> 6, nw = blockDim.x >> 6;
+    double4* L = list_dd(t);
+    const int pc = __popcll(mask);
+    const int incl = wave_incl_scan_int(pc);
+    if (lane == kWave - 1) t.W[wid] = incl;
+    __syncthreads();
+    int r = 1, tot = 1;
+    for (int k = 0; k < nw; ++k) {
+        const int c = t.W[k];
+        r += (k < wid) ? c : 0;
+        tot += c;
+    }
+    if (tot <= maxv) {  // uniform
+        r += incl - pc;
+        if (l == 0) {
+            t.flag[1] = tot;
+            t.V[0] = 0;
+            L[0] = make_double4(0.0, 0.0, 0.0, 0.0);
+        }
+        if (mask) {
+            double4 st;
+            if (t.ls2) {
+                const double2 s2 = ((const double2*)t.LS)[l];
+                st = make_double4(s2.x, 0.0, s2.y, 0.0);
+            } else {
+                st = t.LS[l];
+            }
+#pragma unroll
+            for (int b = 0; b < K; ++b) {
+                if ((mask >> b) & 1ull) {
+                    t.V[r] = (unsigned short)(l * K + b + 1);
+                    L[r] = dd4_add_d(st, make_double2(xs[b], ys[b]));
+                    ++r;
+                }
+            }
+        }
+    }
+    __syncthreads();
+    return tot;
+}
+
+// QuickHull over the QuickHull list: the lower hull of entries 0..m (points
+// in increasing order; entries 0 and m are its ends and always vertices).  R
+// entries per thread, e = 1 + tid + r * blockDim.x.  Each level, every entry
+// still strictly below the chord of its segment (a, b) (the turn (a, e, b)
+// positive, the merges' vertex test) offers minus that turn to the segment's
+// slot as tile_quickhull does; the deepest entry of each segment is a vertex
+// and splits it, and the other entries follow the part that holds them.  An
+// entry on or above its chord drops out.  vert[r]: entry e is an interior
+// vertex.  slots: 3 (m + 2) words of LDS apart from the list.  Block scope;
+// the list is complete (a barrier after its last write);
 // m <= min(1023, R * blockDim.x).  Ends with a barrier.
-template <int K, bool ABS, int R>
+template <int R>
 __device__ inline void list_quickhull(const Tile& t, int m, unsigned long long* slots, bool (&vert)[R]) {
+    const double4* L = list_dd(t);
     const int tid = threadIdx.x, nt = blockDim.x, ns = m + 1;
     unsigned long long* F = slots + 3 * ns;  // the offer words of the three arrays
     for (int i = tid; i < 3 * ns + 3; i += nt) slots[i] = (i < 3 * ns) ? ~0ull : 0ull;
     int a[R], b[R];
     double2 dP[R], dB[R];  // P_e - P_a and P_b - P_a
     bool cand[R];
+    const double4 L0 = L[0], Lm = L[m];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int e = 1 + tid + r * nt;
@@ -784,12 +855,8 @@ __device__ inline void list_quickhull(const Tile& t, int m, unsigned long long* 
         cand[r] = e < m;
         a[r] = 0;
         b[r] = m;
-        dP[r] = make_double2(0.0, 0.0);
-        dB[r] = make_double2(1.0, 0.0);
-        if (cand[r]) {
-            dP[r] = vdiff<K, ABS>(t, 0, e);
-            dB[r] = vdiff<K, ABS>(t, 0, m);
-        }
+        dP[r] = dd4_diff(L0, cand[r] ? L[e] : L0);
+        dB[r] = dd4_diff(L0, Lm);
     }
     __syncthreads();  // the slots are clear
     for (int k = 0;; ++k) {
@@ -798,7 +865,7 @@ __device__ inline void list_quickhull(const Tile& t, int m, unsigned long long* 
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             if (cand[r]) {
-                const double turn = cross2(dP[r], dB[r]);  // vturn(a, e, b)
+                const double turn = cross2(dP[r], dB[r]);
                 if (turn > 0.0) {
                     atomicMin(cur + a[r], qh_key(-turn, 1 + tid + r * nt));
                     F[q] = 1ull;
@@ -820,15 +887,16 @@ __device__ inline void list_quickhull(const Tile& t, int m, unsigned long long* 
                 if (v == e) {
                     vert[r] = true;
                     cand[r] = false;
-                } else if (e < v) {
-                    b[r] = v;
-                    dB[r] = vdiff<K, ABS>(t, a[r], v);
                 } else {
-                    a[r] = v;
-                    dP[r] = vdiff<K, ABS>(t, v, e);
-                    dB[r] = vdiff<K, ABS>(t, v, b[r]);
+                    const bool left = e < v;
+                    a[r] = left ? a[r] : v;
+                    b[r] = left ? v : b[r];
+                    const double4 A = L[a[r]], B = L[b[r]], P = L[e];
+                    dP[r] = dd4_diff(A, P);
+                    dB[r] = dd4_diff(A, B);
                 }
             }
+            __builtin_amdgcn_sched_barrier(0);  // one entry's loads in flight at a time (registers)
         }
         const int o = (k + 2) % 3;
         unsigned long long* old = slots + o * ns;
@@ -838,14 +906,15 @@ __device__ inline void list_quickhull(const Tile& t, int m, unsigned long long* 
 }
 
 // After list_quickhull: its vertices (entry 0, the entries with vert, entry
-// m) move to the front of the list in order (V and VXY), flag[1] = their
+// m) move to the front of the list in order (V and L), flag[1] = their
 // number.  Every read precedes the first barrier.  Ends with a barrier.
 template <int R>
 __device__ inline void list_to_front(const Tile& t, int m, const bool (&vert)[R]) {
+    double4* L = list_dd(t);
     const int tid = threadIdx.x, nt = blockDim.x, lane = lane_id(), wid = tid >> 6, nw = nt >> 6;
     static_assert(R * 8 <= 32, "per-wave counts in W");
     unsigned short pv[R];
-    double2 xy[R];
+    double4 xy[R];
     uint64_t bal[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -853,14 +922,14 @@ __device__ inline void list_to_front(const Tile& t, int m, const bool (&vert)[R]
         bal[r] = __ballot(vert[r]);
         if (lane == 0) t.W[r * nw + wid] = __popcll(bal[r]);
         pv[r] = 0;
-        xy[r] = make_double2(0.0, 0.0);
+        xy[r] = make_double4(0.0, 0.0, 0.0, 0.0);
         if (vert[r]) {
             pv[r] = t.V[e];
-            xy[r] = t.VXY[e];
+            xy[r] = L[e];
         }
     }
     const unsigned short pm = t.V[m];
-    const double2 xym = t.VXY[m];
+    const double4 xym = L[m];
     __syncthreads();
     int base = 1;  // entry 0 stays
 #pragma unroll
@@ -874,13 +943,42 @@ __device__ inline void list_to_front(const Tile& t, int m, const bool (&vert)[R]
         if (vert[r]) {
             const int i = before + __popcll(bal[r] & bits_upto(lane - 1));
             t.V[i] = pv[r];
-            t.VXY[i] = xy[r];
+            L[i] = xy[r];
         }
     }
     if (tid == 0) {
         t.V[base] = pm;
-        t.VXY[base] = xym;
+        L[base] = xym;
         t.flag[1] = base + 1;
+    }
+    __syncthreads();
+}
+
+// tile_edge_slopes on the QuickHull list (after list_to_front): VXY[i] =
+// (slope of the edge from entry i to i + 1, oriented and clipped; clip
+// flag), at most R edges per thread.  Reads precede the barrier that the
+// writes follow (VXY[i] overlaps the list).  Ends with a barrier.
+template <int R>
+__device__ inline void list_edge_slopes(const Tile& t, int increasing, double clo, double chi) {
+    const double4* L = list_dd(t);
+    const int nv = t.flag[1];
+    double sv[R];
+    bool cv[R];
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int i = threadIdx.x + k * t.nl;
+        sv[k] = 0.0;
+        cv[k] = false;
+        if (i < nv - 1) {
+            const double2 d = dd4_diff(L[i], L[i + 1]);
+            sv[k] = finish(d.y / d.x, increasing, clo, chi, cv[k]);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+        const int i = threadIdx.x + k * t.nl;
+        if (i < nv - 1) t.VXY[i] = make_double2(sv[k], cv[k] ? 1.0 : 0.0);
     }
     __syncthreads();
 }
