@@ -505,6 +505,8 @@ struct ChunkArgs {
     double4* cvx;      // [rows*m*kVMax]
     int* cvi;          // [rows*m*kVMax]
     int* cover;        // [rows*m] 1 where the first pass left the chunk to the second, else 0
+    int* clist;        // [rows*m] the chunks the first pass left, in the order they were listed
+    unsigned long long* cctr;  // [2] clist's count word (cover_append), the epoch of a full scan
     int64_t nchunks;   // rows * m
     int cap;           // list entries of this pass (kChunk in the second)
 };
@@ -523,6 +525,34 @@ constexpr int kChunkQh = std::min((16 * (kChunkCap + 1)) / 32 - 1,
                                   (int)((32 * (kChunkLanes + 1) + 16 * kChunkLanes + 8 * (kChunkLanes / 2 + 1) +
                                          4 * kChunkLanes - 48) / 24));
 static_assert(kChunkQh <= 3 * kChunkLanes && kChunkQh <= 1023, "three QuickHull entries per thread, 10-bit keys");
+
+// The first pass lists the chunks it leaves to the second.  The count word
+// holds the call's epoch (its low 40 bits, above) and the count (24 bits:
+// more chunks than that would not fit in memory), so that a word left by an
+// earlier call reads as an empty list and nothing needs clearing.  Should an
+// entry fall outside the list (a word of another process's call with the same
+// tag), the second pass is told to scan every chunk's flag instead; stale
+// entries are harmless, as the second pass fits only chunks whose flag (written
+// by every chunk of this call) is set.
+constexpr unsigned long long kCoverTagShift = 24;
+__device__ inline unsigned long long cover_tag(unsigned long long epoch) {
+    return (epoch & ((1ull << 40) - 1ull)) << kCoverTagShift;
+}
+__device__ inline void cover_append(const ChunkArgs& a, int64_t bid) {
+    const unsigned long long tag = cover_tag(a.r.epoch);
+    unsigned long long old = *(volatile unsigned long long*)a.cctr, nw;
+    for (;;) {
+        nw = ((old >> kCoverTagShift) == (tag >> kCoverTagShift)) ? old + 1ull : tag + 1ull;
+        const unsigned long long got = atomicCAS(a.cctr, old, nw);
+        if (got == old) break;
+        old = got;
+    }
+    const int64_t slot = (int64_t)(nw & ((1ull << kCoverTagShift) - 1ull)) - 1;
+    if (slot < a.nchunks)
+        a.clist[slot] = (int)bid;
+    else
+        atomicExch(a.cctr + 1, a.r.epoch);
+}
 
 // One chunk by the workgroup: its hull stored, its tentative fit written.
 // PASS 0: the first pass (every chunk, a list of kChunkCap entries); 1: the
@@ -612,7 +642,10 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
         if constexpr (PASS == 0) {
             const bool over = tile_count(t, mask) > a.cap + 1;  // uniform
             if (over) {
-                if (threadIdx.x == 0) a.cover[bid] = 1;
+                if (threadIdx.x == 0) {
+                    a.cover[bid] = 1;
+                    cover_append(a, bid);
+                }
                 return;  // nothing else written: the second pass fits the chunk
             }
         }
@@ -667,14 +700,31 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
     chunk_fit<T, 0>(a, blockIdx.x);
 }
 
-// The second pass: workgroup b of the grid takes the chunks b, b + G, b + 2G,
-// ... (G workgroups; flagged chunks come in runs, which this spreads over the
-// grid), reads their flags (written by the first pass, which has completed in
-// stream order) 256 at a time, and fits the flagged ones.
+// The second pass: workgroup b of the grid takes the listed chunks b, b + G,
+// b + 2G, ... (G workgroups, each chunk to one workgroup while there are at
+// most G).  The first pass has completed in stream order.  When the list
+// overflowed, every workgroup instead reads the flags of the chunks b, b + G,
+// ..., 256 at a time (flagged chunks come in runs, which this spreads over
+// the grid), and fits the flagged ones.
 template <typename T>
 __global__ __launch_bounds__(kChunkLanes) void k_chunk_cover(ChunkArgs a) {
-    __shared__ uint64_t sel[kChunkLanes / kWave];
     const int64_t G = gridDim.x;
+    const unsigned long long word = a.cctr[0], tag = cover_tag(a.r.epoch);
+    if (a.cctr[1] != a.r.epoch) {
+        int64_t cnt = ((word >> kCoverTagShift) == (tag >> kCoverTagShift))
+                          ? (int64_t)(word & ((1ull << kCoverTagShift) - 1ull))
+                          : 0;
+        if (cnt > a.nchunks) cnt = a.nchunks;
+        for (int64_t i = blockIdx.x; i < cnt; i += G) {
+            const int64_t c = a.clist[i];
+            if (c >= 0 && c < a.nchunks && a.cover[c] != 0) {  // uniform
+                chunk_fit<T, 1>(a, c);
+                __syncthreads();  // the next chunk reuses the LDS
+            }
+        }
+        return;
+    }
+    __shared__ uint64_t sel[kChunkLanes / kWave];
     for (int64_t i0 = 0; (int64_t)blockIdx.x + i0 * G < a.nchunks; i0 += kChunkLanes) {
         const int64_t c = (int64_t)blockIdx.x + (i0 + threadIdx.x) * G;
         const uint64_t b = __ballot(c < a.nchunks && a.cover[c] != 0);
@@ -1727,6 +1777,8 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
     ca.cvx = (double4*)(a.ws + a.L.cvx);
     ca.cvi = (int*)(a.ws + a.L.cvi);
     ca.cover = (int*)(a.ws + a.L.cover);
+    ca.clist = (int*)(a.ws + a.L.clist);
+    ca.cctr = (unsigned long long*)(a.ws + a.L.cctr);
     ca.nchunks = a.rows * m;
     {
         const size_t smem1 = tile_smem_bytes(kChunkLanes, kChunk, kLaneK);
@@ -1739,11 +1791,11 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
         hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)chunks), dim3(kChunkLanes), smem0, a.stream, ca);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        // two workgroups per CU (the full list) run at a time; a grid of up
-        // to eight times that many (one workgroup per eight chunks) keeps two
-        // flagged chunks from sharing a workgroup unless there are many
+        // two workgroups per CU (the full list) run at a time: one such
+        // generation of workgroups, each taking at most one listed chunk
+        // while there are at most that many
         ca.cap = kChunk;
-        const int64_t cover_grid = std::min<int64_t>(chunks, std::max<int64_t>(512, std::min<int64_t>(chunks / 8, 4096)));
+        const int64_t cover_grid = std::min<int64_t>(chunks, 2 * (int64_t)num_cus());
         hipLaunchKernelGGL(k_chunk_cover<T>, dim3((unsigned)cover_grid), dim3(kChunkLanes), smem1, a.stream, ca);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

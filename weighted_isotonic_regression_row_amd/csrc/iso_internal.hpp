@@ -92,6 +92,8 @@ struct Layout {
     size_t gsn;          // int [rows*ceil(m/kSub)]
     size_t nc;           // int [rows*m]
     size_t cover;        // int [rows*m] 1 where the chunk kernel's first pass left the chunk to its second
+    size_t clist;        // int [rows*m] those chunks, listed
+    size_t cctr;         // u64 [2] the list's count (tagged with the call's epoch), the epoch of a full scan
     size_t mrec;         // MRec [rows*m]
     size_t so;           // double [rows*m]
     size_t cmask;        // u64 [rows*m*kMaskWords]
@@ -133,6 +135,8 @@ inline Layout make_layout(int64_t rows, int64_t n) {
     L.gsn = take(4 * (size_t)rows * (size_t)((L.m + kSub - 1) / kSub));
     L.nc = take(4 * rm);
     L.cover = take(4 * rm);
+    L.clist = take(4 * rm);
+    L.cctr = take(16);
     L.mrec = take(sizeof(MRec) * rm);
     L.so = take(8 * rm);
     L.cmask = take(8 * rm * kMaskWords);
@@ -210,6 +214,19 @@ inline hipError_t ensure_lds(const void* fn, size_t bytes, size_t (&seen)[kMaxDe
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e == hipSuccess) seen[dev] = bytes;
     return e;
+}
+
+// Compute units of the current device (256 on MI355X), cached per device id.
+inline int num_cus() {
+    static int cus[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
 }
 
 // Soft rank (first page, Sec. 7.9): rows of at most this many elements are
