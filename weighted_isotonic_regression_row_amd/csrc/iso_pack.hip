@@ -123,13 +123,31 @@ __device__ inline void packed_wave(const PackArgs& a, int64_t row0, int nrows, i
     // values in the same space), the lane's points and hull
     T* stage = (T*)smem;
     T wv[K];
-    if (a.w) {
-        stage_wave<T, K>((const T*)a.w + row0 * n, span, stage);
+    const T* yb = (const T*)a.y + row0 * n;
+    const T* wb = a.w ? (const T*)a.w + row0 * n : nullptr;
+    if ((((uintptr_t)yb) & 15) == 0 && (wb == nullptr || (((uintptr_t)wb) & 15) == 0)) {
+        // both inputs' loads in flight together
+        StagePieces<T, K> PW, PY;
+        if (wb) stage_fetch<T, K>(wb, span, PW);
+        stage_fetch<T, K>(yb, span, PY);
+        if (wb) {
+            stage_put<T, K>(PW, stage);
+            wave_sync();
 #pragma unroll
-        for (int j = 0; j < K; ++j) wv[j] = (j < cnt) ? stage[off + j] : (T)0;
-        wave_sync();  // every lane has its weights before the values replace them
+            for (int j = 0; j < K; ++j) wv[j] = (j < cnt) ? stage[off + j] : (T)0;
+            wave_sync();  // every lane has its weights before the values replace them
+        }
+        stage_put<T, K>(PY, stage);
+        wave_sync();
+    } else {
+        if (wb) {
+            stage_wave<T, K>(wb, span, stage);
+#pragma unroll
+            for (int j = 0; j < K; ++j) wv[j] = (j < cnt) ? stage[off + j] : (T)0;
+            wave_sync();  // every lane has its weights before the values replace them
+        }
+        stage_wave<T, K>(yb, span, stage);
     }
-    stage_wave<T, K>((const T*)a.y + row0 * n, span, stage);
     double xs[K], ys[K];
     int f = 0;
     {

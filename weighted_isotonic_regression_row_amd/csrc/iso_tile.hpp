@@ -255,49 +255,67 @@ __device__ __forceinline__ uint64_t gw_parts(const double (&xs)[K], const double
 // pieces (one contiguous KiB per load instruction) into the wave's stage, and
 // each lane then reads its own K values.  avail = elements of the span that
 // exist; the rest read as 0.
+//
+// stage_fetch is the global half (a 16-byte aligned span): the lane's pieces
+// into registers, every load issued before any is used, so that a caller
+// fetching two inputs waits for memory once; stage_put writes them to the
+// stage.
 template <typename T, int K>
-__device__ __forceinline__ void stage_wave(const T* __restrict__ base, int avail, T* stage) {
-    constexpr int VW = 16 / (int)sizeof(T);
-    constexpr int NV = K * kWave / VW;
+struct StagePieces {
+    static constexpr int VW = 16 / (int)sizeof(T);
+    static constexpr int NQ = K / VW;  // 16-byte pieces per lane
+    static_assert(K % VW == 0, "a lane's span is a whole number of 16-byte pieces");
+    uint4 v[NQ];
+};
+
+template <typename T, int K>
+__device__ __forceinline__ void stage_fetch(const T* __restrict__ base, int avail, StagePieces<T, K>& P) {
+    constexpr int VW = StagePieces<T, K>::VW, NQ = StagePieces<T, K>::NQ;
     const int lane = lane_id();
-    if ((((uintptr_t)base) & 15) == 0) {
+    if (avail >= K * kWave) {  // uniform: the whole span exists
 #pragma unroll
-        for (int q = 0; q < NV / kWave; ++q) {
+        for (int q = 0; q < NQ; ++q) P.v[q] = *(const uint4*)(base + (q * kWave + lane) * VW);
+    } else {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
             const int e = (q * kWave + lane) * VW;
             if (e + VW <= avail) {
-                *(uint4*)(stage + e) = *(const uint4*)(base + e);
+                P.v[q] = *(const uint4*)(base + e);
             } else {
+                T tv[VW];
 #pragma unroll
-                for (int r = 0; r < VW; ++r) stage[e + r] = (e + r < avail) ? base[e + r] : (T)0;
+                for (int r = 0; r < VW; ++r) tv[r] = (e + r < avail) ? base[e + r] : (T)0;
+                P.v[q] = *(const uint4*)tv;
             }
         }
+    }
+}
+
+template <typename T, int K>
+__device__ __forceinline__ void stage_put(const StagePieces<T, K>& P, T* stage) {
+    constexpr int VW = StagePieces<T, K>::VW, NQ = StagePieces<T, K>::NQ;
+    const int lane = lane_id();
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) *(uint4*)(stage + (q * kWave + lane) * VW) = P.v[q];
+}
+
+template <typename T, int K>
+__device__ __forceinline__ void stage_wave(const T* __restrict__ base, int avail, T* stage) {
+    if ((((uintptr_t)base) & 15) == 0) {
+        StagePieces<T, K> P;
+        stage_fetch<T, K>(base, avail, P);
+        stage_put<T, K>(P, stage);
     } else {
-        for (int e = lane; e < K * kWave; e += kWave) stage[e] = (e < avail) ? base[e] : (T)0;
+        for (int e = lane_id(); e < K * kWave; e += kWave) stage[e] = (e < avail) ? base[e] : (T)0;
     }
     wave_sync();
 }
 
+// The lane's K values from the stage (after stage_put and a wave_sync).
 template <typename T, int K>
-__device__ __forceinline__ void lane_load_staged(const T* __restrict__ base, int avail, T* stage, T (&v)[K]) {
+__device__ __forceinline__ void stage_read(const T* stage, T (&v)[K]) {
     constexpr int VW = 16 / (int)sizeof(T);
-    constexpr int NV = K * kWave / VW;
-    static_assert((K * (int)sizeof(T)) % 16 == 0, "a lane's values are read back as 16-byte pieces");
     const int lane = lane_id();
-    if ((((uintptr_t)base) & 15) == 0) {
-#pragma unroll
-        for (int q = 0; q < NV / kWave; ++q) {
-            const int e = (q * kWave + lane) * VW;
-            if (e + VW <= avail) {
-                *(uint4*)(stage + e) = *(const uint4*)(base + e);
-            } else {
-#pragma unroll
-                for (int r = 0; r < VW; ++r) stage[e + r] = (e + r < avail) ? base[e + r] : (T)0;
-            }
-        }
-    } else {
-        for (int e = lane; e < K * kWave; e += kWave) stage[e] = (e < avail) ? base[e] : (T)0;
-    }
-    wave_sync();
 #pragma unroll
     for (int q = 0; q < K / VW; ++q) {
         const uint4 u = *(const uint4*)(stage + lane * K + q * VW);
@@ -305,6 +323,13 @@ __device__ __forceinline__ void lane_load_staged(const T* __restrict__ base, int
 #pragma unroll
         for (int r = 0; r < VW; ++r) v[q * VW + r] = pu[r];
     }
+}
+
+template <typename T, int K>
+__device__ __forceinline__ void lane_load_staged(const T* __restrict__ base, int avail, T* stage, T (&v)[K]) {
+    static_assert((K * (int)sizeof(T)) % 16 == 0, "a lane's values are read back as 16-byte pieces");
+    stage_wave<T, K>(base, avail, stage);
+    stage_read<T, K>(stage, v);
     wave_sync();  // every lane has its values before the stage is reused
 }
 
@@ -379,13 +404,27 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
             // read back 16 bytes at a time as the sums consume it (the values
             // of y never all sit in registers beside the points)
             T wv[K];
-            if (w) {
-                lane_load_staged<T, K>(w, avail, stage, wv);
+            if ((((uintptr_t)y) & 15) == 0 && (w == nullptr || (((uintptr_t)w) & 15) == 0)) {
+                // both inputs' loads in flight together
+                StagePieces<T, K> PW, PY;
+                if (w) stage_fetch<T, K>(w, avail, PW);
+                stage_fetch<T, K>(y, avail, PY);
+                if (w) {
+                    stage_put<T, K>(PW, stage);
+                    wave_sync();
+                    stage_read<T, K>(stage, wv);
+                    wave_sync();  // every lane has its weights before the values replace them
+                }
+                stage_put<T, K>(PY, stage);
+                wave_sync();
             } else {
+                if (w) lane_load_staged<T, K>(w, avail, stage, wv);
+                stage_wave<T, K>(y, avail, stage);
+            }
+            if (!w) {
 #pragma unroll
                 for (int j = 0; j < K; ++j) wv[j] = (j < cnt) ? (T)1 : (T)0;
             }
-            stage_wave<T, K>(y, avail, stage);
             const int lane = lane_id();
 #pragma unroll
             for (int q = 0; q < K / VW; ++q) {
@@ -441,12 +480,19 @@ __device__ inline uint64_t lane_hull(const T* __restrict__ y, const T* __restric
         }
     }
     if (!STAGED && !done) {
+        // element loads, all issued before the sums use them
+        T yv[K], wv[K];
 #pragma unroll
-        for (int j = 0; j < K; ++j) {
-            const double yi = (j < cnt) ? (double)y[j] : 0.0;
-            const double wi = (j < cnt) ? (w ? (double)w[j] : 1.0) : 0.0;
-            take(j, yi, wi);
+        for (int j = 0; j < K; ++j) yv[j] = (j < cnt) ? y[j] : (T)0;
+        if (w) {
+#pragma unroll
+            for (int j = 0; j < K; ++j) wv[j] = (j < cnt) ? w[j] : (T)0;
+        } else {
+#pragma unroll
+            for (int j = 0; j < K; ++j) wv[j] = (j < cnt) ? (T)1 : (T)0;
         }
+#pragma unroll
+        for (int j = 0; j < K; ++j) take(j, (double)yv[j], (double)wv[j]);
     }
     checks();
     if constexpr (!HULL) return 0ull;
