@@ -309,7 +309,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void k
 // after its right point.  No LDS, no barriers.
 // ---------------------------------------------------------------------------
 template <typename T, int K>
-__global__ __launch_bounds__(256) void k_rows_lane(RowArgs a, int64_t rows) {
+// At most 256 registers a lane (two waves per SIMD): beyond that the
+// accumulation registers count too and only one wave fits.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_rows_lane(RowArgs a, int64_t rows) {
     mark_epoch(a.status, a.epoch);
     const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (row >= rows) return;
@@ -539,15 +541,20 @@ __device__ inline unsigned long long cover_tag(unsigned long long epoch) {
     return (epoch & ((1ull << 40) - 1ull)) << kCoverTagShift;
 }
 __device__ inline void cover_append(const ChunkArgs& a, int64_t bid) {
-    const unsigned long long tag = cover_tag(a.r.epoch);
-    unsigned long long old = *(volatile unsigned long long*)a.cctr, nw;
-    for (;;) {
-        nw = ((old >> kCoverTagShift) == (tag >> kCoverTagShift)) ? old + 1ull : tag + 1ull;
-        const unsigned long long got = atomicCAS(a.cctr, old, nw);
-        if (got == old) break;
-        old = got;
+    const unsigned long long tag = cover_tag(a.r.epoch), cnt_mask = (1ull << kCoverTagShift) - 1ull;
+    // one atomic add per entry; only the call's first appenders, which find
+    // an earlier call's word, replace it by this call's tag (one of them wins
+    // and takes entry 0, the others then add to the new word)
+    unsigned long long old = atomicAdd(a.cctr, 1ull);
+    while ((old & ~cnt_mask) != tag) {
+        const unsigned long long cur = atomicCAS(a.cctr, old + 1ull, tag + 1ull);
+        if (cur == old + 1ull) {
+            old = tag;
+            break;
+        }
+        old = ((cur & ~cnt_mask) == tag) ? atomicAdd(a.cctr, 1ull) : cur - 1ull;
     }
-    const int64_t slot = (int64_t)(nw & ((1ull << kCoverTagShift) - 1ull)) - 1;
+    const int64_t slot = (int64_t)(old & cnt_mask);
     if (slot < a.nchunks)
         a.clist[slot] = (int)bid;
     else
@@ -705,9 +712,10 @@ __global__ __launch_bounds__(kChunkLanes) void k_chunk_hull(ChunkArgs a) {
 // most G).  The first pass has completed in stream order.  When the list
 // overflowed, every workgroup instead reads the flags of the chunks b, b + G,
 // ..., 256 at a time (flagged chunks come in runs, which this spreads over
-// the grid), and fits the flagged ones.
+// the grid), and fits the flagged ones.  Registers are held to 256 a lane, so
+// that two workgroups (the LDS's limit) fit on a CU.
 template <typename T>
-__global__ __launch_bounds__(kChunkLanes) void k_chunk_cover(ChunkArgs a) {
+__global__ __launch_bounds__(kChunkLanes) __attribute__((amdgpu_waves_per_eu(2))) void k_chunk_cover(ChunkArgs a) {
     const int64_t G = gridDim.x;
     const unsigned long long word = a.cctr[0], tag = cover_tag(a.r.epoch);
     if (a.cctr[1] != a.r.epoch) {
