@@ -166,13 +166,13 @@ def test_one_wave_rows_past_the_lds_list(n, dtype, inc):
     _check_vjp(wl, b, gs, gc, grn, n + 7, wl.name)
 
 
-PACK_SIZES = [65, 80, 81, 100, 127, 128, 129, 200, 256, 257, 300, 400, 511, 512]
+PACK_SIZES = [33, 34, 47, 48, 63, 64, 65, 80, 81, 100, 127, 128, 129, 200, 256, 257, 300, 400, 511, 512]
 
 
 @pytest.mark.parametrize("n", PACK_SIZES)
 @pytest.mark.parametrize("dtype", [np.float32, np.float64])
 def test_packed_rows(n, dtype):
-    """Rows of 65 to 512 elements: up to 128 packed several to a wave (the first page, Sec. 3.5; dense waves
+    """Rows of 33 to 512 elements: up to 128 packed several to a wave (the first page, Sec. 3.5; dense waves
     refitted by the second pass with 8 points per lane), longer ones a wave each.  1001 rows (the last wave
     ragged) of noise, trend noise, increasing data (every point a vertex), a sawtooth and integer ties,
     interleaved so that every wave mixes them, with a NaN row and a row with a weight <= 0 among them; both

@@ -60,7 +60,7 @@ def _batch(rows, n, dtype, seed, inc=True, clip=None):
 CASES = [
     ("batch rows", _batch(1000, 5000, np.float32, 2, False, (0.0, 1.0)), _batch(37, 777, np.float64, 3)),
     ("long rows", _batch(2, 30000, np.float64, 5), _batch(1, 9000, np.float32, 7, False, (-0.5, 0.5))),
-    ("lane and pair rows", _batch(5000, 50, np.float32, 9), _batch(300, 24, np.float64, 11, True, (-1.0, 1.0))),
+    ("short rows", _batch(5000, 50, np.float32, 9), _batch(300, 24, np.float64, 11, True, (-1.0, 1.0))),
     ("one long row", _batch(1, 6_500_000, np.float64, 13), _batch(3, 20001, np.float64, 15)),
     ("packed rows", _batch(300_000, 65, np.float32, 17), _batch(1001, 128, np.float64, 19, False, (-0.5, 0.5))),
     ("one-wave rows", _batch(20_000, 300, np.float32, 21, True, (-1.0, 1.0)), _batch(77, 512, np.float64, 23)),

@@ -366,133 +366,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // ---------------------------------------------------------------------------
-// rows of 33 to 64 elements, two lanes per row (first page, Sec. 3.5: a row
-// takes the fewest lanes of 32 points that hold it).  Each lane builds the
-// hull of its 32 points; the pair then merges the two hulls, which share
-// point 32: if the chain turns strictly left there, point 32 stays a vertex;
-// otherwise the bridge (alpha in the left hull, beta in the right) is found by
-// walking outwards from point 32's neighbours (first page, Sec. 4, Lemma 4.2
-// and the walk after it) on the points both lanes wrote to LDS.  Each lane
-// then keeps its own vertices on its side of the bridge, and every element
-// takes the slope of the merged hull's edge above it.  One wave of 32 rows per
-// workgroup.
-// ---------------------------------------------------------------------------
-template <typename T, int K>
-__global__ __launch_bounds__(64) void k_rows_pair(RowArgs a, int64_t rows) {
-    __shared__ double2 Pt[32][2 * K + 1];  // per row: its points 0 .. n, absolute
-    const int rl = threadIdx.x >> 1, h = threadIdx.x & 1;
-    const int64_t row = (int64_t)blockIdx.x * 32 + rl;
-    mark_epoch(a.status, a.epoch);
-    if (row >= rows) return;  // both lanes of a pair leave together
-    const int N = (int)a.n;   // K + 1 .. 2K
-    const int cnt = h ? N - K : K;
-    const int64_t e0 = row * a.n + h * K;
-    double xs[K], ys[K];
-    int f = 0;
-    const uint64_t mask = lane_hull<T, K>((const T*)a.y + e0, a.w ? (const T*)a.w + e0 : nullptr, cnt, !a.increasing,
-                                          xs, ys, f);
-    // the right lane's points are relative to point K, the left lane's total
-    const double X0 = __shfl_xor(xs[K - 1], 1), Y0 = __shfl_xor(ys[K - 1], 1);
-    const double ox = h ? X0 : 0.0, oy = h ? Y0 : 0.0;
-    if (h == 0) Pt[rl][0] = make_double2(0.0, 0.0);
-#pragma unroll
-    for (int j = 0; j < K; ++j)
-        if (j < cnt) Pt[rl][h * K + j + 1] = make_double2(ox + xs[j], oy + ys[j]);
-    const int fr = f | __shfl_xor(f, 1);
-    const uint64_t mo = __shfl_xor(mask, 1);
-    wave_sync();
-    T* out = (T*)a.fit + e0;
-    uint64_t* sb = a.start_bits ? a.start_bits + row * a.words : nullptr;  // one word: n <= 2K <= 64
-    uint64_t* cb = a.clip_bits ? a.clip_bits + row * a.words : nullptr;
-    if (fr) {
-        for (int j = 0; j < cnt; ++j) out[j] = (T)NAN;
-        if (h == 0) {
-            if (sb) {
-                *sb = 0ull;
-                *cb = 0ull;
-            }
-            if (a.row_nan) a.row_nan[row] = 1u;
-            if (fr & 2) report_weight_error(a.status, a.epoch);
-        }
-        return;
-    }
-    // vertex sets: left hull over points 0..K (bit p), right hull over
-    // points K..N (bit p - K); both lanes compute the same bridge
-    const uint64_t VA = 1ull | ((h ? mo : mask) << 1);
-    const uint64_t VB = 1ull | ((h ? mask : mo) << 1);
-    auto turn = [&](int i, int j, int k) {
-        const double2 A = Pt[rl][i];
-        return cross2(sub2(Pt[rl][j], A), sub2(Pt[rl][k], A));
-    };
-    int al = K, be = K;
-    {
-        const int pa = hi_bit(VA & bits_upto(K - 1));
-        const int nb = K + lo_bit(VB & ~1ull);
-        if (!(turn(pa, K, nb) > 0.0)) {
-            al = pa;
-            be = nb;
-            bool moved = true;
-            while (moved) {
-                moved = false;
-                for (;;) {
-                    const uint64_t rest = VB & bits_from(be - K + 1);
-                    if (!rest) break;
-                    const int nx = K + lo_bit(rest);
-                    if (turn(al, be, nx) > 0.0) break;
-                    be = nx;
-                    moved = true;
-                }
-                while (al > 0) {
-                    const int pv = hi_bit(VA & bits_upto(al - 1));
-                    if (turn(pv, al, be) > 0.0) break;
-                    al = pv;
-                    moved = true;
-                }
-            }
-        }
-    }
-    // this lane's vertices of the merged hull (bit b <-> point hK + b + 1)
-    const uint64_t fm = h == 0 ? (mask & bits_upto(al - 1)) : (be <= K + 1 ? mask : (mask & bits_from(be - K - 1)));
-    double2 prev = h == 0 ? make_double2(0.0, 0.0) : Pt[rl][be == K ? K : al];
-    double E[K];
-#pragma unroll
-    for (int b = 0; b < K; ++b) {
-        E[b] = 0.0;
-        if (b < cnt && ((fm >> b) & 1ull)) {
-            const double2 q = make_double2(ox + xs[b], oy + ys[b]);
-            E[b] = (q.y - prev.y) / (q.x - prev.x);
-            prev = q;
-        }
-    }
-    double cur = 0.0;
-    if (h == 0 && al < K) {  // the left lane's elements past alpha lie under the bridge
-        const double2 A = Pt[rl][al], B = Pt[rl][be];
-        cur = (B.y - A.y) / (B.x - A.x);
-    }
-    double vals[K];
-    uint64_t clipm = 0ull;
-#pragma unroll
-    for (int b = K - 1; b >= 0; --b) {
-        if (b < cnt && ((fm >> b) & 1ull)) cur = E[b];
-        bool c = false;
-        vals[b] = finish(cur, a.increasing, a.lo, a.hi, c);
-        if (b < cnt && c) clipm |= 1ull << b;
-    }
-    store_lane<T, K>(out, cnt, vals);
-    // element i starts a block iff point i is a vertex of the merged hull
-    const uint64_t s_own = h == 0 ? ((1ull | (fm << 1)) & bits_upto(K - 1))
-                                  : (((al == K ? 1ull : 0ull) | (fm << 1)) & bits_upto(N - K - 1));
-    const uint64_t s_hi = __shfl_xor(s_own, 1), c_hi = __shfl_xor(clipm, 1);
-    if (h == 0) {
-        if (sb) {
-            *sb = s_own | (s_hi << K);
-            *cb = (clipm & bits_upto(K - 1)) | (c_hi << K);
-        }
-        if (a.row_nan) a.row_nan[row] = 0u;
-    }
-}
-
-// ---------------------------------------------------------------------------
 // chunk hulls of long rows
 // ---------------------------------------------------------------------------
 struct ChunkArgs {
@@ -1739,11 +1612,6 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
             hipLaunchKernelGGL((k_rows_lane<T, 16>), dim3(grid), dim3(256), 0, a.stream, r, (int64_t)a.rows);
         else
             hipLaunchKernelGGL((k_rows_lane<T, 32>), dim3(grid), dim3(256), 0, a.stream, r, (int64_t)a.rows);
-        return hipGetLastError();
-    }
-    if (a.n <= 2 * kLaneRow) {
-        const unsigned grid = (unsigned)((a.rows + 31) / 32);
-        hipLaunchKernelGGL((k_rows_pair<T, 32>), dim3(grid), dim3(64), 0, a.stream, r, (int64_t)a.rows);
         return hipGetLastError();
     }
     if (a.n <= kPackedMax) {

@@ -18,12 +18,15 @@ constexpr int kLdsBytes = 163840;
 // lane; 512 lanes of 12 elements at most).
 constexpr int64_t kSingleMax = 6144;
 // Rows of kPackedMin to kPackedMax elements are packed several to a wave
-// (shorter rows take the lane kernels).  Longer rows take a wave each
-// (k_row_fit with 4 or 8 points per lane), whose output-sensitive finish
-// measured as fast as the packed kernels on noise rows of 160 to 256 and
-// faster on rows whose every point is a vertex (1e5 rows, float32:
-// increasing rows of 160, 0.29 against 0.41 ms packed).
-constexpr int kPackedMin = 65;
+// (shorter rows take the lane kernels).  Rows of 33 to 64 on three or four
+// lanes of 16 points measured about twice as fast on noise as two lanes of 32
+// (1e6x48 float32: 0.40 against 0.97 ms), a third slower on rows whose every
+// point is a vertex.  Longer rows take a wave each (k_row_fit with 4 or 8
+// points per lane), whose output-sensitive finish measured as fast as the
+// packed kernels on noise rows of 160 to 256 and faster on rows whose every
+// point is a vertex (1e5 rows, float32: increasing rows of 160, 0.29 against
+// 0.41 ms packed).
+constexpr int kPackedMin = kLaneRow + 1;
 constexpr int kPackedMax = 128;
 // Rows of up to this many elements take one wave (k_row_fit with 2, 4 or 8
 // points per lane); longer ones several.

@@ -1,7 +1,7 @@
-// Rows of 65 to 128 elements, several to a wave (first page, Sec. 3.5: short
+// Rows of 33 to 128 elements, several to a wave (first page, Sec. 3.5: short
 // rows are packed several to a warp, each on the fewest lanes that hold it).
-// The kernels take any n up to 512 (32 lanes of 16 points, two rows a wave);
-// the launcher sends only rows up to kPackedMax here (iso_pack.hpp).
+// The kernels take rows of up to 512 elements (32 lanes of 16 points, two rows
+// a wave); the launcher sends rows of kPackedMin to kPackedMax here.
 //
 // A wave of 64 lanes takes R = floor(64 / L) consecutive rows, each on L =
 // ceil(n / K) consecutive lanes of K points (K = 16, or 8 in the second

@@ -1,4 +1,4 @@
-// Rows of 65 to 512 elements packed several to a wave (iso_pack.hip).
+// Rows of 33 to 512 elements packed several to a wave (iso_pack.hip).
 #pragma once
 
 #include <hip/hip_runtime.h>
