@@ -1360,19 +1360,15 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_top(MergeArgs a) {
     const int c0 = min(m, tid * per), c1 = min(m, c0 + per);
     double4 loc = make_double4(0.0, 0.0, 0.0, 0.0);
     for (int c = c0; c < c1; ++c) loc = dd4_add(loc, H.tot[c]);
-    double4 v = loc;
-    sbuf[tid] = v;
+    // the threads' sums scanned in each wave (DPP), then the waves' totals
+    // added in order: one barrier
+    const int wv = tid >> 6;
+    const double4 inc = wave_scan_incl(loc, [](double4 p, double4 q) { return dd4_add(p, q); });
+    if (lane_id() == kWave - 1) sbuf[wv] = inc;
     __syncthreads();
-    for (int d = 1; d < NT; d <<= 1) {
-        double4 o = make_double4(0.0, 0.0, 0.0, 0.0);
-        if (tid >= d) o = sbuf[tid - d];
-        __syncthreads();
-        if (tid >= d) v = dd4_add(o, v);
-        sbuf[tid] = v;
-        __syncthreads();
-    }
     double4 ex = make_double4(0.0, 0.0, 0.0, 0.0);
-    if (tid > 0) ex = sbuf[tid - 1];
+    for (int k = 0; k < wv; ++k) ex = dd4_add(ex, sbuf[k]);
+    ex = dd4_add(ex, wave_shift_up1(inc));
     for (int c = c0; c < c1; ++c) {
         a.starts[base + c] = ex;
         ex = dd4_add(ex, H.tot[c]);
