@@ -773,10 +773,23 @@ struct VR {
     int k;  // vertex rank in the chunk hull
 };
 
+// a + b of two double-double numbers with one exact sum of the high parts and
+// the low parts added once (Dekker's shorter addition): its error is of the
+// order of the low parts' rounding, far below what a difference of two points
+// keeps (pdx, pdy round to a double)
+__device__ __forceinline__ void dd_add_short(double ah, double al, double bh, double bl, double& rh, double& rl) {
+    double s, e;
+    two_sum(ah, bh, s, e);
+    e += al + bl;
+    fast_two_sum(s, e, rh, rl);
+}
+
 template <typename T>
 __device__ __forceinline__ PtD ptd(const MCtx& X, int c, int k) {
+    const double4 a = X.st[c - X.st_off], b = vtx_n<T>(X.H, c, k, X.nvc[c - X.nv_off]).v;
     PtD p;
-    p.a = dd4_add(X.st[c - X.st_off], vtx_n<T>(X.H, c, k, X.nvc[c - X.nv_off]).v);
+    dd_add_short(a.x, a.y, b.x, b.y, p.a.x, p.a.y);
+    dd_add_short(a.z, a.w, b.z, b.w, p.a.z, p.a.w);
     return p;
 }
 template <typename T>
@@ -784,16 +797,11 @@ __device__ __forceinline__ PtD ptv(const MCtx& X, VR v) {
     return ptd<T>(X, X.D[v.s].c, v.k);
 }
 
-__device__ __forceinline__ double pdx(const PtD& a, const PtD& b) {
-    double h, l;
-    dd_add(b.a.x, b.a.y, -a.a.x, -a.a.y, h, l);
-    return h + l;
-}
-__device__ __forceinline__ double pdy(const PtD& a, const PtD& b) {
-    double h, l;
-    dd_add(b.a.z, b.a.w, -a.a.z, -a.a.w, h, l);
-    return h + l;
-}
+// b - a, rounded to a double, part by part (high parts, then low parts): the
+// high parts of two nearby points cancel exactly, and the rounding of a
+// distant pair's difference is that of the result itself
+__device__ __forceinline__ double pdx(const PtD& a, const PtD& b) { return (b.a.x - a.a.x) + (b.a.y - a.a.y); }
+__device__ __forceinline__ double pdy(const PtD& a, const PtD& b) { return (b.a.z - a.a.z) + (b.a.w - a.a.w); }
 __device__ __forceinline__ double turnD(const PtD& a, const PtD& b, const PtD& d) {
     return pdx(a, b) * pdy(a, d) - pdy(a, b) * pdx(a, d);
 }
