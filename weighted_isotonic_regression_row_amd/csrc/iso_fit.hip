@@ -1270,10 +1270,22 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_sub(MergeArgs a) {
     for (int h = 1; h < ms; h <<= 1) {
         const int nm = (ms - h + 2 * h - 1) / (2 * h);
         X.D = Dc;
-        for (int k = wid; k < nm; k += nwv) {
-            const int j0 = k * 2 * h;
-            const MRec r = find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h], g, kWave, wins + wid);
-            if (g == 0) MR[k] = r;
+        // one wave per merge, or groups of 16 or 32 lanes when the level has
+        // more merges than waves (the lower levels: several merges of a wave
+        // then run side by side; their bridges lie within a few group steps
+        // of the shared point, and a wave's merges would otherwise run in
+        // turn); the LDS windows need a whole wave
+        int G = kWave;
+        while (G > 16 && (kWave / G) * nwv < nm) G >>= 1;
+        const int per = kWave / G, grp = g / G, gl = g % G;
+        for (int k0 = wid * per; k0 < nm; k0 += nwv * per) {
+            const int k = k0 + grp;
+            if (k < nm) {
+                const int j0 = k * 2 * h;
+                const MRec r =
+                    find_merge<T>(X, j0, j0 + h, NC[j0], NC[j0 + h], gl, G, G == kWave ? wins + wid : nullptr);
+                if (gl == 0) MR[k] = r;
+            }
         }
         __syncthreads();
         rewrite_level(Dc, Dn, NC, MR, ms, h, nm);
