@@ -140,7 +140,7 @@ int iso_fit(const void* y_dev, const void* w_dev, int64_t rows, int64_t n, int i
  *   wants the partition, blocks_out and blocks_mem_dev.
  *   Returns ISO_ETOOBIG, queuing nothing, when iso_workspace_bytes(rows, n,
  *   dtype) exceeds ISO_NOALLOC_SCRATCH_BYTES (128 MiB: any batch of rows of
- *   at most 64 elements, up to about 3e7 rows of 65 to 512, every batch of
+ *   at most 32 elements, up to about 3e7 rows of 33 to 512, every batch of
  *   rows of several waves up to 1000 x 6144 elements, and single rows of up
  *   to about 1.2e7 elements).
  *
