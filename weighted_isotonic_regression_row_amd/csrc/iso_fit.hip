@@ -387,10 +387,11 @@ struct ChunkArgs {
 };
 
 // The first pass gives each chunk a list of kChunkCap entries, small enough
-// for four chunks to share a CU's LDS; a chunk with more candidates than that
-// (rare: dense chunks keep about 620 of 3585 points) is flagged and fitted by
-// the second pass, whose list holds every point.  Every chunk writes its flag,
-// so nothing needs clearing before the call.
+// for four chunks to share a CU's LDS; a chunk that merges lane hulls with
+// more survivors than that (rare on dense rows, whose merging chunks keep
+// about 650 to 1300 of 3585 points; every chunk of a row whose every point is
+// a vertex) is flagged, listed, and fitted by the second pass, whose list
+// holds every point.  Every chunk writes its flag.
 constexpr int kChunkCap = (kLdsBytes / 4 - 512 - (int)tile_smem_bytes(kChunkLanes, 0, kLaneK)) / 18;
 // Candidates the first pass finishes by QuickHull: its list (32 bytes an
 // entry) takes the list's room, its three slot arrays (24 bytes an entry) the
