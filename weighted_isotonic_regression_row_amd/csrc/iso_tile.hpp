@@ -26,7 +26,13 @@
 //                vertex test; the rounds run only if a wrap exceeds its cap.
 //                Candidates may be any superset of the hull's vertices: the
 //                lane hulls' vertices, or for float32 rows of several waves
-//                those of the lanes' half hulls below the tile's chord;
+//                those of the lanes' half hulls below the tile's chord.
+//                Float32 rows of several waves, and the chunks of long rows
+//                with few candidates, skip the lane hulls and the rounds: the
+//                points under the hull of the lane ends are listed and their
+//                hull is found by a workgroup QuickHull (tile_quickhull on
+//                absolute float64 points, list_quickhull on double-double
+//                coordinates);
 //   4. expand    every lane computes the slope of the hull edge above each of
 //                its elements (Sec. 3.4: the edge from the last vertex at or
 //                before the element's left point to the first vertex at or
