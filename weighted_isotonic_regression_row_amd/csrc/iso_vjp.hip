@@ -225,30 +225,6 @@ __global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
     }
 }
 
-// per-row carries across tiles (one thread per row)
-template <int NF>
-__global__ void k_vjp_carry(VjpArgs a, int64_t rows) {
-    using A = Acc<NF>;
-    const int64_t row = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= rows) return;
-    A* head = (A*)a.head;
-    A* tail = (A*)a.tail;
-    A* carry = (A*)a.carry;
-    A* tot = (A*)a.tot;
-    const int64_t b = row * a.ntiles;
-    A c = acc_zero<NF>();
-    for (int t = 0; t < a.ntiles; ++t) {
-        carry[b + t] = c;
-        c = acc_pick(a.has[b + t] != 0, tail[b + t], acc_sum(c, head[b + t]));
-    }
-    A after = c;
-    tot[b + a.ntiles - 1] = after;
-    for (int t = a.ntiles - 2; t >= 0; --t) {
-        if (a.has[b + t + 1]) after = acc_sum(carry[b + t + 1], head[b + t + 1]);
-        tot[b + t] = after;
-    }
-}
-
 // Rows of at most kLaneRow elements, one row per lane: running block sums
 // forward, then each block's totals handed back to its elements.  Whole,
 // aligned rows are read and written with 16-byte accesses.
@@ -473,6 +449,79 @@ __device__ __forceinline__ int max_scan_wave(int v) {
     return wave_scan_incl(v, [](int a, int b) { return a > b ? a : b; });
 }
 
+// Per-row carries across tiles, one workgroup per row.  Tile t hands on the
+// sums of the block open at its end: its tail when a block starts in it, else
+// the carry into it plus its head, so the carries are an exclusive segmented
+// scan of (block starts in t, t's tail or head) over the tiles: each thread
+// composes a run of tiles, the threads' compositions are scanned (DPP in each
+// wave, then the waves' totals in order), and each thread replays its run.
+// tot[t] is the total of the block open at t's end: the carry into the next
+// tile with a block start plus that tile's head, or the row's final sums; a
+// suffix minimum over the threads' first such tiles finds the next one.
+constexpr int kCarryThreads = 256;
+template <int NF>
+__global__ __launch_bounds__(kCarryThreads) void k_vjp_carry(VjpArgs a, int64_t rows) {
+    using A = Acc<NF>;
+    __shared__ SegSum<NF> wpart[kCarryThreads / kWave];
+    __shared__ int nxt[kCarryThreads];
+    __shared__ A fin;
+    const int64_t row = blockIdx.x;
+    if (row >= rows) return;  // uniform
+    A* head = (A*)a.head;
+    A* tail = (A*)a.tail;
+    A* carry = (A*)a.carry;
+    A* tot = (A*)a.tot;
+    const int nt = a.ntiles, tid = threadIdx.x, lane = lane_id(), wid = tid >> 6;
+    const int per = (nt + kCarryThreads - 1) / kCarryThreads;
+    const int t0 = min(nt, tid * per), t1 = min(nt, t0 + per);
+    const int64_t b = row * nt;
+    // 1. the thread's run of tiles composed
+    SegSum<NF> loc;
+    loc.f = 0;
+    loc.a = acc_zero<NF>();
+    int first = INT_MAX;  // the run's first tile with a block start
+    for (int t = t0; t < t1; ++t) {
+        SegSum<NF> e;
+        e.f = a.has[b + t] != 0 ? 1 : 0;
+        e.a = e.f ? tail[b + t] : head[b + t];
+        loc = seg_op(loc, e);
+        if (e.f && first == INT_MAX) first = t;
+    }
+    // 2. exclusive scan of the compositions
+    const SegSum<NF> inc = seg_scan_wave(loc);
+    if (lane == kWave - 1) wpart[wid] = inc;
+    nxt[tid] = first;
+    __syncthreads();
+    SegSum<NF> ex = seg_move<0x138, 0xf>(inc);  // the previous lane's (nothing in lane 0)
+    SegSum<NF> pre;
+    pre.f = 0;
+    pre.a = acc_zero<NF>();
+    for (int k = 0; k < wid; ++k) pre = seg_op(pre, wpart[k]);
+    ex = seg_op(pre, ex);
+    // 3. the carries into the run's tiles (the scan starts from zero sums)
+    A c = ex.a;
+    for (int t = t0; t < t1; ++t) {
+        carry[b + t] = c;
+        c = acc_pick(a.has[b + t] != 0, tail[b + t], acc_sum(c, head[b + t]));
+    }
+    if (t0 < nt && t1 == nt) fin = c;  // the thread holding the last tile
+    // 4. the first tile with a block start after each thread's run: suffix
+    // minimum over the threads (every run's carries written before it is read)
+    for (int d = 1; d < kCarryThreads; d <<= 1) {
+        __syncthreads();
+        const int v = (tid + d < kCarryThreads) ? min(nxt[tid], nxt[tid + d]) : nxt[tid];
+        __syncthreads();
+        nxt[tid] = v;
+    }
+    __syncthreads();
+    const int s = (tid + 1 < kCarryThreads) ? nxt[tid + 1] : INT_MAX;
+    A after = (s < nt) ? acc_sum(carry[b + s], head[b + s]) : fin;
+    for (int t = t1 - 1; t >= t0; --t) {
+        tot[b + t] = after;
+        if (a.has[b + t]) after = acc_sum(carry[b + t], head[b + t]);
+    }
+}
+
 template <int NF>
 __host__ __device__ inline size_t vjp_row_smem_bytes(int nl) {
     // slots [nl] + per wave (flag, sums) and max-scan values
@@ -670,7 +719,7 @@ static hipError_t launch_vjp_t(const VjpLaunch& l) {
     hipLaunchKernelGGL((k_vjp_tile<T, NF>), dim3((unsigned)tiles), dim3(512), vjp_smem_bytes<NF>(a.T), l.stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_vjp_carry<NF>, dim3((unsigned)((l.rows + 63) / 64)), dim3(64), 0, l.stream, a, l.rows);
+    hipLaunchKernelGGL(k_vjp_carry<NF>, dim3((unsigned)l.rows), dim3(kCarryThreads), 0, l.stream, a, l.rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.mode = 2;
