@@ -74,6 +74,38 @@ struct VjpArgs {
 };
 
 template <int NF>
+struct SegSum {
+    int f;  // a block starts inside the span
+    Acc<NF> a;
+};
+// (earlier, later): the later span's sums restart if a block starts in it
+template <int NF>
+__device__ __forceinline__ SegSum<NF> seg_op(const SegSum<NF>& x, const SegSum<NF>& y) {
+    SegSum<NF> r;
+    r.f = x.f | y.f;
+#pragma unroll
+    for (int k = 0; k < NF; ++k) r.a.v[k] = y.f ? y.a.v[k] : x.a.v[k] + y.a.v[k];
+    return r;
+}
+template <int CTRL, int ROWS, int NF>
+__device__ __forceinline__ SegSum<NF> seg_move(const SegSum<NF>& x) {
+    SegSum<NF> r;
+    r.f = dpp_move<CTRL, ROWS>(x.f);
+#pragma unroll
+    for (int k = 0; k < NF; ++k) r.a.v[k] = dpp_move<CTRL, ROWS>(x.a.v[k]);
+    return r;
+}
+template <int NF>
+__device__ __forceinline__ SegSum<NF> seg_scan_wave(SegSum<NF> x) {
+    x = seg_op(seg_move<0x111, 0xf>(x), x);
+    x = seg_op(seg_move<0x112, 0xf>(x), x);
+    x = seg_op(seg_move<0x114, 0xf>(x), x);
+    x = seg_op(seg_move<0x118, 0xf>(x), x);
+    x = seg_op(seg_move<0x142, 0xa>(x), x);
+    x = seg_op(seg_move<0x143, 0xc>(x), x);
+    return x;
+}
+template <int NF>
 __host__ __device__ inline size_t vjp_smem_bytes(int T) {
     const int G = (T + 63) / 64;
     return sizeof(Acc<NF>) * (size_t)T + (size_t)G * (sizeof(Acc<NF>) * 2 + sizeof(int) * 3) + 64;
@@ -161,21 +193,39 @@ __global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
         }
     }
     __syncthreads();
-    // phase 2: carries across groups and the next block start after each group
-    if (threadIdx.x == 0) {
-        A c = acc_zero<NF>();
-        if (a.mode == 2) c = carry[ti];
-        for (int q = 0; q < G; ++q) {
-            gcarry[q] = c;
-            const A t = gtail[q];
-            c = acc_pick(ghas[q] != 0, t, acc_sum(c, t));
+    // phase 2: carries across groups and the next block start after each
+    // group, by wave 0 with one lane per group (G <= 64): an exclusive
+    // segmented scan of the groups' (block starts in it, sums since its last
+    // start) from the carry into the tile, and a suffix minimum of the groups'
+    // first block starts
+    if (wid == 0) {
+        A cin = acc_zero<NF>();
+        if (a.mode == 2) cin = carry[ti];
+        SegSum<NF> e;
+        e.f = (lane < G && ghas[lane] != 0) ? 1 : 0;
+        e.a = (lane < G) ? gtail[lane] : acc_zero<NF>();
+        const SegSum<NF> inc = seg_scan_wave(e);
+        SegSum<NF> start;
+        start.f = 0;
+        start.a = cin;
+        const SegSum<NF> ex = seg_op(start, seg_move<0x138, 0xf>(inc));
+        if (lane < G) gcarry[lane] = ex.a;
+        // the sums open at the tile's end (lane G - 1's inclusive scan from cin)
+        SegSum<NF> fin = seg_op(start, inc);
+        A c;
+#pragma unroll
+        for (int k = 0; k < NF; ++k) c.v[k] = __shfl(fin.a.v[k], G - 1, kWave);
+        int nx = (lane < G && ghas[lane]) ? lane * 64 + gfirst[lane] : N;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int o = __shfl_down(nx, d, kWave);
+            if (lane + d < kWave) nx = min(nx, o);
         }
-        int nx = N;
-        for (int q = G - 1; q >= 0; --q) {
-            gnext[q] = nx;
-            if (ghas[q]) nx = q * 64 + gfirst[q];
-        }
-        if (a.mode == 1) {
+        // nx: the first start in groups >= lane; gnext wants groups > lane
+        const int after = __shfl_down(nx, 1, kWave);
+        if (lane < G) gnext[lane] = (lane + 1 < G) ? after : N;
+        nx = __shfl(nx, 0, kWave);  // the tile's first block start (N if none)
+        if (a.mode == 1 && lane == 0) {
             // tail: the open block at the tile's end (no carry in this pass);
             // the head is read after the carries are added below
             tail[ti] = c;
@@ -413,38 +463,6 @@ __global__ __launch_bounds__(64) void k_vjp_pair(VjpArgs a, int64_t rows) {
 //      block's totals and writes the products.
 constexpr int kVjpK = 8;
 
-template <int NF>
-struct SegSum {
-    int f;  // a block starts inside the span
-    Acc<NF> a;
-};
-// (earlier, later): the later span's sums restart if a block starts in it
-template <int NF>
-__device__ __forceinline__ SegSum<NF> seg_op(const SegSum<NF>& x, const SegSum<NF>& y) {
-    SegSum<NF> r;
-    r.f = x.f | y.f;
-#pragma unroll
-    for (int k = 0; k < NF; ++k) r.a.v[k] = y.f ? y.a.v[k] : x.a.v[k] + y.a.v[k];
-    return r;
-}
-template <int CTRL, int ROWS, int NF>
-__device__ __forceinline__ SegSum<NF> seg_move(const SegSum<NF>& x) {
-    SegSum<NF> r;
-    r.f = dpp_move<CTRL, ROWS>(x.f);
-#pragma unroll
-    for (int k = 0; k < NF; ++k) r.a.v[k] = dpp_move<CTRL, ROWS>(x.a.v[k]);
-    return r;
-}
-template <int NF>
-__device__ __forceinline__ SegSum<NF> seg_scan_wave(SegSum<NF> x) {
-    x = seg_op(seg_move<0x111, 0xf>(x), x);
-    x = seg_op(seg_move<0x112, 0xf>(x), x);
-    x = seg_op(seg_move<0x114, 0xf>(x), x);
-    x = seg_op(seg_move<0x118, 0xf>(x), x);
-    x = seg_op(seg_move<0x142, 0xa>(x), x);
-    x = seg_op(seg_move<0x143, 0xc>(x), x);
-    return x;
-}
 __device__ __forceinline__ int max_scan_wave(int v) {
     return wave_scan_incl(v, [](int a, int b) { return a > b ? a : b; });
 }
