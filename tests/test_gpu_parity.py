@@ -235,6 +235,29 @@ def test_families(kind, n, dtype):
         check_partition(*gpu_blocks(b), wl.y, wl.w, True, None, None, wl.name)
 
 
+@pytest.mark.parametrize("kind", workloads.FAMILIES)
+@pytest.mark.parametrize("dtype", [np.float64, np.float32])
+def test_vjp_long_row_families(kind, dtype):
+    """Rows of four 4096-element tiles and a ragged tail, of every data family,
+    plus a row of two blocks that meet exactly at a tile boundary: the fit's
+    partition, then both backward products against the oracle.  Decreasing
+    and constant rows are one block, so whole tiles hold no block start;
+    increasing rows start a block at every element."""
+    n = 4 * 4096 + 77
+    wl = workloads.family(kind, 3, n, seed=11, dtype=dtype, weights="uniform")
+    i = np.arange(n)
+    two = np.where(i < 8192, -1e-6 * i, 1.0 - 1e-6 * (i - 8192)).astype(dtype)
+    wl.y = np.concatenate([wl.y, two[None, :]])
+    wl.w = np.concatenate([wl.w, workloads.rng(12).uniform(0.5, 2.0, (1, n)).astype(dtype)])
+    fit, b, *_ = gpu_fit(wl)
+    z, *_ = oracle_fit(wl)
+    check_fit(fit.cpu().numpy(), z, wl.y, dtype, True, wl.name)
+    gs, gc, grn = gpu_blocks(b)
+    check_partition(gs, gc, grn, wl.y, wl.w, True, None, None, wl.name)
+    assert gs[3, 8192] and gs[3].sum() == 2
+    _check_vjp(wl, b, gs, gc, grn, 17, wl.name)
+
+
 @pytest.mark.parametrize("n", [2500, 5000, 6144])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 def test_rows_past_the_lds_list_mixed_with_others(n, dtype):

@@ -12,12 +12,15 @@
 // (then 0), and W_B = sum_B w.  The partition is the forward pass's own (its
 // block-start bits), as the page's tests require.
 //
-// A tile of up to 8192 elements is one workgroup: a segmented inclusive scan
-// of (g', w) -- and w y when the weight product is asked for -- inside each
-// 64-element group (wave64 shuffles), a carry across groups, then every
-// element reads its block's totals at the block's last element.  Rows longer
-// than one tile go through three launches: per-tile partial sums, a per-row
-// carry pass, and the tile pass with those carries.
+// Rows of up to 6144 elements are one workgroup, kVjpK elements per lane: each
+// lane sums its elements' blocks in registers, a segmented scan over the
+// lanes carries the sums of the block open at each lane's start, and every
+// element then takes its block's totals, found where the block ends.  Longer
+// rows are cut into tiles of kVjpTile elements and take three launches: the
+// sums of each tile's head (before its first block start) and tail (from its
+// last block start), which reads only those elements; a per-row carry pass
+// over the tiles; and the same per-lane kernel on every tile, started from
+// the sums carried into it and given the totals of the block open at its end.
 #include <math.h>
 
 #include "iso_device.hpp"
@@ -60,7 +63,6 @@ struct VjpArgs {
     void* out;      // grad_y, or nullptr
     void* out_w;    // grad_w, or nullptr
     int64_t n, words;
-    int T;       // elements per tile
     int ntiles;  // tiles per row
     const uint64_t* sb;
     const uint64_t* cb;
@@ -70,7 +72,6 @@ struct VjpArgs {
     int* has;     // [rows * ntiles] tile holds a block start
     void* carry;  // Acc [rows * ntiles] open block's sums before the tile
     void* tot;    // Acc [rows * ntiles] totals of the block open at the tile's end
-    int mode;     // 0: whole row in one tile; 1: partial sums; 2: tile pass of a long row
 };
 
 template <int NF>
@@ -105,176 +106,6 @@ __device__ __forceinline__ SegSum<NF> seg_scan_wave(SegSum<NF> x) {
     x = seg_op(seg_move<0x143, 0xc>(x), x);
     return x;
 }
-template <int NF>
-__host__ __device__ inline size_t vjp_smem_bytes(int T) {
-    const int G = (T + 63) / 64;
-    return sizeof(Acc<NF>) * (size_t)T + (size_t)G * (sizeof(Acc<NF>) * 2 + sizeof(int) * 3) + 64;
-}
-
-template <typename T, int NF>
-__global__ __launch_bounds__(512) void k_vjp_tile(VjpArgs a) {
-    using A = Acc<NF>;
-    extern __shared__ __align__(32) char smem[];
-    const int64_t bid = blockIdx.x;
-    const int64_t row = bid / a.ntiles;
-    const int tile = (int)(bid % a.ntiles);
-    const int64_t t0 = (int64_t)tile * a.T;
-    const int N = (int)((a.n - t0) < a.T ? (a.n - t0) : a.T);
-    const int G = (N + 63) / 64;
-    A* F = (A*)smem;
-    A* gtail = F + a.T;
-    A* gcarry = gtail + G;
-    int* ghas = (int*)(gcarry + G);
-    int* gfirst = ghas + G;
-    int* gnext = gfirst + G;
-
-    const T* g = (const T*)a.g + row * a.n + t0;
-    const T* w = a.w ? (const T*)a.w + row * a.n + t0 : nullptr;
-    const T* y = (NF == 3) ? (const T*)a.y + row * a.n + t0 : nullptr;
-    T* out = a.out ? (T*)a.out + row * a.n + t0 : nullptr;
-    T* out_w = (NF == 3) ? (T*)a.out_w + row * a.n + t0 : nullptr;
-    const uint64_t* sb = a.sb + row * a.words + t0 / 64;
-    const uint64_t* cb = a.cb + row * a.words + t0 / 64;
-    const int64_t ti = row * a.ntiles + tile;
-    A* head = (A*)a.head;
-    A* tail = (A*)a.tail;
-    A* carry = (A*)a.carry;
-    A* tot_open = (A*)a.tot;
-
-    if (a.row_nan[row]) {
-        if (a.mode != 1) {
-            for (int i = threadIdx.x; i < N; i += blockDim.x) {
-                if (out) out[i] = (T)NAN;
-                if (NF == 3) out_w[i] = (T)NAN;
-            }
-        } else if (threadIdx.x == 0) {
-            A u = acc_zero<NF>();
-            u.v[1] = 1.0;
-            head[ti] = u;
-            tail[ti] = u;
-            a.has[ti] = 1;
-        }
-        return;
-    }
-
-    const int lane = lane_id();
-    const int wid = threadIdx.x >> 6;
-    const int nw = blockDim.x >> 6;
-    // phase 1: segmented scan inside each group
-    for (int q = wid; q < G; q += nw) {
-        const int e = q * 64 + lane;
-        const bool valid = e < N;
-        const uint64_t vmask = (N - q * 64 >= 64) ? ~0ull : ((1ull << (N - q * 64)) - 1ull);
-        const uint64_t sw = sb[q] & vmask;
-        const uint64_t cw = cb[q];
-        A v = acc_zero<NF>();
-        if (valid) {
-            v.v[0] = ((cw >> lane) & 1ull) ? 0.0 : (double)g[e];
-            v.v[1] = w ? (double)w[e] : 1.0;
-            if (NF == 3) v.v[NF - 1] = v.v[1] * (double)y[e];
-        }
-        int fl = (int)((sw >> lane) & 1ull);
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            A o;
-#pragma unroll
-            for (int k = 0; k < NF; ++k) o.v[k] = __shfl_up(v.v[k], d, 64);
-            const int of = __shfl_up(fl, d, 64);
-            if (lane >= d) {
-                if (!fl) v = acc_sum(o, v);
-                fl |= of;
-            }
-        }
-        if (valid) F[e] = v;
-        if (lane == 63) {
-            gtail[q] = v;
-            ghas[q] = sw != 0ull;
-            gfirst[q] = sw ? lo_bit(sw) : 64;
-        }
-    }
-    __syncthreads();
-    // phase 2: carries across groups and the next block start after each
-    // group, by wave 0 with one lane per group (G <= 64): an exclusive
-    // segmented scan of the groups' (block starts in it, sums since its last
-    // start) from the carry into the tile, and a suffix minimum of the groups'
-    // first block starts
-    if (wid == 0) {
-        A cin = acc_zero<NF>();
-        if (a.mode == 2) cin = carry[ti];
-        SegSum<NF> e;
-        e.f = (lane < G && ghas[lane] != 0) ? 1 : 0;
-        e.a = (lane < G) ? gtail[lane] : acc_zero<NF>();
-        const SegSum<NF> inc = seg_scan_wave(e);
-        SegSum<NF> start;
-        start.f = 0;
-        start.a = cin;
-        const SegSum<NF> ex = seg_op(start, seg_move<0x138, 0xf>(inc));
-        if (lane < G) gcarry[lane] = ex.a;
-        // the sums open at the tile's end (lane G - 1's inclusive scan from cin)
-        SegSum<NF> fin = seg_op(start, inc);
-        A c;
-#pragma unroll
-        for (int k = 0; k < NF; ++k) c.v[k] = __shfl(fin.a.v[k], G - 1, kWave);
-        int nx = (lane < G && ghas[lane]) ? lane * 64 + gfirst[lane] : N;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int o = __shfl_down(nx, d, kWave);
-            if (lane + d < kWave) nx = min(nx, o);
-        }
-        // nx: the first start in groups >= lane; gnext wants groups > lane
-        const int after = __shfl_down(nx, 1, kWave);
-        if (lane < G) gnext[lane] = (lane + 1 < G) ? after : N;
-        nx = __shfl(nx, 0, kWave);  // the tile's first block start (N if none)
-        if (a.mode == 1 && lane == 0) {
-            // tail: the open block at the tile's end (no carry in this pass);
-            // the head is read after the carries are added below
-            tail[ti] = c;
-            a.has[ti] = (nx < N) ? 1 : 0;
-            if (nx >= N) head[ti] = c;  // no start: the whole tile
-            gfirst[0] = nx;             // group 0's first start is no longer needed
-        }
-    }
-    __syncthreads();
-    // phase 3: add the carry where no block starts between the group start and e
-    for (int q = wid; q < G; q += nw) {
-        const int e = q * 64 + lane;
-        if (e < N) {
-            const uint64_t sw = sb[q];
-            if ((sw & bits_upto(lane)) == 0ull) F[e] = acc_sum(F[e], gcarry[q]);
-        }
-    }
-    __syncthreads();
-    if (a.mode == 1) {
-        // head: the tile's prefix before its first block start
-        if (threadIdx.x == 0) {
-            const int nx = gfirst[0];
-            if (nx < N) head[ti] = acc_pick(nx > 0, F[max(nx, 1) - 1], acc_zero<NF>());
-        }
-        return;
-    }
-    // phase 4: every element takes its block's totals, found at the block's end
-    A open_total = acc_zero<NF>();
-    if (a.mode == 2) open_total = tot_open[ti];
-    for (int q = wid; q < G; q += nw) {
-        const int e = q * 64 + lane;
-        if (e < N) {
-            const uint64_t vmask = (N - q * 64 >= 64) ? ~0ull : ((1ull << (N - q * 64)) - 1ull);
-            const uint64_t later = sb[q] & vmask & bits_from(lane + 1);
-            const int nxt = later ? q * 64 + lo_bit(later) : gnext[q];
-            const A tb = acc_pick(nxt < N, F[min(nxt, N) - 1], acc_pick(a.mode == 2, open_total, F[N - 1]));
-            const double gw = tb.v[0] / tb.v[1];  // G_B / W_B
-            if (out) {
-                const double wv = w ? (double)w[e] : 1.0;
-                out[e] = (T)(wv * gw);
-            }
-            if (NF == 3) {
-                const double mean = tb.v[NF - 1] / tb.v[1];
-                out_w[e] = (T)(gw * ((double)y[e] - mean));
-            }
-        }
-    }
-}
-
 // Rows of at most kLaneRow elements, one row per lane: running block sums
 // forward, then each block's totals handed back to its elements.  Whole,
 // aligned rows are read and written with 16-byte accesses.
@@ -448,17 +279,21 @@ __global__ __launch_bounds__(64) void k_vjp_pair(VjpArgs a, int64_t rows) {
     }
 }
 
-// Rows of kLaneRow < n <= kSingleMax elements, one workgroup per row, all
-// sums in registers (kVjpK elements per lane):
+// Rows of kLaneRow < n <= kSingleMax elements, one workgroup per row, and the
+// kVjpTile-element tiles of longer rows, one workgroup per tile, all sums in
+// registers (kVjpK elements per lane):
 //   1. each lane forms the segmented prefix sums of its elements (reset at
 //      every block start);
 //   2. a segmented scan over the lanes (DPP inside each wave, the waves'
 //      aggregates through LDS) gives every lane the sums of the block that is
 //      open when the lane begins, and a max-scan gives, for the block open at
-//      each lane's end, the lane where that block began;
+//      each lane's end, the lane where that block began (a tile's scan starts
+//      from the sums carried into it);
 //   3. the lane where a block that began in an earlier lane ends writes the
-//      block's totals to that lane's LDS slot; after one barrier the lanes
-//      that the block spans read them;
+//      block's totals to that lane's LDS slot (a block open at a tile's start
+//      has a slot of its own, and a tile's last element holds the totals of
+//      the block open at the tile's end); after one barrier the lanes that the
+//      block spans read them;
 //   4. a backward pass over each lane's elements hands every element its
 //      block's totals and writes the products.
 constexpr int kVjpK = 8;
@@ -542,44 +377,56 @@ __global__ __launch_bounds__(kCarryThreads) void k_vjp_carry(VjpArgs a, int64_t 
 
 template <int NF>
 __host__ __device__ inline size_t vjp_row_smem_bytes(int nl) {
-    // slots [nl] + per wave (flag, sums) and max-scan values
-    return sizeof(Acc<NF>) * (size_t)nl + 16 * (sizeof(Acc<NF>) + 2 * sizeof(int)) + 64;
+    // slots [nl + 1] + per wave (flag, sums) and max-scan values
+    return sizeof(Acc<NF>) * (size_t)(nl + 1) + 16 * (sizeof(Acc<NF>) + 2 * sizeof(int)) + 64;
 }
 
+// NaN products over [t0, t0 + N) of a row whose fit was NaN.
 template <typename T, int NF>
-__global__ __launch_bounds__(1024) void k_vjp_row(VjpArgs a) {
+__device__ __forceinline__ void vjp_nan_span(const VjpArgs& a, int64_t row, int64_t t0, int N) {
+    T* out = a.out ? (T*)a.out + row * a.n + t0 : nullptr;
+    T* out_w = (NF == 3) ? (T*)a.out_w + row * a.n + t0 : nullptr;
+    for (int i = threadIdx.x; i < N; i += blockDim.x) {
+        if (out) out[i] = (T)NAN;
+        if (NF == 3) out_w[i] = (T)NAN;
+    }
+}
+
+// The products over [t0, t0 + N) of one row, kVjpK elements per lane.  cin
+// holds the sums of the block open where the span begins (zero for a whole
+// row).  In a tile (TILE) the block open at the span's end may run on into
+// later tiles, so its elements take open_total, that block's totals over the
+// whole row.
+template <typename T, int NF, bool TILE>
+__device__ __forceinline__ void vjp_span(const VjpArgs& a, int64_t row, int64_t t0, int N, const Acc<NF>& cin0,
+                                         const Acc<NF>& open_total, char* smem) {
     using A = Acc<NF>;
     constexpr int K = kVjpK;
-    extern __shared__ __align__(32) char smem[];
-    const int64_t row = blockIdx.x;
-    const int N = (int)a.n;
     const int l = threadIdx.x, lane = lane_id(), wid = l >> 6;
+    // slot b + 1: the totals of a block that began in lane b; slot 0: of the
+    // block open at the span's start
     A* slot = (A*)smem;
-    A* wsum = slot + blockDim.x;
+    A* wsum = slot + blockDim.x + 1;
     int* wflag = (int*)(wsum + 16);
     int* wmax = wflag + 16;
-    const T* g = (const T*)a.g + row * a.n;
-    const T* w = a.w ? (const T*)a.w + row * a.n : nullptr;
-    const T* y = (NF == 3) ? (const T*)a.y + row * a.n : nullptr;
-    T* out = a.out ? (T*)a.out + row * a.n : nullptr;
-    T* out_w = (NF == 3) ? (T*)a.out_w + row * a.n : nullptr;
-    if (a.row_nan[row]) {  // uniform: before any barrier
-        for (int i = l; i < N; i += blockDim.x) {
-            if (out) out[i] = (T)NAN;
-            if (NF == 3) out_w[i] = (T)NAN;
-        }
-        return;
-    }
+    const int64_t base = row * a.n + t0;
+    const T* g = (const T*)a.g + base;
+    const T* w = a.w ? (const T*)a.w + base : nullptr;
+    const T* y = (NF == 3) ? (const T*)a.y + base : nullptr;
+    T* out = a.out ? (T*)a.out + base : nullptr;
+    T* out_w = (NF == 3) ? (T*)a.out_w + base : nullptr;
     const int e0 = l * K;
     const int cnt = min(max(N - e0, 0), K);
-    const int words = (N + 63) / 64;
-    // start bits of elements e0 .. e0 + K (one past the lane), clip bits of the lane's
+    // start bits of elements e0 .. e0 + K (one past the lane), clip bits of the
+    // lane's; t0 and e0 are multiples of K, so a lane's bits sit in one word
     uint32_t sbit = 0, cbit = 0;
     if (cnt > 0) {
-        const int q = e0 >> 6, off = e0 & 63;
+        const int64_t pos = t0 + e0;
+        const int64_t q = pos >> 6;
+        const int off = (int)(pos & 63);
         const uint64_t* sb = a.sb + row * a.words;
         const uint64_t* cb = a.cb + row * a.words;
-        const uint64_t s0 = sb[q], s1 = (q + 1 < words) ? sb[q + 1] : 0ull;
+        const uint64_t s0 = sb[q], s1 = (q + 1 < a.words) ? sb[q + 1] : 0ull;
         const uint64_t win = (s0 >> off) | (off ? (s1 << (64 - off)) : 0ull);
         sbit = (uint32_t)(win & ((1ull << (K + 1)) - 1ull));
         cbit = (uint32_t)((cb[q] >> off) & ((1ull << K) - 1ull));
@@ -627,7 +474,7 @@ __global__ __launch_bounds__(1024) void k_vjp_row(VjpArgs a) {
     __syncthreads();
     SegSum<NF> pre;
     pre.f = 0;
-    pre.a = acc_zero<NF>();
+    pre.a = cin0;
     int pmax = 0;
     for (int k = 0; k < wid; ++k) {
         SegSum<NF> o;
@@ -641,16 +488,21 @@ __global__ __launch_bounds__(1024) void k_vjp_row(VjpArgs a) {
 #pragma unroll
     for (int k = 0; k < NF; ++k) ex.a.v[k] = dpp_move<0x138, 0xf>(inc.a.v[k]);
     const SegSum<NF> cin = seg_op(pre, ex);  // sums of the block open when the lane begins
-    // lanes (+1) where blocks began: the last one before the lane holds the
-    // block open at its start, the last one up to it the block open at its end
-    const int begin_open = max(pmax, dpp_move<0x138, 0xf>(mx)) - 1;
-    const int end_open = max(pmax, mx) - 1;
+    // lanes (+1) where blocks began (0: before the span): the last one before
+    // the lane holds the block open at its start, the last one up to it the
+    // block open at its end
+    const int begin_open = max(pmax, dpp_move<0x138, 0xf>(mx));
+    const int end_open = max(pmax, mx);
     // the carry reaches the elements before the lane's first start
     const int first = own ? (__ffs((int)own) - 1) : K;
 #pragma unroll
     for (int j = 0; j < K; ++j) P[j] = acc_pick(j < first, acc_sum(cin.a, P[j]), P[j]);
+    if (TILE) {
+#pragma unroll
+        for (int j = 0; j < K; ++j) P[j] = acc_pick(e0 + j == N - 1, open_total, P[j]);
+    }
     // 3. a block that began in an earlier lane and ends here: totals to its slot
-    //    (element j ends a block when it is the row's last or j + 1 starts one)
+    //    (element j ends a block when it is the span's last or j + 1 starts one)
     int last_end = -1, first_end = K;
 #pragma unroll
     for (int j = 0; j < K; ++j) {
@@ -660,7 +512,7 @@ __global__ __launch_bounds__(1024) void k_vjp_row(VjpArgs a) {
             if (first_end == K) first_end = j;
         }
     }
-    if (first_end < K && first_end < first && begin_open >= 0) {
+    if (first_end < K && first_end < first) {
         A v = acc_zero<NF>();
 #pragma unroll
         for (int j = 0; j < K; ++j) v = acc_pick(j == first_end, P[j], v);  // no indexed access to registers
@@ -691,6 +543,142 @@ __global__ __launch_bounds__(1024) void k_vjp_row(VjpArgs a) {
 }
 
 template <typename T, int NF>
+__global__ __launch_bounds__(1024) void k_vjp_row(VjpArgs a) {
+    extern __shared__ __align__(32) char smem[];
+    const int64_t row = blockIdx.x;
+    if (a.row_nan[row]) {  // uniform: before any barrier
+        vjp_nan_span<T, NF>(a, row, 0, (int)a.n);
+        return;
+    }
+    vjp_span<T, NF, false>(a, row, 0, (int)a.n, acc_zero<NF>(), acc_zero<NF>(), smem);
+}
+
+// One tile of a long row, after the carry pass.
+template <typename T, int NF>
+__global__ __launch_bounds__(kVjpTile / kVjpK) void k_vjp_tile(VjpArgs a) {
+    extern __shared__ __align__(32) char smem[];
+    const int64_t row = blockIdx.x / a.ntiles;
+    const int tile = (int)(blockIdx.x % a.ntiles);
+    const int64_t t0 = (int64_t)tile * kVjpTile;
+    const int N = (int)((a.n - t0) < kVjpTile ? (a.n - t0) : kVjpTile);
+    if (a.row_nan[row]) {  // uniform: before any barrier
+        vjp_nan_span<T, NF>(a, row, t0, N);
+        return;
+    }
+    const int64_t ti = row * a.ntiles + tile;
+    vjp_span<T, NF, true>(a, row, t0, N, ((const Acc<NF>*)a.carry)[ti], ((const Acc<NF>*)a.tot)[ti], smem);
+}
+
+// Sums of the tile's elements [lo, hi), kPartThreads apart per thread.  Each
+// round issues kPartUnroll loads of every input before using any (the index
+// clamped into the range, the value masked after).
+constexpr int kPartThreads = 256;
+constexpr int kPartUnroll = 4;
+template <typename T, int NF>
+__device__ __forceinline__ Acc<NF> part_sum(const T* g, const T* w, const T* y, const uint64_t* cb, int lo, int hi) {
+    constexpr int U = kPartUnroll;
+    Acc<NF> s = acc_zero<NF>();
+    for (int b = lo + (int)threadIdx.x; b < hi; b += U * kPartThreads) {
+        double gv[U], wv[U], yv[U];
+        uint64_t cw[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = min(b + u * kPartThreads, hi - 1);
+            gv[u] = (double)g[e];
+            wv[u] = w ? (double)w[e] : 1.0;
+            yv[u] = 0.0;
+            if constexpr (NF == 3) yv[u] = (double)y[e];
+            cw[u] = cb[e >> 6];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = b + u * kPartThreads;
+            const bool in = e < hi;
+            const bool clip = ((cw[u] >> (e & 63)) & 1ull) != 0ull;
+            s.v[0] += (in && !clip) ? gv[u] : 0.0;
+            s.v[1] += in ? wv[u] : 0.0;
+            if (NF == 3) s.v[NF - 1] += in ? wv[u] * yv[u] : 0.0;
+        }
+    }
+    return s;
+}
+
+// The carry pass's input for one tile: the sums before its first block start
+// (head), from its last block start to its end (tail), and whether it holds a
+// start; without a start both are the whole tile's sums.  The start bits give
+// the two positions, so only the head's and the tail's elements are read.
+template <typename T, int NF>
+__global__ __launch_bounds__(kPartThreads) void k_vjp_part(VjpArgs a) {
+    using A = Acc<NF>;
+    __shared__ A part[2][kPartThreads / kWave];
+    const int64_t row = blockIdx.x / a.ntiles;
+    const int tile = (int)(blockIdx.x % a.ntiles);
+    const int64_t t0 = (int64_t)tile * kVjpTile;
+    const int N = (int)((a.n - t0) < kVjpTile ? (a.n - t0) : kVjpTile);
+    const int64_t ti = row * a.ntiles + tile;
+    A* head = (A*)a.head;
+    A* tail = (A*)a.tail;
+    if (a.row_nan[row]) {
+        if (threadIdx.x == 0) {
+            A u = acc_zero<NF>();
+            u.v[1] = 1.0;
+            head[ti] = u;
+            tail[ti] = u;
+            a.has[ti] = 1;
+        }
+        return;
+    }
+    const uint64_t* sb = a.sb + row * a.words + t0 / 64;
+    const uint64_t* cb = a.cb + row * a.words + t0 / 64;
+    // the tile's first and last block starts, by every wave from its start words
+    static_assert(kVjpTile <= 64 * kWave, "one start word per lane");
+    const int lane = lane_id(), wid = threadIdx.x >> 6;
+    const int nwords = (N + 63) / 64;
+    uint64_t word = 0ull;
+    if (lane < nwords) {
+        word = sb[lane];
+        const int rem = N - lane * 64;
+        if (rem < 64) word &= (1ull << rem) - 1ull;
+    }
+    const uint64_t nz = __ballot(word != 0ull);
+    const bool has = nz != 0ull;
+    int fs = N, ls = N;
+    if (has) {
+        const int fw = lo_bit(nz), lw = hi_bit(nz);
+        fs = fw * 64 + lo_bit(__shfl(word, fw, kWave));
+        ls = lw * 64 + hi_bit(__shfl(word, lw, kWave));
+    }
+    const int64_t base = row * a.n + t0;
+    const T* g = (const T*)a.g + base;
+    const T* w = a.w ? (const T*)a.w + base : nullptr;
+    const T* y = (NF == 3) ? (const T*)a.y + base : nullptr;
+    A h = part_sum<T, NF>(g, w, y, cb, 0, fs);
+    A t = acc_zero<NF>();
+    if (has) t = part_sum<T, NF>(g, w, y, cb, ls, N);
+#pragma unroll
+    for (int m = kWave / 2; m >= 1; m >>= 1) {
+        h = acc_sum(h, shfl_xor_acc(h, m));
+        t = acc_sum(t, shfl_xor_acc(t, m));
+    }
+    if (lane == 0) {
+        part[0][wid] = h;
+        part[1][wid] = t;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        A hs = part[0][0], ts = part[1][0];
+#pragma unroll
+        for (int k = 1; k < kPartThreads / kWave; ++k) {
+            hs = acc_sum(hs, part[0][k]);
+            ts = acc_sum(ts, part[1][k]);
+        }
+        head[ti] = hs;
+        tail[ti] = acc_pick(has, ts, hs);
+        a.has[ti] = has ? 1 : 0;
+    }
+}
+
+template <typename T, int NF>
 static hipError_t launch_vjp_t(const VjpLaunch& l) {
     VjpArgs a{};
     a.g = l.g;
@@ -716,15 +704,12 @@ static hipError_t launch_vjp_t(const VjpLaunch& l) {
             hipLaunchKernelGGL((k_vjp_pair<T, NF, 32>), grid, dim3(64), 0, l.stream, a, l.rows);
         return hipGetLastError();
     }
-    static size_t seen[kMaxDevices] = {};
-    (void)ensure_lds((const void*)k_vjp_tile<T, NF>, vjp_smem_bytes<NF>((int)kSingleMax), seen);
     if (l.n <= kSingleMax) {
         const int nl = (int)(((l.n + kVjpK - 1) / kVjpK + 63) / 64 * 64);
         hipLaunchKernelGGL((k_vjp_row<T, NF>), dim3((unsigned)l.rows), dim3(nl), vjp_row_smem_bytes<NF>(nl), l.stream,
                            a);
         return hipGetLastError();
     }
-    a.T = kVjpTile;
     a.ntiles = (int)((l.n + kVjpTile - 1) / kVjpTile);
     const size_t tiles = (size_t)l.rows * (size_t)a.ntiles;
     Acc<NF>* p = (Acc<NF>*)(l.ws + l.L.vjp);
@@ -733,15 +718,14 @@ static hipError_t launch_vjp_t(const VjpLaunch& l) {
     a.carry = p + 2 * tiles;
     a.tot = p + 3 * tiles;
     a.has = (int*)(p + 4 * tiles);
-    a.mode = 1;
-    hipLaunchKernelGGL((k_vjp_tile<T, NF>), dim3((unsigned)tiles), dim3(512), vjp_smem_bytes<NF>(a.T), l.stream, a);
+    hipLaunchKernelGGL((k_vjp_part<T, NF>), dim3((unsigned)tiles), dim3(kPartThreads), 0, l.stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_vjp_carry<NF>, dim3((unsigned)l.rows), dim3(kCarryThreads), 0, l.stream, a, l.rows);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    a.mode = 2;
-    hipLaunchKernelGGL((k_vjp_tile<T, NF>), dim3((unsigned)tiles), dim3(512), vjp_smem_bytes<NF>(a.T), l.stream, a);
+    constexpr int nl = kVjpTile / kVjpK;
+    hipLaunchKernelGGL((k_vjp_tile<T, NF>), dim3((unsigned)tiles), dim3(nl), vjp_row_smem_bytes<NF>(nl), l.stream, a);
     return hipGetLastError();
 }
 
