@@ -19,8 +19,9 @@
 // rows are cut into tiles of kVjpTile elements and take three launches: the
 // sums of each tile's head (before its first block start) and tail (from its
 // last block start), which reads only those elements; a per-row carry pass
-// over the tiles; and the same per-lane kernel on every tile, started from
-// the sums carried into it and given the totals of the block open at its end.
+// over the tiles; and the same per-lane kernel on every tile, given the
+// totals of the blocks open at its start and at its end, so that it reads g
+// only between its first and last block start and every g is read once.
 #include <math.h>
 
 #include "iso_device.hpp"
@@ -381,6 +382,27 @@ __host__ __device__ inline size_t vjp_row_smem_bytes(int nl) {
     return sizeof(Acc<NF>) * (size_t)(nl + 1) + 16 * (sizeof(Acc<NF>) + 2 * sizeof(int)) + 64;
 }
 
+// The first and last block starts (fs, ls) of a tile of N <= 64 * 64
+// elements from its start words sb[0 .. (N + 63) / 64), found by every wave
+// on its own (N, N without a start).
+__device__ __forceinline__ void tile_start_span(const uint64_t* sb, int N, int& fs, int& ls) {
+    const int lane = lane_id();
+    uint64_t word = 0ull;
+    if (lane < (N + 63) / 64) {
+        word = sb[lane];
+        const int rem = N - lane * 64;
+        if (rem < 64) word &= (1ull << rem) - 1ull;
+    }
+    const uint64_t nz = __ballot(word != 0ull);
+    fs = N;
+    ls = N;
+    if (nz != 0ull) {
+        const int fw = lo_bit(nz), lw = hi_bit(nz);
+        fs = fw * 64 + lo_bit(__shfl(word, fw, kWave));
+        ls = lw * 64 + hi_bit(__shfl(word, lw, kWave));
+    }
+}
+
 // NaN products over [t0, t0 + N) of a row whose fit was NaN.
 template <typename T, int NF>
 __device__ __forceinline__ void vjp_nan_span(const VjpArgs& a, int64_t row, int64_t t0, int N) {
@@ -392,14 +414,15 @@ __device__ __forceinline__ void vjp_nan_span(const VjpArgs& a, int64_t row, int6
     }
 }
 
-// The products over [t0, t0 + N) of one row, kVjpK elements per lane.  cin
-// holds the sums of the block open where the span begins (zero for a whole
-// row).  In a tile (TILE) the block open at the span's end may run on into
-// later tiles, so its elements take open_total, that block's totals over the
-// whole row.
+// The products over [t0, t0 + N) of one row, kVjpK elements per lane.  In a
+// tile (TILE) of a longer row, the block open at the tile's start (ending at
+// fs - 1, fs the tile's first block start) has the totals head_total, and
+// the block open at its end (from ls, its last block start, or the whole
+// tile without a start) has open_total; both come from the carry pass, so
+// the tile reads g only in [fs, ls), where its other blocks lie.
 template <typename T, int NF, bool TILE>
-__device__ __forceinline__ void vjp_span(const VjpArgs& a, int64_t row, int64_t t0, int N, const Acc<NF>& cin0,
-                                         const Acc<NF>& open_total, char* smem) {
+__device__ __forceinline__ void vjp_span(const VjpArgs& a, int64_t row, int64_t t0, int N, int fs, int ls,
+                                         const Acc<NF>& head_total, const Acc<NF>& open_total, char* smem) {
     using A = Acc<NF>;
     constexpr int K = kVjpK;
     const int l = threadIdx.x, lane = lane_id(), wid = l >> 6;
@@ -435,8 +458,12 @@ __device__ __forceinline__ void vjp_span(const VjpArgs& a, int64_t row, int64_t 
     double gv[K], wv[K], yv[K];
 #pragma unroll
     for (int j = 0; j < K; ++j) gv[j] = wv[j] = yv[j] = 0.0;
+    // a tile's lane reads g only where it meets [fs, ls); the clip bits mask
+    // the rest, whose sums no block uses
+    const bool need_g = !TILE || (e0 < ls && e0 + cnt > fs);
+    if (TILE) cbit |= ~(uint32_t)(bits_range(max(fs - e0, 0), ls - 1 - e0) & 0xFFFFFFFFull);
     if (cnt > 0) {
-        load_lane<T, K>(g + e0, cnt, gv);
+        if (need_g) load_lane<T, K>(g + e0, cnt, gv);
         if (w) {
             load_lane<T, K>(w + e0, cnt, wv);
         } else {
@@ -474,7 +501,7 @@ __device__ __forceinline__ void vjp_span(const VjpArgs& a, int64_t row, int64_t 
     __syncthreads();
     SegSum<NF> pre;
     pre.f = 0;
-    pre.a = cin0;
+    pre.a = acc_zero<NF>();
     int pmax = 0;
     for (int k = 0; k < wid; ++k) {
         SegSum<NF> o;
@@ -499,7 +526,10 @@ __device__ __forceinline__ void vjp_span(const VjpArgs& a, int64_t row, int64_t 
     for (int j = 0; j < K; ++j) P[j] = acc_pick(j < first, acc_sum(cin.a, P[j]), P[j]);
     if (TILE) {
 #pragma unroll
-        for (int j = 0; j < K; ++j) P[j] = acc_pick(e0 + j == N - 1, open_total, P[j]);
+        for (int j = 0; j < K; ++j) {
+            P[j] = acc_pick(e0 + j == fs - 1, head_total, P[j]);
+            P[j] = acc_pick(e0 + j == N - 1, open_total, P[j]);
+        }
     }
     // 3. a block that began in an earlier lane and ends here: totals to its slot
     //    (element j ends a block when it is the span's last or j + 1 starts one)
@@ -550,12 +580,14 @@ __global__ __launch_bounds__(1024) void k_vjp_row(VjpArgs a) {
         vjp_nan_span<T, NF>(a, row, 0, (int)a.n);
         return;
     }
-    vjp_span<T, NF, false>(a, row, 0, (int)a.n, acc_zero<NF>(), acc_zero<NF>(), smem);
+    vjp_span<T, NF, false>(a, row, 0, (int)a.n, 0, 0, acc_zero<NF>(), acc_zero<NF>(), smem);
 }
 
-// One tile of a long row, after the carry pass.
+// One tile of a long row, after the carry pass.  Capped at four waves per
+// SIMD (two workgroups per CU): the weight product's registers would otherwise
+// leave room for one.
 template <typename T, int NF>
-__global__ __launch_bounds__(kVjpTile / kVjpK) void k_vjp_tile(VjpArgs a) {
+__global__ __launch_bounds__(kVjpTile / kVjpK) __attribute__((amdgpu_waves_per_eu(4))) void k_vjp_tile(VjpArgs a) {
     extern __shared__ __align__(32) char smem[];
     const int64_t row = blockIdx.x / a.ntiles;
     const int tile = (int)(blockIdx.x % a.ntiles);
@@ -566,7 +598,10 @@ __global__ __launch_bounds__(kVjpTile / kVjpK) void k_vjp_tile(VjpArgs a) {
         return;
     }
     const int64_t ti = row * a.ntiles + tile;
-    vjp_span<T, NF, true>(a, row, t0, N, ((const Acc<NF>*)a.carry)[ti], ((const Acc<NF>*)a.tot)[ti], smem);
+    int fs, ls;
+    tile_start_span(a.sb + row * a.words + t0 / 64, N, fs, ls);
+    const Acc<NF> ht = acc_sum(((const Acc<NF>*)a.carry)[ti], ((const Acc<NF>*)a.head)[ti]);
+    vjp_span<T, NF, true>(a, row, t0, N, fs, ls, ht, ((const Acc<NF>*)a.tot)[ti], smem);
 }
 
 // Sums of the tile's elements [lo, hi), kPartThreads apart per thread.  Each
@@ -628,26 +663,12 @@ __global__ __launch_bounds__(kPartThreads) void k_vjp_part(VjpArgs a) {
         }
         return;
     }
-    const uint64_t* sb = a.sb + row * a.words + t0 / 64;
     const uint64_t* cb = a.cb + row * a.words + t0 / 64;
-    // the tile's first and last block starts, by every wave from its start words
     static_assert(kVjpTile <= 64 * kWave, "one start word per lane");
     const int lane = lane_id(), wid = threadIdx.x >> 6;
-    const int nwords = (N + 63) / 64;
-    uint64_t word = 0ull;
-    if (lane < nwords) {
-        word = sb[lane];
-        const int rem = N - lane * 64;
-        if (rem < 64) word &= (1ull << rem) - 1ull;
-    }
-    const uint64_t nz = __ballot(word != 0ull);
-    const bool has = nz != 0ull;
-    int fs = N, ls = N;
-    if (has) {
-        const int fw = lo_bit(nz), lw = hi_bit(nz);
-        fs = fw * 64 + lo_bit(__shfl(word, fw, kWave));
-        ls = lw * 64 + hi_bit(__shfl(word, lw, kWave));
-    }
+    int fs, ls;
+    tile_start_span(a.sb + row * a.words + t0 / 64, N, fs, ls);
+    const bool has = fs < N;
     const int64_t base = row * a.n + t0;
     const T* g = (const T*)a.g + base;
     const T* w = a.w ? (const T*)a.w + base : nullptr;
