@@ -18,10 +18,11 @@ host's cores on a bounded sample of the same input:
          unit weights, increasing: the fit with its blocks and the product in y
          of an N(0,1) upstream gradient, one step = both;
   cfg4:  1 row x 6.5e6 float64, calibration-shaped (sorted scores, counts as
-         weights, rational labels), increasing, clipped to [0, 1];
+         weights, rational labels), increasing, clipped to [0, 1]; both
+         backward products timed as well (the three launches of long rows);
   dense: 32 rows x 2^22 float64, y_i = i/n with 1% of positions pushed down by
          |N(0, 0.01)|, w ~ U(0.5, 1.5), increasing (k_chunk_hull, k_merge_sub,
-         k_merge_top, k_fixup);
+         k_merge_top, k_fixup); both backward products timed as well;
   all_vertices: 32 rows x 2^22 float64 increasing data (every point a hull
          vertex, the first page's Sec. 7.5 regime), w ~ U(0.1, 1.1);
   soft rank: 4096 x 512 float32 standard normal scores, forward and backward
@@ -275,9 +276,10 @@ FIT_LEGS = {
 }
 
 
-def fit_leg(name, steps, warmup, cpu_seconds, no_cpu):
-    """A fit-only leg: wall-clock ms per step, event-timed fit calls, elements/s,
-    the fraction of HBM peak, and the oracle on the host on the same input."""
+def fit_leg(name, steps, warmup, cpu_seconds, no_cpu, backward=False):
+    """A fit leg: wall-clock ms per step, event-timed fit calls, elements/s,
+    the fraction of HBM peak, and the oracle on the host on the same input;
+    with `backward`, both products of the fit event-timed as well."""
     desc, bpe, cap, cpu_rows = FIT_LEGS[name]
     wl = make_inputs(name)
     log(f"{name}: {wl.name} {wl.y.shape}")
@@ -290,6 +292,8 @@ def fit_leg(name, steps, warmup, cpu_seconds, no_cpu):
            "elements_per_s": elems / (ms * 1e-3), "algorithmic_bytes": algo, "bytes_per_element": bpe,
            "hbm_frac_end_to_end": algo / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
            "hbm_frac_events": algo / (kmean * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    if backward:
+        leg["backward"] = time_backward(wl, k)
     if not no_cpu:
         log(f"cpu baseline ({name}) ...")
         leg["cpu_baseline"] = cpu_baseline(wl, seconds=cpu_seconds, max_rows=cpu_rows)
@@ -499,10 +503,10 @@ def main():
         del wl
 
     if args.workload in ("cfg4",) + fits:
-        rec["cfg4"] = fit_leg("cfg4", args.steps, args.warmup, args.cpu_seconds / 2, args.no_cpu)
+        rec["cfg4"] = fit_leg("cfg4", args.steps, args.warmup, args.cpu_seconds / 2, args.no_cpu, backward=True)
 
     if args.workload in ("dense", "both") + fits:
-        dense = fit_leg("dense", args.steps, args.warmup, args.cpu_seconds / 2, args.no_cpu)
+        dense = fit_leg("dense", args.steps, args.warmup, args.cpu_seconds / 2, args.no_cpu, backward=True)
         ach = dense["algorithmic_bytes"] / (dense["fit_ms_events_mean"] * 1e-3) / 1e9
         dense["roofline"] = {"bound": "hbm", "timed": "the whole fit call (k_chunk_hull, k_chunk_cover, "
                                                       "k_merge_sub, k_merge_top, k_fixup), events on the launch "
