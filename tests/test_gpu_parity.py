@@ -355,7 +355,7 @@ def test_partition_is_valid_on_tie_data():
             assert np.all(np.abs(f[r, a:e] - m) <= 1e-12 * max(1.0, abs(m)))
 
 
-@pytest.mark.parametrize("n", [512, 5000, 20000, 70001])
+@pytest.mark.parametrize("n", [512, 5000, 8192, 12288, 20000, 70001])
 @pytest.mark.parametrize("dtype", [np.float64, np.float32])
 def test_vjp_matches_oracle(n, dtype):
     import weighted_isotonic_regression_row_amd as iso
