@@ -406,6 +406,44 @@ def test_vjp_w_matches_oracle(n, dtype, weighted):
     assert np.max(np.abs(np.sum(wv * gwn, axis=1))) <= 50 * tol * max(1.0, np.abs(wv * gwn).sum(axis=1).max())
 
 
+@pytest.mark.parametrize("n", [16, 40, 300, 5000, 20001])
+def test_vjp_non_finite_gradient_stays_in_its_block(n):
+    """An infinite or NaN upstream gradient reaches only its own block (the
+    product is a sum over the block, Appendix C of the first page): +inf, NaN
+    and -inf in one row each, on every backward kernel shape (one row per lane,
+    two lanes, one workgroup, tiles with carries).  Both products match the
+    oracle's on the finite elements, and the non-finite elements are exactly
+    the block that holds the value (the oracle's compensated sums turn an
+    infinity into NaN, so only finiteness is compared there)."""
+    import weighted_isotonic_regression_row_amd as iso
+    wl = workloads.family("trend_noise", 3, n, seed=n % 71, dtype=np.float64, weights="uniform")
+    fit, b, y, w = gpu_fit(wl)
+    gs, gc, grn = gpu_blocks(b)
+    g = workloads.rng(5).standard_normal(wl.y.shape)
+    pos = [n // 3, n // 2, (2 * n) // 3]
+    for r, v in enumerate((np.inf, np.nan, -np.inf)):
+        g[r, pos[r]] = v
+    gy, gw = iso.iso_vjp_yw(to_dev(g), b, y)
+    w64 = wl.w.astype(np.float64)
+    ref_y = oracle.vjp(g, gs, gc, grn, w64)
+    ref_w = oracle.vjp_w(g, wl.y.astype(np.float64), gs, gc, grn, w64)
+    for r in range(3):
+        starts = np.flatnonzero(gs[r])
+        lo = starts[starts <= pos[r]].max()
+        later = starts[starts > pos[r]]
+        hi = later.min() if later.size else n
+        block = np.zeros(n, dtype=bool)
+        block[lo:hi] = True
+        assert not np.isfinite(ref_y[r][block]).any()
+        assert np.isfinite(ref_y[r][~block]).all()
+    for got, ref, name in ((gy, ref_y, "grad_y"), (gw, ref_w, "grad_w")):
+        got = got.cpu().numpy()
+        assert np.array_equal(np.isfinite(got), np.isfinite(ref)), f"{name}: non-finite pattern"
+        ok = np.isfinite(ref)
+        err = float(np.max(np.abs(got[ok] - ref[ok]), initial=0.0))
+        assert err <= 1e-12 * max(1.0, float(np.abs(ref[ok]).max(initial=0.0))), f"{name} off by {err:.3e}"
+
+
 @pytest.mark.parametrize("n", [300, 20000])
 def test_vjp_w_nan_rows(n):
     import weighted_isotonic_regression_row_amd as iso
