@@ -530,7 +530,7 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
                 return;  // nothing else written: the second pass fits the chunk
             }
         }
-        tile_merges<K, ABS>(t, mask, xs, ys);
+        tile_merges<K, ABS>(t, mask, xs, ys, false, 1 << 30, PASS == 1);
     }
     if (PASS == 0 && threadIdx.x == 0) a.cover[bid] = 0;
     __syncthreads();  // every lane's final mask in M

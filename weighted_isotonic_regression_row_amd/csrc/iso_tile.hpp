@@ -1690,14 +1690,32 @@ __device__ inline bool tile_wrap(const Tile& t) {
 // On return the sorted vertex list of the whole tile is V, VXY [0, flag[1]).
 // With wrap, the output-sensitive finish (tile_wrap) is tried first when the
 // lane hulls kept at most 3/5 of the points, and (wrap_max) at most
-// wrap_max candidates.
+// wrap_max candidates.  With junctions (chunk coordinates, not ABS), the
+// lanes' chains are first tested for a strict left turn at every lane
+// junction: the entry before the shared point, the shared point and the entry
+// after it, the very triple that each merge below tests first.  When every
+// junction turns left, each merge would find its bridge at the shared point
+// and move nothing, so the compacted list and masks are final (every point
+// of a convex chunk a vertex, the first page's Sec. 7.5 regime).
 template <int K, bool ABS>
 __device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (&xs)[K], const double (&ys)[K],
-                                   bool wrap = false, int wrap_max = 1 << 30) {
+                                   bool wrap = false, int wrap_max = 1 << 30, bool junctions = false) {
     const int used = (t.N + K - 1) / K;
     const int l = threadIdx.x, lane = lane_id(), wid = l >> 6, nw = blockDim.x >> 6;
     const int nwu = (used + kWave - 1) / kWave;  // waves holding elements
     tile_compact<K, ABS>(t, mask, xs, ys);
+    if (!ABS && junctions) {
+        int left = 1;
+        if (l >= 1 && l < used) {
+            const int s = t.I[l] - 1;  // lane l - 1's end, shared with lane l
+            left = (vturn<K, ABS>(t, s - 1, s, s + 1) > 0.0) ? 1 : 0;
+        }
+        if (__syncthreads_and(left)) {
+            t.M[l] = mask;  // I and flag[1] as compacted
+            __syncthreads();
+            return;
+        }
+    }
     if (wrap && 5 * t.flag[1] <= 3 * t.N + 5 && t.flag[1] <= wrap_max && tile_wrap<K, ABS>(t)) {
         tile_masks_short<K>(t, mask);
         return;
