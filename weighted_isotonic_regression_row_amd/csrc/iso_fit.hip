@@ -480,8 +480,19 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
     // the chunk's last point.  The coarse hull is found by QuickHull (one
     // lane end per thread) on a plain copy of the lane starts.
     const int cnt = min(max(N - (int)threadIdx.x * K, 0), K);
-    uint64_t cand;
-    {
+    // The second pass first tests whether the lanes' hulls already form one
+    // convex chain (every point of the chunk a vertex, the first page's Sec.
+    // 7.5 regime): that chain is then the chunk's hull, and neither the coarse
+    // filter nor the merges run.  (A convex chain lies under the chord of any
+    // two of its points, so the filter would keep every point of it.)
+    bool chain = false;
+    if constexpr (PASS == 1 && !ABS) {
+        mask = lane_gift_wrap<K>(xs, ys, cnt);
+        tile_compact<K, ABS>(t, mask, xs, ys);
+        chain = tile_junctions_left<K, ABS>(t, mask);  // uniform
+    }
+    uint64_t cand = ~0ull;
+    if (!chain) {
         const int used = (N + K - 1) / K;
         double2* E = (double2*)t.VXY;  // free until the candidates are listed
         unsigned long long* slots = (unsigned long long*)(E + kChunkLanes + 1);
@@ -504,7 +515,7 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
         list_quickhull<3>(t, m, (unsigned long long*)t.LS, vert);
         list_to_front<3>(t, m, vert);
         tile_masks<K>(t, mask);
-    } else {
+    } else if (!chain) {
         // the lane hulls' vertices among the candidates, and every lane's
         // last point, so that each lane's node is still a convex chain from
         // its start to its end (the merges need both ends: a node starts at
@@ -516,9 +527,9 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
             int f2 = 0;
             mask = lane_hull<T, K>(y + (int64_t)l * K, w ? w + (int64_t)l * K : nullptr, cnt, !a.r.increasing, xs,
                                    ys, f2);
-        } else {
+        } else if constexpr (ABS) {
             mask = lane_gift_wrap<K>(xs, ys, cnt);
-        }
+        }  // (the second pass's float64 lane hulls are in mask already)
         mask &= cand | end;
         if constexpr (PASS == 0) {
             const bool over = tile_count(t, mask) > a.cap + 1;  // uniform

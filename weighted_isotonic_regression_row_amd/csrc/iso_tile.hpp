@@ -1687,6 +1687,25 @@ __device__ inline bool tile_wrap(const Tile& t) {
 //   3c. the waves' nodes are merged in a tree, one wave per merge;
 //   3d. the final lane masks are rebuilt from the list, and I[l] = index of
 //       lane l's first vertex.
+// After tile_compact: whether every lane junction of the list turns strictly
+// left (the entry before the shared point, the shared point and the entry
+// after it); if so the list is one convex chain, and the lanes' masks are
+// stored as compacted (I and flag[1] already are).  Block scope; ends with a
+// barrier.
+template <int K, bool ABS>
+__device__ inline bool tile_junctions_left(const Tile& t, uint64_t mask) {
+    const int used = (t.N + K - 1) / K, l = threadIdx.x;
+    int left = 1;
+    if (l >= 1 && l < used) {
+        const int s = t.I[l] - 1;  // lane l - 1's end, shared with lane l
+        left = (vturn<K, ABS>(t, s - 1, s, s + 1) > 0.0) ? 1 : 0;
+    }
+    if (!__syncthreads_and(left)) return false;
+    t.M[l] = mask;
+    __syncthreads();
+    return true;
+}
+
 // On return the sorted vertex list of the whole tile is V, VXY [0, flag[1]).
 // With wrap, the output-sensitive finish (tile_wrap) is tried first when the
 // lane hulls kept at most 3/5 of the points, and (wrap_max) at most
@@ -1704,18 +1723,7 @@ __device__ inline void tile_merges(const Tile& t, uint64_t& mask, const double (
     const int l = threadIdx.x, lane = lane_id(), wid = l >> 6, nw = blockDim.x >> 6;
     const int nwu = (used + kWave - 1) / kWave;  // waves holding elements
     tile_compact<K, ABS>(t, mask, xs, ys);
-    if (!ABS && junctions) {
-        int left = 1;
-        if (l >= 1 && l < used) {
-            const int s = t.I[l] - 1;  // lane l - 1's end, shared with lane l
-            left = (vturn<K, ABS>(t, s - 1, s, s + 1) > 0.0) ? 1 : 0;
-        }
-        if (__syncthreads_and(left)) {
-            t.M[l] = mask;  // I and flag[1] as compacted
-            __syncthreads();
-            return;
-        }
-    }
+    if (!ABS && junctions && tile_junctions_left<K, ABS>(t, mask)) return;
     if (wrap && 5 * t.flag[1] <= 3 * t.N + 5 && t.flag[1] <= wrap_max && tile_wrap<K, ABS>(t)) {
         tile_masks_short<K>(t, mask);
         return;
