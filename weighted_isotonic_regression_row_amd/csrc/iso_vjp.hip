@@ -288,12 +288,11 @@ __global__ __launch_bounds__(64) void k_vjp_pair(VjpArgs a, int64_t rows) {
 //   2. a segmented scan over the lanes (DPP inside each wave, the waves'
 //      aggregates through LDS) gives every lane the sums of the block that is
 //      open when the lane begins, and a max-scan gives, for the block open at
-//      each lane's end, the lane where that block began (a tile's scan starts
-//      from the sums carried into it);
+//      each lane's end, the lane where that block began;
 //   3. the lane where a block that began in an earlier lane ends writes the
-//      block's totals to that lane's LDS slot (a block open at a tile's start
-//      has a slot of its own, and a tile's last element holds the totals of
-//      the block open at the tile's end); after one barrier the lanes that the
+//      block's totals to that lane's LDS slot (in a tile, the blocks open at
+//      its start and at its end take their totals from the carry pass: the
+//      first has a slot of its own); after one barrier the lanes that the
 //      block spans read them;
 //   4. a backward pass over each lane's elements hands every element its
 //      block's totals and writes the products.
