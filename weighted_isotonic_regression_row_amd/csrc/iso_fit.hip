@@ -509,10 +509,11 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
     // so that the branches below hold registers apart)
     int m = kChunk;
     if constexpr (PASS == 0) m = __builtin_amdgcn_readfirstlane(list_compact<K>(t, cand, xs, ys, kChunkQh + 1) - 1);
-    if (PASS == 0 && m > a.cap) {
-        // more candidates than the first pass's list holds, before any lane
-        // hull (every point of an increasing row is one): the second pass
-        // fits the chunk, with room for every point
+    if (PASS == 0 && m > a.cap && m >= N) {
+        // every point a candidate, more than the first pass's list holds
+        // (every point of an increasing row is a vertex): the second pass
+        // fits the chunk, with room for every point.  Chunks whose lane hulls
+        // may still shrink their candidates below the list's size stay here.
         if (threadIdx.x == 0) {
             a.cover[bid] = 1;
             cover_append(a, bid);
