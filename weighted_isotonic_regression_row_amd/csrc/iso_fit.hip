@@ -384,6 +384,7 @@ struct ChunkArgs {
     unsigned long long* cctr;  // [2] clist's count word (cover_append), the epoch of a full scan
     int64_t nchunks;   // rows * m
     int cap;           // list entries of this pass (kChunk in the second)
+    int early;         // the call has chunks enough to keep the second pass busy
 };
 
 // The first pass gives each chunk a list of kChunkCap entries, small enough
@@ -509,11 +510,13 @@ __device__ inline void chunk_fit(const ChunkArgs& a, int64_t bid) {
     // so that the branches below hold registers apart)
     int m = kChunk;
     if constexpr (PASS == 0) m = __builtin_amdgcn_readfirstlane(list_compact<K>(t, cand, xs, ys, kChunkQh + 1) - 1);
-    if (PASS == 0 && m > a.cap && m >= N) {
+    if (PASS == 0 && a.early && m > a.cap && m >= N) {
         // every point a candidate, more than the first pass's list holds
         // (every point of an increasing row is a vertex): the second pass
         // fits the chunk, with room for every point.  Chunks whose lane hulls
-        // may still shrink their candidates below the list's size stay here.
+        // may still shrink their candidates below the list's size stay here,
+        // and so do all chunks of a call with few of them, where the second
+        // pass would take one chunk's latency per workgroup.
         if (threadIdx.x == 0) {
             a.cover[bid] = 1;
             cover_append(a, bid);
@@ -1703,6 +1706,7 @@ static hipError_t launch_fit_t(const FitLaunch& a) {
         (void)ensure_lds((const void*)k_chunk_cover<T>, smem1, seen1);
         const int64_t chunks = a.rows * m;
         ca.cap = kChunkCap;
+        ca.early = (chunks >= 16 * (int64_t)num_cus()) ? 1 : 0;
         hipLaunchKernelGGL(k_chunk_hull<T>, dim3((unsigned)chunks), dim3(kChunkLanes), smem0, a.stream, ca);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
