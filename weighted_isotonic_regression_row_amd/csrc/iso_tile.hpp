@@ -1677,16 +1677,6 @@ __device__ inline bool tile_wrap(const Tile& t) {
     return true;
 }
 
-// Steps 3a-3d: merges of the lane hulls into the tile's hull.
-//   3a. one block-wide compaction writes the list of every lane hull's
-//       vertices in order (the lane's points xs, ys are not needed after it);
-//       each lane's node is the index range of its vertices and the point
-//       before them;
-//   3b. rounds inside each wave (nodes of up to 64 lanes) with node ranges
-//       passed between lanes by shuffles;
-//   3c. the waves' nodes are merged in a tree, one wave per merge;
-//   3d. the final lane masks are rebuilt from the list, and I[l] = index of
-//       lane l's first vertex.
 // After tile_compact: whether every lane junction of the list turns strictly
 // left (the entry before the shared point, the shared point and the entry
 // after it); if so the list is one convex chain, and the lanes' masks are
@@ -1706,6 +1696,16 @@ __device__ inline bool tile_junctions_left(const Tile& t, uint64_t mask) {
     return true;
 }
 
+// Steps 3a-3d: merges of the lane hulls into the tile's hull.
+//   3a. one block-wide compaction writes the list of every lane hull's
+//       vertices in order (the lane's points xs, ys are not needed after it);
+//       each lane's node is the index range of its vertices and the point
+//       before them;
+//   3b. rounds inside each wave (nodes of up to 64 lanes) with node ranges
+//       passed between lanes by shuffles;
+//   3c. the waves' nodes are merged in a tree, one wave per merge;
+//   3d. the final lane masks are rebuilt from the list, and I[l] = index of
+//       lane l's first vertex.
 // On return the sorted vertex list of the whole tile is V, VXY [0, flag[1]).
 // With wrap, the output-sensitive finish (tile_wrap) is tried first when the
 // lane hulls kept at most 3/5 of the points, and (wrap_max) at most
